@@ -1,0 +1,234 @@
+"""Python access to the plain CPU oracle (``dflash_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py``; never by the product package.
+
+The C library is compiled with gcc (``build()``); every function here only
+marshals arguments.  Inputs are torch CPU tensors in the workload's storage
+dtype (fp32 or bf16); outputs are numpy float64 arrays already rounded to the
+storage precision (fp32 values for logits).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dflash_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+MAX_LAYERS = 64
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = C.CDLL(_LIB)
+        vp, i32, i64, dp = C.c_void_p, C.c_int32, C.c_int64, C.POINTER(C.c_double)
+        L.orc_round_bf16.restype = C.c_double
+        L.orc_round_bf16.argtypes = [C.c_double]
+        L.orc_round_array_bf16.argtypes = [vp, i64, vp]
+        L.orc_feature_layers.argtypes = [i32, vp]
+        L.orc_rmsnorm.argtypes = [vp, i32, vp, i32, C.c_double, vp]
+        L.orc_rope.argtypes = [vp, i32, i64, C.c_double]
+        L.orc_fuse_rows.argtypes = [vp, vp, i64, vp, i32, vp]
+        L.orc_inject_rows.argtypes = [vp, vp, i64, vp, i32, i64, vp, vp]
+        L.orc_draft_block.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp, vp]
+        L.orc_accept.argtypes = [vp, vp, i32, vp, vp]
+        L.orc_target_forward.argtypes = [vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp]
+        for f in ("orc_fuse_rows", "orc_inject_rows", "orc_draft_block", "orc_target_forward"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+class _Model(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("hidden", C.c_int32), ("n_layers", C.c_int32),
+        ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+        ("ffn", C.c_int32), ("vocab", C.c_int32), ("block", C.c_int32), ("mask_id", C.c_int32),
+        ("rope_base", C.c_double), ("eps", C.c_double),
+        ("fc", C.c_void_p), ("fc_norm", C.c_void_p),
+        ("attn_norm", C.c_void_p * MAX_LAYERS), ("wq", C.c_void_p * MAX_LAYERS),
+        ("wk", C.c_void_p * MAX_LAYERS), ("wv", C.c_void_p * MAX_LAYERS),
+        ("wo", C.c_void_p * MAX_LAYERS), ("mlp_norm", C.c_void_p * MAX_LAYERS),
+        ("wg", C.c_void_p * MAX_LAYERS), ("wu", C.c_void_p * MAX_LAYERS),
+        ("wd", C.c_void_p * MAX_LAYERS),
+        ("final_norm", C.c_void_p), ("embed", C.c_void_p), ("lm_head", C.c_void_p),
+    ]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.device.type == "cpu" and t.is_contiguous()
+    return t.data_ptr()
+
+
+def _dptr(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+class Model:
+    """An oracle view of a model given as a dict of CPU tensors (kept alive here)."""
+
+    def __init__(self, shape, weights: Dict[str, torch.Tensor], n_layers: Optional[int] = None):
+        self.shape = shape
+        self.w = weights
+        L = shape.draft_layers if n_layers is None else n_layers
+        self.n_layers = L
+        m = _Model()
+        m.dtype = 0 if shape.dtype == "fp32" else 1
+        m.hidden, m.n_layers = shape.hidden, L
+        m.n_q_heads, m.n_kv_heads, m.head_dim = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+        m.ffn, m.vocab, m.block, m.mask_id = shape.ffn, shape.vocab, shape.block, shape.mask_id
+        m.rope_base, m.eps = shape.rope_base, shape.eps
+        m.fc, m.fc_norm = _ptr(weights.get("fc")), _ptr(weights.get("fc_norm"))
+        for l in range(L):
+            for name in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "wg", "wu", "wd"):
+                getattr(m, name)[l] = _ptr(weights.get(f"{name}.{l}"))
+        m.final_norm = _ptr(weights.get("final_norm"))
+        m.embed, m.lm_head = _ptr(weights.get("embed")), _ptr(weights.get("lm_head"))
+        self.s = m
+
+    @property
+    def ref(self):
+        return C.byref(self.s)
+
+
+def round_bf16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    f = np.vectorize(lib().orc_round_bf16, otypes=[np.float64])
+    return f(x)
+
+
+def feature_layers(target_layers: int) -> List[int]:
+    out = (C.c_int32 * 5)()
+    lib().orc_feature_layers(target_layers, out)
+    return list(out)
+
+
+def rmsnorm(x: np.ndarray, gain: torch.Tensor, dtype: str, eps: float) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    lib().orc_rmsnorm(_dptr(x), x.shape[-1], _ptr(gain), 0 if dtype == "fp32" else 1, eps, _dptr(out))
+    return out
+
+
+def rope(v: np.ndarray, pos: int, base: float) -> np.ndarray:
+    v = np.array(v, dtype=np.float64, copy=True)
+    lib().orc_rope(_dptr(v), v.shape[-1], pos, base)
+    return v
+
+
+def to_storage(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """Oracle values (already rounded to the storage type) as a storage tensor; exact."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    return t.to(torch.float32 if dtype == "fp32" else torch.bfloat16).contiguous()
+
+
+def fuse_rows(model: Model, slabs: Sequence[torch.Tensor], rows: Sequence[int]) -> np.ndarray:
+    H = model.shape.hidden
+    slabs = [s.contiguous() for s in slabs]
+    assert len(slabs) == 5
+    ld = slabs[0].stride(0)
+    arr = (C.c_void_p * 5)(*[s.data_ptr() for s in slabs])
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(rows_a), H), dtype=np.float64)
+    rc = lib().orc_fuse_rows(model.ref, arr, ld, rows_a.ctypes.data, len(rows_a), _dptr(out))
+    assert rc == 0
+    return out
+
+
+def inject_rows(model: Model, fused: torch.Tensor, rows: Sequence[int], pos0: int):
+    s = model.shape
+    fused = fused.contiguous()
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    NK = s.n_kv_heads * s.head_dim
+    k = np.empty((model.n_layers, len(rows_a), NK), dtype=np.float64)
+    v = np.empty_like(k)
+    rc = lib().orc_inject_rows(model.ref, _ptr(fused), fused.stride(0), rows_a.ctypes.data,
+                               len(rows_a), pos0, _dptr(k), _dptr(v))
+    assert rc == 0
+    return k, v
+
+
+def draft_block(model: Model, ctx_k: Optional[torch.Tensor], ctx_v: Optional[torch.Tensor],
+                C_len: int, anchor: int, want_logits: bool = True, want_trace: bool = False):
+    """ctx_k / ctx_v: storage tensors [L, >=C, nkv, d] (or None when C == 0)."""
+    s = model.shape
+    L, B, V, H = model.n_layers, s.block, s.vocab, s.hidden
+    if C_len > 0:
+        ctx_k = ctx_k.contiguous()
+        ctx_v = ctx_v.contiguous()
+        kp = (C.c_void_p * L)(*[ctx_k[l].data_ptr() for l in range(L)])
+        vp = (C.c_void_p * L)(*[ctx_v[l].data_ptr() for l in range(L)])
+    else:
+        kp = vp = None
+    logits = np.empty((B, V), dtype=np.float32) if want_logits else None
+    tokens = np.empty(B, dtype=np.int32)
+    gap = np.empty(B, dtype=np.float64)
+    trace = np.empty((L + 1, B, H), dtype=np.float64) if want_trace else None
+    rc = lib().orc_draft_block(model.ref, kp, vp, C_len, anchor,
+                               logits.ctypes.data if logits is not None else None,
+                               tokens.ctypes.data, gap.ctypes.data,
+                               trace.ctypes.data if trace is not None else None)
+    assert rc == 0
+    return {"logits": logits, "tokens": tokens, "gap": gap, "trace": trace}
+
+
+def accept(drafts: Sequence[int], target: Sequence[int]):
+    d = np.ascontiguousarray(drafts, dtype=np.int32)
+    g = np.ascontiguousarray(target, dtype=np.int32)
+    assert d.shape == g.shape
+    k, b = C.c_int32(), C.c_int32()
+    lib().orc_accept(d.ctypes.data, g.ctypes.data, len(d), C.byref(k), C.byref(b))
+    return k.value, b.value
+
+
+class TargetCache:
+    """Dense fp64 KV cache of the oracle's causal target."""
+
+    def __init__(self, model: Model, cap: int):
+        s = model.shape
+        NK = s.n_kv_heads * s.head_dim
+        self.cap = cap
+        self.k = np.zeros((model.n_layers, cap, NK), dtype=np.float64)
+        self.v = np.zeros_like(self.k)
+
+
+def target_forward(model: Model, cache: TargetCache, tokens: Sequence[int], pos0: int,
+                   capture: Optional[Sequence[int]] = None):
+    s = model.shape
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    n = len(t)
+    am = np.empty(n, dtype=np.int32)
+    gap = np.empty(n, dtype=np.float64)
+    cap_a = np.ascontiguousarray(capture, dtype=np.int32) if capture is not None else None
+    hid = np.empty((5, n, s.hidden), dtype=np.float64) if capture is not None else None
+    rc = lib().orc_target_forward(model.ref, t.ctypes.data, n, pos0, _dptr(cache.k), _dptr(cache.v),
+                                  cache.cap, cap_a.ctypes.data if cap_a is not None else None,
+                                  hid.ctypes.data if hid is not None else None,
+                                  am.ctypes.data, gap.ctypes.data)
+    assert rc == 0
+    return {"argmax": am, "gap": gap, "hidden": hid}
