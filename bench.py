@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash draft step on one MI355X.
+
+One step = one pass of the whole draft-side hot path over one block:
+  draft_block (embed, every draft layer, LM head + argmax)
+  -> verify_accept against a synthetic target argmax
+  -> fuse_context of the 16 verified rows' target features (5 layers, Linear + RMSNorm)
+  -> inject_kv of those 16 rows into every layer's paged draft KV cache
+  -> rollback to C + k + 1 (then back to C so every step sees the same context)
+Inputs are seeded synthetic tensors of the Qwen3-8B-shaped draft (hidden 4096,
+36 target layers, 5 draft layers, 32/8 heads x 128, FFN 12288, vocab 151936,
+bf16) with a 4096-token injected context, already resident in HBM.
+
+Prints progress to stderr and ONE JSON line to stdout.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DFlash 16-token draft blocks/s + drafted tok/s at 8B shape, 4K/36K ctx; % HBM peak"
+HBM_PEAK = 8.0e12       # MI355X HBM3E, bytes/s
+BF16_PEAK = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(s, C):
+    """Algorithmic HBM bytes of one draft block and of one full step."""
+    e = s.elem_bytes
+    H, F, V, nq, nkv, d, L = s.hidden, s.ffn, s.vocab, s.n_q_heads, s.n_kv_heads, s.head_dim, s.draft_layers
+    layer_w = (H * nq * d + 2 * H * nkv * d + nq * d * H + 3 * H * F) * e
+    lm = V * H * e
+    kv = L * C * 2 * nkv * d * e
+    draft = L * layer_w + lm + kv + 2 * H * e
+    fuse16 = 5 * H * H * e + 16 * 5 * H * e + 16 * H * e
+    inject16 = L * 2 * nkv * d * H * e + 16 * H * e + L * 16 * 2 * nkv * d * e
+    return {"draft": draft, "lm_head": lm + 16 * H * e, "layer_weights": L * layer_w, "kv": kv,
+            "fuse16": fuse16, "inject16": inject16, "step": draft + fuse16 + inject16}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_8b_4k")
+    ap.add_argument("--long-ctx", type=int, default=36864, help="second context length measured (0: skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run its own "
+              "sequences' draft steps independently). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_context_amd as dl
+    import dflash_inputs as di
+
+    torch.cuda.set_device(0)
+    s = di.SHAPES[args.workload]
+    C = s.ctx
+    t0 = time.time()
+    w_cpu = di.draft_weights(s)
+    w = {k: v.cuda() for k, v in w_cpu.items()}
+    torch.cuda.synchronize()
+    log(f"[bench] weights {sum(v.numel() for v in w.values()) * s.elem_bytes / 1e9:.2f} GB ready in {time.time() - t0:.1f}s")
+
+    sel = dl.feature_layers(s.target_layers)
+
+    def prepare(ctx_len, tag):
+        ctx = dl.DFlash(s, w, max_ctx=ctx_len + 64, max_rows=max(ctx_len, 16))
+        chunk = 8192
+        for r0 in range(0, ctx_len, chunk):
+            M = min(chunk, ctx_len - r0)
+            hid = {l: di.normal((M, s.hidden), s.seed, f"hidden.{tag}.{l}.{r0}", 1.0, s.torch_dtype).cuda()
+                   for l in sel}
+            fused = ctx.fuse_context([hid.get(l) for l in range(s.target_layers)])
+            ctx.inject_kv(fused, r0)
+        torch.cuda.synchronize()
+        return ctx
+
+    step_hidden = [di.target_hidden(s, l, 16, tag="step").cuda() if l in sel else None
+                   for l in range(s.target_layers)]
+    u, r, last = di.target_coins(s)
+    u_d, r_d = u.cuda(), r.cuda()
+    fused_buf = torch.empty(16, s.hidden, dtype=s.torch_dtype, device="cuda")
+    tok_buf = torch.empty(s.block, dtype=torch.int32, device="cuda")
+    res_buf = torch.empty(2, dtype=torch.int32, device="cuda")
+    res_host = torch.empty(2, dtype=torch.int32).pin_memory()
+
+    def make_step(ctx, C0):
+        anchor = torch.tensor([di.anchor_token(s)], dtype=torch.int32, device="cuda")
+        stats = {"k": 0, "n": 0}
+
+        def step():
+            tokens, _ = ctx.draft_block(anchor, tokens=tok_buf)
+            g = di.synthetic_target_argmax(tokens, u_d, r_d, last, s.vocab)
+            ctx.verify_accept(tokens, g, out=res_buf)
+            fused = ctx.fuse_context(step_hidden, out=fused_buf)
+            ctx.inject_kv(fused, C0)
+            res_host.copy_(res_buf, non_blocking=True)
+            torch.cuda.current_stream().synchronize()
+            k = int(res_host[0])
+            ctx.rollback(C0 + k + 1)
+            ctx.rollback(C0)
+            anchor.copy_(res_buf[1:2])
+            stats["k"] += k
+            stats["n"] += 1
+
+        return step, stats
+
+    def timed(ctx, C0, steps, warmup, trace_cls=None):
+        step, stats = make_step(ctx, C0)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        if trace_cls is not None:
+            st = dl.lib().dflash_trace_enable(ctx.h, trace_cls, steps * 8)
+            assert st == 0
+        stats["k"] = stats["n"] = 0
+        t = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        trace = None
+        if trace_cls is not None:
+            import ctypes as C_
+            ms, n = C_.c_double(), C_.c_int32()
+            dl.lib().dflash_trace_read(ctx.h, C_.byref(ms), C_.byref(n))
+            trace = (ms.value, n.value)
+            dl.lib().dflash_trace_enable(ctx.h, 0, 0)
+        return dt, stats, trace
+
+    # ---- headline: context C, LM head traced live over the timed region
+    t0 = time.time()
+    ctx = prepare(C, "ctx")
+    log(f"[bench] prefill fuse+inject of {C} rows done in {time.time() - t0:.1f}s")
+    dt, stats, tr = timed(ctx, C, args.steps, args.warmup, trace_cls=1)
+    ab = alg_bytes(s, C)
+    bps = args.steps / dt
+    lm_ms = tr[0] / max(tr[1], 1)
+    lm_ach = ab["lm_head"] / (lm_ms * 1e-3)
+    log(f"[bench] {args.steps} steps in {dt:.3f}s: {bps:.1f} blocks/s; LM head {lm_ms * 1e3:.1f} us/launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(bps, 2),
+        "unit": "draft blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) target features, N(0,0.02) random-init weights)",
+        "config": {"workload": args.workload, "hidden": s.hidden, "target_layers": s.target_layers,
+                   "draft_layers": s.draft_layers, "heads": f"{s.n_q_heads}/{s.n_kv_heads}x{s.head_dim}",
+                   "ffn": s.ffn, "vocab": s.vocab, "ctx": C, "block": s.block,
+                   "step": "draft_block+verify_accept+fuse(16)+inject(16)+rollback"},
+        "drafted_tok_per_s": round(15 * bps, 1),
+        "hbm_frac_step": round(ab["step"] * bps / HBM_PEAK, 4),
+        "alg_bytes_per_step": ab["step"],
+        "mean_accept_k": stats["k"] / max(stats["n"], 1),
+        "roofline": {"bound": "hbm", "kernel": "skinny_kernel<OpLMHead> (LM head + argmax)",
+                     "achieved": round(lm_ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(lm_ach / HBM_PEAK, 4), "traffic": None,
+                     "alg_bytes_per_launch": ab["lm_head"], "avg_launch_us": round(lm_ms * 1e3, 2)},
+    }
+
+    # ---- per-kernel-class breakdown (separate short traced runs, not the timed region)
+    if not args.no_breakdown:
+        per_layer = {"qkv": (4, (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * s.hidden * s.elem_bytes),
+                     "attn": (6, ab["kv"] // s.draft_layers),
+                     "o_proj": (5, s.n_q_heads * s.head_dim * s.hidden * s.elem_bytes),
+                     "gate_up": (2, 2 * s.ffn * s.hidden * s.elem_bytes),
+                     "down": (3, s.ffn * s.hidden * s.elem_bytes),
+                     "lm_head": (1, ab["lm_head"]),
+                     "draft": (7, ab["draft"]),
+                     "fuse16": (8, ab["fuse16"]),
+                     "inject16": (9, ab["inject16"])}
+        bd = {}
+        for name, (cls, byts) in per_layer.items():
+            _, _, tr2 = timed(ctx, C, 30, 2, trace_cls=cls)
+            us = tr2[0] / max(tr2[1], 1) * 1e3
+            bd[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
+        out["breakdown_ctx"] = bd
+        log(f"[bench] breakdown {json.dumps(bd)}")
+
+    # ---- long context
+    if args.long_ctx:
+        del ctx
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        ctx2 = prepare(args.long_ctx, "long")
+        log(f"[bench] prefill of {args.long_ctx} rows done in {time.time() - t0:.1f}s")
+        dt2, _, tr2 = timed(ctx2, args.long_ctx, args.steps, args.warmup, trace_cls=7)
+        ab2 = alg_bytes(s, args.long_ctx)
+        bps2 = args.steps / dt2
+        dr_us = tr2[0] / max(tr2[1], 1) * 1e3
+        out["long_ctx"] = {"ctx": args.long_ctx, "blocks_per_s": round(bps2, 2),
+                           "drafted_tok_per_s": round(15 * bps2, 1),
+                           "hbm_frac_step": round(ab2["step"] * bps2 / HBM_PEAK, 4),
+                           "draft_pass_us": round(dr_us, 1),
+                           "draft_pass_hbm_frac": round(ab2["draft"] / (dr_us * 1e-6) / HBM_PEAK, 4)}
+        log(f"[bench] long ctx: {json.dumps(out['long_ctx'])}")
+        del ctx2
+
+    # ---- CPU oracle baseline: one full step of the oracle on a bounded sample
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        m = orc.Model(s, w_cpu)
+        k, v = di.context_kv(s, C)
+        hid16 = [di.target_hidden(s, l, 16, tag="step") for l in sel]
+        anchor = di.anchor_token(s)
+        t = time.perf_counter()
+        ref = orc.draft_block(m, k, v, C, anchor, want_logits=False)
+        g = di.synthetic_target_argmax(ref["tokens"], u.numpy(), r.numpy(), last, s.vocab)
+        orc.accept(ref["tokens"], g)
+        f16 = orc.fuse_rows(m, hid16, range(16))
+        orc.inject_rows(m, orc.to_storage(f16, s.dtype), range(16), C)
+        cpu_s = time.perf_counter() - t
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        out["cpu_baseline"] = {"value": round(1.0 / cpu_s, 5), "unit": "draft blocks/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"1 full step (draft block at C={C} + accept + fuse/inject of 16 rows), "
+                                         f"fp64 oracle, {cpu_s:.1f}s"}
+        log(f"[bench] cpu oracle step {cpu_s:.1f}s with {threads} threads")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

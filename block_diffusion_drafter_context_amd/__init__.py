@@ -1,0 +1,252 @@
+"""Python binding of libdflash (ctypes): argument marshalling only.
+
+Every step of the DFlash draft path runs in the HIP kernels of
+``libdflash.so``; this module only converts torch tensors to pointers, calls
+the C ABI (``include/dflash.h``) and raises on error.  There is no fallback:
+if the library is missing, importing the context class fails loudly.
+
+PyTorch provides the device memory (weights, workspace, KV pool, outputs) and
+the stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from .stats import spec_stats  # noqa: F401  (host-side bookkeeping)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+MAX_LAYERS = 64
+
+DFLASH_F32, DFLASH_BF16 = 0, 1
+_STATUS = {0: "DFLASH_OK", -1: "DFLASH_ERR_INVAL", -2: "DFLASH_ERR_CAPACITY", -3: "DFLASH_ERR_HIP",
+           -4: "DFLASH_ERR_UNSUPPORTED", -5: "DFLASH_ERR_STATE"}
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, msg: str = ""):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+
+
+class Config(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("hidden", C.c_int32), ("target_layers", C.c_int32),
+        ("draft_layers", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("ffn", C.c_int32), ("vocab", C.c_int32), ("block", C.c_int32),
+        ("mask_id", C.c_int32), ("page_size", C.c_int32), ("max_ctx", C.c_int32),
+        ("max_rows", C.c_int32), ("rope_base", C.c_double), ("eps", C.c_double),
+        ("page_seed", C.c_uint64),
+    ]
+
+
+class Weights(C.Structure):
+    _fields_ = [
+        ("fc", C.c_void_p), ("fc_norm", C.c_void_p),
+        ("attn_norm", C.c_void_p * MAX_LAYERS), ("wq", C.c_void_p * MAX_LAYERS),
+        ("wk", C.c_void_p * MAX_LAYERS), ("wv", C.c_void_p * MAX_LAYERS),
+        ("wo", C.c_void_p * MAX_LAYERS), ("mlp_norm", C.c_void_p * MAX_LAYERS),
+        ("wg", C.c_void_p * MAX_LAYERS), ("wu", C.c_void_p * MAX_LAYERS),
+        ("wd", C.c_void_p * MAX_LAYERS),
+        ("final_norm", C.c_void_p), ("embed", C.c_void_p), ("lm_head", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdflash.so (built in-tree by ``build.py``); raise if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libdflash.so not built at {LIB_PATH}; run block_diffusion_drafter_context_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        st = C.c_int
+        L.dflash_status_str.restype = C.c_char_p
+        L.dflash_status_str.argtypes = [C.c_int]
+        L.dflash_last_error.restype = C.c_char_p
+        L.dflash_last_error.argtypes = [vp]
+        L.dflash_feature_layers.restype = st
+        L.dflash_feature_layers.argtypes = [i32, vp]
+        L.dflash_page_table.restype = st
+        L.dflash_page_table.argtypes = [vp, vp, i32]
+        L.dflash_workspace_size.restype = st
+        L.dflash_workspace_size.argtypes = [vp, C.POINTER(sz), C.POINTER(sz)]
+        L.dflash_create.restype = st
+        L.dflash_create.argtypes = [vp, vp, vp, sz, vp, sz, vp, C.POINTER(vp)]
+        L.dflash_destroy.restype = st
+        L.dflash_destroy.argtypes = [vp]
+        L.dflash_length.restype = i32
+        L.dflash_length.argtypes = [vp]
+        L.dflash_fuse_context.restype = st
+        L.dflash_fuse_context.argtypes = [vp, vp, i64, i32, vp, vp]
+        L.dflash_inject_kv.restype = st
+        L.dflash_inject_kv.argtypes = [vp, vp, i64, i32, i32, vp]
+        L.dflash_draft_block.restype = st
+        L.dflash_draft_block.argtypes = [vp, vp, vp, vp, vp]
+        L.dflash_verify_accept.restype = st
+        L.dflash_verify_accept.argtypes = [vp, vp, vp, vp, vp]
+        L.dflash_rollback.restype = st
+        L.dflash_rollback.argtypes = [vp, i32]
+        L.dflash_load_kv.restype = st
+        L.dflash_load_kv.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.dflash_read_kv.restype = st
+        L.dflash_read_kv.argtypes = [vp, i32, i32, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def feature_layers(target_layers: int):
+    out = (C.c_int32 * 5)()
+    st = lib().dflash_feature_layers(target_layers, out)
+    if st:
+        raise DFlashError(st, "feature_layers")
+    return list(out)
+
+
+def make_config(shape, max_ctx: int, max_rows: int = 16, page_seed: int = 0) -> Config:
+    """Config from a workload shape (``dflash_inputs.Shape`` or any object with the same fields)."""
+    c = Config()
+    c.dtype = DFLASH_F32 if shape.dtype == "fp32" else DFLASH_BF16
+    c.hidden, c.target_layers, c.draft_layers = shape.hidden, shape.target_layers, shape.draft_layers
+    c.n_q_heads, c.n_kv_heads, c.head_dim = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    c.ffn, c.vocab, c.block, c.mask_id = shape.ffn, shape.vocab, shape.block, shape.mask_id
+    c.page_size, c.max_ctx, c.max_rows = shape.page_size, max_ctx, max_rows
+    c.rope_base, c.eps, c.page_seed = shape.rope_base, shape.eps, page_seed
+    return c
+
+
+def workspace_size(cfg: Config):
+    ws, kv = C.c_size_t(), C.c_size_t()
+    st = lib().dflash_workspace_size(C.byref(cfg), C.byref(ws), C.byref(kv))
+    if st:
+        raise DFlashError(st, "workspace_size")
+    return ws.value, kv.value
+
+
+def page_table(cfg: Config):
+    n = (cfg.max_ctx + cfg.page_size - 1) // cfg.page_size
+    out = (C.c_int32 * max(n, 1))()
+    st = lib().dflash_page_table(C.byref(cfg), out, max(n, 1))
+    if st:
+        raise DFlashError(st, "page_table")
+    return list(out)[:n]
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+class DFlash:
+    """A libdflash context over device weights given as a dict of CUDA tensors.
+
+    Weight names: fc, fc_norm, final_norm, embed, lm_head and per layer l:
+    attn_norm.l, wq.l, wk.l, wv.l, wo.l, mlp_norm.l, wg.l, wu.l, wd.l.
+    """
+
+    def __init__(self, shape, weights: Dict[str, torch.Tensor], max_ctx: int, max_rows: int = 16,
+                 page_seed: int = 0, device=None):
+        self.shape = shape
+        self.cfg = make_config(shape, max_ctx, max_rows, page_seed)
+        self.weights = weights  # keep alive
+        self.device = torch.device("cuda") if device is None else torch.device(device)
+        w = Weights()
+        w.fc, w.fc_norm = _p(weights.get("fc")), _p(weights.get("fc_norm"))
+        for l in range(shape.draft_layers):
+            for name in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "wg", "wu", "wd"):
+                t = weights.get(f"{name}.{l}")
+                getattr(w, name)[l] = _p(t)
+        w.final_norm, w.embed, w.lm_head = _p(weights.get("final_norm")), _p(weights.get("embed")), _p(weights.get("lm_head"))
+        self._w = w
+        ws, kv = workspace_size(self.cfg)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        self.kv_pool = torch.empty(max(kv, 256), dtype=torch.uint8, device=self.device)
+        h = C.c_void_p()
+        st = lib().dflash_create(C.byref(self.cfg), C.byref(w), self.workspace.data_ptr(), ws,
+                                 self.kv_pool.data_ptr(), kv, _stream(), C.byref(h))
+        if st:
+            raise DFlashError(st, "create")
+        self.h = h
+        self.dtype = shape.torch_dtype
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h:
+            lib().dflash_destroy(h)
+            self.h = None
+
+    def _check(self, st: int, what: str):
+        if st:
+            msg = lib().dflash_last_error(self.h)
+            raise DFlashError(st, f"{what}: {msg.decode() if msg else ''}")
+
+    @property
+    def length(self) -> int:
+        return lib().dflash_length(self.h)
+
+    def fuse_context(self, layer_hidden: Sequence[Optional[torch.Tensor]], out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+        """layer_hidden: one tensor [M, H] (or None) per target layer."""
+        assert len(layer_hidden) == self.cfg.target_layers
+        ref = next(t for t in layer_hidden if t is not None)
+        M, ld = ref.shape[0], ref.stride(0)
+        if out is None:
+            out = torch.empty(M, self.shape.hidden, dtype=self.dtype, device=self.device)
+        arr = (C.c_void_p * len(layer_hidden))(*[_p(t) for t in layer_hidden])
+        self._check(lib().dflash_fuse_context(self.h, arr, ld, M, out.data_ptr(), _stream(stream)), "fuse_context")
+        return out
+
+    def inject_kv(self, fused: torch.Tensor, pos0: Optional[int] = None, stream=None):
+        pos0 = self.length if pos0 is None else pos0
+        self._check(lib().dflash_inject_kv(self.h, fused.data_ptr(), fused.stride(0), fused.shape[0], pos0,
+                                           _stream(stream)), "inject_kv")
+
+    def draft_block(self, anchor: torch.Tensor, tokens: Optional[torch.Tensor] = None, want_logits: bool = False,
+                    logits: Optional[torch.Tensor] = None, stream=None):
+        """anchor: device int32[1].  Returns (tokens int32[B], logits fp32[B, V] or None)."""
+        B, V = self.shape.block, self.shape.vocab
+        if tokens is None:
+            tokens = torch.empty(B, dtype=torch.int32, device=self.device)
+        if want_logits and logits is None:
+            logits = torch.empty(B, V, dtype=torch.float32, device=self.device)
+        self._check(lib().dflash_draft_block(self.h, anchor.data_ptr(), _p(logits), tokens.data_ptr(),
+                                             _stream(stream)), "draft_block")
+        return tokens, logits
+
+    def verify_accept(self, draft: torch.Tensor, target: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(2, dtype=torch.int32, device=self.device)
+        self._check(lib().dflash_verify_accept(self.h, draft.data_ptr(), target.data_ptr(), out.data_ptr(),
+                                               _stream(stream)), "verify_accept")
+        return out
+
+    def rollback(self, new_len: int):
+        self._check(lib().dflash_rollback(self.h, new_len), "rollback")
+
+    def load_kv(self, k: torch.Tensor, v: torch.Tensor, pos0: Optional[int] = None, stream=None):
+        """k, v: [Ld, M, nkv, d] contiguous device tensors (already rotated K)."""
+        pos0 = self.length if pos0 is None else pos0
+        assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+        self._check(lib().dflash_load_kv(self.h, k.data_ptr(), v.data_ptr(), k.shape[1], pos0, _stream(stream)),
+                    "load_kv")
+
+    def read_kv(self, pos0: int, M: int, stream=None):
+        s = self.shape
+        k = torch.empty(s.draft_layers, M, s.n_kv_heads, s.head_dim, dtype=self.dtype, device=self.device)
+        v = torch.empty_like(k)
+        self._check(lib().dflash_read_kv(self.h, pos0, M, k.data_ptr(), v.data_ptr(), _stream(stream)), "read_kv")
+        return k, v

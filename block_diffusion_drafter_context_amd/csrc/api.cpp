@@ -1,0 +1,333 @@
+// api.cpp -- the extern "C" surface of libdflash (see include/dflash.h):
+// argument checks, context state (length, page table) and launch order.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "host.h"
+#include "kernels.h"
+
+using namespace dflash;
+
+struct dflash_ctx {
+    DevCtx dev;
+    Tracer tracer;
+    std::vector<hipEvent_t> events;
+    dflash_config cfg;
+    int32_t length = 0;
+    int device = 0;
+    std::string err;
+};
+
+namespace {
+
+dflash_status fail(dflash_ctx* c, dflash_status st, const std::string& msg) {
+    if (c) c->err = msg;
+    return st;
+}
+
+dflash_status hip_fail(dflash_ctx* c, hipError_t e, const char* where) {
+    std::string m = std::string(where) + ": " + hipGetErrorString(e);
+    return fail(c, DFLASH_ERR_HIP, m);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Check that the current HIP device is the one the context was created on.
+dflash_status check_device(dflash_ctx* c) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(c, e, "hipGetDevice");
+    if (dev != c->device) return fail(c, DFLASH_ERR_STATE, "current HIP device differs from the context's device");
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_str(int st) {
+    switch (st) {
+        case DFLASH_OK: return "DFLASH_OK";
+        case DFLASH_ERR_INVAL: return "DFLASH_ERR_INVAL";
+        case DFLASH_ERR_CAPACITY: return "DFLASH_ERR_CAPACITY";
+        case DFLASH_ERR_HIP: return "DFLASH_ERR_HIP";
+        case DFLASH_ERR_UNSUPPORTED: return "DFLASH_ERR_UNSUPPORTED";
+        case DFLASH_ERR_STATE: return "DFLASH_ERR_STATE";
+        default: return "DFLASH_ERR_UNKNOWN";
+    }
+}
+
+const char* dflash_last_error(const dflash_ctx* c) { return c ? c->err.c_str() : ""; }
+
+dflash_status dflash_feature_layers(int32_t target_layers, int32_t* out) {
+    if (!out || target_layers < 8) return DFLASH_ERR_INVAL;
+    feature_layers(target_layers, out);
+    return DFLASH_OK;
+}
+
+dflash_status dflash_page_table(const dflash_config* cfg, int32_t* out, int32_t n) {
+    Dims d;
+    std::string err;
+    dflash_status st = validate_config(cfg, &d, &err);
+    if (st != DFLASH_OK) return st;
+    if (!out || n < d.n_pages) return DFLASH_ERR_INVAL;
+    std::vector<int32_t> pt = make_page_table(d.n_pages, cfg->page_seed);
+    std::copy(pt.begin(), pt.end(), out);
+    return DFLASH_OK;
+}
+
+dflash_status dflash_workspace_size(const dflash_config* cfg, size_t* ws, size_t* kv) {
+    Dims d;
+    std::string err;
+    dflash_status st = validate_config(cfg, &d, &err);
+    if (st != DFLASH_OK) return st;
+    if (!ws || !kv) return DFLASH_ERR_INVAL;
+    // sized for the largest device this library targets: 256 compute units
+    Layout L = compute_layout(d, 256);
+    *ws = L.total;
+    *kv = L.kv_total;
+    return DFLASH_OK;
+}
+
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, void* workspace, size_t ws_bytes,
+                            void* kv_pool, size_t kv_bytes, void* stream, dflash_ctx** out) {
+    if (!out) return DFLASH_ERR_INVAL;
+    *out = nullptr;
+    Dims d;
+    std::string err;
+    dflash_status st = validate_config(cfg, &d, &err);
+    if (st != DFLASH_OK) return st;
+    if (!w || !workspace || (!kv_pool && d.max_ctx > 0)) return DFLASH_ERR_INVAL;
+    if (!aligned(workspace, 256) || !aligned(kv_pool, 256)) return DFLASH_ERR_INVAL;
+    if (!w->fc || !w->fc_norm) return DFLASH_ERR_INVAL;
+    for (int l = 0; l < d.Ld; ++l)
+        if (!w->wk[l] || !w->wv[l]) return DFLASH_ERR_INVAL;
+
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DFLASH_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return DFLASH_ERR_HIP;
+    cus = std::min(std::max(cus, 1), 256);
+    Layout L = compute_layout(d, cus);
+    if (ws_bytes < L.total || kv_bytes < L.kv_total) return DFLASH_ERR_CAPACITY;
+
+    dflash_ctx* c = new (std::nothrow) dflash_ctx();
+    if (!c) return DFLASH_ERR_CAPACITY;
+    c->cfg = *cfg;
+    c->device = dev;
+    DevCtx& x = c->dev;
+    x.dm = d;
+    x.lay = L;
+    x.ws = static_cast<char*>(workspace);
+    x.kv = static_cast<char*>(kv_pool);
+    x.num_cus = cus;
+    x.fc = w->fc;
+    x.fc_norm = w->fc_norm;
+    for (int l = 0; l < DFLASH_MAX_LAYERS; ++l) {
+        x.attn_norm[l] = w->attn_norm[l];
+        x.wq[l] = w->wq[l];
+        x.wk[l] = w->wk[l];
+        x.wv[l] = w->wv[l];
+        x.wo[l] = w->wo[l];
+        x.mlp_norm[l] = w->mlp_norm[l];
+        x.wg[l] = w->wg[l];
+        x.wu[l] = w->wu[l];
+        x.wd[l] = w->wd[l];
+    }
+    x.final_norm = w->final_norm;
+    x.embed = w->embed;
+    x.lm_head = w->lm_head;
+    x.tracer = &c->tracer;
+
+    // rotary table: angle = pos * base^(-2i/d) in fp64, cos/sin stored as fp32
+    const int half = d.d / 2;
+    std::vector<float> cs((size_t)L.n_rope_pos * half), sn((size_t)L.n_rope_pos * half);
+    std::vector<double> inv(half);
+    for (int i = 0; i < half; ++i) inv[i] = std::pow(d.rope_base, -2.0 * i / d.d);
+    for (int p = 0; p < L.n_rope_pos; ++p)
+        for (int i = 0; i < half; ++i) {
+            const double a = (double)p * inv[i];
+            cs[(size_t)p * half + i] = (float)std::cos(a);
+            sn[(size_t)p * half + i] = (float)std::sin(a);
+        }
+    std::vector<int32_t> pt = make_page_table(d.n_pages, cfg->page_seed);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if ((e = hipMemcpyAsync(x.ws + L.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(x.ws + L.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+        (pt.size() && (e = hipMemcpyAsync(x.ws + L.page_table, pt.data(), pt.size() * 4, hipMemcpyHostToDevice, s)) !=
+                          hipSuccess) ||
+        (e = hipMemsetAsync(x.ws + L.tile_cnt, 0, (size_t)L.max_tiles * 4, s)) != hipSuccess ||
+        (e = hipMemsetAsync(x.ws + L.counters, 0, 64 * 4, s)) != hipSuccess ||
+        (e = hipMemsetAsync(x.ws + L.best, 0, 16 * 8, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess) {
+        delete c;
+        return DFLASH_ERR_HIP;
+    }
+    *out = c;
+    return DFLASH_OK;
+}
+
+static void drop_events(dflash_ctx* c) {
+    for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
+    c->events.clear();
+    c->tracer = Tracer();
+}
+
+dflash_status dflash_destroy(dflash_ctx* c) {
+    if (c) drop_events(c);
+    delete c;
+    return DFLASH_OK;
+}
+
+int32_t dflash_length(const dflash_ctx* c) { return c ? c->length : -1; }
+
+dflash_status dflash_fuse_context(dflash_ctx* c, const void* const* layer_hidden, int64_t ld, int32_t M,
+                                  void* fused_out, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!layer_hidden || !fused_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (M < 1 || M > d.max_rows) return fail(c, DFLASH_ERR_CAPACITY, "M must be in [1, max_rows]");
+    if (ld < d.H || ld % (16 / d.elem)) return fail(c, DFLASH_ERR_INVAL, "ld must be >= H and keep rows 16-byte aligned");
+    int32_t sel[5];
+    feature_layers(d.Lt, sel);
+    const void* slabs[5];
+    for (int i = 0; i < 5; ++i) {
+        slabs[i] = layer_hidden[sel[i]];
+        if (!slabs[i] || !aligned(slabs[i], 16)) return fail(c, DFLASH_ERR_INVAL, "selected layer pointer null or misaligned");
+    }
+    if (!aligned(fused_out, 16)) return fail(c, DFLASH_ERR_INVAL, "fused_out misaligned");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_fuse(c->dev, slabs, ld, M, fused_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "fuse launch");
+    return DFLASH_OK;
+}
+
+dflash_status dflash_inject_kv(dflash_ctx* c, const void* fused, int64_t ld, int32_t M, int32_t pos0, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!fused || !aligned(fused, 16)) return fail(c, DFLASH_ERR_INVAL, "fused null or misaligned");
+    if (ld < d.H || ld % (16 / d.elem)) return fail(c, DFLASH_ERR_INVAL, "ld must be >= H and keep rows 16-byte aligned");
+    if (M < 1 || M > d.max_rows) return fail(c, DFLASH_ERR_CAPACITY, "M must be in [1, max_rows]");
+    if (pos0 != c->length) return fail(c, DFLASH_ERR_STATE, "pos0 must equal the current length");
+    if ((long long)pos0 + M > d.max_ctx) return fail(c, DFLASH_ERR_CAPACITY, "injection would exceed max_ctx");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_inject(c->dev, fused, ld, M, pos0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "inject launch");
+    c->length = pos0 + M;
+    return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* anchor, float* logits_out, int32_t* tokens_out,
+                                 void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const DevCtx& x = c->dev;
+    if (!anchor || !tokens_out) return fail(c, DFLASH_ERR_INVAL, "null anchor or tokens_out");
+    if (!x.embed || !x.lm_head || !x.final_norm) return fail(c, DFLASH_ERR_INVAL, "draft needs embed, lm_head, final_norm");
+    for (int l = 0; l < x.dm.Ld; ++l)
+        if (!x.attn_norm[l] || !x.wq[l] || !x.wo[l] || !x.mlp_norm[l] || !x.wg[l] || !x.wu[l] || !x.wd[l])
+            return fail(c, DFLASH_ERR_INVAL, "draft needs every layer's weights");
+    if (logits_out && !aligned(logits_out, 4)) return fail(c, DFLASH_ERR_INVAL, "logits_out misaligned");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_draft_block(x, c->length, anchor, logits_out, tokens_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "draft launch");
+    return DFLASH_OK;
+}
+
+dflash_status dflash_verify_accept(dflash_ctx* c, const int32_t* draft, const int32_t* target, int32_t* result_out,
+                                   void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (!draft || !target || !result_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_accept(c->dev, draft, target, result_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "accept launch");
+    return DFLASH_OK;
+}
+
+dflash_status dflash_rollback(dflash_ctx* c, int32_t new_len) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (new_len < 0 || new_len > c->length) return fail(c, DFLASH_ERR_INVAL, "new_len must be in [0, length]");
+    c->length = new_len;
+    return DFLASH_OK;
+}
+
+dflash_status dflash_load_kv(dflash_ctx* c, const void* k, const void* v, int32_t M, int32_t pos0, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!k || !v) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (M < 1) return fail(c, DFLASH_ERR_INVAL, "M must be >= 1");
+    if (pos0 != c->length) return fail(c, DFLASH_ERR_STATE, "pos0 must equal the current length");
+    if ((long long)pos0 + M > d.max_ctx) return fail(c, DFLASH_ERR_CAPACITY, "load would exceed max_ctx");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_kv_copy(c->dev, const_cast<void*>(k), const_cast<void*>(v), M, pos0, true,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "kv copy launch");
+    c->length = pos0 + M;
+    return DFLASH_OK;
+}
+
+dflash_status dflash_read_kv(dflash_ctx* c, int32_t pos0, int32_t M, void* k_out, void* v_out, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (!k_out || !v_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (M < 1 || pos0 < 0 || (long long)pos0 + M > c->length)
+        return fail(c, DFLASH_ERR_INVAL, "range must lie inside [0, length)");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_kv_copy(c->dev, k_out, v_out, M, pos0, false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "kv copy launch");
+    return DFLASH_OK;
+}
+
+dflash_status dflash_trace_enable(dflash_ctx* c, int32_t kernel_class, int32_t max_launches) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (kernel_class < DFLASH_TRACE_OFF || kernel_class > DFLASH_TRACE_INJECT || max_launches < 0 ||
+        max_launches > (1 << 20))
+        return fail(c, DFLASH_ERR_INVAL, "bad trace class or launch count");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(c, e, "hipDeviceSynchronize");
+    drop_events(c);
+    if (kernel_class == DFLASH_TRACE_OFF || max_launches == 0) return DFLASH_OK;
+    c->events.resize((size_t)2 * max_launches);
+    for (size_t i = 0; i < c->events.size(); ++i) {
+        if ((e = hipEventCreate(&c->events[i])) != hipSuccess) {
+            c->events.resize(i);
+            drop_events(c);
+            return hip_fail(c, e, "hipEventCreate");
+        }
+    }
+    c->tracer.cls = kernel_class;
+    c->tracer.max = max_launches;
+    c->tracer.n = 0;
+    c->tracer.ev = c->events.data();
+    return DFLASH_OK;
+}
+
+dflash_status dflash_trace_read(dflash_ctx* c, double* total_ms, int32_t* launches) {
+    if (!c || !total_ms || !launches) return DFLASH_ERR_INVAL;
+    double tot = 0.0;
+    for (int i = 0; i < c->tracer.n; ++i) {
+        hipError_t e = hipEventSynchronize(c->events[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, c->events[2 * i], c->events[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventElapsedTime");
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = c->tracer.n;
+    return DFLASH_OK;
+}
+
+}  // extern "C"

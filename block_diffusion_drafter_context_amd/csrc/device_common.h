@@ -1,0 +1,122 @@
+// device_common.h -- element types, conversions and MFMA fragments for gfx950.
+//
+// Storage types: float (fp32) and bf16 held as uint16_t bit patterns.
+// Matrix-core fragments follow the 16x16 MFMA operand layout of CDNA:
+//   A (16 x 32, row m, reduction k):  lane l holds row m = l % 16 and the eight
+//                                     reduction slots of lane group g = l / 16;
+//   B (32 x 16, reduction k, col n):  lane l holds col n = l % 16, same slots;
+//   D (16 x 16 fp32):                 lane l holds rows 4*(l/16) + i, i = 0..3,
+//                                     of column l % 16.
+// The hardware pairs A and B by (lane group, slot), so any fixed assignment of
+// the 32 reduction indices to (group, slot) that both operands share gives the
+// full dot product.  We use k = 8*g + slot unless a kernel says otherwise.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (NaN becomes a quiet NaN)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (bf16_t)0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float to_f32(float v) { return v; }
+    __device__ __forceinline__ static float from_f32(float v) { return v; }
+    __device__ __forceinline__ static float round(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+    __device__ __forceinline__ static float to_f32(bf16_t v) { return bf16_to_f32(v); }
+    __device__ __forceinline__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
+    __device__ __forceinline__ static float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+// Eight consecutive reduction elements of one row: one MFMA operand slot set.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+    uint4 v;
+    __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ float get(int i) const {
+        uint32_t w = (&v.x)[i >> 1];
+        return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    __device__ __forceinline__ void set8(const float* f) {
+        uint32_t w[4];
+        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
+template <> struct Frag<float> {
+    float4 a, b;
+    __device__ __forceinline__ void zero() { a = make_float4(0, 0, 0, 0); b = a; }
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ float get(int i) const { return i < 4 ? (&a.x)[i] : (&b.x)[i - 4]; }
+    __device__ __forceinline__ void set8(const float* f) {
+        a = make_float4(f[0], f[1], f[2], f[3]);
+        b = make_float4(f[4], f[5], f[6], f[7]);
+    }
+};
+
+// acc (16x16) += A(16x32) * B(32x16)
+__device__ __forceinline__ void mma(f32x4_t& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v), __builtin_bit_cast(bf16x8_t, b.v),
+                                                  acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4_t& acc, const Frag<float>& a, const Frag<float>& b) {
+    // slot s of every lane group forms one 16x16x4 fp32 product
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, b.a.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, b.a.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.z, b.a.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.w, b.a.w, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.x, b.b.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.y, b.b.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, b.b.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// sum / max over the 16 lanes that share a lane group (same l / 16)
+__device__ __forceinline__ float group16_sum(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    return v;
+}
+__device__ __forceinline__ float group16_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1, 64));
+    v = fmaxf(v, __shfl_xor(v, 2, 64));
+    v = fmaxf(v, __shfl_xor(v, 4, 64));
+    v = fmaxf(v, __shfl_xor(v, 8, 64));
+    return v;
+}
+// reduce across the 4 lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float cross4_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+__device__ __forceinline__ float cross4_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+}  // namespace dflash

@@ -1,0 +1,61 @@
+// host.h -- host-only logic of libdflash: config validation, workspace layout,
+// page table, length bookkeeping.  No HIP dependency, so it is unit-testable on
+// a machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+
+namespace dflash {
+
+// Launch geometry shared by host and device code.
+constexpr int kWaveSize = 64;
+constexpr int kSkinnyWavesPerWG = 4;     // skinny (M <= 16) GEMM: 256-thread workgroups
+constexpr int kSkinnyNT = 2;             // 16-column blocks per skinny tile
+constexpr int kAttnChunk = 64;           // keys per attention step
+constexpr int kMaxSplits = 256;          // context splits of the split-KV attention
+constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
+
+struct Dims {
+    int dtype, H, Lt, Ld, nq, nkv, d, F, V, B, mask_id, page, max_ctx, max_rows, n_pages, elem;
+    double rope_base, eps;
+};
+
+// Byte offsets of every region inside the caller's workspace (256-byte aligned).
+struct Layout {
+    size_t rope_cos, rope_sin, page_table;
+    size_t x, q, kblk, vblkT, obuf, hbuf;
+    size_t rstd, ss_part, partial, tile_cnt, counters, best;
+    size_t attn_o, attn_ml;
+    size_t total;
+    size_t kv_total;      // bytes of the KV pool
+    size_t kv_layer_kv;   // bytes of one (layer, K-or-V) page array
+    int nwaves;           // skinny-GEMM waves per launch
+    int max_tiles;        // largest tile count of any skinny GEMM
+    int max_ss_tiles;     // tiles of an N = H skinny GEMM (row sum-of-squares partials)
+    int n_rope_pos;       // positions covered by the rotary table
+};
+
+// Validate a config; on failure returns a status and writes a message.
+dflash_status validate_config(const dflash_config* cfg, Dims* out, std::string* err);
+
+// Workspace layout for validated dims.  `num_cus` sizes the skinny-GEMM grid.
+Layout compute_layout(const Dims& d, int num_cus);
+
+// Physical page of each logical page: identity, or a seeded Fisher-Yates
+// shuffle (splitmix64 stream) when seed != 0.
+std::vector<int32_t> make_page_table(int n_pages, uint64_t seed);
+
+// The five fused target layers: round_half_up(1 + i*(L-3)/4), i = 0..4.
+void feature_layers(int target_layers, int32_t out[5]);
+
+// Attention split plan for a context of C keys: keys per split (multiple of
+// kAttnChunk) and number of context splits (the block keys get one more).
+void attn_split_plan(int C, int nkv, int num_cus, int* keys_per_split, int* n_splits);
+
+}  // namespace dflash

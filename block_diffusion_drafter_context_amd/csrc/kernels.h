@@ -1,0 +1,66 @@
+// kernels.h -- launch entry points of the libdflash HIP kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "host.h"
+
+namespace dflash {
+
+// Optional per-launch timing of one kernel class (HIP event pairs).
+struct Tracer {
+    int cls = 0;
+    int max = 0;
+    int n = 0;
+    hipEvent_t* ev = nullptr;  // 2 * max events
+    void begin(int k, hipStream_t s) {
+        if (k == cls && n < max) (void)hipEventRecord(ev[2 * n], s);
+    }
+    void end(int k, hipStream_t s) {
+        if (k == cls && n < max) {
+            (void)hipEventRecord(ev[2 * n + 1], s);
+            ++n;
+        }
+    }
+};
+
+// Everything a launcher needs about one context: dims, layout and the base
+// pointers of the caller's buffers.
+struct DevCtx {
+    Dims dm;
+    Layout lay;
+    char* ws;   // workspace base
+    char* kv;   // KV pool base
+    int num_cus;
+    const void* fc;
+    const void* fc_norm;
+    const void* attn_norm[DFLASH_MAX_LAYERS];
+    const void* wq[DFLASH_MAX_LAYERS];
+    const void* wk[DFLASH_MAX_LAYERS];
+    const void* wv[DFLASH_MAX_LAYERS];
+    const void* wo[DFLASH_MAX_LAYERS];
+    const void* mlp_norm[DFLASH_MAX_LAYERS];
+    const void* wg[DFLASH_MAX_LAYERS];
+    const void* wu[DFLASH_MAX_LAYERS];
+    const void* wd[DFLASH_MAX_LAYERS];
+    const void* final_norm;
+    const void* embed;
+    const void* lm_head;
+    Tracer* tracer;
+};
+
+// One draft block over the first C context positions.
+hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits,
+                              int32_t* tokens, hipStream_t s);
+// Context fusion of M rows (selected slabs given in ascending layer order).
+hipError_t launch_fuse(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out,
+                       hipStream_t s);
+// KV injection of M rows of fused features at positions pos0...
+hipError_t launch_inject(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s);
+// Greedy acceptance.
+hipError_t launch_accept(const DevCtx& c, const int32_t* draft, const int32_t* target, int32_t* out,
+                         hipStream_t s);
+// Copy dense [Ld, M, nkv, d] K/V into (to_pages) or out of the pages.
+hipError_t launch_kv_copy(const DevCtx& c, void* k, void* v, int M, int pos0, bool to_pages, hipStream_t s);
+
+}  // namespace dflash

@@ -1,0 +1,1235 @@
+// kernels.hip -- HIP kernels of libdflash for CDNA4 (gfx950).
+//
+// Method (web pages):
+//  [A] "DFlash 深度解析：块扩散模型如何让 LLM 推理加速 6 倍——2026 投机解码完全指南"
+//      (chenxutan.com/d/2993) §2.2 feature fusion / KV injection / block draft,
+//      §3.3 shared embedding and LM head, §4.6 one kernel call for all block positions.
+//  [B] "从 ICML 论文到你的显卡：llama.cpp 吞下 DFlash…" (arex-research.com), 技术内幕.
+//
+// Kernels:
+//  * skinny_kernel<T, Op>  -- the weight-streaming GEMM for M <= 16 rows.  Every
+//    projection of the draft pass (QKV+RoPE, O+residual, gate/up+SwiGLU,
+//    down+residual, LM head+argmax) and the per-step fusion/injection of 16
+//    verified rows run through it.  Work is split "stream-K" style: the
+//    (column tile x 32-wide K chunk) space is cut into equal contiguous ranges,
+//    one per wave, so every wave streams the same number of weight bytes; a tile
+//    split between waves is finished by the last contributor, which sums the
+//    fp32 partials in a fixed order (deterministic).  Each chunk is one or two
+//    16x16x32 MFMAs per 16-column block.
+//  * attn_split_kernel<T>  -- split-KV attention of the B block queries of one
+//    kv-head group over [injected context keys ; block keys], MFMA for both
+//    products, online softmax in fp32.  attn_merge_kernel combines the splits.
+//  * big_gemm_kernel<T, Op> -- MFMA tiled GEMM for M > 16 rows (prefill-side
+//    fusion and injection), epilogue staged through LDS.
+//  * small kernels: embedding rows, row RMSNorm, acceptance scan, KV copy.
+#include "device_common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace dflash {
+
+// ============================================================================
+// stream-K skinny GEMM
+// ============================================================================
+
+struct SkinnyCommon {
+    int M;          // valid rows (<= 16)
+    int K;          // reduction length (multiple of 8)
+    int nchunks;    // ceil(K / 32)
+    int ntiles;
+    int per_wave;   // chunks per wave
+    float* partial;          // [nwaves][2][NT][256]
+    unsigned* tile_cnt;      // [ntiles], zero between launches
+    unsigned* done_cnt;      // tile-completion counter, zero between launches
+};
+
+struct NoState {};
+
+constexpr int kP = 4;  // chunks per pipelined load group
+
+// Activation prologues ------------------------------------------------------
+
+// u = round(x * rstd[row] * gain[k])  (RMSNorm applied on load)
+template <typename T>
+struct NormA {
+    const T* x;
+    int ld;
+    const float* rstd;
+    const T* gain;
+    __device__ __forceinline__ void load(Frag<T>& f, int row, int k) const {
+        Frag<T> xv, gv;
+        xv.load(x + (long long)row * ld + k);
+        gv.load(gain + k);
+        const float r = rstd[row];
+        float v[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) v[s] = xv.get(s) * r * gv.get(s);
+        f.set8(v);
+    }
+};
+
+template <typename T>
+struct PlainA {
+    const T* x;
+    long long ld;
+    __device__ __forceinline__ void load(Frag<T>& f, int row, int k) const { f.load(x + row * ld + k); }
+};
+
+// five hidden-state slabs read as one concatenated row (never materialised)
+template <typename T>
+struct SlabA {
+    const T* slab[5];
+    long long ld;
+    int H;
+    __device__ __forceinline__ void load(Frag<T>& f, int row, int k) const {
+        const int s = k / H;
+        f.load(slab[s] + row * ld + (k - s * H));
+    }
+};
+
+template <typename T, class Op, class AL>
+__device__ __forceinline__ void skinny_segment(const Op& op, const AL& al, const T* b0, const T* b1, int ch0,
+                                               int ch1, int K, int row, int grp, bool row_ok, f32x4_t acc[2]) {
+    const T* w0 = b0 + (long long)row * K + grp * 8;
+    const T* w1 = b1 ? b1 + (long long)row * K + grp * 8 : nullptr;
+    Frag<T> cw0[kP], cw1[kP], ca[kP];
+    auto load_group = [&](int c, Frag<T>* lw0, Frag<T>* lw1, Frag<T>* la) {
+#pragma unroll
+        for (int p = 0; p < kP; ++p) {
+            const int ch = c + p;
+            const int k = ch * 32 + grp * 8;
+            if (ch < ch1 && k < K) {
+                lw0[p].load(w0 + ch * 32);
+                if (w1) lw1[p].load(w1 + ch * 32); else lw1[p].zero();
+                if (row_ok) al.load(la[p], row, k); else la[p].zero();
+            } else {
+                lw0[p].zero();
+                lw1[p].zero();
+                la[p].zero();
+            }
+        }
+    };
+    load_group(ch0, cw0, cw1, ca);
+    for (int c = ch0; c < ch1; c += kP) {
+        Frag<T> nw0[kP], nw1[kP], na[kP];
+        const bool more = c + kP < ch1;
+        if (more) load_group(c + kP, nw0, nw1, na);
+#pragma unroll
+        for (int p = 0; p < kP; ++p) {
+            mma(acc[0], ca[p], cw0[p]);
+            mma(acc[1], ca[p], cw1[p]);
+        }
+        if (more) {
+#pragma unroll
+            for (int p = 0; p < kP; ++p) {
+                cw0[p] = nw0[p];
+                cw1[p] = nw1[p];
+                ca[p] = na[p];
+            }
+        }
+    }
+}
+
+template <typename T, class Op>
+__global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
+    const int lane = threadIdx.x & 63;
+    const int wave = blockIdx.x * kSkinnyWavesPerWG + (threadIdx.x >> 6);
+    const int row = lane & 15, grp = lane >> 4;
+    const bool row_ok = row < c.M;
+    typename Op::State st;
+    op.wave_begin(st);
+
+    const long long total = (long long)c.ntiles * c.nchunks;
+    const long long start = (long long)wave * c.per_wave;
+    const long long end = start + c.per_wave < total ? start + c.per_wave : total;
+    const int first_tile = start < total ? (int)(start / c.nchunks) : -1;
+
+    for (long long i = start; i < end;) {
+        const int tile = (int)(i / c.nchunks);
+        const long long tbeg = (long long)tile * c.nchunks;
+        const long long seg_end = end < tbeg + c.nchunks ? end : tbeg + c.nchunks;
+        const int ch0 = (int)(i - tbeg), ch1 = (int)(seg_end - tbeg);
+        f32x4_t acc[2] = {zero4(), zero4()};
+        skinny_segment<T>(op, op.a, op.b_rows(tile, 0), op.b_rows(tile, 1), ch0, ch1, c.K, row, grp, row_ok, acc);
+        i = seg_end;
+        if (!(ch0 == 0 && ch1 == c.nchunks)) {
+            // partial tile: publish, and let the last contributor finish it
+            const int slot = tile == first_tile ? 0 : 1;
+            float* mine = c.partial + ((long long)wave * 2 + slot) * (kSkinnyNT * 256);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) mine[b * 256 + ii * 64 + lane] = acc[b][ii];
+            __threadfence();
+            const int w_first = (int)(tbeg / c.per_wave);
+            const int w_last = (int)((tbeg + c.nchunks - 1) / c.per_wave);
+            unsigned old = 0;
+            if (lane == 0) old = atomicAdd(&c.tile_cnt[tile], 1u);
+            old = __shfl(old, 0, 64);
+            if (old != (unsigned)(w_last - w_first)) continue;
+            __threadfence();
+            acc[0] = zero4();
+            acc[1] = zero4();
+            for (int w = w_first; w <= w_last; ++w) {
+                const int ft = (int)(((long long)w * c.per_wave) / c.nchunks);
+                const float* src = c.partial + ((long long)w * 2 + (ft == tile ? 0 : 1)) * (kSkinnyNT * 256);
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) acc[b][ii] += __builtin_nontemporal_load(src + b * 256 + ii * 64 + lane);
+            }
+            if (lane == 0) atomicExch(&c.tile_cnt[tile], 0u);
+        }
+        op.epilogue(tile, acc, lane, st);
+        if (Op::kDoneHook) {
+            __threadfence();
+            unsigned old = 0;
+            if (lane == 0) old = atomicAdd(c.done_cnt, 1u);
+            old = __shfl(old, 0, 64);
+            if (old == (unsigned)(c.ntiles - 1)) {
+                __threadfence();
+                op.done_hook(lane, c.ntiles);
+                if (lane == 0) atomicExch(c.done_cnt, 0u);
+            }
+        }
+    }
+    op.wave_end(st, lane);
+}
+
+// Ops ------------------------------------------------------------------------
+
+// q, k (rotated) and v of the block rows.  Tiles pair the 16-column blocks
+// (16i, 16i + d/2) of one head so each rotary pair sits in one lane.
+template <typename T>
+struct OpQKV {
+    using State = NoState;
+    static constexpr bool kDoneHook = false;
+    NormA<T> a;
+    const T* wq;
+    const T* wk;
+    const T* wv;
+    int H, nq, nkv, d, M, pos0;
+    int tq, tk;  // tiles of q and of k (= of v)
+    const float* cosT;
+    const float* sinT;
+    T* qout;
+    T* kout;
+    T* vTout;
+    __device__ __forceinline__ void decode(int tile, int& kind, int& h, int& i) const {
+        const int per = d / 32;
+        int t = tile;
+        kind = 0;
+        if (t >= tq) { t -= tq; kind = 1; if (t >= tk) { t -= tk; kind = 2; } }
+        h = t / per;
+        i = t - h * per;
+    }
+    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+        int kind, h, i;
+        decode(tile, kind, h, i);
+        const T* W = kind == 0 ? wq : (kind == 1 ? wk : wv);
+        return W + (long long)(h * d + 16 * i + blk * (d / 2)) * H;
+    }
+    __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void wave_end(State&, int) const {}
+    __device__ __forceinline__ void done_hook(int, int) const {}
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+        int kind, h, i;
+        decode(tile, kind, h, i);
+        const int dim = 16 * i + (lane & 15), half = d / 2;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int j = 4 * (lane >> 4) + ii;
+            if (j >= M) continue;
+            float x0 = acc[0][ii], x1 = acc[1][ii];
+            if (kind != 2) {
+                const long long t = (long long)(pos0 + j) * half + dim;
+                const float cs = cosT[t], sn = sinT[t];
+                const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
+                x0 = r0;
+                x1 = r1;
+            }
+            if (kind == 0) {
+                T* o = qout + (long long)j * nq * d + h * d;
+                o[dim] = Elem<T>::from_f32(x0);
+                o[dim + half] = Elem<T>::from_f32(x1);
+            } else if (kind == 1) {
+                T* o = kout + (long long)j * nkv * d + h * d;
+                o[dim] = Elem<T>::from_f32(x0);
+                o[dim + half] = Elem<T>::from_f32(x1);
+            } else {
+                T* o = vTout + (long long)h * d * 16;
+                o[dim * 16 + j] = Elem<T>::from_f32(x0);
+                o[(dim + half) * 16 + j] = Elem<T>::from_f32(x1);
+            }
+        }
+    }
+};
+
+// x += round(A . W^T) (residual add, both rounded), then the row statistics
+// of the new x for the next RMSNorm: per-tile partial sums of squares, and the
+// last finished tile turns them into rstd (fixed summation order).
+template <typename T>
+struct OpResid {
+    using State = NoState;
+    static constexpr bool kDoneHook = true;
+    PlainA<T> a;
+    const T* w;
+    int N, K, M;
+    T* x;
+    float* ss_part;
+    float* rstd_out;
+    float eps;
+    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+        const int n0 = 32 * tile + 16 * blk;
+        return n0 < N ? w + (long long)n0 * K : nullptr;
+    }
+    __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void wave_end(State&, int) const {}
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+        float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int n = 32 * tile + 16 * b + (lane & 15);
+            if (n >= N) continue;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int j = 4 * (lane >> 4) + ii;
+                if (j >= M) continue;
+                T* p = x + (long long)j * N + n;
+                const float xn = Elem<T>::round(Elem<T>::to_f32(*p) + Elem<T>::round(acc[b][ii]));
+                *p = Elem<T>::from_f32(xn);
+                sq[ii] += xn * xn;
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const float s = group16_sum(sq[ii]);
+            if ((lane & 15) == 0) ss_part[tile * 16 + 4 * (lane >> 4) + ii] = s;
+        }
+    }
+    __device__ __forceinline__ void done_hook(int lane, int ntiles) const {
+        // lane handles row j = lane & 15 over tiles t = g, g+4, ... (g = lane >> 4)
+        const int j = lane & 15, g = lane >> 4;
+        float s = 0.f;
+        for (int t = g; t < ntiles; t += 4) s += __builtin_nontemporal_load(ss_part + t * 16 + j);
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        if (lane < 16) rstd_out[j] = 1.0f / sqrtf(s / (float)N + eps);
+    }
+};
+
+// h = round(silu(u . Wg^T) * (u . Wu^T)); tile t pairs column block t of Wg and Wu.
+template <typename T>
+struct OpSwiGLU {
+    using State = NoState;
+    static constexpr bool kDoneHook = false;
+    NormA<T> a;
+    const T* wg;
+    const T* wu;
+    int F, K, M;
+    T* h;
+    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+        return (blk == 0 ? wg : wu) + (long long)(16 * tile) * K;
+    }
+    __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void wave_end(State&, int) const {}
+    __device__ __forceinline__ void done_hook(int, int) const {}
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+        const int n = 16 * tile + (lane & 15);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int j = 4 * (lane >> 4) + ii;
+            if (j >= M) continue;
+            const float g = acc[0][ii], u = acc[1][ii];
+            const float sg = g / (1.0f + __expf(-g));
+            h[(long long)j * F + n] = Elem<T>::from_f32(sg * u);
+        }
+    }
+};
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered_bits(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// LM head (shared with the target) with a fused argmax: fp32 logits, ties to
+// the lowest id.  Each wave keeps a running best per row; the workgroup
+// reduces its waves through LDS and publishes one packed (value, ~id) key per
+// row with a 64-bit atomic max, which is order independent; the last
+// workgroup writes the tokens.
+template <typename T>
+struct OpLMHead {
+    struct State {
+        float v[4];
+        int idx[4];
+    };
+    static constexpr bool kDoneHook = false;
+    NormA<T> a;
+    const T* w;
+    int V, K, M;
+    float* logits;                 // [M, V] or null
+    unsigned long long* best;      // [16] packed keys, zero on entry
+    unsigned* wg_cnt;              // workgroup completion counter
+    int32_t* tokens;               // [M]
+    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+        const int n0 = 32 * tile + 16 * blk;
+        return n0 < V ? w + (long long)n0 * K : nullptr;
+    }
+    __device__ __forceinline__ void wave_begin(State& s) const {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) { s.v[ii] = -INFINITY; s.idx[ii] = 0x7FFFFFFF; }
+    }
+    __device__ __forceinline__ void done_hook(int, int) const {}
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State& s) const {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int n = 32 * tile + 16 * b + (lane & 15);
+            if (n >= V) continue;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int j = 4 * (lane >> 4) + ii;
+                const float v = acc[b][ii];
+                if (logits && j < M) logits[(long long)j * V + n] = v;
+                if (v > s.v[ii] || (v == s.v[ii] && n < s.idx[ii])) { s.v[ii] = v; s.idx[ii] = n; }
+            }
+        }
+    }
+    __device__ void wave_end(State& s, int lane) const {
+        __shared__ float sv[kSkinnyWavesPerWG][16];
+        __shared__ int si[kSkinnyWavesPerWG][16];
+        const int wv = threadIdx.x >> 6;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            float v = s.v[ii];
+            int id = s.idx[ii];
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                const float ov = __shfl_xor(v, m, 64);
+                const int oi = __shfl_xor(id, m, 64);
+                if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+            }
+            if ((lane & 15) == 0) {
+                sv[wv][4 * (lane >> 4) + ii] = v;
+                si[wv][4 * (lane >> 4) + ii] = id;
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < 16) {
+            const int j = threadIdx.x;
+            float v = sv[0][j];
+            int id = si[0][j];
+            for (int q = 1; q < kSkinnyWavesPerWG; ++q)
+                if (sv[q][j] > v || (sv[q][j] == v && si[q][j] < id)) { v = sv[q][j]; id = si[q][j]; }
+            if (j < M && id != 0x7FFFFFFF) {
+                const unsigned long long key = ((unsigned long long)ordered_bits(v) << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)id);
+                atomicMax(best + j, key);
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned old = atomicAdd(wg_cnt, 1u);
+            sv[0][0] = __uint_as_float(old == gridDim.x - 1 ? 1u : 0u);
+        }
+        __syncthreads();
+        if (__float_as_uint(sv[0][0]) == 1u) {
+            __threadfence();
+            if (threadIdx.x < 16) {
+                const int j = threadIdx.x;
+                if (j < M) {
+                    const unsigned long long key = atomicOr(best + j, 0ull);
+                    tokens[j] = (int32_t)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
+                }
+                atomicExch(best + j, 0ull);
+            }
+            if (threadIdx.x == 0) atomicExch(wg_cnt, 0u);
+        }
+    }
+};
+
+// y = round(W_fc . concat(slabs)) for M <= 16 rows (RMSNorm follows separately).
+template <typename T>
+struct OpFuse {
+    using State = NoState;
+    static constexpr bool kDoneHook = false;
+    SlabA<T> a;
+    const T* w;
+    int H, K, M;
+    T* out;
+    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+        const int n0 = 32 * tile + 16 * blk;
+        return n0 < H ? w + (long long)n0 * K : nullptr;
+    }
+    __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void wave_end(State&, int) const {}
+    __device__ __forceinline__ void done_hook(int, int) const {}
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int n = 32 * tile + 16 * b + (lane & 15);
+            if (n >= H) continue;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int j = 4 * (lane >> 4) + ii;
+                if (j < M) out[(long long)j * H + n] = Elem<T>::from_f32(acc[b][ii]);
+            }
+        }
+    }
+};
+
+// Paged draft-KV addressing: per (layer, K|V) an array of pages; K pages are
+// [nkv][page][d] (key rows), V pages [nkv][d][page] (value columns, so the
+// attention's P.V operand reads runs of consecutive positions).
+struct KVPages {
+    char* base;
+    const int32_t* table;
+    long long layer_kv_bytes;  // bytes of one (layer, K|V) page array
+    int page, nkv, d, elem;
+    __device__ __forceinline__ long long page_elems() const { return (long long)nkv * page * d; }
+    template <typename T>
+    __device__ __forceinline__ T* kpage(int l, int pos, int& slot) const {
+        const int p = pos / page;
+        slot = pos - p * page;
+        return reinterpret_cast<T*>(base + (2LL * l) * layer_kv_bytes) + (long long)table[p] * page_elems();
+    }
+    template <typename T>
+    __device__ __forceinline__ T* vpage(int l, int pos, int& slot) const {
+        const int p = pos / page;
+        slot = pos - p * page;
+        return reinterpret_cast<T*>(base + (2LL * l + 1) * layer_kv_bytes) + (long long)table[p] * page_elems();
+    }
+};
+
+// Injection of M <= 16 rows into every layer.  Tile order: layer, K|V, head,
+// pair i of blocks (16i, 16i + d/2).
+template <typename T>
+struct OpInject {
+    using State = NoState;
+    static constexpr bool kDoneHook = false;
+    PlainA<T> a;
+    const T* wk[DFLASH_MAX_LAYERS];
+    const T* wv[DFLASH_MAX_LAYERS];
+    int H, nkv, d, M, pos0;
+    const float* cosT;
+    const float* sinT;
+    KVPages kv;
+    __device__ __forceinline__ void decode(int tile, int& l, int& kind, int& h, int& i) const {
+        const int per = d / 32;
+        const int per_kind = nkv * per;
+        l = tile / (2 * per_kind);
+        int t = tile - l * 2 * per_kind;
+        kind = t / per_kind;
+        t -= kind * per_kind;
+        h = t / per;
+        i = t - h * per;
+    }
+    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+        int l, kind, h, i;
+        decode(tile, l, kind, h, i);
+        return (kind == 0 ? wk[l] : wv[l]) + (long long)(h * d + 16 * i + blk * (d / 2)) * H;
+    }
+    __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void wave_end(State&, int) const {}
+    __device__ __forceinline__ void done_hook(int, int) const {}
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+        int l, kind, h, i;
+        decode(tile, l, kind, h, i);
+        const int dim = 16 * i + (lane & 15), half = d / 2;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int j = 4 * (lane >> 4) + ii;
+            if (j >= M) continue;
+            const int pos = pos0 + j;
+            float x0 = acc[0][ii], x1 = acc[1][ii];
+            int slot;
+            if (kind == 0) {
+                const long long t = (long long)pos * half + dim;
+                const float cs = cosT[t], sn = sinT[t];
+                const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
+                T* pg = kv.kpage<T>(l, pos, slot) + ((long long)h * kv.page + slot) * d;
+                pg[dim] = Elem<T>::from_f32(r0);
+                pg[dim + half] = Elem<T>::from_f32(r1);
+            } else {
+                T* pg = kv.vpage<T>(l, pos, slot) + (long long)h * d * kv.page;
+                pg[(long long)dim * kv.page + slot] = Elem<T>::from_f32(x0);
+                pg[(long long)(dim + half) * kv.page + slot] = Elem<T>::from_f32(x1);
+            }
+        }
+    }
+};
+
+template <typename T, class Op>
+static hipError_t run_skinny(const DevCtx& c, const Op& op, int M, int K, int ntiles, hipStream_t s) {
+    SkinnyCommon sc;
+    sc.M = M;
+    sc.K = K;
+    sc.nchunks = (K + 31) / 32;
+    sc.ntiles = ntiles;
+    const long long total = (long long)ntiles * sc.nchunks;
+    long long nw = c.lay.nwaves;
+    long long per = (total + nw - 1) / nw;
+    per = ((per + kP - 1) / kP) * kP;
+    if (per < kP) per = kP;
+    sc.per_wave = (int)per;
+    const long long waves = (total + per - 1) / per;
+    sc.partial = reinterpret_cast<float*>(c.ws + c.lay.partial);
+    sc.tile_cnt = reinterpret_cast<unsigned*>(c.ws + c.lay.tile_cnt);
+    sc.done_cnt = reinterpret_cast<unsigned*>(c.ws + c.lay.counters);
+    const int grid = (int)((waves + kSkinnyWavesPerWG - 1) / kSkinnyWavesPerWG);
+    hipLaunchKernelGGL((skinny_kernel<T, Op>), dim3(grid), dim3(64 * kSkinnyWavesPerWG), 0, s, op, sc);
+    return hipGetLastError();
+}
+
+// ============================================================================
+// split-KV attention
+// ============================================================================
+
+struct AttnArgs {
+    const void* q;      // [16][nq*d]
+    const void* kblk;   // [16][nkv*d]
+    const void* vblkT;  // [nkv][d][16]
+    KVPages kv;
+    int layer, C, B, nq, nkv, group, kps, n_splits;
+    float scale_log2;   // log2(e) / sqrt(d)
+    float* part_o;      // [(n_splits+1)][nq][16][d]
+    float* part_ml;     // [(n_splits+1)][nq][16][2]
+};
+
+// One workgroup = one (split, kv head); one wave per query head of the group.
+// Scores are formed transposed, S^T = K Q^T (keys on MFMA rows, the 16 block
+// rows on columns), so that the probabilities land exactly in the B-operand
+// layout of O^T += V^T P^T and never leave registers.
+template <typename T, int D>
+__global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = blockIdx.y, split = blockIdx.x;
+    const int hq = g * a.group + w;
+    const int grp = lane >> 4, col = lane & 15;
+    const T* q = reinterpret_cast<const T*>(a.q);
+
+    Frag<T> qf[D / 32];
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc) {
+        if (col < a.B) qf[kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
+        else qf[kc].zero();
+    }
+    float m = -INFINITY, l = 0.f;
+    f32x4_t o[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db] = zero4();
+
+    const bool ctx = split < a.n_splits;
+    const int kbeg = ctx ? split * a.kps : 0;
+    const int kend = ctx ? min(a.C, kbeg + a.kps) : a.B;
+
+    for (int key0 = kbeg; key0 < kend; key0 += kAttnChunk) {
+        // ---- S^T for 64 keys (4 blocks of 16)
+        const T* kbase;
+        long long krow_stride;
+        const T* vbase;
+        long long vrow_stride;
+        int slot0 = 0;
+        if (ctx) {
+            kbase = a.kv.kpage<T>(a.layer, key0, slot0) + ((long long)g * a.kv.page + slot0) * D;
+            krow_stride = D;
+            vbase = a.kv.vpage<T>(a.layer, key0, slot0) + (long long)g * D * a.kv.page + slot0;
+            vrow_stride = a.kv.page;
+        } else {
+            kbase = reinterpret_cast<const T*>(a.kblk) + (long long)g * D;
+            krow_stride = (long long)a.nkv * D;
+            vbase = reinterpret_cast<const T*>(a.vblkT) + (long long)g * D * 16;
+            vrow_stride = 16;
+        }
+        f32x4_t s[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            s[kb] = zero4();
+            const int key = key0 + kb * 16 + col;
+            const bool ok = key < kend;
+#pragma unroll
+            for (int kc = 0; kc < D / 32; ++kc) {
+                Frag<T> kf;
+                if (ok) kf.load(kbase + (long long)(kb * 16 + col) * krow_stride + kc * 32 + grp * 8);
+                else kf.zero();
+                mma(s[kb], kf, qf[kc]);
+            }
+        }
+        // ---- online softmax (log2 domain); lane column = query row `col`
+        float mx = m;
+        float p[4][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int key = key0 + kb * 16 + 4 * grp + ii;
+                p[kb][ii] = key < kend ? s[kb][ii] * a.scale_log2 : -INFINITY;
+                mx = fmaxf(mx, p[kb][ii]);
+            }
+        mx = cross4_max(mx);
+        const float alpha = exp2f(m - mx);
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const float e = Elem<T>::round(exp2f(p[kb][ii] - mx));
+                p[kb][ii] = e;
+                ps += e;
+            }
+        ps = cross4_sum(ps);
+        l = l * alpha + ps;
+        m = mx;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
+        // ---- O^T += V^T P^T, 32 keys per MFMA: slots 0-3 = keys 4grp..4grp+3 of
+        //      block 2t, slots 4-7 = the same keys of block 2t+1
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            Frag<T> pf;
+            float pv[8];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) { pv[ii] = p[2 * t][ii]; pv[4 + ii] = p[2 * t + 1][ii]; }
+            pf.set8(pv);
+            const int ka = key0 + 32 * t + 4 * grp;      // first run of 4 keys
+            const int kb2 = ka + 16;                     // second run
+            const bool oka = ka < kend, okb = kb2 < kend;  // runs never straddle kend except the block tail
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) {
+                const T* vr = vbase + (long long)(16 * db + col) * vrow_stride + (32 * t + 4 * grp);
+                float vv[8];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    vv[ii] = (oka && ka + ii < kend) ? Elem<T>::to_f32(vr[ii]) : 0.f;
+                    vv[4 + ii] = (okb && kb2 + ii < kend) ? Elem<T>::to_f32(vr[16 + ii]) : 0.f;
+                }
+                Frag<T> vf;
+                vf.set8(vv);
+                mma(o[db], vf, pf);
+            }
+        }
+    }
+    // ---- partial results
+    const long long pidx = ((long long)split * a.nq + hq) * 16;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            a.part_o[(pidx + col) * D + 16 * db + 4 * grp + ii] = o[db][ii];
+    if (grp == 0) {
+        a.part_ml[(pidx + col) * 2 + 0] = m;
+        a.part_ml[(pidx + col) * 2 + 1] = l;
+    }
+}
+
+// out[j][hq*d + dim] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s   (rounded)
+template <typename T>
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float* part_o, const float* part_ml, int n_parts,
+                                                         int nq, int d, int B, T* out) {
+    const int hq = blockIdx.x / 16, j = blockIdx.x % 16;
+    if (j >= B) return;
+    const int dim = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < n_parts; ++s) M = fmaxf(M, part_ml[(((long long)s * nq + hq) * 16 + j) * 2]);
+    float L = 0.f, acc = 0.f;
+    for (int s = 0; s < n_parts; ++s) {
+        const long long idx = ((long long)s * nq + hq) * 16 + j;
+        const float wgt = exp2f(part_ml[idx * 2] - M);
+        L += wgt * part_ml[idx * 2 + 1];
+        if (dim < d) acc += wgt * part_o[idx * d + dim];
+    }
+    if (dim < d) out[(long long)j * nq * d + hq * d + dim] = Elem<T>::from_f32(acc / L);
+}
+
+// ============================================================================
+// small kernels
+// ============================================================================
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+    // 256 threads: wave reduce, then across 4 waves
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+// Block rows: embedding of [anchor, mask, ...] and their RMS statistics.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_t* anchor, int mask_id, int V,
+                                                    int H, float eps, T* x, float* rstd, unsigned long long* best) {
+    __shared__ float red[4];
+    const int j = blockIdx.x;
+    const int tok = j == 0 ? min(max(anchor[0], 0), V - 1) : mask_id;  // out-of-range anchors are clamped
+    const T* src = embed + (long long)tok * H;
+    T* dst = x + (long long)j * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) {
+        const T v = src[i];
+        dst[i] = v;
+        const float f = Elem<T>::to_f32(v);
+        ss += f * f;
+    }
+    ss = block_sum_256(ss, red);
+    if (threadIdx.x == 0) {
+        rstd[j] = 1.0f / sqrtf(ss / (float)H + eps);
+        best[j] = 0ull;
+    }
+}
+
+// In-place row RMSNorm: y = round(y * rstd * gain)
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(T* y, int H, const T* gain, float eps) {
+    __shared__ float red[4];
+    T* row = y + (long long)blockIdx.x * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) {
+        const float f = Elem<T>::to_f32(row[i]);
+        ss += f * f;
+    }
+    ss = block_sum_256(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += 256)
+        row[i] = Elem<T>::from_f32(Elem<T>::to_f32(row[i]) * r * Elem<T>::to_f32(gain[i]));
+}
+
+// k = leading agreements of draft[1..B-1] with target[0..B-2]; bonus = target[k]
+__global__ __launch_bounds__(64) void accept_kernel(const int32_t* draft, const int32_t* target, int B,
+                                                    int32_t* out) {
+    const int j = threadIdx.x;
+    const bool miss = j < B - 1 && draft[j + 1] != target[j];
+    const unsigned long long mm = __ballot(miss);
+    const int k = mm ? __ffsll((long long)mm) - 1 : B - 1;
+    if (j == 0) {
+        out[0] = k;
+        out[1] = target[k];
+    }
+}
+
+// dense [Ld][M][nkv][d] <-> pages
+template <typename T>
+__global__ __launch_bounds__(256) void kv_copy_kernel(KVPages kv, T* k, T* v, int M, int pos0, int Ld, bool to_pages) {
+    const long long n_per = (long long)M * kv.nkv * kv.d;
+    const long long total = (long long)Ld * n_per;
+    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        const int l = (int)(e / n_per);
+        long long r = e - l * n_per;
+        const int i = (int)(r / (kv.nkv * kv.d));
+        r -= (long long)i * kv.nkv * kv.d;
+        const int h = (int)(r / kv.d), dim = (int)(r - (long long)h * kv.d);
+        int slot;
+        T* kp = kv.kpage<T>(l, pos0 + i, slot) + ((long long)h * kv.page + slot) * kv.d + dim;
+        T* vp = kv.vpage<T>(l, pos0 + i, slot) + ((long long)h * kv.d + dim) * kv.page + slot;
+        if (to_pages) { *kp = k[e]; *vp = v[e]; }
+        else { k[e] = *kp; v[e] = *vp; }
+    }
+}
+
+// ============================================================================
+// large-M MFMA GEMM (prefill-side fusion and injection)
+// ============================================================================
+
+// Logical output column block cb (16 columns) -> physical weight row pointer.
+template <typename T>
+struct BigFuseOp {
+    SlabA<T> a;
+    const T* w;
+    int H;       // N = H, K = 5H
+    T* out;      // [M][H]
+    __device__ __forceinline__ const T* a_row(int r, int k) const {
+        const int s = k / H;
+        return a.slab[s] + r * a.ld + (k - s * H);
+    }
+    __device__ __forceinline__ const T* b_block(int cb, int K) const { return w + (long long)cb * 16 * K; }
+    __device__ __forceinline__ void store(int r, int n0, const float* ctile, int ld_tile, int tid, int M, int N) const {
+        // 64 x 64 tile, 256 threads
+        for (int e = tid; e < 64 * 64; e += 256) {
+            const int rr = e / 64, cc = e % 64;
+            const int gr = r + rr, gc = n0 + cc;
+            if (gr < M && gc < N) out[(long long)gr * H + gc] = Elem<T>::from_f32(ctile[rr * ld_tile + cc]);
+        }
+    }
+};
+
+template <typename T>
+struct BigInjectOp {
+    PlainA<T> a;
+    const T* wk[DFLASH_MAX_LAYERS];
+    const T* wv[DFLASH_MAX_LAYERS];
+    int H, nkv, d, pos0;
+    const float* cosT;
+    const float* sinT;
+    KVPages kv;
+    __device__ __forceinline__ const T* a_row(int r, int k) const { return a.x + r * a.ld + k; }
+    // logical block cb: layer, kind, head, pair i, half (blocks 2p and 2p+1 are rotary partners)
+    __device__ __forceinline__ void decode(int cb, int& l, int& kind, int& h, int& i, int& half) const {
+        half = cb & 1;
+        int p = cb >> 1;
+        const int per = d / 32;
+        const int per_kind = nkv * per;
+        l = p / (2 * per_kind);
+        p -= l * 2 * per_kind;
+        kind = p / per_kind;
+        p -= kind * per_kind;
+        h = p / per;
+        i = p - h * per;
+    }
+    __device__ __forceinline__ const T* b_block(int cb, int K) const {
+        int l, kind, h, i, half;
+        decode(cb, l, kind, h, i, half);
+        return (kind == 0 ? wk[l] : wv[l]) + (long long)(h * d + 16 * i + half * (d / 2)) * K;
+    }
+    __device__ __forceinline__ void store(int r, int n0, const float* ctile, int ld_tile, int tid, int M, int N) const {
+        for (int e = tid; e < 64 * 64; e += 256) {
+            const int rr = e / 64, cc = e % 64;
+            const int gr = r + rr, gc = n0 + cc;
+            if (gr >= M || gc >= N) continue;
+            int l, kind, h, i, half;
+            decode(gc / 16, l, kind, h, i, half);
+            const int dim = 16 * i + (gc & 15) + half * (d / 2);
+            const float own = ctile[rr * ld_tile + cc];
+            const int pos = pos0 + gr;
+            int slot;
+            if (kind == 0) {
+                const float other = ctile[rr * ld_tile + (cc ^ 16)];
+                const long long t = (long long)pos * (d / 2) + 16 * i + (gc & 15);
+                const float cs = cosT[t], sn = sinT[t];
+                const float val = half == 0 ? own * cs - other * sn : other * sn + own * cs;
+                T* pg = kv.kpage<T>(l, pos, slot) + ((long long)h * kv.page + slot) * d;
+                pg[dim] = Elem<T>::from_f32(val);
+            } else {
+                T* pg = kv.vpage<T>(l, pos, slot) + (long long)h * d * kv.page;
+                pg[(long long)dim * kv.page + slot] = Elem<T>::from_f32(own);
+            }
+        }
+    }
+};
+
+template <typename T, class Op>
+__global__ __launch_bounds__(256) void big_gemm_kernel(Op op, int M, int N, int K) {
+    constexpr int BK = 32;
+    constexpr int PAD = 16 / (int)sizeof(T) * 0 + (sizeof(T) == 2 ? 8 : 4);
+    __shared__ __attribute__((aligned(16))) T As[64][BK + PAD];
+    __shared__ __attribute__((aligned(16))) T Bs[64][BK + PAD];
+    __shared__ float Cs[64][65];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int grp = lane >> 4, rl = lane & 15;
+    f32x4_t acc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+    constexpr int PIECES = 64 * BK / 8;  // 8-element pieces per operand tile
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        for (int pc = tid; pc < PIECES; pc += 256) {
+            const int r = pc / (BK / 8), kq = pc % (BK / 8);
+            const int k = k0 + kq * 8;
+            Frag<T> fa, fb;
+            if (m0 + r < M && k < K) fa.load(op.a_row(m0 + r, k)); else fa.zero();
+            const int n = n0 + r;
+            if (n < N && k < K) fb.load(op.b_block(n / 16, K) + (long long)(n % 16) * K + k); else fb.zero();
+            *reinterpret_cast<Frag<T>*>(&As[r][kq * 8]) = fa;
+            *reinterpret_cast<Frag<T>*>(&Bs[r][kq * 8]) = fb;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) {
+            Frag<T> fa = *reinterpret_cast<const Frag<T>*>(&As[wm * 32 + bm * 16 + rl][grp * 8]);
+#pragma unroll
+            for (int bn = 0; bn < 2; ++bn) {
+                Frag<T> fb = *reinterpret_cast<const Frag<T>*>(&Bs[wn * 32 + bn * 16 + rl][grp * 8]);
+                mma(acc[bm][bn], fa, fb);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                Cs[wm * 32 + bm * 16 + 4 * grp + ii][wn * 32 + bn * 16 + rl] = acc[bm][bn][ii];
+    __syncthreads();
+    op.store(m0, n0, &Cs[0][0], 65, tid, M, N);
+}
+
+// ============================================================================
+// launchers
+// ============================================================================
+
+template <typename T>
+static KVPages make_pages(const DevCtx& c) {
+    KVPages kv;
+    kv.base = c.kv;
+    kv.table = reinterpret_cast<const int32_t*>(c.ws + c.lay.page_table);
+    kv.layer_kv_bytes = (long long)c.lay.kv_layer_kv;
+    kv.page = c.dm.page;
+    kv.nkv = c.dm.nkv;
+    kv.d = c.dm.d;
+    kv.elem = c.dm.elem;
+    return kv;
+}
+
+#define WS(type, field) reinterpret_cast<type>(c.ws + c.lay.field)
+
+template <typename T>
+static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, float* logits, int32_t* tokens,
+                                hipStream_t s) {
+    const Dims& d = c.dm;
+    const int H = d.H, B = d.B, nq = d.nq, nkv = d.nkv, D = d.d, F = d.F;
+    T* x = WS(T*, x);
+    T* q = WS(T*, q);
+    T* kblk = WS(T*, kblk);
+    T* vblkT = WS(T*, vblkT);
+    T* obuf = WS(T*, obuf);
+    T* hbuf = WS(T*, hbuf);
+    float* rstd = WS(float*, rstd);
+    float* ss = WS(float*, ss_part);
+    unsigned long long* best = WS(unsigned long long*, best);
+    unsigned* counters = WS(unsigned*, counters);
+    const float* cosT = WS(const float*, rope_cos);
+    const float* sinT = WS(const float*, rope_sin);
+    const float eps = (float)d.eps;
+    hipError_t e;
+
+    hipLaunchKernelGGL((embed_kernel<T>), dim3(B), dim3(256), 0, s, (const T*)c.embed, anchor, d.mask_id, d.V, H, eps, x,
+                       rstd, best);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    int kps, ns;
+    attn_split_plan(C, nkv, c.num_cus, &kps, &ns);
+    const int group = nq / nkv;
+
+    for (int l = 0; l < d.Ld; ++l) {
+        OpQKV<T> qkv;
+        qkv.a = NormA<T>{x, H, rstd, (const T*)c.attn_norm[l]};
+        qkv.wq = (const T*)c.wq[l];
+        qkv.wk = (const T*)c.wk[l];
+        qkv.wv = (const T*)c.wv[l];
+        qkv.H = H;
+        qkv.nq = nq;
+        qkv.nkv = nkv;
+        qkv.d = D;
+        qkv.M = B;
+        qkv.pos0 = C;
+        qkv.tq = nq * D / 32;
+        qkv.tk = nkv * D / 32;
+        qkv.cosT = cosT;
+        qkv.sinT = sinT;
+        qkv.qout = q;
+        qkv.kout = kblk;
+        qkv.vTout = vblkT;
+        c.tracer->begin(DFLASH_TRACE_QKV, s);
+        if ((e = run_skinny<T>(c, qkv, B, H, qkv.tq + 2 * qkv.tk, s)) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_QKV, s);
+
+        AttnArgs aa;
+        aa.q = q;
+        aa.kblk = kblk;
+        aa.vblkT = vblkT;
+        aa.kv = make_pages<T>(c);
+        aa.layer = l;
+        aa.C = C;
+        aa.B = B;
+        aa.nq = nq;
+        aa.nkv = nkv;
+        aa.group = group;
+        aa.kps = kps;
+        aa.n_splits = ns;
+        aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+        aa.part_o = WS(float*, attn_o);
+        aa.part_ml = WS(float*, attn_ml);
+        c.tracer->begin(DFLASH_TRACE_ATTN, s);
+        if (D == 128)
+            hipLaunchKernelGGL((attn_split_kernel<T, 128>), dim3(ns + 1, nkv), dim3(64 * group), 0, s, aa);
+        else
+            hipLaunchKernelGGL((attn_split_kernel<T, 64>), dim3(ns + 1, nkv), dim3(64 * group), 0, s, aa);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(128), 0, s, aa.part_o, aa.part_ml, ns + 1, nq,
+                           D, B, obuf);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_ATTN, s);
+
+        OpResid<T> op;
+        op.a = PlainA<T>{obuf, (long long)nq * D};
+        op.w = (const T*)c.wo[l];
+        op.N = H;
+        op.K = nq * D;
+        op.M = B;
+        op.x = x;
+        op.ss_part = ss;
+        op.rstd_out = rstd;
+        op.eps = eps;
+        c.tracer->begin(DFLASH_TRACE_O_PROJ, s);
+        if ((e = run_skinny<T>(c, op, B, nq * D, (H + 31) / 32, s)) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_O_PROJ, s);
+
+        OpSwiGLU<T> sw;
+        sw.a = NormA<T>{x, H, rstd, (const T*)c.mlp_norm[l]};
+        sw.wg = (const T*)c.wg[l];
+        sw.wu = (const T*)c.wu[l];
+        sw.F = F;
+        sw.K = H;
+        sw.M = B;
+        sw.h = hbuf;
+        c.tracer->begin(DFLASH_TRACE_GATE_UP, s);
+        if ((e = run_skinny<T>(c, sw, B, H, F / 16, s)) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_GATE_UP, s);
+
+        OpResid<T> dn;
+        dn.a = PlainA<T>{hbuf, (long long)F};
+        dn.w = (const T*)c.wd[l];
+        dn.N = H;
+        dn.K = F;
+        dn.M = B;
+        dn.x = x;
+        dn.ss_part = ss;
+        dn.rstd_out = rstd;
+        dn.eps = eps;
+        c.tracer->begin(DFLASH_TRACE_DOWN, s);
+        if ((e = run_skinny<T>(c, dn, B, F, (H + 31) / 32, s)) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_DOWN, s);
+    }
+
+    OpLMHead<T> lm;
+    lm.a = NormA<T>{x, H, rstd, (const T*)c.final_norm};
+    lm.w = (const T*)c.lm_head;
+    lm.V = d.V;
+    lm.K = H;
+    lm.M = B;
+    lm.logits = logits;
+    lm.best = best;
+    lm.wg_cnt = counters + 1;
+    lm.tokens = tokens;
+    c.tracer->begin(DFLASH_TRACE_LM_HEAD, s);
+    if ((e = run_skinny<T>(c, lm, B, H, (d.V + 31) / 32, s)) != hipSuccess) return e;
+    c.tracer->end(DFLASH_TRACE_LM_HEAD, s);
+    return hipSuccess;
+}
+
+hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits, int32_t* tokens,
+                              hipStream_t s) {
+    c.tracer->begin(DFLASH_TRACE_DRAFT, s);
+    hipError_t e = c.dm.dtype == DFLASH_F32 ? draft_block_t<float>(c, C, anchor, logits, tokens, s)
+                                            : draft_block_t<bf16_t>(c, C, anchor, logits, tokens, s);
+    if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_DRAFT, s);
+    return e;
+}
+
+template <typename T>
+static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out, hipStream_t s) {
+    const int H = c.dm.H;
+    SlabA<T> sa;
+    for (int i = 0; i < 5; ++i) sa.slab[i] = (const T*)slabs[i];
+    sa.ld = ld;
+    sa.H = H;
+    hipError_t e;
+    if (M <= 16) {
+        OpFuse<T> op;
+        op.a = sa;
+        op.w = (const T*)c.fc;
+        op.H = H;
+        op.K = 5 * H;
+        op.M = M;
+        op.out = (T*)out;
+        c.tracer->begin(DFLASH_TRACE_FUSE, s);
+        if ((e = run_skinny<T>(c, op, M, 5 * H, (H + 31) / 32, s)) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_FUSE, s);
+    } else {
+        BigFuseOp<T> op;
+        op.a = sa;
+        op.w = (const T*)c.fc;
+        op.H = H;
+        op.out = (T*)out;
+        c.tracer->begin(DFLASH_TRACE_FUSE, s);
+        hipLaunchKernelGGL((big_gemm_kernel<T, BigFuseOp<T>>), dim3((H + 63) / 64, (M + 63) / 64), dim3(256), 0, s, op,
+                           M, H, 5 * H);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_FUSE, s);
+    }
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M), dim3(256), 0, s, (T*)out, H, (const T*)c.fc_norm,
+                       (float)c.dm.eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_fuse(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out, hipStream_t s) {
+    if (c.dm.dtype == DFLASH_F32) return fuse_t<float>(c, slabs, ld, M, out, s);
+    return fuse_t<bf16_t>(c, slabs, ld, M, out, s);
+}
+
+template <typename T>
+static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s) {
+    const Dims& d = c.dm;
+    const float* cosT = WS(const float*, rope_cos);
+    const float* sinT = WS(const float*, rope_sin);
+    if (M <= 16) {
+        OpInject<T> op;
+        op.a = PlainA<T>{(const T*)fused, ld};
+        for (int l = 0; l < d.Ld; ++l) {
+            op.wk[l] = (const T*)c.wk[l];
+            op.wv[l] = (const T*)c.wv[l];
+        }
+        op.H = d.H;
+        op.nkv = d.nkv;
+        op.d = d.d;
+        op.M = M;
+        op.pos0 = pos0;
+        op.cosT = cosT;
+        op.sinT = sinT;
+        op.kv = make_pages<T>(c);
+        c.tracer->begin(DFLASH_TRACE_INJECT, s);
+        hipError_t e = run_skinny<T>(c, op, M, d.H, d.Ld * 2 * d.nkv * d.d / 32, s);
+        if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_INJECT, s);
+        return e;
+    }
+    BigInjectOp<T> op;
+    op.a = PlainA<T>{(const T*)fused, ld};
+    for (int l = 0; l < d.Ld; ++l) {
+        op.wk[l] = (const T*)c.wk[l];
+        op.wv[l] = (const T*)c.wv[l];
+    }
+    op.H = d.H;
+    op.nkv = d.nkv;
+    op.d = d.d;
+    op.pos0 = pos0;
+    op.cosT = cosT;
+    op.sinT = sinT;
+    op.kv = make_pages<T>(c);
+    const int N = d.Ld * 2 * d.nkv * d.d;
+    c.tracer->begin(DFLASH_TRACE_INJECT, s);
+    hipLaunchKernelGGL((big_gemm_kernel<T, BigInjectOp<T>>), dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, op, M,
+                       N, d.H);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_INJECT, s);
+    return e;
+}
+
+hipError_t launch_inject(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s) {
+    if (c.dm.dtype == DFLASH_F32) return inject_t<float>(c, fused, ld, M, pos0, s);
+    return inject_t<bf16_t>(c, fused, ld, M, pos0, s);
+}
+
+hipError_t launch_accept(const DevCtx& c, const int32_t* draft, const int32_t* target, int32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, s, draft, target, c.dm.B, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_copy(const DevCtx& c, void* k, void* v, int M, int pos0, bool to_pages, hipStream_t s) {
+    const long long total = (long long)c.dm.Ld * M * c.dm.nkv * c.dm.d;
+    int grid = (int)std::min<long long>((total + 255) / 256, 65536);
+    if (grid < 1) grid = 1;
+    if (c.dm.dtype == DFLASH_F32)
+        hipLaunchKernelGGL((kv_copy_kernel<float>), dim3(grid), dim3(256), 0, s, make_pages<float>(c), (float*)k,
+                           (float*)v, M, pos0, c.dm.Ld, to_pages);
+    else
+        hipLaunchKernelGGL((kv_copy_kernel<bf16_t>), dim3(grid), dim3(256), 0, s, make_pages<bf16_t>(c), (bf16_t*)k,
+                           (bf16_t*)v, M, pos0, c.dm.Ld, to_pages);
+    return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,224 @@
+/*
+ * dflash.h -- C ABI of libdflash: the DFlash single-pass block-diffusion draft
+ * with KV injection and greedy block verification, on one AMD MI355X (gfx950).
+ *
+ * Method sources (web pages):
+ *  [A] "DFlash 深度解析：块扩散模型如何让 LLM 推理加速 6 倍——2026 投机解码完全指南"
+ *      (chenxutan.com/d/2993): §2.2 feature fusion, KV injection, block draft;
+ *      §3.3 shared embedding and LM head; §5.1-5.2; §8.2 linear verification.
+ *  [B] "从 ICML 论文到你的显卡：llama.cpp 吞下 DFlash，本地推理进入 2 倍速时代"
+ *      (arex-research.com), section 技术内幕: accept up to the first error;
+ *      injected K/V live in the draft's KV cache of every layer.
+ *  [C] "我在llama.cpp中测试了最新合并的DFlash在Qwen 3.6 27B本地AI上的表现…"
+ *      (bittide.aicompass.dev): one pass fills a 15-token block; greedy is lossless.
+ *
+ * Conventions shared by every call:
+ *  - Status: every call returns a dflash_status; 0 is success, negative values
+ *    are errors.  On an error nothing is enqueued and the context is unchanged;
+ *    dflash_last_error() gives a message.  No call aborts or throws.
+ *  - Pointers: "device" pointers are HIP device memory on the context's GPU;
+ *    "host" pointers are ordinary host memory.  The caller owns every buffer;
+ *    the library borrows them until the work enqueued on `stream` completes.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Device work is asynchronous on it; argument checks are host-side
+ *    and synchronous.  One context must not be used from two streams at once.
+ *  - Layouts: matrices are row-major [out_features, in_features]; activations
+ *    are row-major [rows, features] with a row stride `ld` in elements.
+ *  - Element type: every floating-point tensor a context touches has the
+ *    context's dtype (fp32 or bf16), except logits (always fp32).
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_MAX_LAYERS 64
+#define DFLASH_NUM_FEATURES 5
+#define DFLASH_MAX_BLOCK 16
+
+typedef enum {
+    DFLASH_OK = 0,
+    DFLASH_ERR_INVAL = -1,       /* bad argument, shape or pointer */
+    DFLASH_ERR_CAPACITY = -2,    /* would exceed max_ctx / max_rows / workspace */
+    DFLASH_ERR_HIP = -3,         /* a HIP runtime call failed (message has the HIP string) */
+    DFLASH_ERR_UNSUPPORTED = -4, /* shape or dtype outside what the kernels handle */
+    DFLASH_ERR_STATE = -5        /* call out of order (e.g. inject at pos0 != length) */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Model and capacity description.  All fields are required. */
+typedef struct {
+    int32_t dtype;          /* dflash_dtype */
+    int32_t hidden;         /* H: target and draft hidden size (multiple of 32) */
+    int32_t target_layers;  /* target decoder layers (>= 8); 5 of them feed the fusion */
+    int32_t draft_layers;   /* Ld, 1..DFLASH_MAX_LAYERS */
+    int32_t n_q_heads;      /* nq, multiple of n_kv_heads */
+    int32_t n_kv_heads;     /* nkv */
+    int32_t head_dim;       /* d: 64 or 128 */
+    int32_t ffn;            /* F: SwiGLU width (multiple of 16) */
+    int32_t vocab;          /* V: shared vocabulary (multiple of 16) */
+    int32_t block;          /* B: draft block length, 2..16 (1 anchor + B-1 masks) */
+    int32_t mask_id;        /* token id of the mask token, 0 <= mask_id < V */
+    int32_t page_size;      /* tokens per KV page: 256 (multiple of 64) */
+    int32_t max_ctx;        /* capacity of the draft KV cache in tokens */
+    int32_t max_rows;       /* largest M accepted by fuse/inject in one call */
+    double rope_base;       /* rotary base theta (e.g. 10000) */
+    double eps;             /* RMSNorm epsilon (e.g. 1e-6) */
+    uint64_t page_seed;     /* 0: identity page table; else a seeded shuffle of physical pages */
+} dflash_config;
+
+/* Device pointers to the weights (borrowed for the context's lifetime).
+ * Unused entries may be NULL: a context used only for fuse/inject needs
+ * fc, fc_norm, wk and wv; the draft additionally needs the rest. */
+typedef struct {
+    const void* fc;          /* [H, 5H] context fusion Linear (no bias) */
+    const void* fc_norm;     /* [H] RMSNorm gain after the fusion */
+    const void* attn_norm[DFLASH_MAX_LAYERS]; /* [H] pre-attention RMSNorm gain */
+    const void* wq[DFLASH_MAX_LAYERS];        /* [nq*d, H] */
+    const void* wk[DFLASH_MAX_LAYERS];        /* [nkv*d, H]: block keys AND injected context keys */
+    const void* wv[DFLASH_MAX_LAYERS];        /* [nkv*d, H]: block values AND injected values */
+    const void* wo[DFLASH_MAX_LAYERS];        /* [H, nq*d] */
+    const void* mlp_norm[DFLASH_MAX_LAYERS];  /* [H] pre-MLP RMSNorm gain */
+    const void* wg[DFLASH_MAX_LAYERS];        /* [F, H] SwiGLU gate */
+    const void* wu[DFLASH_MAX_LAYERS];        /* [F, H] SwiGLU up */
+    const void* wd[DFLASH_MAX_LAYERS];        /* [H, F] down */
+    const void* final_norm;  /* [H] */
+    const void* embed;       /* [V, H] shared with the target ([A] §3.3) */
+    const void* lm_head;     /* [V, H] shared with the target ([A] §3.3) */
+} dflash_weights;
+
+typedef struct dflash_ctx dflash_ctx;
+
+/* Human-readable name of a status code (static string). */
+const char* dflash_status_str(int status);
+
+/* Message of the last failed call on ctx (static empty string if none / ctx NULL). */
+const char* dflash_last_error(const dflash_ctx* ctx);
+
+/* The five target layers (0-based decoder-layer outputs, ascending) whose
+ * hidden states feed the fusion: spaced uniformly from the second layer to the
+ * third-from-last output, rounded half up ([A] §2.2 feature-fusion
+ * pseudocode).  out: host int32[5].  INVAL if target_layers < 8. */
+dflash_status dflash_feature_layers(int32_t target_layers, int32_t* out);
+
+/* Physical page of each logical page of the draft KV cache (introspection of the
+ * cache layout; pure host computation).  out: host int32[n], n >= number of
+ * pages = ceil(max_ctx / page_size).  Each (layer, K|V) page array holds pages
+ * of page_size positions: K pages are [nkv][page_size][d], V pages
+ * [nkv][d][page_size]; the KV pool is [Ld][K,V][pages]. */
+dflash_status dflash_page_table(const dflash_config* cfg, int32_t* out, int32_t n);
+
+/* Device memory the caller must provide to dflash_create: `workspace_bytes` of
+ * scratch (activations, partial sums, rotary table, page table, counters) and
+ * `kv_bytes` for the paged draft KV cache.  Pure host computation; INVAL or
+ * UNSUPPORTED if the config is not valid. */
+dflash_status dflash_workspace_size(const dflash_config* cfg, size_t* workspace_bytes, size_t* kv_bytes);
+
+/* Create a context.  `workspace` and `kv_pool` are device buffers of at least
+ * the sizes above (256-byte aligned); they and the weights stay borrowed until
+ * dflash_destroy.  The library never allocates device memory itself.  Fills the
+ * rotary table (fp64 angles, fp32 cos/sin) and the page table and zeroes the
+ * counters, enqueued on `stream`.  Length starts at 0. */
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
+                            void* workspace, size_t workspace_bytes,
+                            void* kv_pool, size_t kv_bytes,
+                            void* stream, dflash_ctx** out);
+
+/* Destroy a context (host state only; the caller frees its buffers). NULL is a no-op. */
+dflash_status dflash_destroy(dflash_ctx* ctx);
+
+/* Current draft-KV length: number of context positions injected and kept. */
+int32_t dflash_length(const dflash_ctx* ctx);
+
+/* Context fusion ([A] §2.2 feature fusion; [B] KV Injection):
+ *   fused[i] = RMSNorm_fc( W_fc . concat(h_{s0}[i], ..., h_{s4}[i]) ),  i < M
+ * where s0..s4 = dflash_feature_layers(target_layers).
+ * layer_hidden: host array of target_layers device pointers; entry l points at
+ *   target layer l's hidden states [M, H] with row stride ld (elements).  Only
+ *   the five selected entries are read; the others may be NULL.
+ * fused_out: device [M, H], row stride H.  1 <= M <= max_rows. */
+dflash_status dflash_fuse_context(dflash_ctx* ctx, const void* const* layer_hidden, int64_t ld,
+                                  int32_t M, void* fused_out, void* stream);
+
+/* KV injection ([A] §2.2 kv_injection, §5.2; [B] KV Injection): for every draft
+ * layer l and row i < M,
+ *   K_l[pos0+i] = RoPE(W_k^l . fused[i], pos0+i),  V_l[pos0+i] = W_v^l . fused[i]
+ * written into the paged draft KV cache.  fused: device [M, H], row stride ld.
+ * Requires pos0 == dflash_length(ctx) (STATE otherwise) and pos0 + M <= max_ctx
+ * (CAPACITY otherwise; nothing written).  Afterwards length = pos0 + M. */
+dflash_status dflash_inject_kv(dflash_ctx* ctx, const void* fused, int64_t ld,
+                               int32_t M, int32_t pos0, void* stream);
+
+/* One block-diffusion draft pass ([A] §2.2 draft_inference, §5.1; [B] 技术内幕; [C]):
+ * rows [anchor, mask x (B-1)] at positions C..C+B-1 (C = current length) are
+ * embedded with the shared embedding, run through every draft layer attending
+ * without a mask to all C injected context keys and all B block keys, then the
+ * final RMSNorm, the shared LM head and a per-row argmax (ties: lowest id).
+ * anchor: device int32[1] (an id outside [0, V) is clamped into it).  tokens_out: device int32[B]; entry j >= 1 is the
+ * draft for position C+j (entry 0 is the anchor row's own argmax, unused by
+ * verification).  logits_out: device fp32 [B, V] or NULL.
+ * Requires all draft weights; INVAL otherwise.  Context is not modified. */
+dflash_status dflash_draft_block(dflash_ctx* ctx, const int32_t* anchor, float* logits_out,
+                                 int32_t* tokens_out, void* stream);
+
+/* Greedy block verification ([B] 技术内幕; [A] §1.2, §8.2 linear verification):
+ *   k = number of leading j in 1..B-1 with draft[j] == target[j-1],  bonus = target[k].
+ * draft: device int32[B] (as written by dflash_draft_block); target: device
+ * int32[B], target[j] = the target's greedy token for position C+j+1.
+ * result_out: device int32[2] = {k, bonus}.  The emitted tokens are
+ * draft[1..k] followed by bonus. */
+dflash_status dflash_verify_accept(dflash_ctx* ctx, const int32_t* draft, const int32_t* target,
+                                   int32_t* result_out, void* stream);
+
+/* Roll the draft KV cache back to new_len tokens (0 <= new_len <= length, INVAL
+ * otherwise): after injecting the B verified rows of a step at C, the caller
+ * rolls back to C + k + 1 so only the anchor and the accepted drafts remain
+ * as context.  Host metadata only; pages past new_len become free. */
+dflash_status dflash_rollback(dflash_ctx* ctx, int32_t new_len);
+
+/* Load already-rotated K and V for positions [pos0, pos0+M) of every layer
+ * (restoring a saved cache, or K/V computed elsewhere).  k, v: device
+ * [Ld, M, nkv, d] contiguous.  Same pos0/capacity rules as dflash_inject_kv. */
+dflash_status dflash_load_kv(dflash_ctx* ctx, const void* k, const void* v,
+                             int32_t M, int32_t pos0, void* stream);
+
+/* Read K and V of positions [pos0, pos0+M) (pos0 + M <= length) of every layer
+ * into device k_out, v_out [Ld, M, nkv, d] contiguous. */
+dflash_status dflash_read_kv(dflash_ctx* ctx, int32_t pos0, int32_t M,
+                             void* k_out, void* v_out, void* stream);
+
+/* Kernel classes that can be traced with dflash_trace_enable. */
+typedef enum {
+    DFLASH_TRACE_OFF = 0,
+    DFLASH_TRACE_LM_HEAD = 1,  /* LM head + argmax launch of dflash_draft_block */
+    DFLASH_TRACE_GATE_UP = 2,  /* SwiGLU gate/up projection, every layer */
+    DFLASH_TRACE_DOWN = 3,     /* down projection + residual, every layer */
+    DFLASH_TRACE_QKV = 4,      /* q/k/v projection + rotary, every layer */
+    DFLASH_TRACE_O_PROJ = 5,   /* attention output projection + residual, every layer */
+    DFLASH_TRACE_ATTN = 6,     /* split-KV attention + merge, every layer */
+    DFLASH_TRACE_DRAFT = 7,    /* the whole dflash_draft_block call */
+    DFLASH_TRACE_FUSE = 8,     /* fusion GEMM of dflash_fuse_context (without its RMSNorm) */
+    DFLASH_TRACE_INJECT = 9    /* injection of dflash_inject_kv */
+} dflash_trace_class;
+
+/* Tracing aid: while enabled, every launch of the given kernel class is
+ * bracketed by a pair of HIP events recorded on its stream, for up to
+ * max_launches launches (later ones are not timed).  Enabling again (or with
+ * DFLASH_TRACE_OFF) discards previous records.  Events are host-side HIP
+ * objects; no device memory is allocated. */
+dflash_status dflash_trace_enable(dflash_ctx* ctx, int32_t kernel_class, int32_t max_launches);
+
+/* Wait for the recorded events and report the summed duration (ms) of the
+ * timed launches and their count.  Host pointers. */
+dflash_status dflash_trace_read(dflash_ctx* ctx, double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
