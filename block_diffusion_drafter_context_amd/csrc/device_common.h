@@ -90,6 +90,19 @@ __device__ __forceinline__ void mma(f32x4_t& acc, const Frag<float>& a, const Fr
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, acc, 0, 0, 0);
 }
 
+// Device-coherent (agent scope) accesses for data one workgroup hands to
+// another inside a kernel.  They carry the scope bits that make the access
+// coherent across the XCDs' L2s, so no L2 writeback / invalidate fence is
+// needed; wait_vmem() orders them before a following atomic.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
 // sum / max over the 16 lanes that share a lane group (same l / 16)

@@ -27,7 +27,7 @@ dflash_status validate_config(const dflash_config* c, Dims* o, std::string* err)
     if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads)
         return fail(DFLASH_ERR_INVAL, "n_q_heads must be a positive multiple of n_kv_heads");
-    if (c->n_q_heads / c->n_kv_heads > 16) return fail(DFLASH_ERR_UNSUPPORTED, "at most 16 query heads per kv head");
+    if (c->n_q_heads / c->n_kv_heads > 8) return fail(DFLASH_ERR_UNSUPPORTED, "at most 8 query heads per kv head");
     if (c->ffn <= 0 || c->ffn % 16) return fail(DFLASH_ERR_UNSUPPORTED, "ffn must be a positive multiple of 16");
     if (c->vocab <= 0 || c->vocab % 16) return fail(DFLASH_ERR_UNSUPPORTED, "vocab must be a positive multiple of 16");
     if (c->block < 2 || c->block > DFLASH_MAX_BLOCK) return fail(DFLASH_ERR_INVAL, "block must be in [2, 16]");

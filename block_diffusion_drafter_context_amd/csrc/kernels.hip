@@ -162,35 +162,36 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) mine[b * 256 + ii * 64 + lane] = acc[b][ii];
-            __threadfence();
+                for (int ii = 0; ii < 4; ++ii) st_agent(mine + b * 256 + ii * 64 + lane, acc[b][ii]);
+            wait_vmem();
             const int w_first = (int)(tbeg / c.per_wave);
             const int w_last = (int)((tbeg + c.nchunks - 1) / c.per_wave);
             unsigned old = 0;
             if (lane == 0) old = atomicAdd(&c.tile_cnt[tile], 1u);
             old = __shfl(old, 0, 64);
             if (old != (unsigned)(w_last - w_first)) continue;
-            __threadfence();
+            compiler_fence();
             acc[0] = zero4();
             acc[1] = zero4();
             for (int w = w_first; w <= w_last; ++w) {
                 const int ft = (int)(((long long)w * c.per_wave) / c.nchunks);
                 const float* src = c.partial + ((long long)w * 2 + (ft == tile ? 0 : 1)) * (kSkinnyNT * 256);
+                float v[8];
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int q = 0; q < 8; ++q) v[q] = ld_agent(src + (q >> 2) * 256 + (q & 3) * 64 + lane);
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) acc[b][ii] += __builtin_nontemporal_load(src + b * 256 + ii * 64 + lane);
+                for (int q = 0; q < 8; ++q) acc[q >> 2][q & 3] += v[q];
             }
             if (lane == 0) atomicExch(&c.tile_cnt[tile], 0u);
         }
         op.epilogue(tile, acc, lane, st);
         if (Op::kDoneHook) {
-            __threadfence();
+            wait_vmem();
             unsigned old = 0;
             if (lane == 0) old = atomicAdd(c.done_cnt, 1u);
             old = __shfl(old, 0, 64);
             if (old == (unsigned)(c.ntiles - 1)) {
-                __threadfence();
+                compiler_fence();
                 op.done_hook(lane, c.ntiles);
                 if (lane == 0) atomicExch(c.done_cnt, 0u);
             }
@@ -307,14 +308,23 @@ struct OpResid {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const float s = group16_sum(sq[ii]);
-            if ((lane & 15) == 0) ss_part[tile * 16 + 4 * (lane >> 4) + ii] = s;
+            if ((lane & 15) == 0) st_agent(ss_part + tile * 16 + 4 * (lane >> 4) + ii, s);
         }
     }
     __device__ __forceinline__ void done_hook(int lane, int ntiles) const {
         // lane handles row j = lane & 15 over tiles t = g, g+4, ... (g = lane >> 4)
         const int j = lane & 15, g = lane >> 4;
         float s = 0.f;
-        for (int t = g; t < ntiles; t += 4) s += __builtin_nontemporal_load(ss_part + t * 16 + j);
+        int t = g;
+        for (; t + 12 < ntiles; t += 16) {  // four independent loads in flight
+            const float a0 = ld_agent(ss_part + t * 16 + j), a1 = ld_agent(ss_part + (t + 4) * 16 + j);
+            const float a2 = ld_agent(ss_part + (t + 8) * 16 + j), a3 = ld_agent(ss_part + (t + 12) * 16 + j);
+            s += a0;
+            s += a1;
+            s += a2;
+            s += a3;
+        }
+        for (; t < ntiles; t += 4) s += ld_agent(ss_part + t * 16 + j);
         s += __shfl_xor(s, 16, 64);
         s += __shfl_xor(s, 32, 64);
         if (lane < 16) rstd_out[j] = 1.0f / sqrtf(s / (float)N + eps);
@@ -430,8 +440,8 @@ struct OpLMHead {
                 const unsigned long long key = ((unsigned long long)ordered_bits(v) << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)id);
                 atomicMax(best + j, key);
             }
+            wait_vmem();
         }
-        __threadfence();
         __syncthreads();
         if (threadIdx.x == 0) {
             const unsigned old = atomicAdd(wg_cnt, 1u);
@@ -439,7 +449,7 @@ struct OpLMHead {
         }
         __syncthreads();
         if (__float_as_uint(sv[0][0]) == 1u) {
-            __threadfence();
+            compiler_fence();
             if (threadIdx.x < 16) {
                 const int j = threadIdx.x;
                 if (j < M) {
@@ -601,12 +611,45 @@ struct AttnArgs {
     float* part_ml;     // [(n_splits+1)][nq][16][2]
 };
 
+// Four consecutive positions of one V^T row (one half of a P.V operand slot set).
+template <typename T> struct VRun;
+template <> struct VRun<bf16_t> {
+    uint2 v;
+    __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ void load_masked(const bf16_t* p, int n_ok) {
+        uint32_t e[4];
+        for (int i = 0; i < 4; ++i) e[i] = i < n_ok ? p[i] : 0u;
+        v = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+    }
+};
+template <> struct VRun<float> {
+    float4 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+    __device__ __forceinline__ void load_masked(const float* p, int n_ok) {
+        float e[4];
+        for (int i = 0; i < 4; ++i) e[i] = i < n_ok ? p[i] : 0.f;
+        v = make_float4(e[0], e[1], e[2], e[3]);
+    }
+};
+__device__ __forceinline__ Frag<bf16_t> join_runs(const VRun<bf16_t>& a, const VRun<bf16_t>& b) {
+    Frag<bf16_t> f;
+    f.v = make_uint4(a.v.x, a.v.y, b.v.x, b.v.y);
+    return f;
+}
+__device__ __forceinline__ Frag<float> join_runs(const VRun<float>& a, const VRun<float>& b) {
+    Frag<float> f;
+    f.a = a.v;
+    f.b = b.v;
+    return f;
+}
+
 // One workgroup = one (split, kv head); one wave per query head of the group.
 // Scores are formed transposed, S^T = K Q^T (keys on MFMA rows, the 16 block
 // rows on columns), so that the probabilities land exactly in the B-operand
-// layout of O^T += V^T P^T and never leave registers.
+// layout of O^T += V^T P^T and never leave registers.  All K and V loads of a
+// 64-key chunk are issued before any arithmetic on it.
 template <typename T, int D>
-__global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = blockIdx.y, split = blockIdx.x;
     const int hq = g * a.group + w;
@@ -629,7 +672,6 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
     const int kend = ctx ? min(a.C, kbeg + a.kps) : a.B;
 
     for (int key0 = kbeg; key0 < kend; key0 += kAttnChunk) {
-        // ---- S^T for 64 keys (4 blocks of 16)
         const T* kbase;
         long long krow_stride;
         const T* vbase;
@@ -646,19 +688,36 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
             vbase = reinterpret_cast<const T*>(a.vblkT) + (long long)g * D * 16;
             vrow_stride = 16;
         }
+        const int nvalid = kend - key0;  // keys of this chunk that exist (may exceed 64)
+        // ---- issue every load of the chunk
+        Frag<T> kf[4][D / 32];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const bool ok = kb * 16 + col < nvalid;
+#pragma unroll
+            for (int kc = 0; kc < D / 32; ++kc) {
+                if (ok) kf[kb][kc].load(kbase + (long long)(kb * 16 + col) * krow_stride + kc * 32 + grp * 8);
+                else kf[kb][kc].zero();
+            }
+        }
+        VRun<T> va[2][D / 16], vb[2][D / 16];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int oa = 32 * t + 4 * grp, ob = oa + 16;  // chunk offsets of the two runs
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) {
+                const T* vr = vbase + (long long)(16 * db + col) * vrow_stride;
+                if (oa + 4 <= nvalid) va[t][db].load(vr + oa); else va[t][db].load_masked(vr + oa, nvalid - oa);
+                if (ob + 4 <= nvalid) vb[t][db].load(vr + ob); else vb[t][db].load_masked(vr + ob, nvalid - ob);
+            }
+        }
+        // ---- S^T for 64 keys (4 blocks of 16)
         f32x4_t s[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             s[kb] = zero4();
-            const int key = key0 + kb * 16 + col;
-            const bool ok = key < kend;
 #pragma unroll
-            for (int kc = 0; kc < D / 32; ++kc) {
-                Frag<T> kf;
-                if (ok) kf.load(kbase + (long long)(kb * 16 + col) * krow_stride + kc * 32 + grp * 8);
-                else kf.zero();
-                mma(s[kb], kf, qf[kc]);
-            }
+            for (int kc = 0; kc < D / 32; ++kc) mma(s[kb], kf[kb][kc], qf[kc]);
         }
         // ---- online softmax (log2 domain); lane column = query row `col`
         float mx = m;
@@ -667,8 +726,8 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const int key = key0 + kb * 16 + 4 * grp + ii;
-                p[kb][ii] = key < kend ? s[kb][ii] * a.scale_log2 : -INFINITY;
+                const int kk = kb * 16 + 4 * grp + ii;
+                p[kb][ii] = kk < nvalid ? s[kb][ii] * a.scale_log2 : -INFINITY;
                 mx = fmaxf(mx, p[kb][ii]);
             }
         mx = cross4_max(mx);
@@ -678,7 +737,7 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const float e = Elem<T>::round(exp2f(p[kb][ii] - mx));
+                const float e = exp2f(p[kb][ii] - mx);
                 p[kb][ii] = e;
                 ps += e;
             }
@@ -688,29 +747,31 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
         // ---- O^T += V^T P^T, 32 keys per MFMA: slots 0-3 = keys 4grp..4grp+3 of
-        //      block 2t, slots 4-7 = the same keys of block 2t+1
+        //      block 2t, slots 4-7 = the same keys of block 2t+1.  For bf16 the
+        //      probabilities enter as a hi + lo pair of bf16 values (two MFMAs
+        //      sharing the V operand), so P keeps ~16 significant bits.
+        constexpr bool kSplitP = sizeof(T) == 2;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            Frag<T> pf;
-            float pv[8];
+            Frag<T> pf, pf_lo;
+            float pv[8], pl[8];
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) { pv[ii] = p[2 * t][ii]; pv[4 + ii] = p[2 * t + 1][ii]; }
+            if (kSplitP) {
+#pragma unroll
+                for (int q8 = 0; q8 < 8; ++q8) {
+                    const float hi = Elem<T>::round(pv[q8]);
+                    pl[q8] = pv[q8] - hi;
+                    pv[q8] = hi;
+                }
+                pf_lo.set8(pl);
+            }
             pf.set8(pv);
-            const int ka = key0 + 32 * t + 4 * grp;      // first run of 4 keys
-            const int kb2 = ka + 16;                     // second run
-            const bool oka = ka < kend, okb = kb2 < kend;  // runs never straddle kend except the block tail
 #pragma unroll
             for (int db = 0; db < D / 16; ++db) {
-                const T* vr = vbase + (long long)(16 * db + col) * vrow_stride + (32 * t + 4 * grp);
-                float vv[8];
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    vv[ii] = (oka && ka + ii < kend) ? Elem<T>::to_f32(vr[ii]) : 0.f;
-                    vv[4 + ii] = (okb && kb2 + ii < kend) ? Elem<T>::to_f32(vr[16 + ii]) : 0.f;
-                }
-                Frag<T> vf;
-                vf.set8(vv);
+                const Frag<T> vf = join_runs(va[t][db], vb[t][db]);
                 mma(o[db], vf, pf);
+                if (kSplitP) mma(o[db], vf, pf_lo);
             }
         }
     }
@@ -728,22 +789,64 @@ __global__ __launch_bounds__(1024) void attn_split_kernel(AttnArgs a) {
 }
 
 // out[j][hq*d + dim] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s   (rounded)
+// One workgroup per (query head, block row): the split weights are formed once
+// in LDS, then 4 groups of D threads each sum a quarter of the splits.
 template <typename T>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* part_o, const float* part_ml, int n_parts,
+__global__ __launch_bounds__(512) void attn_merge_kernel(const float* part_o, const float* part_ml, int n_parts,
                                                          int nq, int d, int B, T* out) {
+    __shared__ float wgt[kMaxSplits + 1];
+    __shared__ float red[4][128];
+    __shared__ float stat[2];
     const int hq = blockIdx.x / 16, j = blockIdx.x % 16;
     if (j >= B) return;
-    const int dim = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < n_parts; ++s) M = fmaxf(M, part_ml[(((long long)s * nq + hq) * 16 + j) * 2]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < n_parts; ++s) {
-        const long long idx = ((long long)s * nq + hq) * 16 + j;
-        const float wgt = exp2f(part_ml[idx * 2] - M);
-        L += wgt * part_ml[idx * 2 + 1];
-        if (dim < d) acc += wgt * part_o[idx * d + dim];
+    const int tid = threadIdx.x;
+    for (int s = tid; s < n_parts; s += 512) wgt[s] = part_ml[(((long long)s * nq + hq) * 16 + j) * 2];
+    __syncthreads();
+    if (tid < 64) {
+        float M = -INFINITY;
+        for (int s = tid; s < n_parts; s += 64) M = fmaxf(M, wgt[s]);
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        if (tid == 0) stat[0] = M;
     }
-    if (dim < d) out[(long long)j * nq * d + hq * d + dim] = Elem<T>::from_f32(acc / L);
+    __syncthreads();
+    const float M = stat[0];
+    float Lp = 0.f;
+    for (int s = tid; s < n_parts; s += 512) {
+        const float wv = exp2f(wgt[s] - M);
+        Lp += wv * part_ml[(((long long)s * nq + hq) * 16 + j) * 2 + 1];
+        wgt[s] = wv;
+    }
+    // sum of L over the block (fixed order: per-thread partials, then tree)
+    __shared__ float lred[512];
+    lred[tid] = Lp;
+    __syncthreads();
+    for (int o = 256; o >= 1; o >>= 1) {
+        if (tid < o) lred[tid] += lred[tid + o];
+        __syncthreads();
+    }
+    const float L = lred[0];
+    const int grp = tid / 128, dim = tid % 128;
+    float acc = 0.f;
+    if (dim < d) {
+        int s = grp;
+        for (; s + 12 < n_parts; s += 16) {
+            const long long b = ((long long)s * nq + hq) * 16 + j;
+            const long long st = (long long)4 * nq * 16;
+            const float a0 = part_o[b * d + dim], a1 = part_o[(b + st) * d + dim];
+            const float a2 = part_o[(b + 2 * st) * d + dim], a3 = part_o[(b + 3 * st) * d + dim];
+            acc += wgt[s] * a0;
+            acc += wgt[s + 4] * a1;
+            acc += wgt[s + 8] * a2;
+            acc += wgt[s + 12] * a3;
+        }
+        for (; s < n_parts; s += 4) acc += wgt[s] * part_o[(((long long)s * nq + hq) * 16 + j) * d + dim];
+    }
+    red[grp][dim] = acc;
+    __syncthreads();
+    if (grp == 0 && dim < d) {
+        const float v = (red[0][dim] + red[1][dim]) + (red[2][dim] + red[3][dim]);
+        out[(long long)j * nq * d + hq * d + dim] = Elem<T>::from_f32(v / L);
+    }
 }
 
 // ============================================================================
@@ -761,20 +864,30 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 }
 
 // Block rows: embedding of [anchor, mask, ...] and their RMS statistics.
+// 16-byte accesses; every thread's loads are issued before any use.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_t* anchor, int mask_id, int V,
                                                     int H, float eps, T* x, float* rstd, unsigned long long* best) {
     __shared__ float red[4];
     const int j = blockIdx.x;
     const int tok = j == 0 ? min(max(anchor[0], 0), V - 1) : mask_id;  // out-of-range anchors are clamped
-    const T* src = embed + (long long)tok * H;
-    T* dst = x + (long long)j * H;
+    const Frag<T>* src = reinterpret_cast<const Frag<T>*>(embed + (long long)tok * H);
+    Frag<T>* dst = reinterpret_cast<Frag<T>*>(x + (long long)j * H);
+    const int n8 = H / 8;  // H is a multiple of 32
     float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const T v = src[i];
-        dst[i] = v;
-        const float f = Elem<T>::to_f32(v);
-        ss += f * f;
+    constexpr int U = 4;
+    for (int i0 = threadIdx.x; i0 < n8; i0 += 256 * U) {
+        Frag<T> v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * 256 < n8) v[u] = src[i0 + u * 256];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * 256 < n8) {
+                dst[i0 + u * 256] = v[u];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += v[u].get(e) * v[u].get(e);
+            }
     }
     ss = block_sum_256(ss, red);
     if (threadIdx.x == 0) {
@@ -783,20 +896,50 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_
     }
 }
 
-// In-place row RMSNorm: y = round(y * rstd * gain)
+// In-place row RMSNorm: y = round(y * rstd * gain); the row is held in registers.
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(T* y, int H, const T* gain, float eps) {
     __shared__ float red[4];
-    T* row = y + (long long)blockIdx.x * H;
+    Frag<T>* row = reinterpret_cast<Frag<T>*>(y + (long long)blockIdx.x * H);
+    const Frag<T>* gv = reinterpret_cast<const Frag<T>*>(gain);
+    const int n8 = H / 8;
+    constexpr int U = 4;  // rows up to 256 * 4 * 8 = 8192 elements stay in registers
+    Frag<T> v[U];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const float f = Elem<T>::to_f32(row[i]);
-        ss += f * f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = threadIdx.x + u * 256;
+        if (i < n8) v[u] = row[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = threadIdx.x + u * 256;
+        if (i < n8)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[u].get(e) * v[u].get(e);
+    }
+    for (int i = threadIdx.x + U * 256; i < n8; i += 256) {
+        const Frag<T> t = row[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += t.get(e) * t.get(e);
     }
     ss = block_sum_256(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += 256)
-        row[i] = Elem<T>::from_f32(Elem<T>::to_f32(row[i]) * r * Elem<T>::to_f32(gain[i]));
+    auto norm = [&](const Frag<T>& t, int i) {
+        const Frag<T> g = gv[i];
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = t.get(e) * r * g.get(e);
+        Frag<T> f;
+        f.set8(o);
+        row[i] = f;
+    };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = threadIdx.x + u * 256;
+        if (i < n8) norm(v[u], i);
+    }
+    for (int i = threadIdx.x + U * 256; i < n8; i += 256) norm(row[i], i);
 }
 
 // k = leading agreements of draft[1..B-1] with target[0..B-2]; bonus = target[k]
@@ -1050,7 +1193,7 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
         else
             hipLaunchKernelGGL((attn_split_kernel<T, 64>), dim3(ns + 1, nkv), dim3(64 * group), 0, s, aa);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(128), 0, s, aa.part_o, aa.part_ml, ns + 1, nq,
+        hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(512), 0, s, aa.part_o, aa.part_ml, ns + 1, nq,
                            D, B, obuf);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_ATTN, s);

@@ -58,7 +58,7 @@ typedef struct {
     int32_t hidden;         /* H: target and draft hidden size (multiple of 32) */
     int32_t target_layers;  /* target decoder layers (>= 8); 5 of them feed the fusion */
     int32_t draft_layers;   /* Ld, 1..DFLASH_MAX_LAYERS */
-    int32_t n_q_heads;      /* nq, multiple of n_kv_heads */
+    int32_t n_q_heads;      /* nq, multiple of n_kv_heads, at most 8 per kv head */
     int32_t n_kv_heads;     /* nkv */
     int32_t head_dim;       /* d: 64 or 128 */
     int32_t ffn;            /* F: SwiGLU width (multiple of 16) */

@@ -273,11 +273,12 @@ static void decoder_layer(const orc_model* m, int32_t l, double* x, int32_t R, c
                 double den = 0.0;
                 for (int64_t j = 0; j < nvis; ++j) { sc[j] = exp(sc[j] - mx); den += sc[j]; }
                 double* oh = o + r * NQ + (int64_t)h * d;
-                for (int32_t i = 0; i < d; ++i) {
-                    double s = 0.0;
-                    for (int64_t j = 0; j < nvis; ++j) s += sc[j] * kv_get(vs, dt, j, (int64_t)g * d + i, NK);
-                    oh[i] = orc_round(s / den, dt);
-                }
+                /* o_i = sum_j p_j v_{j,i}: every o_i accumulates over keys in index order */
+                double acc[256];
+                for (int32_t i = 0; i < d; ++i) acc[i] = 0.0;
+                for (int64_t j = 0; j < nvis; ++j)
+                    for (int32_t i = 0; i < d; ++i) acc[i] += sc[j] * kv_get(vs, dt, j, (int64_t)g * d + i, NK);
+                for (int32_t i = 0; i < d; ++i) oh[i] = orc_round(acc[i] / den, dt);
             }
         free(sc);
     }
@@ -338,6 +339,7 @@ int orc_draft_block(const orc_model* m, const void* const* ctx_k, const void* co
 {
     const int32_t H = m->hidden, B = m->block, dt = m->dtype;
     const int64_t NK = (int64_t)m->n_kv_heads * m->head_dim;
+    if (m->head_dim > 256) return -1;
     double* x = (double*)malloc(sizeof(double) * (size_t)B * H);
     double* kb = (double*)malloc(sizeof(double) * (size_t)B * NK);
     double* vb = (double*)malloc(sizeof(double) * (size_t)B * NK);
@@ -389,7 +391,7 @@ int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int
 {
     const int32_t H = m->hidden, dt = m->dtype;
     const int64_t NK = (int64_t)m->n_kv_heads * m->head_dim;
-    if (pos0 + n > cap) return -1;
+    if (pos0 + n > cap || m->head_dim > 256) return -1;
     double* x = (double*)malloc(sizeof(double) * (size_t)n * H);
     int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
     if (!x || !pos) return -1;

@@ -12,7 +12,13 @@ MID_BF16_D64 = MID_BF16.replace(name="mid_bf16_d64", n_q_heads=8, n_kv_heads=4, 
 MID_FP32_G5 = di.Shape("mid_fp32_g5", "fp32", hidden=320, target_layers=9, draft_layers=1, n_q_heads=10,
                        n_kv_heads=2, head_dim=64, ffn=688, vocab=1024, ctx=100, seed=23)
 
-TIE_GAP = 1e-3
+# Token exactness is required except where the oracle's top-2 gap is below the
+# noise two correct implementations can differ by.  fp32: 1e-3.  bf16: the
+# logit tolerance 2e-2 -- with bf16 storage points, fp32 instead of fp64
+# accumulation alone (same definition, same rounding points) moves logits by
+# ~1e-2, so gaps below that can reorder.  A mismatching GPU token must still be
+# a near-argmax of the oracle's logits (within the same band).
+TIE_GAP = {"fp32": 1e-3, "bf16": 2e-2}
 
 
 def dev(w):
@@ -49,9 +55,18 @@ def assert_logits(got, ref, dtype):
         assert err <= 2e-2, f"bf16 logits absolute error {err:.3g}"
 
 
-def assert_tokens(got, ref, gap):
+def assert_tokens(got, ref, gap, logits=None, ref_logits=None, dtype="bf16"):
+    """Returns the number of exempt mismatches."""
     got, ref = np.asarray(got), np.asarray(ref)
+    tol = TIE_GAP[dtype]
     mism = np.flatnonzero(got != ref)
     for j in mism:
-        assert gap[j] < TIE_GAP, f"token mismatch at row {j}: gpu {got[j]} oracle {ref[j]} gap {gap[j]}"
+        extra = ""
+        if logits is not None:
+            extra = (f"; row max|dlogit| {np.abs(np.asarray(logits[j], np.float64) - ref_logits[j]).max():.3g}, "
+                     f"all rows {np.abs(np.asarray(logits, np.float64) - ref_logits).max():.3g}")
+        assert gap[j] < tol, f"token mismatch at row {j}: gpu {got[j]} oracle {ref[j]} gap {gap[j]:.3g}{extra}"
+        if ref_logits is not None:
+            short = float(ref_logits[j].max()) - float(ref_logits[j][got[j]])
+            assert short < tol, f"row {j}: gpu token {got[j]} is {short:.3g} below the oracle max"
     return len(mism)

@@ -1,0 +1,122 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench
+times: the Qwen3-8B-shaped draft at 4096 and 36864 context, the 27B-class draft
+at 36864 context (complete blocks against the oracle), and prefill-side fusion
+and injection of 32768 rows (sampled rows / positions the oracle computes one
+by one, including the ragged last tile)."""
+import numpy as np
+import pytest
+import torch
+
+import dflash_inputs as di
+from tests.gpu_helpers import assert_logits, assert_rows_close, assert_tokens, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_diffusion_drafter_context_amd as m
+    m.lib()
+    return m
+
+
+def _draft_case(dl, orc, s, C):
+    w = di.draft_weights(s)
+    ctx = dl.DFlash(s, dev(w), max_ctx=C + 64, page_seed=17)
+    k, v = di.context_kv(s, C)
+    ctx.load_kv(k.cuda(), v.cuda())
+    anchor = di.anchor_token(s)
+    a = torch.tensor([anchor], dtype=torch.int32, device="cuda")
+    tok, lg = ctx.draft_block(a, want_logits=True)
+    torch.cuda.synchronize()
+    print(f"[fullsize] {s.name} C={C}: gpu done", flush=True)
+    ref = orc.draft_block(orc.Model(s, w), k, v, C, anchor)
+    lg = lg.cpu().numpy()
+    print(f"[fullsize] {s.name} C={C}: max|dlogit| {np.abs(lg - ref['logits']).max():.3g}", flush=True)
+    assert_logits(lg, ref["logits"], s.dtype)
+    n_ex = assert_tokens(tok.cpu().numpy(), ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype)
+    print(f"[fullsize] {s.name} C={C}: exempt near-tie token mismatches {n_ex}/{s.block}", flush=True)
+    # the per-step verification against the synthetic target
+    u, r, last = di.target_coins(s)
+    g = di.synthetic_target_argmax(tok.cpu().numpy(), u.numpy(), r.numpy(), last, s.vocab)
+    res = ctx.verify_accept(tok, torch.from_numpy(g).cuda()).cpu().tolist()
+    assert tuple(res) == orc.accept(tok.cpu().numpy(), g)
+    return ctx, w
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_4k_draft(dl, orc):
+    _draft_case(dl, orc, di.SHAPES["qwen3_8b_4k"], 4096)
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_36k_draft(dl, orc):
+    _draft_case(dl, orc, di.SHAPES["qwen3_8b_36k"], 36864)
+
+
+@pytest.mark.timeout(1200)
+def test_dense27b_36k_draft(dl, orc):
+    _draft_case(dl, orc, di.SHAPES["dense27b_36k"], 36864)
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_step_fuse_inject_16(dl, orc):
+    """Per-step path at full size: fuse the 16 verified rows' target features,
+    and inject 16 rows after a 4096-token context (skinny-GEMM kernels).  The
+    injection input is a generated stand-in for fused features, so each call is
+    checked against the oracle on identical inputs."""
+    s = di.SHAPES["qwen3_8b_4k"]
+    w = di.draft_weights(s, need_draft=False, need_lm=False)
+    ctx = dl.DFlash(s, dev(w), max_ctx=4096 + 64, max_rows=16, page_seed=4)
+    k, v = di.context_kv(s, 4096)
+    ctx.load_kv(k.cuda(), v.cuda())
+    sel = orc.feature_layers(s.target_layers)
+    hid = {l: di.target_hidden(s, l, 16, tag="step") for l in sel}
+    fused = ctx.fuse_context([hid[l].cuda() if l in hid else None for l in range(s.target_layers)])
+    feat = di.fused_context(s, 16, tag="verified")
+    ctx.inject_kv(feat.cuda(), 4096)
+    gk, gv = ctx.read_kv(4096, 16)
+    torch.cuda.synchronize()
+    m = orc.Model(s, w)
+    rf = orc.fuse_rows(m, [hid[l] for l in sel], range(16))
+    assert_rows_close(fused.float().cpu().numpy(), rf, s.dtype, "fuse16")
+    rk, rv = orc.inject_rows(m, feat, range(16), 4096)
+    L = s.draft_layers
+    assert_rows_close(gk.float().cpu().numpy().reshape(L * 16, -1), rk.reshape(L * 16, -1), s.dtype, "K16")
+    assert_rows_close(gv.float().cpu().numpy().reshape(L * 16, -1), rv.reshape(L * 16, -1), s.dtype, "V16")
+    # the injected rows did not disturb the context before them
+    k0, v0 = ctx.read_kv(4000, 96)
+    torch.cuda.synchronize()
+    assert torch.equal(k0.cpu(), k[:, 4000:4096]) and torch.equal(v0.cpu(), v[:, 4000:4096])
+
+
+@pytest.mark.timeout(1200)
+def test_prefill_fuse_inject_32k_sampled(dl, orc):
+    """Fusion GEMM (M=32768, K=25600, N=5120) and injection of 32768 rows into
+    256-token pages, checked on sampled rows including the ragged edges."""
+    s = di.SHAPES["fusion_prefill_32k"]
+    M = s.ctx
+    w = di.draft_weights(s, need_draft=False, need_lm=False)
+    ctx = dl.DFlash(s, dev(w), max_ctx=M, max_rows=M, page_seed=8)
+    sel = orc.feature_layers(s.target_layers)
+    hid = {l: di.target_hidden(s, l, M) for l in sel}
+    dev_hid = [hid[l].cuda() if l in hid else None for l in range(s.target_layers)]
+    fused = ctx.fuse_context(dev_hid)
+    torch.cuda.synchronize()
+    del dev_hid
+    rows = [0, 1, 63, 64, 4095, 17000, 32704, M - 1]
+    m = orc.Model(s, w)
+    rf = orc.fuse_rows(m, [hid[l] for l in sel], rows)
+    assert_rows_close(fused[rows].float().cpu().numpy(), rf, s.dtype, "fuse32k")
+    # injection of synthetic fused features (independent of the fusion output)
+    feat = di.fused_context(s, M, tag="prefill")
+    ctx.inject_kv(feat.cuda(), 0)
+    torch.cuda.synchronize()
+    rk, rv = orc.inject_rows(m, feat, rows, 0)
+    L = s.draft_layers
+    for i, r in enumerate(rows):
+        gk, gv = ctx.read_kv(r, 1)
+        assert_rows_close(gk.float().cpu().numpy().reshape(L, -1), rk[:, i], s.dtype, f"K pos {r}")
+        assert_rows_close(gv.float().cpu().numpy().reshape(L, -1), rv[:, i], s.dtype, f"V pos {r}")

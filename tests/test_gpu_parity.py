@@ -137,7 +137,7 @@ def _draft_pair(dl, orc, shape, C, anchor, page_seed=3, w=None):
 def test_draft_block_matches_oracle(dl, orc, shape, C):
     tok, lg, ref, _ = _draft_pair(dl, orc, shape, C, anchor=shape.vocab // 3)
     assert_logits(lg, ref["logits"], shape.dtype)
-    assert_tokens(tok, ref["tokens"], ref["gap"])
+    assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], shape.dtype)
 
 
 @pytest.mark.parametrize("B", [7, 2])
@@ -146,7 +146,7 @@ def test_draft_short_block(dl, orc, B):
     tok, lg, ref, _ = _draft_pair(dl, orc, s, 130, anchor=11)
     assert tok.shape == (B,) and lg.shape == (B, s.vocab)
     assert_logits(lg, ref["logits"], s.dtype)
-    assert_tokens(tok, ref["tokens"], ref["gap"])
+    assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype)
 
 
 def test_draft_deterministic_and_logits_optional(dl, orc):
@@ -186,7 +186,7 @@ def test_tiny_full_chain(dl, orc):
     to_kv = lambda a: orc.to_storage(a, s.dtype).view(s.draft_layers, s.ctx, s.n_kv_heads, s.head_dim)
     ref = orc.draft_block(m, to_kv(rk), to_kv(rv), s.ctx, anchor)
     assert_logits(lg.cpu().numpy(), ref["logits"], s.dtype)
-    assert_tokens(tok.cpu().numpy(), ref["tokens"], ref["gap"])
+    assert_tokens(tok.cpu().numpy(), ref["tokens"], ref["gap"], lg.cpu().numpy(), ref["logits"], s.dtype)
     u, r, last = di.target_coins(s)
     g = di.synthetic_target_argmax(tok.cpu().numpy(), u.numpy(), r.numpy(), last, s.vocab)
     res = ctx.verify_accept(tok, torch.from_numpy(g).cuda())
