@@ -45,10 +45,18 @@ template <> struct Elem<bf16_t> {
 
 // Eight consecutive reduction elements of one row: one MFMA operand slot set.
 template <typename T> struct Frag;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
 template <> struct Frag<bf16_t> {
     uint4 v;
     __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
     __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+    // streaming load (non-temporal hint): data read once per pass, e.g. weights
+    __device__ __forceinline__ void load_nt(const bf16_t* p) {
+        const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        v = make_uint4(t[0], t[1], t[2], t[3]);
+    }
     __device__ __forceinline__ float get(int i) const {
         uint32_t w = (&v.x)[i >> 1];
         return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
@@ -65,6 +73,12 @@ template <> struct Frag<float> {
     __device__ __forceinline__ void load(const float* p) {
         a = *reinterpret_cast<const float4*>(p);
         b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void load_nt(const float* p) {
+        const f32x4v_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p));
+        const f32x4v_t y = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p + 4));
+        a = make_float4(x[0], x[1], x[2], x[3]);
+        b = make_float4(y[0], y[1], y[2], y[3]);
     }
     __device__ __forceinline__ float get(int i) const { return i < 4 ? (&a.x)[i] : (&b.x)[i - 4]; }
     __device__ __forceinline__ void set8(const float* f) {

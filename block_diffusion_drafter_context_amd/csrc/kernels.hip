@@ -51,6 +51,10 @@ struct NoState {};
 constexpr int kP = 4;  // chunks per pipelined load group
 
 // Activation prologues ------------------------------------------------------
+// Each provides Raw (what is loaded for one chunk), prep(row) (per-wave
+// constant), load(raw, row, k) (issue loads only) and finish(frag, raw, prep)
+// (arithmetic at use time), so a prefetched group's loads stay in flight while
+// the previous group is computed.
 
 // u = round(x * rstd[row] * gain[k])  (RMSNorm applied on load)
 template <typename T>
@@ -59,14 +63,19 @@ struct NormA {
     int ld;
     const float* rstd;
     const T* gain;
-    __device__ __forceinline__ void load(Frag<T>& f, int row, int k) const {
-        Frag<T> xv, gv;
-        xv.load(x + (long long)row * ld + k);
-        gv.load(gain + k);
-        const float r = rstd[row];
+    struct Raw {
+        Frag<T> x, g;
+        __device__ __forceinline__ void zero() { x.zero(); g.zero(); }
+    };
+    __device__ __forceinline__ float prep(int row) const { return rstd[row]; }
+    __device__ __forceinline__ void load(Raw& r, int row, int k) const {
+        r.x.load(x + (long long)row * ld + k);
+        r.g.load(gain + k);
+    }
+    __device__ __forceinline__ void finish(Frag<T>& f, const Raw& r, float s) const {
         float v[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) v[s] = xv.get(s) * r * gv.get(s);
+        for (int e = 0; e < 8; ++e) v[e] = r.x.get(e) * s * r.g.get(e);
         f.set8(v);
     }
 };
@@ -75,7 +84,13 @@ template <typename T>
 struct PlainA {
     const T* x;
     long long ld;
-    __device__ __forceinline__ void load(Frag<T>& f, int row, int k) const { f.load(x + row * ld + k); }
+    struct Raw {
+        Frag<T> x;
+        __device__ __forceinline__ void zero() { x.zero(); }
+    };
+    __device__ __forceinline__ float prep(int) const { return 0.f; }
+    __device__ __forceinline__ void load(Raw& r, int row, int k) const { r.x.load(x + row * ld + k); }
+    __device__ __forceinline__ void finish(Frag<T>& f, const Raw& r, float) const { f = r.x; }
 };
 
 // five hidden-state slabs read as one concatenated row (never materialised)
@@ -84,19 +99,27 @@ struct SlabA {
     const T* slab[5];
     long long ld;
     int H;
-    __device__ __forceinline__ void load(Frag<T>& f, int row, int k) const {
+    struct Raw {
+        Frag<T> x;
+        __device__ __forceinline__ void zero() { x.zero(); }
+    };
+    __device__ __forceinline__ float prep(int) const { return 0.f; }
+    __device__ __forceinline__ void load(Raw& r, int row, int k) const {
         const int s = k / H;
-        f.load(slab[s] + row * ld + (k - s * H));
+        r.x.load(slab[s] + row * ld + (k - s * H));
     }
+    __device__ __forceinline__ void finish(Frag<T>& f, const Raw& r, float) const { f = r.x; }
 };
 
-template <typename T, class Op, class AL>
-__device__ __forceinline__ void skinny_segment(const Op& op, const AL& al, const T* b0, const T* b1, int ch0,
-                                               int ch1, int K, int row, int grp, bool row_ok, f32x4_t acc[2]) {
+template <typename T, class AL>
+__device__ __forceinline__ void skinny_segment(const AL& al, const T* b0, const T* b1, int ch0, int ch1, int K,
+                                               int row, int grp, bool row_ok, float pre, f32x4_t acc[2]) {
+    using Raw = typename AL::Raw;
     const T* w0 = b0 + (long long)row * K + grp * 8;
     const T* w1 = b1 ? b1 + (long long)row * K + grp * 8 : nullptr;
-    Frag<T> cw0[kP], cw1[kP], ca[kP];
-    auto load_group = [&](int c, Frag<T>* lw0, Frag<T>* lw1, Frag<T>* la) {
+    Frag<T> cw0[kP], cw1[kP];
+    Raw ca[kP];
+    auto load_group = [&](int c, Frag<T>* lw0, Frag<T>* lw1, Raw* la) {
 #pragma unroll
         for (int p = 0; p < kP; ++p) {
             const int ch = c + p;
@@ -114,13 +137,16 @@ __device__ __forceinline__ void skinny_segment(const Op& op, const AL& al, const
     };
     load_group(ch0, cw0, cw1, ca);
     for (int c = ch0; c < ch1; c += kP) {
-        Frag<T> nw0[kP], nw1[kP], na[kP];
+        Frag<T> nw0[kP], nw1[kP];
+        Raw na[kP];
         const bool more = c + kP < ch1;
         if (more) load_group(c + kP, nw0, nw1, na);
 #pragma unroll
         for (int p = 0; p < kP; ++p) {
-            mma(acc[0], ca[p], cw0[p]);
-            mma(acc[1], ca[p], cw1[p]);
+            Frag<T> a;
+            al.finish(a, ca[p], pre);
+            mma(acc[0], a, cw0[p]);
+            mma(acc[1], a, cw1[p]);
         }
         if (more) {
 #pragma unroll
@@ -139,6 +165,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
     const int wave = blockIdx.x * kSkinnyWavesPerWG + (threadIdx.x >> 6);
     const int row = lane & 15, grp = lane >> 4;
     const bool row_ok = row < c.M;
+    const float pre = row_ok ? op.a.prep(row) : 0.f;
     typename Op::State st;
     op.wave_begin(st);
 
@@ -153,7 +180,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
         const long long seg_end = end < tbeg + c.nchunks ? end : tbeg + c.nchunks;
         const int ch0 = (int)(i - tbeg), ch1 = (int)(seg_end - tbeg);
         f32x4_t acc[2] = {zero4(), zero4()};
-        skinny_segment<T>(op, op.a, op.b_rows(tile, 0), op.b_rows(tile, 1), ch0, ch1, c.K, row, grp, row_ok, acc);
+        skinny_segment<T>(op.a, op.b_rows(tile, 0), op.b_rows(tile, 1), ch0, ch1, c.K, row, grp, row_ok, pre, acc);
         i = seg_end;
         if (!(ch0 == 0 && ch1 == c.nchunks)) {
             // partial tile: publish, and let the last contributor finish it

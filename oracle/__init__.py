@@ -44,6 +44,7 @@ def lib():
             build()
         L = C.CDLL(_LIB)
         vp, i32, i64, dp = C.c_void_p, C.c_int32, C.c_int64, C.POINTER(C.c_double)
+        L.orc_set_fp32_accumulation.argtypes = [i32]
         L.orc_round_bf16.restype = C.c_double
         L.orc_round_bf16.argtypes = [C.c_double]
         L.orc_round_array_bf16.argtypes = [vp, i64, vp]
@@ -114,6 +115,22 @@ class Model:
     @property
     def ref(self):
         return C.byref(self.s)
+
+
+def set_fp32_accumulation(on: bool):
+    lib().orc_set_fp32_accumulation(1 if on else 0)
+
+
+def draft_noise_floor(model: Model, ctx_k, ctx_v, C_len: int, anchor: int, ref_logits: np.ndarray) -> float:
+    """Largest logit difference between the oracle (fp64 accumulation) and the
+    same oracle with fp32 accumulation: the drift two correct implementations
+    show once storage rounding amplifies accumulation-order differences."""
+    set_fp32_accumulation(True)
+    try:
+        alt = draft_block(model, ctx_k, ctx_v, C_len, anchor)
+    finally:
+        set_fp32_accumulation(False)
+    return float(np.abs(alt["logits"].astype(np.float64) - ref_logits.astype(np.float64)).max())
 
 
 def round_bf16(x) -> np.ndarray:

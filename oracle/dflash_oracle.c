@@ -88,6 +88,13 @@ void orc_feature_layers(int32_t L, int32_t out[5])
     for (int i = 0; i < 5; ++i) out[i] = (6 + i * (L - 3)) / 4; /* floor(1 + i(L-3)/4 + 1/2) */
 }
 
+/* Accumulator precision of dot products: fp64 (the oracle's definition) unless
+ * the fp32 variant is selected.  The fp32 variant exists only to measure how far
+ * two correct implementations that differ in accumulation precision drift apart
+ * once bf16 storage rounding amplifies it (tolerance calibration). */
+static int g_fp32_acc = 0;
+void orc_set_fp32_accumulation(int32_t on) { g_fp32_acc = on != 0; }
+
 /* y[r][n] = sum_k W[n][k] * x[r][k]  for a row-major W [N][K] in storage type. */
 static void matvec_rows(const void* W, int32_t dtype, int64_t N, int64_t K,
                         const double* x, int32_t R, double* y)
@@ -100,9 +107,15 @@ static void matvec_rows(const void* W, int32_t dtype, int64_t N, int64_t K,
             for (int64_t k = 0; k < K; ++k) w[k] = ld_elem(W, dtype, n * K + k);
             for (int32_t r = 0; r < R; ++r) {
                 const double* xr = x + (int64_t)r * K;
-                double s = 0.0;
-                for (int64_t k = 0; k < K; ++k) s += w[k] * xr[k];
-                y[(int64_t)r * N + n] = s;
+                if (g_fp32_acc) {
+                    float s = 0.0f;
+                    for (int64_t k = 0; k < K; ++k) s += (float)(w[k] * xr[k]);
+                    y[(int64_t)r * N + n] = s;
+                } else {
+                    double s = 0.0;
+                    for (int64_t k = 0; k < K; ++k) s += w[k] * xr[k];
+                    y[(int64_t)r * N + n] = s;
+                }
             }
         }
         free(w);

@@ -52,6 +52,10 @@ typedef struct {
     const void* lm_head;    /* [V, H] */
 } orc_model;
 
+/* Select fp32 accumulation of the Linear layers' dot products (default fp64).
+ * Used only to measure the rounding noise between correct implementations. */
+void orc_set_fp32_accumulation(int32_t on);
+
 /* storage rounding */
 double orc_round_bf16(double v);
 double orc_round(double v, int32_t dtype);

@@ -44,7 +44,13 @@ def assert_rows_close(got, ref, dtype, what=""):
     assert not bad.any(), f"{what}: rows {np.flatnonzero(bad)[:8]} err {err[bad][:8]} rowmax {mx[bad][:8]}"
 
 
-def assert_logits(got, ref, dtype):
+def bf16_logit_tol(noise_floor=None):
+    """bf16 logits: 2e-2 absolute, widened to twice the oracle's own fp32-vs-fp64
+    accumulation drift when that is larger (deep / wide shapes)."""
+    return 2e-2 if noise_floor is None else max(2e-2, 2.0 * noise_floor)
+
+
+def assert_logits(got, ref, dtype, noise_floor=None):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if dtype == "fp32":
@@ -52,13 +58,14 @@ def assert_logits(got, ref, dtype):
         assert rel.max() <= 1e-4, f"fp32 logits relative error {rel.max():.3g}"
     else:
         err = np.abs(got - ref).max()
-        assert err <= 2e-2, f"bf16 logits absolute error {err:.3g}"
+        tol = bf16_logit_tol(noise_floor)
+        assert err <= tol, f"bf16 logits absolute error {err:.3g} > {tol:.3g} (noise floor {noise_floor})"
 
 
-def assert_tokens(got, ref, gap, logits=None, ref_logits=None, dtype="bf16"):
+def assert_tokens(got, ref, gap, logits=None, ref_logits=None, dtype="bf16", noise_floor=None):
     """Returns the number of exempt mismatches."""
     got, ref = np.asarray(got), np.asarray(ref)
-    tol = TIE_GAP[dtype]
+    tol = TIE_GAP[dtype] if dtype == "fp32" else bf16_logit_tol(noise_floor)
     mism = np.flatnonzero(got != ref)
     for j in mism:
         extra = ""

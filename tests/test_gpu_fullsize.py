@@ -32,11 +32,14 @@ def _draft_case(dl, orc, s, C):
     tok, lg = ctx.draft_block(a, want_logits=True)
     torch.cuda.synchronize()
     print(f"[fullsize] {s.name} C={C}: gpu done", flush=True)
-    ref = orc.draft_block(orc.Model(s, w), k, v, C, anchor)
+    m = orc.Model(s, w)
+    ref = orc.draft_block(m, k, v, C, anchor)
+    noise = orc.draft_noise_floor(m, k, v, C, anchor, ref["logits"])
     lg = lg.cpu().numpy()
-    print(f"[fullsize] {s.name} C={C}: max|dlogit| {np.abs(lg - ref['logits']).max():.3g}", flush=True)
-    assert_logits(lg, ref["logits"], s.dtype)
-    n_ex = assert_tokens(tok.cpu().numpy(), ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype)
+    print(f"[fullsize] {s.name} C={C}: max|dlogit| {np.abs(lg - ref['logits']).max():.3g}, "
+          f"oracle fp32-vs-fp64 drift {noise:.3g}", flush=True)
+    assert_logits(lg, ref["logits"], s.dtype, noise)
+    n_ex = assert_tokens(tok.cpu().numpy(), ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype, noise)
     print(f"[fullsize] {s.name} C={C}: exempt near-tie token mismatches {n_ex}/{s.block}", flush=True)
     # the per-step verification against the synthetic target
     u, r, last = di.target_coins(s)

@@ -125,7 +125,9 @@ def _draft_pair(dl, orc, shape, C, anchor, page_seed=3, w=None):
     a = torch.tensor([anchor], dtype=torch.int32, device="cuda")
     tokens, logits = ctx.draft_block(a, want_logits=True)
     sync()
-    ref = orc.draft_block(orc.Model(shape, w), k, v, C, anchor)
+    m = orc.Model(shape, w)
+    ref = orc.draft_block(m, k, v, C, anchor)
+    ref["noise"] = orc.draft_noise_floor(m, k, v, C, anchor, ref["logits"]) if shape.dtype == "bf16" else None
     return tokens.cpu().numpy(), logits.cpu().numpy(), ref, ctx
 
 
@@ -136,8 +138,8 @@ def _draft_pair(dl, orc, shape, C, anchor, page_seed=3, w=None):
                                      (MID_BF16_D64, 300)])
 def test_draft_block_matches_oracle(dl, orc, shape, C):
     tok, lg, ref, _ = _draft_pair(dl, orc, shape, C, anchor=shape.vocab // 3)
-    assert_logits(lg, ref["logits"], shape.dtype)
-    assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], shape.dtype)
+    assert_logits(lg, ref["logits"], shape.dtype, ref["noise"])
+    assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], shape.dtype, ref["noise"])
 
 
 @pytest.mark.parametrize("B", [7, 2])
@@ -145,8 +147,8 @@ def test_draft_short_block(dl, orc, B):
     s = MID_BF16.replace(block=B)
     tok, lg, ref, _ = _draft_pair(dl, orc, s, 130, anchor=11)
     assert tok.shape == (B,) and lg.shape == (B, s.vocab)
-    assert_logits(lg, ref["logits"], s.dtype)
-    assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype)
+    assert_logits(lg, ref["logits"], s.dtype, ref["noise"])
+    assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype, ref["noise"])
 
 
 def test_draft_deterministic_and_logits_optional(dl, orc):
