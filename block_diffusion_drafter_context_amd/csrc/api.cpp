@@ -145,6 +145,18 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     x.embed = w->embed;
     x.lm_head = w->lm_head;
     x.tracer = &c->tracer;
+    for (int l = 0; l < DFLASH_MAX_LAYERS; ++l) {
+        const bool in = l < d.Ld;
+        x.sw_wq[l] = in ? x.ws + L.sw_wq[l] : nullptr;
+        x.sw_wk[l] = in ? x.ws + L.sw_wk[l] : nullptr;
+        x.sw_wv[l] = in ? x.ws + L.sw_wv[l] : nullptr;
+        x.sw_wo[l] = in ? x.ws + L.sw_wo[l] : nullptr;
+        x.sw_wg[l] = in ? x.ws + L.sw_wg[l] : nullptr;
+        x.sw_wu[l] = in ? x.ws + L.sw_wu[l] : nullptr;
+        x.sw_wd[l] = in ? x.ws + L.sw_wd[l] : nullptr;
+    }
+    x.sw_lm = x.ws + L.sw_lm;
+    x.sw_fc = x.ws + L.sw_fc;
 
     // rotary table: angle = pos * base^(-2i/d) in fp64, cos/sin stored as fp32
     const int half = d.d / 2;
@@ -160,6 +172,27 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     std::vector<int32_t> pt = make_page_table(d.n_pages, cfg->page_seed);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    // swizzled copies of every streamed weight that was given
+    const long long nqd = (long long)d.nq * d.d, nkd = (long long)d.nkv * d.d;
+    struct Job { const void* src; long long N, K; const void* dst; };
+    std::vector<Job> jobs;
+    jobs.push_back({w->fc, d.H, 5LL * d.H, x.sw_fc});
+    if (w->lm_head) jobs.push_back({w->lm_head, d.V, d.H, x.sw_lm});
+    for (int l = 0; l < d.Ld; ++l) {
+        jobs.push_back({w->wk[l], nkd, d.H, x.sw_wk[l]});
+        jobs.push_back({w->wv[l], nkd, d.H, x.sw_wv[l]});
+        if (w->wq[l]) jobs.push_back({w->wq[l], nqd, d.H, x.sw_wq[l]});
+        if (w->wo[l]) jobs.push_back({w->wo[l], d.H, nqd, x.sw_wo[l]});
+        if (w->wg[l]) jobs.push_back({w->wg[l], d.F, d.H, x.sw_wg[l]});
+        if (w->wu[l]) jobs.push_back({w->wu[l], d.F, d.H, x.sw_wu[l]});
+        if (w->wd[l]) jobs.push_back({w->wd[l], d.H, d.F, x.sw_wd[l]});
+    }
+    for (const Job& j : jobs) {
+        if ((e = launch_swizzle(d.dtype, j.src, (int)j.N, (int)j.K, const_cast<void*>(j.dst), s)) != hipSuccess) {
+            delete c;
+            return DFLASH_ERR_HIP;
+        }
+    }
     if ((e = hipMemcpyAsync(x.ws + L.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
         (e = hipMemcpyAsync(x.ws + L.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
         (pt.size() && (e = hipMemcpyAsync(x.ws + L.page_table, pt.data(), pt.size() * 4, hipMemcpyHostToDevice, s)) !=

@@ -57,6 +57,15 @@ template <> struct Frag<bf16_t> {
         const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
         v = make_uint4(t[0], t[1], t[2], t[3]);
     }
+    // one lane's slot set of a swizzled 512-element block (see host.h)
+    __device__ __forceinline__ void load_sw(const bf16_t* block, int lane) { load_nt(block + lane * 8); }
+    // keep (m = ~0u) or clear (m = 0) all elements without a branch
+    __device__ __forceinline__ void mask(uint32_t m) {
+        v.x &= m;
+        v.y &= m;
+        v.z &= m;
+        v.w &= m;
+    }
     __device__ __forceinline__ float get(int i) const {
         uint32_t w = (&v.x)[i >> 1];
         return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
@@ -79,6 +88,22 @@ template <> struct Frag<float> {
         const f32x4v_t y = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(p + 4));
         a = make_float4(x[0], x[1], x[2], x[3]);
         b = make_float4(y[0], y[1], y[2], y[3]);
+    }
+    __device__ __forceinline__ void load_sw(const float* block, int lane) {
+        const f32x4v_t x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(block + lane * 4));
+        const f32x4v_t y = __builtin_nontemporal_load(reinterpret_cast<const f32x4v_t*>(block + 256 + lane * 4));
+        a = make_float4(x[0], x[1], x[2], x[3]);
+        b = make_float4(y[0], y[1], y[2], y[3]);
+    }
+    __device__ __forceinline__ void mask(uint32_t m) {
+        a.x = __uint_as_float(__float_as_uint(a.x) & m);
+        a.y = __uint_as_float(__float_as_uint(a.y) & m);
+        a.z = __uint_as_float(__float_as_uint(a.z) & m);
+        a.w = __uint_as_float(__float_as_uint(a.w) & m);
+        b.x = __uint_as_float(__float_as_uint(b.x) & m);
+        b.y = __uint_as_float(__float_as_uint(b.y) & m);
+        b.z = __uint_as_float(__float_as_uint(b.z) & m);
+        b.w = __uint_as_float(__float_as_uint(b.w) & m);
     }
     __device__ __forceinline__ float get(int i) const { return i < 4 ? (&a.x)[i] : (&b.x)[i - 4]; }
     __device__ __forceinline__ void set8(const float* f) {

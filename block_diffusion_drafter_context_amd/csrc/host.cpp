@@ -87,7 +87,9 @@ Layout compute_layout(const Dims& d, int num_cus) {
     const int blk = 16 * kSkinnyNT;
     L.max_ss_tiles = (d.H + blk - 1) / blk;
     L.ss_part = take((size_t)L.max_ss_tiles * 16 * 4);
-    L.nwaves = std::max(num_cus, 1) * 8;
+    // 4 waves per CU: measured best for every skinny-GEMM shape of the draft
+    // pass (fewer concurrent weight streams keep DRAM pages open longer)
+    L.nwaves = std::max(num_cus, 1) * 4;
     L.partial = take((size_t)L.nwaves * 2 * kSkinnyNT * 256 * 4);
     // tiles of every skinny GEMM: qkv, o, gate/up, down, lm head, fuse, inject
     long long t = 0;
@@ -104,6 +106,18 @@ Layout compute_layout(const Dims& d, int num_cus) {
     const size_t parts = (size_t)(kMaxSplits + 1) * d.nq * 16;
     L.attn_o = take(parts * d.d * 4);
     L.attn_ml = take(parts * 2 * 4);
+    const int e = d.elem;
+    for (int l = 0; l < d.Ld; ++l) {
+        L.sw_wq[l] = take(swizzled_bytes(nqd, d.H, e));
+        L.sw_wk[l] = take(swizzled_bytes(nkd, d.H, e));
+        L.sw_wv[l] = take(swizzled_bytes(nkd, d.H, e));
+        L.sw_wo[l] = take(swizzled_bytes(d.H, nqd, e));
+        L.sw_wg[l] = take(swizzled_bytes(d.F, d.H, e));
+        L.sw_wu[l] = take(swizzled_bytes(d.F, d.H, e));
+        L.sw_wd[l] = take(swizzled_bytes(d.H, d.F, e));
+    }
+    L.sw_lm = take(swizzled_bytes(d.V, d.H, e));
+    L.sw_fc = take(swizzled_bytes(d.H, 5LL * d.H, e));
     L.total = off;
     L.kv_layer_kv = (size_t)d.n_pages * d.nkv * d.page * d.d * es;
     L.kv_total = L.kv_layer_kv * 2 * d.Ld;

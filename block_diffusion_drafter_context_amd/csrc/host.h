@@ -27,8 +27,23 @@ struct Dims {
 };
 
 // Byte offsets of every region inside the caller's workspace (256-byte aligned).
+// Weights streamed by the skinny GEMM are kept a second time in the MFMA
+// operand order ("swizzled"): for W [N][K], block (n/16, k/32) is one
+// contiguous group of 64 lanes x 8 elements, lane l holding
+// W[16*(n/16) + l%16][32*(k/32) + 8*(l/16) .. +8]; K is zero-padded to a
+// multiple of 32.  For fp32 the 8 elements of a lane are split into two
+// 16-byte halves stored as two consecutive 1 KB planes.  One wave instruction
+// then reads 1 KB of contiguous memory.
+inline size_t swizzled_bytes(long long N, long long K, int elem) {
+    return (size_t)((N + 15) / 16) * (size_t)((K + 31) / 32) * 512 * (size_t)elem;
+}
+
 struct Layout {
     size_t rope_cos, rope_sin, page_table;
+    // swizzled weight copies (offsets into the workspace)
+    size_t sw_wq[DFLASH_MAX_LAYERS], sw_wk[DFLASH_MAX_LAYERS], sw_wv[DFLASH_MAX_LAYERS], sw_wo[DFLASH_MAX_LAYERS];
+    size_t sw_wg[DFLASH_MAX_LAYERS], sw_wu[DFLASH_MAX_LAYERS], sw_wd[DFLASH_MAX_LAYERS];
+    size_t sw_lm, sw_fc;
     size_t x, q, kblk, vblkT, obuf, hbuf;
     size_t rstd, ss_part, partial, tile_cnt, counters, best;
     size_t attn_o, attn_ml;

@@ -46,8 +46,21 @@ struct DevCtx {
     const void* final_norm;
     const void* embed;
     const void* lm_head;
+    // swizzled copies (inside the workspace) of the weights the skinny GEMM streams
+    const void* sw_wq[DFLASH_MAX_LAYERS];
+    const void* sw_wk[DFLASH_MAX_LAYERS];
+    const void* sw_wv[DFLASH_MAX_LAYERS];
+    const void* sw_wo[DFLASH_MAX_LAYERS];
+    const void* sw_wg[DFLASH_MAX_LAYERS];
+    const void* sw_wu[DFLASH_MAX_LAYERS];
+    const void* sw_wd[DFLASH_MAX_LAYERS];
+    const void* sw_lm;
+    const void* sw_fc;
     Tracer* tracer;
 };
+
+// Write the swizzled copy of a row-major [N][K] matrix (N % 16 == 0, K % 8 == 0).
+hipError_t launch_swizzle(int dtype, const void* W, int N, int K, void* out, hipStream_t s);
 
 // One draft block over the first C context positions.
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits,

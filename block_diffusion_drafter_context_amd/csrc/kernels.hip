@@ -111,51 +111,64 @@ struct SlabA {
     __device__ __forceinline__ void finish(Frag<T>& f, const Raw& r, float) const { f = r.x; }
 };
 
+// Swizzled stream of one 16-column block: chunk ch is the 512-element block at
+// stream + 512 * ch (see host.h).
+template <typename T>
+__device__ __forceinline__ const T* sw_stream(const T* base, int col_block, int nchunks) {
+    return base + (long long)col_block * nchunks * 512;
+}
+
+// One segment [ch0, ch1) of 32-wide K chunks of one tile, whose two column
+// blocks are the swizzled streams s0 and s1 (s1 may be null).  Loads are
+// issued unconditionally (out-of-range chunks re-read the last valid chunk and
+// are masked to zero at use), and the loop is unrolled twice over two register
+// sets (ping-pong, no copies), so the next group's loads stay in flight while
+// the current group is computed.
 template <typename T, class AL>
-__device__ __forceinline__ void skinny_segment(const AL& al, const T* b0, const T* b1, int ch0, int ch1, int K,
-                                               int row, int grp, bool row_ok, float pre, f32x4_t acc[2]) {
+__device__ __forceinline__ void skinny_segment(const AL& al, const T* s0, const T* s1, int ch0, int ch1, int K,
+                                               int lane, int row, int grp, bool row_ok, float pre, f32x4_t acc[2]) {
     using Raw = typename AL::Raw;
-    const T* w0 = b0 + (long long)row * K + grp * 8;
-    const T* w1 = b1 ? b1 + (long long)row * K + grp * 8 : nullptr;
-    Frag<T> cw0[kP], cw1[kP];
-    Raw ca[kP];
-    auto load_group = [&](int c, Frag<T>* lw0, Frag<T>* lw1, Raw* la) {
+    const int arow = row_ok ? row : 0;
+    const T* w1s = s1 ? s1 : s0;
+    const int klast = K - 8;  // last valid 8-element group of an activation row
+    struct Group {
+        Frag<T> w0[kP], w1[kP];
+        Raw a[kP];
+    };
+    auto load_group = [&](int c, Group& g) {
 #pragma unroll
         for (int p = 0; p < kP; ++p) {
-            const int ch = c + p;
-            const int k = ch * 32 + grp * 8;
-            if (ch < ch1 && k < K) {
-                lw0[p].load(w0 + ch * 32);
-                if (w1) lw1[p].load(w1 + ch * 32); else lw1[p].zero();
-                if (row_ok) al.load(la[p], row, k); else la[p].zero();
-            } else {
-                lw0[p].zero();
-                lw1[p].zero();
-                la[p].zero();
-            }
+            const int ch = min(c + p, ch1 - 1);
+            const int k = min(ch * 32 + grp * 8, klast);
+            g.w0[p].load_sw(s0 + (long long)ch * 512, lane);
+            g.w1[p].load_sw(w1s + (long long)ch * 512, lane);
+            al.load(g.a[p], arow, k);
         }
     };
-    load_group(ch0, cw0, cw1, ca);
-    for (int c = ch0; c < ch1; c += kP) {
-        Frag<T> nw0[kP], nw1[kP];
-        Raw na[kP];
-        const bool more = c + kP < ch1;
-        if (more) load_group(c + kP, nw0, nw1, na);
+    auto compute = [&](int c, const Group& g) {
 #pragma unroll
         for (int p = 0; p < kP; ++p) {
             Frag<T> a;
-            al.finish(a, ca[p], pre);
-            mma(acc[0], a, cw0[p]);
-            mma(acc[1], a, cw1[p]);
+            al.finish(a, g.a[p], pre);
+            const bool ok = row_ok && (c + p < ch1) && ((c + p) * 32 + grp * 8 < K);
+            a.mask(ok ? 0xFFFFFFFFu : 0u);
+            mma(acc[0], a, g.w0[p]);
+            mma(acc[1], a, g.w1[p]);
         }
-        if (more) {
-#pragma unroll
-            for (int p = 0; p < kP; ++p) {
-                cw0[p] = nw0[p];
-                cw1[p] = nw1[p];
-                ca[p] = na[p];
-            }
-        }
+    };
+    // sched_barrier(0) keeps the compiler from sinking a group's loads next to
+    // their uses (it otherwise trades the overlap for registers)
+    Group ga, gb;
+    load_group(ch0, ga);
+    for (int c = ch0; c < ch1; c += 2 * kP) {
+        load_group(c + kP, gb);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c, ga);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(c + 2 * kP, ga);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c + kP, gb);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -180,7 +193,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
         const long long seg_end = end < tbeg + c.nchunks ? end : tbeg + c.nchunks;
         const int ch0 = (int)(i - tbeg), ch1 = (int)(seg_end - tbeg);
         f32x4_t acc[2] = {zero4(), zero4()};
-        skinny_segment<T>(op.a, op.b_rows(tile, 0), op.b_rows(tile, 1), ch0, ch1, c.K, row, grp, row_ok, pre, acc);
+        skinny_segment<T>(op.a, op.b_rows(tile, 0, c.nchunks), op.b_rows(tile, 1, c.nchunks), ch0, ch1, c.K, lane, row,
+                          grp, row_ok, pre, acc);
         i = seg_end;
         if (!(ch0 == 0 && ch1 == c.nchunks)) {
             // partial tile: publish, and let the last contributor finish it
@@ -254,11 +268,11 @@ struct OpQKV {
         h = t / per;
         i = t - h * per;
     }
-    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+    __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
         int kind, h, i;
         decode(tile, kind, h, i);
         const T* W = kind == 0 ? wq : (kind == 1 ? wk : wv);
-        return W + (long long)(h * d + 16 * i + blk * (d / 2)) * H;
+        return sw_stream(W, (h * d + 16 * i + blk * (d / 2)) / 16, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
@@ -310,9 +324,9 @@ struct OpResid {
     float* ss_part;
     float* rstd_out;
     float eps;
-    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+    __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
         const int n0 = 32 * tile + 16 * blk;
-        return n0 < N ? w + (long long)n0 * K : nullptr;
+        return n0 < N ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
@@ -368,8 +382,8 @@ struct OpSwiGLU {
     const T* wu;
     int F, K, M;
     T* h;
-    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
-        return (blk == 0 ? wg : wu) + (long long)(16 * tile) * K;
+    __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
+        return sw_stream(blk == 0 ? wg : wu, tile, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
@@ -414,9 +428,9 @@ struct OpLMHead {
     unsigned long long* best;      // [16] packed keys, zero on entry
     unsigned* wg_cnt;              // workgroup completion counter
     int32_t* tokens;               // [M]
-    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+    __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
         const int n0 = 32 * tile + 16 * blk;
-        return n0 < V ? w + (long long)n0 * K : nullptr;
+        return n0 < V ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State& s) const {
 #pragma unroll
@@ -499,9 +513,9 @@ struct OpFuse {
     const T* w;
     int H, K, M;
     T* out;
-    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+    __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
         const int n0 = 32 * tile + 16 * blk;
-        return n0 < H ? w + (long long)n0 * K : nullptr;
+        return n0 < H ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
@@ -566,10 +580,10 @@ struct OpInject {
         h = t / per;
         i = t - h * per;
     }
-    __device__ __forceinline__ const T* b_rows(int tile, int blk) const {
+    __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
         int l, kind, h, i;
         decode(tile, l, kind, h, i);
-        return (kind == 0 ? wk[l] : wv[l]) + (long long)(h * d + 16 * i + blk * (d / 2)) * H;
+        return sw_stream(kind == 0 ? wk[l] : wv[l], (h * d + 16 * i + blk * (d / 2)) / 16, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
@@ -1001,6 +1015,34 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(KVPages kv, T* k, T* v, in
     }
 }
 
+// Swizzled copy of W [N][K]: one wave per 512-element block (layout in host.h).
+template <typename T>
+__global__ __launch_bounds__(64) void swizzle_kernel(const T* W, int N, int K, T* out) {
+    const int kc = blockIdx.x, nb = blockIdx.y, lane = threadIdx.x;
+    const int nchunks = gridDim.x;
+    const int row = 16 * nb + (lane & 15), k0 = 32 * kc + 8 * (lane >> 4);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (k0 + e < K) ? Elem<T>::to_f32(W[(long long)row * K + k0 + e]) : 0.f;
+    T* blk = out + ((long long)nb * nchunks + kc) * 512;
+    if (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) blk[lane * 8 + e] = Elem<T>::from_f32(v[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) blk[(e < 4 ? 0 : 256) + lane * 4 + (e & 3)] = Elem<T>::from_f32(v[e]);
+    }
+}
+
+hipError_t launch_swizzle(int dtype, const void* W, int N, int K, void* out, hipStream_t s) {
+    const dim3 grid((K + 31) / 32, N / 16);
+    if (dtype == DFLASH_F32)
+        hipLaunchKernelGGL((swizzle_kernel<float>), grid, dim3(64), 0, s, (const float*)W, N, K, (float*)out);
+    else
+        hipLaunchKernelGGL((swizzle_kernel<bf16_t>), grid, dim3(64), 0, s, (const bf16_t*)W, N, K, (bf16_t*)out);
+    return hipGetLastError();
+}
+
 // ============================================================================
 // large-M MFMA GEMM (prefill-side fusion and injection)
 // ============================================================================
@@ -1178,9 +1220,9 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
     for (int l = 0; l < d.Ld; ++l) {
         OpQKV<T> qkv;
         qkv.a = NormA<T>{x, H, rstd, (const T*)c.attn_norm[l]};
-        qkv.wq = (const T*)c.wq[l];
-        qkv.wk = (const T*)c.wk[l];
-        qkv.wv = (const T*)c.wv[l];
+        qkv.wq = (const T*)c.sw_wq[l];
+        qkv.wk = (const T*)c.sw_wk[l];
+        qkv.wv = (const T*)c.sw_wv[l];
         qkv.H = H;
         qkv.nq = nq;
         qkv.nkv = nkv;
@@ -1227,7 +1269,7 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
 
         OpResid<T> op;
         op.a = PlainA<T>{obuf, (long long)nq * D};
-        op.w = (const T*)c.wo[l];
+        op.w = (const T*)c.sw_wo[l];
         op.N = H;
         op.K = nq * D;
         op.M = B;
@@ -1241,8 +1283,8 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
 
         OpSwiGLU<T> sw;
         sw.a = NormA<T>{x, H, rstd, (const T*)c.mlp_norm[l]};
-        sw.wg = (const T*)c.wg[l];
-        sw.wu = (const T*)c.wu[l];
+        sw.wg = (const T*)c.sw_wg[l];
+        sw.wu = (const T*)c.sw_wu[l];
         sw.F = F;
         sw.K = H;
         sw.M = B;
@@ -1253,7 +1295,7 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
 
         OpResid<T> dn;
         dn.a = PlainA<T>{hbuf, (long long)F};
-        dn.w = (const T*)c.wd[l];
+        dn.w = (const T*)c.sw_wd[l];
         dn.N = H;
         dn.K = F;
         dn.M = B;
@@ -1268,7 +1310,7 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
 
     OpLMHead<T> lm;
     lm.a = NormA<T>{x, H, rstd, (const T*)c.final_norm};
-    lm.w = (const T*)c.lm_head;
+    lm.w = (const T*)c.sw_lm;
     lm.V = d.V;
     lm.K = H;
     lm.M = B;
@@ -1302,7 +1344,7 @@ static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long 
     if (M <= 16) {
         OpFuse<T> op;
         op.a = sa;
-        op.w = (const T*)c.fc;
+        op.w = (const T*)c.sw_fc;
         op.H = H;
         op.K = 5 * H;
         op.M = M;
@@ -1341,8 +1383,8 @@ static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int
         OpInject<T> op;
         op.a = PlainA<T>{(const T*)fused, ld};
         for (int l = 0; l < d.Ld; ++l) {
-            op.wk[l] = (const T*)c.wk[l];
-            op.wv[l] = (const T*)c.wv[l];
+            op.wk[l] = (const T*)c.sw_wk[l];
+            op.wv[l] = (const T*)c.sw_wv[l];
         }
         op.H = d.H;
         op.nkv = d.nkv;

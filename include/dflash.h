@@ -123,8 +123,10 @@ dflash_status dflash_workspace_size(const dflash_config* cfg, size_t* workspace_
 /* Create a context.  `workspace` and `kv_pool` are device buffers of at least
  * the sizes above (256-byte aligned); they and the weights stay borrowed until
  * dflash_destroy.  The library never allocates device memory itself.  Fills the
- * rotary table (fp64 angles, fp32 cos/sin) and the page table and zeroes the
- * counters, enqueued on `stream`.  Length starts at 0. */
+ * rotary table (fp64 angles, fp32 cos/sin) and the page table, zeroes the
+ * counters and writes a copy of every streamed weight matrix into the
+ * workspace in the matrix-core operand order (so the weights must not change
+ * while the context lives), enqueued on `stream`.  Length starts at 0. */
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
                             void* workspace, size_t workspace_bytes,
                             void* kv_pool, size_t kv_bytes,

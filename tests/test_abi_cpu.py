@@ -57,7 +57,11 @@ def test_workspace_size_and_validation(dl):
     ws, kv = dl.workspace_size(cfg)
     pages = (cfg.max_ctx + 255) // 256
     assert kv == 2 * s.draft_layers * pages * 256 * s.n_kv_heads * s.head_dim * 2
-    assert 0 < ws < 512 * 2 ** 20
+    # the workspace holds the matrix-core-ordered copy of every streamed weight
+    H, F, V, L = s.hidden, s.ffn, s.vocab, s.draft_layers
+    nq, nkv, d = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim, s.head_dim
+    weights = 2 * (L * (H * nq + 2 * H * nkv + nq * H + 3 * H * F) + V * H + 5 * H * H)
+    assert weights < ws < weights + 512 * 2 ** 20
     for field, bad in (("head_dim", 96), ("block", 17), ("block", 1), ("vocab", 1000), ("dtype", 7),
                        ("mask_id", s.vocab), ("n_q_heads", 30), ("page_size", 100), ("hidden", 4100)):
         c = dl.make_config(s, max_ctx=4096)
