@@ -148,8 +148,8 @@ void attn_split_plan(int C, int nkv, int num_cus, int* kps, int* ns) {
         *ns = 0;
         return;
     }
-    // aim for about two workgroups per CU over all kv heads, at least one chunk each
-    long long target = std::max(1LL, (long long)2 * num_cus / std::max(nkv, 1));
+    // one round of workgroups over all kv heads: kAttnWGPerCU per CU
+    long long target = std::max(1LL, (long long)kAttnWGPerCU * num_cus / std::max(nkv, 1));
     long long per = (C + target - 1) / target;
     per = ((per + kAttnChunk - 1) / kAttnChunk) * kAttnChunk;
     per = std::max<long long>(per, kAttnChunk);

@@ -18,6 +18,8 @@ constexpr int kWaveSize = 64;
 constexpr int kSkinnyWavesPerWG = 4;     // skinny (M <= 16) GEMM: 256-thread workgroups
 constexpr int kSkinnyNT = 2;             // 16-column blocks per skinny tile
 constexpr int kAttnChunk = 64;           // keys per attention step
+constexpr int kAttnStages = 2;           // attention chunks resident in LDS per workgroup
+constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU
 constexpr int kMaxSplits = 256;          // context splits of the split-KV attention
 constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
 

@@ -534,6 +534,17 @@ struct OpFuse {
     }
 };
 
+// ---------------------------------------------------------------------------
+// V pages store the positions of every 32-slot group in the order
+//   0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31
+// so that the 8 positions one lane feeds to a 32-key P.V matrix-core step
+// (4 from each 16-key half) are 8 consecutive elements.
+__host__ __device__ __forceinline__ int vslot(int slot) {
+    const int k = slot & 31;
+    const int pos = k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3);
+    return (slot & ~31) | pos;
+}
+
 // Paged draft-KV addressing: per (layer, K|V) an array of pages; K pages are
 // [nkv][page][d] (key rows), V pages [nkv][d][page] (value columns, so the
 // attention's P.V operand reads runs of consecutive positions).
@@ -608,8 +619,8 @@ struct OpInject {
                 pg[dim + half] = Elem<T>::from_f32(r1);
             } else {
                 T* pg = kv.vpage<T>(l, pos, slot) + (long long)h * d * kv.page;
-                pg[(long long)dim * kv.page + slot] = Elem<T>::from_f32(x0);
-                pg[(long long)(dim + half) * kv.page + slot] = Elem<T>::from_f32(x1);
+                pg[(long long)dim * kv.page + vslot(slot)] = Elem<T>::from_f32(x0);
+                pg[(long long)(dim + half) * kv.page + vslot(slot)] = Elem<T>::from_f32(x1);
             }
         }
     }
@@ -684,148 +695,302 @@ __device__ __forceinline__ Frag<float> join_runs(const VRun<float>& a, const VRu
     return f;
 }
 
-// One workgroup = one (split, kv head); one wave per query head of the group.
-// Scores are formed transposed, S^T = K Q^T (keys on MFMA rows, the 16 block
-// rows on columns), so that the probabilities land exactly in the B-operand
-// layout of O^T += V^T P^T and never leave registers.  All K and V loads of a
-// 64-key chunk are issued before any arithmetic on it.
-template <typename T, int D>
-__global__ __launch_bounds__(512) void attn_split_kernel(AttnArgs a) {
+// Online-softmax state of one query head (16 block rows, one per lane column).
+template <int D>
+struct HeadAcc {
+    float m, l;
+    f32x4_t o[D / 16];
+};
+
+// Softmax update for 64 keys whose S^T blocks are s[0..3] (keys kb*16 + 4grp + ii)
+// and P.V with V fragments from vfrag(t, db) (keys 32t + {4grp..4grp+3, 16+4grp..}).
+// Keys >= nvalid are masked.  For bf16 the probabilities enter as a hi + lo pair
+// of bf16 values (two MFMAs sharing the V operand), so P keeps ~16 bits.
+template <typename T, int D, class VF>
+__device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], int nvalid, float scale_log2, int grp,
+                                           VF&& vfrag) {
+    float mx = h.m;
+    float p[4][4];
+    const bool full = nvalid >= 64;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int kk = kb * 16 + 4 * grp + ii;
+            p[kb][ii] = (full || kk < nvalid) ? s[kb][ii] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, p[kb][ii]);
+        }
+    mx = cross4_max(mx);
+    const float alpha = exp2f(h.m - mx);
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const float e = exp2f(p[kb][ii] - mx);
+            p[kb][ii] = e;
+            ps += e;
+        }
+    ps = cross4_sum(ps);
+    h.l = h.l * alpha + ps;
+    h.m = mx;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) h.o[db] *= alpha;
+    constexpr bool kSplitP = sizeof(T) == 2;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float pv[8], pl[8];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) { pv[ii] = p[2 * t][ii]; pv[4 + ii] = p[2 * t + 1][ii]; }
+        Frag<T> pf, pf_lo;
+        if (kSplitP) {
+#pragma unroll
+            for (int q8 = 0; q8 < 8; ++q8) {
+                const float hi = Elem<T>::round(pv[q8]);
+                pl[q8] = pv[q8] - hi;
+                pv[q8] = hi;
+            }
+            pf_lo.set8(pl);
+        }
+        pf.set8(pv);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const Frag<T> vf = vfrag(t, db);
+            mma(h.o[db], vf, pf);
+            if (kSplitP) mma(h.o[db], vf, pf_lo);
+        }
+    }
+}
+
+// Zero the elements of a V fragment whose keys (32t + 4grp + {0..3}, 32t + 16 +
+// 4grp + {0..3}) are >= nvalid (positions never written may hold anything).
+__device__ __forceinline__ void mask_vfrag(Frag<bf16_t>& f, int t, int grp, int nvalid) {
+    const int a = 32 * t + 4 * grp, b = a + 16;
+    uint32_t m[4];
+    m[0] = (a + 0 < nvalid ? 0xFFFFu : 0u) | (a + 1 < nvalid ? 0xFFFF0000u : 0u);
+    m[1] = (a + 2 < nvalid ? 0xFFFFu : 0u) | (a + 3 < nvalid ? 0xFFFF0000u : 0u);
+    m[2] = (b + 0 < nvalid ? 0xFFFFu : 0u) | (b + 1 < nvalid ? 0xFFFF0000u : 0u);
+    m[3] = (b + 2 < nvalid ? 0xFFFFu : 0u) | (b + 3 < nvalid ? 0xFFFF0000u : 0u);
+    f.v.x &= m[0];
+    f.v.y &= m[1];
+    f.v.z &= m[2];
+    f.v.w &= m[3];
+}
+__device__ __forceinline__ void mask_vfrag(Frag<float>& f, int t, int grp, int nvalid) {
+    const int a = 32 * t + 4 * grp, b = a + 16;
+    f.a.x = a + 0 < nvalid ? f.a.x : 0.f;
+    f.a.y = a + 1 < nvalid ? f.a.y : 0.f;
+    f.a.z = a + 2 < nvalid ? f.a.z : 0.f;
+    f.a.w = a + 3 < nvalid ? f.a.w : 0.f;
+    f.b.x = b + 0 < nvalid ? f.b.x : 0.f;
+    f.b.y = b + 1 < nvalid ? f.b.y : 0.f;
+    f.b.z = b + 2 < nvalid ? f.b.z : 0.f;
+    f.b.w = b + 3 < nvalid ? f.b.w : 0.f;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Fragment read from an LDS tile of rows of `ncol` 16-byte columns whose
+// columns are XOR-swizzled by row; c16 = first logical 16-byte column.
+__device__ __forceinline__ Frag<bf16_t> lds_frag_t(const char* base, int row, int ncol, int c16, bf16_t*) {
+    Frag<bf16_t> f;
+    f.v = *reinterpret_cast<const uint4*>(base + (row * ncol + (c16 ^ (row % ncol))) * 16);
+    return f;
+}
+__device__ __forceinline__ Frag<float> lds_frag_t(const char* base, int row, int ncol, int c16, float*) {
+    Frag<float> f;
+    f.a = *reinterpret_cast<const float4*>(base + (row * ncol + (c16 ^ (row % ncol))) * 16);
+    f.b = *reinterpret_cast<const float4*>(base + (row * ncol + ((c16 + 1) ^ (row % ncol))) * 16);
+    return f;
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> lds_frag(const char* base, int row, int ncol, int c16) {
+    return lds_frag_t(base, row, ncol, c16, static_cast<T*>(nullptr));
+}
+
+// One workgroup (4 waves) = one (split, kv head).  Each 64-key chunk of the
+// split is brought into LDS once with direct global->LDS 16-byte loads (double
+// buffered), its 16-byte columns XOR-swizzled by row so fragment reads are
+// bank-conflict free; each wave then computes its query head(s) (HPW per wave)
+// from LDS.  Scores are formed transposed, S^T = K Q^T, so the probabilities
+// land in the B-operand layout of O^T += V^T P^T and never leave registers.
+template <typename T, int D, int HPW>
+__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
+    constexpr int CH = kAttnChunk;                  // keys per chunk (64)
+    constexpr int KCOL = D * (int)sizeof(T) / 16;   // 16-byte columns of a K row
+    constexpr int VCOL = CH * (int)sizeof(T) / 16;  // 16-byte columns of a V^T row
+    constexpr int NI = (CH * KCOL + D * VCOL) / 64 / 4;  // direct loads per wave per chunk
+    constexpr int STAGE = (CH * KCOL + D * VCOL) * 16;   // bytes per stage
+    constexpr int NS = kAttnStages;  // chunks in LDS: one computed while the next streams in
+    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE];
+
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = blockIdx.y, split = blockIdx.x;
-    const int hq = g * a.group + w;
     const int grp = lane >> 4, col = lane & 15;
     const T* q = reinterpret_cast<const T*>(a.q);
 
-    Frag<T> qf[D / 32];
+    Frag<T> qf[HPW][D / 32];
+    HeadAcc<D> acc[HPW];
+    if constexpr (NS == 2) {  // Q first: the code shape the compiler handles for the 2-stage form
 #pragma unroll
-    for (int kc = 0; kc < D / 32; ++kc) {
-        if (col < a.B) qf[kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
-        else qf[kc].zero();
-    }
-    float m = -INFINITY, l = 0.f;
-    f32x4_t o[D / 16];
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db] = zero4();
-
-    const bool ctx = split < a.n_splits;
-    const int kbeg = ctx ? split * a.kps : 0;
-    const int kend = ctx ? min(a.C, kbeg + a.kps) : a.B;
-
-    for (int key0 = kbeg; key0 < kend; key0 += kAttnChunk) {
-        const T* kbase;
-        long long krow_stride;
-        const T* vbase;
-        long long vrow_stride;
-        int slot0 = 0;
-        if (ctx) {
-            kbase = a.kv.kpage<T>(a.layer, key0, slot0) + ((long long)g * a.kv.page + slot0) * D;
-            krow_stride = D;
-            vbase = a.kv.vpage<T>(a.layer, key0, slot0) + (long long)g * D * a.kv.page + slot0;
-            vrow_stride = a.kv.page;
-        } else {
-            kbase = reinterpret_cast<const T*>(a.kblk) + (long long)g * D;
-            krow_stride = (long long)a.nkv * D;
-            vbase = reinterpret_cast<const T*>(a.vblkT) + (long long)g * D * 16;
-            vrow_stride = 16;
-        }
-        const int nvalid = kend - key0;  // keys of this chunk that exist (may exceed 64)
-        // ---- issue every load of the chunk
-        Frag<T> kf[4][D / 32];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const bool ok = kb * 16 + col < nvalid;
+        for (int hh = 0; hh < HPW; ++hh) {
+            const int hq = g * a.group + min(w + 4 * hh, a.group - 1);
 #pragma unroll
             for (int kc = 0; kc < D / 32; ++kc) {
-                if (ok) kf[kb][kc].load(kbase + (long long)(kb * 16 + col) * krow_stride + kc * 32 + grp * 8);
-                else kf[kb][kc].zero();
+                if (col < a.B) qf[hh][kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
+                else qf[hh][kc].zero();
             }
+            acc[hh].m = -INFINITY;
+            acc[hh].l = 0.f;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) acc[hh].o[db] = zero4();
         }
-        VRun<T> va[2][D / 16], vb[2][D / 16];
+    }
+    auto load_q = [&]() {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int oa = 32 * t + 4 * grp, ob = oa + 16;  // chunk offsets of the two runs
+        for (int hh = 0; hh < HPW; ++hh) {
+            const int hi = w + 4 * hh;
+            const int hq = g * a.group + min(hi, a.group - 1);
 #pragma unroll
-            for (int db = 0; db < D / 16; ++db) {
-                const T* vr = vbase + (long long)(16 * db + col) * vrow_stride;
-                if (oa + 4 <= nvalid) va[t][db].load(vr + oa); else va[t][db].load_masked(vr + oa, nvalid - oa);
-                if (ob + 4 <= nvalid) vb[t][db].load(vr + ob); else vb[t][db].load_masked(vr + ob, nvalid - ob);
+            for (int kc = 0; kc < D / 32; ++kc) {
+                if (col < a.B) qf[hh][kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
+                else qf[hh][kc].zero();
             }
+            acc[hh].m = -INFINITY;
+            acc[hh].l = 0.f;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) acc[hh].o[db] = zero4();
         }
-        // ---- S^T for 64 keys (4 blocks of 16)
-        f32x4_t s[4];
+    };
+
+    constexpr bool kEarlyQ = NS == 2;
+    if (split < a.n_splits) {
+        const int kbeg = split * a.kps;
+        const int kend = min(a.C, kbeg + a.kps);
+        const int nch = (kend - kbeg + CH - 1) / CH;
+        // issue the direct loads of chunk c into stage st
+        auto issue = [&](int c, int st) {
+            const int key0 = kbeg + c * CH;
+            int slot0;
+            const T* kp = a.kv.kpage<T>(a.layer, key0, slot0) + ((long long)g * a.kv.page + slot0) * D;
+            const T* vp = a.kv.vpage<T>(a.layer, key0, slot0) + (long long)g * D * a.kv.page + slot0;
+            const int rmax = kend - 1 - key0;  // last written key row of this chunk
+            char* base = lds + st * STAGE;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            s[kb] = zero4();
-#pragma unroll
-            for (int kc = 0; kc < D / 32; ++kc) mma(s[kb], kf[kb][kc], qf[kc]);
-        }
-        // ---- online softmax (log2 domain); lane column = query row `col`
-        float mx = m;
-        float p[4][4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int kk = kb * 16 + 4 * grp + ii;
-                p[kb][ii] = kk < nvalid ? s[kb][ii] * a.scale_log2 : -INFINITY;
-                mx = fmaxf(mx, p[kb][ii]);
-            }
-        mx = cross4_max(mx);
-        const float alpha = exp2f(m - mx);
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const float e = exp2f(p[kb][ii] - mx);
-                p[kb][ii] = e;
-                ps += e;
-            }
-        ps = cross4_sum(ps);
-        l = l * alpha + ps;
-        m = mx;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
-        // ---- O^T += V^T P^T, 32 keys per MFMA: slots 0-3 = keys 4grp..4grp+3 of
-        //      block 2t, slots 4-7 = the same keys of block 2t+1.  For bf16 the
-        //      probabilities enter as a hi + lo pair of bf16 values (two MFMAs
-        //      sharing the V operand), so P keeps ~16 significant bits.
-        constexpr bool kSplitP = sizeof(T) == 2;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            Frag<T> pf, pf_lo;
-            float pv[8], pl[8];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) { pv[ii] = p[2 * t][ii]; pv[4 + ii] = p[2 * t + 1][ii]; }
-            if (kSplitP) {
-#pragma unroll
-                for (int q8 = 0; q8 < 8; ++q8) {
-                    const float hi = Elem<T>::round(pv[q8]);
-                    pl[q8] = pv[q8] - hi;
-                    pv[q8] = hi;
+            for (int j = 0; j < NI; ++j) {
+                const int inst = w * NI + j;
+                const int P = inst * 64 + lane;  // 16-byte piece of the stage
+                const char* src;
+                if (P < CH * KCOL) {
+                    const int r = P / KCOL, pc = P % KCOL;
+                    const int c16 = pc ^ (r % KCOL);
+                    src = reinterpret_cast<const char*>(kp + (long long)min(r, rmax) * D) + c16 * 16;
+                } else {
+                    const int Q = P - CH * KCOL;
+                    const int dim = Q / VCOL, pc = Q % VCOL;
+                    const int c16 = pc ^ (dim % VCOL);
+                    src = reinterpret_cast<const char*>(vp + (long long)dim * a.kv.page) + c16 * 16;
                 }
-                pf_lo.set8(pl);
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(base + inst * 1024), 16, 0, 0);
             }
-            pf.set8(pv);
+        };
+        // prologue: chunks 0 .. NS-2 in flight before anything else
+        if constexpr (NS == 2) {
+            issue(0, 0);
+        } else {
+            for (int c = 0; c < NS - 1; ++c)
+                if (c < nch) issue(c, c);
+            load_q();
+        }
+        for (int c = 0; c < nch; ++c) {
+            if constexpr (NS == 2) {
+                if (c + 1 < nch) {
+                    issue(c + 1, (c + 1) & 1);
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+            } else {
+                if (c + NS - 1 < nch) issue(c + NS - 1, (c + NS - 1) % NS);
+                // wait for this wave's loads of chunk c: later chunks may stay in flight
+                const int later = min(NS - 1, nch - 1 - c);
+                if (later >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * NI) : "memory");
+                else if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
+                else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+                else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+            const char* kl = lds + (NS == 2 ? (c & 1) : (c % NS)) * STAGE;
+            const char* vl = kl + CH * KCOL * 16;
+            const int nvalid = kend - (kbeg + c * CH);
 #pragma unroll
-            for (int db = 0; db < D / 16; ++db) {
-                const Frag<T> vf = join_runs(va[t][db], vb[t][db]);
-                mma(o[db], vf, pf);
-                if (kSplitP) mma(o[db], vf, pf_lo);
+            for (int hh = 0; hh < HPW; ++hh) {
+                if (w + 4 * hh >= a.group) break;
+                f32x4_t sc[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    sc[kb] = zero4();
+                    const int r = kb * 16 + col;
+#pragma unroll
+                    for (int kc = 0; kc < D / 32; ++kc) {
+                        const Frag<T> kf = lds_frag<T>(kl, r, KCOL, (kc * 32 + grp * 8) * (int)sizeof(T) / 16);
+                        mma(sc[kb], kf, qf[hh][kc]);
+                    }
+                }
+                softmax_pv<T, D>(acc[hh], sc, nvalid, a.scale_log2, grp, [&](int t, int db) {
+                    Frag<T> vf = lds_frag<T>(vl, 16 * db + col, VCOL, (32 * t + 8 * grp) * (int)sizeof(T) / 16);
+                    if (nvalid < CH) mask_vfrag(vf, t, grp, nvalid);  // never-written positions of the last chunk
+                    return vf;
+                });
             }
+            __syncthreads();  // stage (c % NS) is overwritten by chunk c + NS
+        }
+    } else {
+        if (!kEarlyQ) load_q();
+        // the block's own B keys (rows >= B were never written)
+        const T* kb_ = reinterpret_cast<const T*>(a.kblk) + (long long)g * D;
+        const T* vb_ = reinterpret_cast<const T*>(a.vblkT) + (long long)g * D * 16;
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            if (w + 4 * hh >= a.group) break;
+            f32x4_t sc[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                sc[kb] = zero4();
+                const int r = min(kb * 16 + col, a.B - 1);
+#pragma unroll
+                for (int kc = 0; kc < D / 32; ++kc) {
+                    Frag<T> kf;
+                    kf.load(kb_ + (long long)r * a.nkv * D + kc * 32 + grp * 8);
+                    mma(sc[kb], kf, qf[hh][kc]);
+                }
+            }
+            softmax_pv<T, D>(acc[hh], sc, a.B, a.scale_log2, grp, [&](int t, int db) {
+                VRun<T> ra, rb;
+                const T* vr = vb_ + (long long)(16 * db + col) * 16;
+                if (t == 0) ra.load(vr + 4 * grp); else ra.load_masked(vr, 0);
+                rb.load_masked(vr, 0);  // keys 16..31 do not exist
+                Frag<T> vf = join_runs(ra, rb);
+                mask_vfrag(vf, t, grp, a.B);
+                return vf;
+            });
         }
     }
     // ---- partial results
-    const long long pidx = ((long long)split * a.nq + hq) * 16;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
+    for (int hh = 0; hh < HPW; ++hh) {
+        if (w + 4 * hh >= a.group) break;
+        const int hq = g * a.group + w + 4 * hh;
+        const long long pidx = ((long long)split * a.nq + hq) * 16;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            a.part_o[(pidx + col) * D + 16 * db + 4 * grp + ii] = o[db][ii];
-    if (grp == 0) {
-        a.part_ml[(pidx + col) * 2 + 0] = m;
-        a.part_ml[(pidx + col) * 2 + 1] = l;
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                a.part_o[(pidx + col) * D + 16 * db + 4 * grp + ii] = acc[hh].o[db][ii];
+        if (grp == 0) {
+            a.part_ml[(pidx + col) * 2 + 0] = acc[hh].m;
+            a.part_ml[(pidx + col) * 2 + 1] = acc[hh].l;
+        }
     }
 }
 
@@ -1009,7 +1174,7 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(KVPages kv, T* k, T* v, in
         const int h = (int)(r / kv.d), dim = (int)(r - (long long)h * kv.d);
         int slot;
         T* kp = kv.kpage<T>(l, pos0 + i, slot) + ((long long)h * kv.page + slot) * kv.d + dim;
-        T* vp = kv.vpage<T>(l, pos0 + i, slot) + ((long long)h * kv.d + dim) * kv.page + slot;
+        T* vp = kv.vpage<T>(l, pos0 + i, slot) + ((long long)h * kv.d + dim) * kv.page + vslot(slot);
         if (to_pages) { *kp = k[e]; *vp = v[e]; }
         else { k[e] = *kp; v[e] = *vp; }
     }
@@ -1117,7 +1282,7 @@ struct BigInjectOp {
                 pg[dim] = Elem<T>::from_f32(val);
             } else {
                 T* pg = kv.vpage<T>(l, pos, slot) + (long long)h * d * kv.page;
-                pg[(long long)dim * kv.page + slot] = Elem<T>::from_f32(own);
+                pg[(long long)dim * kv.page + vslot(slot)] = Elem<T>::from_f32(own);
             }
         }
     }
@@ -1257,10 +1422,11 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
         aa.part_o = WS(float*, attn_o);
         aa.part_ml = WS(float*, attn_ml);
         c.tracer->begin(DFLASH_TRACE_ATTN, s);
-        if (D == 128)
-            hipLaunchKernelGGL((attn_split_kernel<T, 128>), dim3(ns + 1, nkv), dim3(64 * group), 0, s, aa);
-        else
-            hipLaunchKernelGGL((attn_split_kernel<T, 64>), dim3(ns + 1, nkv), dim3(64 * group), 0, s, aa);
+        const dim3 agrid(ns + 1, nkv), ablk(256);
+        if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1>), agrid, ablk, 0, s, aa);
+        else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2>), agrid, ablk, 0, s, aa);
+        else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1>), agrid, ablk, 0, s, aa);
+        else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2>), agrid, ablk, 0, s, aa);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(512), 0, s, aa.part_o, aa.part_ml, ns + 1, nq,
                            D, B, obuf);
