@@ -45,6 +45,23 @@ def alg_bytes(s, C):
             "fuse16": fuse16, "inject16": inject16, "step": draft + fuse16 + inject16}
 
 
+def profiled_traffic(workload):
+    """HBM bytes per LM-head launch from the committed counter passes, or None
+    when they were taken on another workload or on different kernel sources."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "lm_head_qwen3_8b_4k_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -54,6 +71,8 @@ def main():
     ap.add_argument("--long-ctx", type=int, default=36864, help="second context length measured (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="after timing, copy this many GiB device-to-device (plain copy kernel for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (each GPU would run its own "
@@ -176,9 +195,18 @@ def main():
         "mean_accept_k": stats["k"] / max(stats["n"], 1),
         "roofline": {"bound": "hbm", "kernel": "skinny_kernel<OpLMHead> (LM head + argmax)",
                      "achieved": round(lm_ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(lm_ach / HBM_PEAK, 4), "traffic": None,
+                     "frac": round(lm_ach / HBM_PEAK, 4), "traffic": profiled_traffic(args.workload),
                      "alg_bytes_per_launch": ab["lm_head"], "avg_launch_us": round(lm_ms * 1e3, 2)},
     }
+
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+        del src, dst
 
     # ---- per-kernel-class breakdown (separate short traced runs, not the timed region)
     if not args.no_breakdown:
