@@ -98,6 +98,8 @@ def lib():
         L.dflash_load_kv.argtypes = [vp, vp, vp, i32, i32, vp]
         L.dflash_read_kv.restype = st
         L.dflash_read_kv.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.dflash_target_forward.restype = st
+        L.dflash_target_forward.argtypes = [vp, vp, i32, vp, vp, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -233,6 +235,28 @@ class DFlash:
         self._check(lib().dflash_verify_accept(self.h, draft.data_ptr(), target.data_ptr(), out.data_ptr(),
                                                _stream(stream)), "verify_accept")
         return out
+
+    def target_forward(self, tokens: torch.Tensor, argmax: Optional[torch.Tensor] = None, want_logits: bool = False,
+                       logits: Optional[torch.Tensor] = None, capture: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                       stream=None):
+        """Causal forward of tokens (device int32[M], M <= 16) at positions length..length+M-1.
+        capture: 5 tensors [>= M, H] with one common row stride (or None entries).
+        Returns (argmax int32[M], logits fp32[M, V] or None)."""
+        M, V = tokens.shape[0], self.shape.vocab
+        if argmax is None:
+            argmax = torch.empty(M, dtype=torch.int32, device=self.device)
+        if want_logits and logits is None:
+            logits = torch.empty(M, V, dtype=torch.float32, device=self.device)
+        cap, ld = None, 0
+        if capture is not None:
+            assert len(capture) == 5
+            live = [t for t in capture if t is not None]
+            ld = live[0].stride(0) if live else self.shape.hidden
+            assert all(t.stride(0) == ld for t in live)
+            cap = (C.c_void_p * 5)(*[_p(t) for t in capture])
+        self._check(lib().dflash_target_forward(self.h, tokens.data_ptr(), M, _p(logits), argmax.data_ptr(), cap, ld,
+                                                _stream(stream)), "target_forward")
+        return argmax, logits
 
     def rollback(self, new_len: int):
         self._check(lib().dflash_rollback(self.h, new_len), "rollback")

@@ -107,7 +107,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     if (st != DFLASH_OK) return st;
     if (!w || !workspace || (!kv_pool && d.max_ctx > 0)) return DFLASH_ERR_INVAL;
     if (!aligned(workspace, 256) || !aligned(kv_pool, 256)) return DFLASH_ERR_INVAL;
-    if (!w->fc || !w->fc_norm) return DFLASH_ERR_INVAL;
+    if (!w->fc != !w->fc_norm) return DFLASH_ERR_INVAL;  // fusion weights come as a pair, or not at all
     for (int l = 0; l < d.Ld; ++l)
         if (!w->wk[l] || !w->wv[l]) return DFLASH_ERR_INVAL;
 
@@ -176,7 +176,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     const long long nqd = (long long)d.nq * d.d, nkd = (long long)d.nkv * d.d;
     struct Job { const void* src; long long N, K; const void* dst; };
     std::vector<Job> jobs;
-    jobs.push_back({w->fc, d.H, 5LL * d.H, x.sw_fc});
+    if (w->fc) jobs.push_back({w->fc, d.H, 5LL * d.H, x.sw_fc});
     if (w->lm_head) jobs.push_back({w->lm_head, d.V, d.H, x.sw_lm});
     for (int l = 0; l < d.Ld; ++l) {
         jobs.push_back({w->wk[l], nkd, d.H, x.sw_wk[l]});
@@ -227,6 +227,7 @@ dflash_status dflash_fuse_context(dflash_ctx* c, const void* const* layer_hidden
     if (!c) return DFLASH_ERR_INVAL;
     const Dims& d = c->dev.dm;
     if (!layer_hidden || !fused_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (!c->dev.fc) return fail(c, DFLASH_ERR_STATE, "context was created without fusion weights");
     if (M < 1 || M > d.max_rows) return fail(c, DFLASH_ERR_CAPACITY, "M must be in [1, max_rows]");
     if (ld < d.H || ld % (16 / d.elem)) return fail(c, DFLASH_ERR_INVAL, "ld must be >= H and keep rows 16-byte aligned");
     int32_t sel[5];
@@ -295,6 +296,33 @@ dflash_status dflash_rollback(dflash_ctx* c, int32_t new_len) {
     return DFLASH_OK;
 }
 
+dflash_status dflash_target_forward(dflash_ctx* c, const int32_t* tokens, int32_t M, float* logits_out,
+                                    int32_t* argmax_out, void* const* capture, int64_t capture_ld, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const DevCtx& x = c->dev;
+    const Dims& d = x.dm;
+    if (!tokens || !argmax_out) return fail(c, DFLASH_ERR_INVAL, "null tokens or argmax_out");
+    if (M < 1 || M > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 16]");
+    if (!x.embed || !x.lm_head || !x.final_norm) return fail(c, DFLASH_ERR_INVAL, "needs embed, lm_head, final_norm");
+    for (int l = 0; l < d.Ld; ++l)
+        if (!x.attn_norm[l] || !x.wq[l] || !x.wo[l] || !x.mlp_norm[l] || !x.wg[l] || !x.wu[l] || !x.wd[l])
+            return fail(c, DFLASH_ERR_INVAL, "needs every layer's weights");
+    if (logits_out && !aligned(logits_out, 4)) return fail(c, DFLASH_ERR_INVAL, "logits_out misaligned");
+    if (capture) {
+        if (capture_ld < d.H) return fail(c, DFLASH_ERR_INVAL, "capture_ld must be >= H");
+        for (int i = 0; i < DFLASH_NUM_FEATURES; ++i)
+            if (capture[i] && !aligned(capture[i], d.elem)) return fail(c, DFLASH_ERR_INVAL, "capture buffer misaligned");
+    }
+    if ((long long)c->length + M > d.max_ctx) return fail(c, DFLASH_ERR_CAPACITY, "forward would exceed max_ctx");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_causal_forward(x, c->length, tokens, M, logits_out, argmax_out, capture, capture_ld,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "target forward launch");
+    c->length += M;
+    return DFLASH_OK;
+}
+
 dflash_status dflash_load_kv(dflash_ctx* c, const void* k, const void* v, int32_t M, int32_t pos0, void* stream) {
     if (!c) return DFLASH_ERR_INVAL;
     const Dims& d = c->dev.dm;
@@ -325,7 +353,7 @@ dflash_status dflash_read_kv(dflash_ctx* c, int32_t pos0, int32_t M, void* k_out
 
 dflash_status dflash_trace_enable(dflash_ctx* c, int32_t kernel_class, int32_t max_launches) {
     if (!c) return DFLASH_ERR_INVAL;
-    if (kernel_class < DFLASH_TRACE_OFF || kernel_class > DFLASH_TRACE_INJECT || max_launches < 0 ||
+    if (kernel_class < DFLASH_TRACE_OFF || kernel_class > DFLASH_TRACE_TARGET || max_launches < 0 ||
         max_launches > (1 << 20))
         return fail(c, DFLASH_ERR_INVAL, "bad trace class or launch count");
     hipError_t e = hipDeviceSynchronize();

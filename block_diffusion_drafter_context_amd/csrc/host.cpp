@@ -162,4 +162,10 @@ void attn_split_plan(int C, int nkv, int num_cus, int* kps, int* ns) {
     *ns = (int)n;
 }
 
+int causal_split_keys(int max_ctx) {
+    long long per = (std::max(max_ctx, 1) + (long long)kMaxSplits - 1) / kMaxSplits;
+    per = ((per + kAttnChunk - 1) / kAttnChunk) * kAttnChunk;
+    return (int)std::max<long long>(per, 4 * kAttnChunk);
+}
+
 }  // namespace dflash

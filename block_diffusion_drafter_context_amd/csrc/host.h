@@ -75,4 +75,9 @@ void feature_layers(int target_layers, int32_t out[5]);
 // kAttnChunk) and number of context splits (the block keys get one more).
 void attn_split_plan(int C, int nkv, int num_cus, int* keys_per_split, int* n_splits);
 
+// Keys per split of the causal forward: fixed for a context (it depends on
+// max_ctx only), so split boundaries sit at the same absolute positions in
+// every call.
+int causal_split_keys(int max_ctx);
+
 }  // namespace dflash

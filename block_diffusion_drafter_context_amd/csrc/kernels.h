@@ -65,6 +65,9 @@ hipError_t launch_swizzle(int dtype, const void* W, int N, int K, void* out, hip
 // One draft block over the first C context positions.
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits,
                               int32_t* tokens, hipStream_t s);
+// Causal forward of M <= 16 tokens at positions C..C+M-1 (K/V appended to the cache).
+hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits,
+                                 int32_t* argmax, void* const* capture, long long capture_ld, hipStream_t s);
 // Context fusion of M rows (selected slabs given in ascending layer order).
 hipError_t launch_fuse(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out,
                        hipStream_t s);

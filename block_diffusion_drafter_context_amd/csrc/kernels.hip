@@ -243,6 +243,40 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
 
 // Ops ------------------------------------------------------------------------
 
+// V pages store the positions of every 32-slot group in the order
+//   0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31
+// so that the 8 positions one lane feeds to a 32-key P.V matrix-core step
+// (4 from each 16-key half) are 8 consecutive elements.
+__host__ __device__ __forceinline__ int vslot(int slot) {
+    const int k = slot & 31;
+    const int pos = k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3);
+    return (slot & ~31) | pos;
+}
+
+// Paged draft-KV addressing: per (layer, K|V) an array of pages; K pages are
+// [nkv][page][d] (key rows), V pages [nkv][d][page] (value columns, so the
+// attention's P.V operand reads runs of consecutive positions).
+struct KVPages {
+    char* base;
+    const int32_t* table;
+    long long layer_kv_bytes;  // bytes of one (layer, K|V) page array
+    int page, nkv, d, elem;
+    __device__ __forceinline__ long long page_elems() const { return (long long)nkv * page * d; }
+    template <typename T>
+    __device__ __forceinline__ T* kpage(int l, int pos, int& slot) const {
+        const int p = pos / page;
+        slot = pos - p * page;
+        return reinterpret_cast<T*>(base + (2LL * l) * layer_kv_bytes) + (long long)table[p] * page_elems();
+    }
+    template <typename T>
+    __device__ __forceinline__ T* vpage(int l, int pos, int& slot) const {
+        const int p = pos / page;
+        slot = pos - p * page;
+        return reinterpret_cast<T*>(base + (2LL * l + 1) * layer_kv_bytes) + (long long)table[p] * page_elems();
+    }
+};
+
+
 // q, k (rotated) and v of the block rows.  Tiles pair the 16-column blocks
 // (16i, 16i + d/2) of one head so each rotary pair sits in one lane.
 template <typename T>
@@ -258,8 +292,10 @@ struct OpQKV {
     const float* cosT;
     const float* sinT;
     T* qout;
-    T* kout;
-    T* vTout;
+    T* kout;      // block keys [16][nkv*d], or null: keys go to the cache
+    T* vTout;     // block values [nkv][d][16], or null: values go to the cache
+    KVPages kv;   // cache pages of `layer` (used when kout is null)
+    int layer;
     __device__ __forceinline__ void decode(int tile, int& kind, int& h, int& i) const {
         const int per = d / 32;
         int t = tile;
@@ -297,6 +333,17 @@ struct OpQKV {
                 T* o = qout + (long long)j * nq * d + h * d;
                 o[dim] = Elem<T>::from_f32(x0);
                 o[dim + half] = Elem<T>::from_f32(x1);
+            } else if (!kout) {
+                int slot;
+                if (kind == 1) {
+                    T* pg = kv.kpage<T>(layer, pos0 + j, slot) + ((long long)h * kv.page + slot) * d;
+                    pg[dim] = Elem<T>::from_f32(x0);
+                    pg[dim + half] = Elem<T>::from_f32(x1);
+                } else {
+                    T* pg = kv.vpage<T>(layer, pos0 + j, slot) + (long long)h * d * kv.page;
+                    pg[(long long)dim * kv.page + vslot(slot)] = Elem<T>::from_f32(x0);
+                    pg[(long long)(dim + half) * kv.page + vslot(slot)] = Elem<T>::from_f32(x1);
+                }
             } else if (kind == 1) {
                 T* o = kout + (long long)j * nkv * d + h * d;
                 o[dim] = Elem<T>::from_f32(x0);
@@ -324,6 +371,8 @@ struct OpResid {
     float* ss_part;
     float* rstd_out;
     float eps;
+    T* cap = nullptr;        // optional copy of the updated rows (stride cap_ld)
+    long long cap_ld = 0;
     __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
         const int n0 = 32 * tile + 16 * blk;
         return n0 < N ? sw_stream(w, n0 / 16, nch) : nullptr;
@@ -343,6 +392,7 @@ struct OpResid {
                 T* p = x + (long long)j * N + n;
                 const float xn = Elem<T>::round(Elem<T>::to_f32(*p) + Elem<T>::round(acc[b][ii]));
                 *p = Elem<T>::from_f32(xn);
+                if (cap) cap[(long long)j * cap_ld + n] = Elem<T>::from_f32(xn);
                 sq[ii] += xn * xn;
             }
         }
@@ -534,39 +584,6 @@ struct OpFuse {
     }
 };
 
-// ---------------------------------------------------------------------------
-// V pages store the positions of every 32-slot group in the order
-//   0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31
-// so that the 8 positions one lane feeds to a 32-key P.V matrix-core step
-// (4 from each 16-key half) are 8 consecutive elements.
-__host__ __device__ __forceinline__ int vslot(int slot) {
-    const int k = slot & 31;
-    const int pos = k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3);
-    return (slot & ~31) | pos;
-}
-
-// Paged draft-KV addressing: per (layer, K|V) an array of pages; K pages are
-// [nkv][page][d] (key rows), V pages [nkv][d][page] (value columns, so the
-// attention's P.V operand reads runs of consecutive positions).
-struct KVPages {
-    char* base;
-    const int32_t* table;
-    long long layer_kv_bytes;  // bytes of one (layer, K|V) page array
-    int page, nkv, d, elem;
-    __device__ __forceinline__ long long page_elems() const { return (long long)nkv * page * d; }
-    template <typename T>
-    __device__ __forceinline__ T* kpage(int l, int pos, int& slot) const {
-        const int p = pos / page;
-        slot = pos - p * page;
-        return reinterpret_cast<T*>(base + (2LL * l) * layer_kv_bytes) + (long long)table[p] * page_elems();
-    }
-    template <typename T>
-    __device__ __forceinline__ T* vpage(int l, int pos, int& slot) const {
-        const int p = pos / page;
-        slot = pos - p * page;
-        return reinterpret_cast<T*>(base + (2LL * l + 1) * layer_kv_bytes) + (long long)table[p] * page_elems();
-    }
-};
 
 // Injection of M <= 16 rows into every layer.  Tile order: layer, K|V, head,
 // pair i of blocks (16i, 16i + d/2).
@@ -658,6 +675,7 @@ struct AttnArgs {
     const void* vblkT;  // [nkv][d][16]
     KVPages kv;
     int layer, C, B, nq, nkv, group, kps, n_splits;
+    int causal_base;    // >= 0: causal, query row j sees keys 0..causal_base+j; -1: no mask
     float scale_log2;   // log2(e) / sqrt(d)
     float* part_o;      // [(n_splits+1)][nq][16][d]
     float* part_ml;     // [(n_splits+1)][nq][16][2]
@@ -704,8 +722,10 @@ struct HeadAcc {
 
 // Softmax update for 64 keys whose S^T blocks are s[0..3] (keys kb*16 + 4grp + ii)
 // and P.V with V fragments from vfrag(t, db) (keys 32t + {4grp..4grp+3, 16+4grp..}).
-// Keys >= nvalid are masked.  For bf16 the probabilities enter as a hi + lo pair
-// of bf16 values (two MFMAs sharing the V operand), so P keeps ~16 bits.
+// Keys >= nvalid (this lane's query row) are masked; a row with no visible key
+// yet keeps m = -inf, l = 0, o = 0.  For bf16 the probabilities enter as a
+// hi + lo pair of bf16 values (two MFMAs sharing the V operand), so P keeps
+// ~16 bits.
 template <typename T, int D, class VF>
 __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], int nvalid, float scale_log2, int grp,
                                            VF&& vfrag) {
@@ -721,13 +741,14 @@ __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], in
             mx = fmaxf(mx, p[kb][ii]);
         }
     mx = cross4_max(mx);
-    const float alpha = exp2f(h.m - mx);
+    const float mref = mx == -INFINITY ? 0.f : mx;  // all keys masked so far: exp2(-inf) = 0
+    const float alpha = exp2f(h.m - mref);
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const float e = exp2f(p[kb][ii] - mx);
+            const float e = exp2f(p[kb][ii] - mref);
             p[kb][ii] = e;
             ps += e;
         }
@@ -923,6 +944,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
             const char* kl = lds + (NS == 2 ? (c & 1) : (c % NS)) * STAGE;
             const char* vl = kl + CH * KCOL * 16;
             const int nvalid = kend - (kbeg + c * CH);
+            // keys this lane's query row may see (causal: positions <= causal_base + row)
+            const int nvis = a.causal_base >= 0 ? min(nvalid, a.causal_base + col + 1 - (kbeg + c * CH)) : nvalid;
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
                 if (w + 4 * hh >= a.group) break;
@@ -937,7 +960,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
                         mma(sc[kb], kf, qf[hh][kc]);
                     }
                 }
-                softmax_pv<T, D>(acc[hh], sc, nvalid, a.scale_log2, grp, [&](int t, int db) {
+                softmax_pv<T, D>(acc[hh], sc, nvis, a.scale_log2, grp, [&](int t, int db) {
                     Frag<T> vf = lds_frag<T>(vl, 16 * db + col, VCOL, (32 * t + 8 * grp) * (int)sizeof(T) / 16);
                     if (nvalid < CH) mask_vfrag(vf, t, grp, nvalid);  // never-written positions of the last chunk
                     return vf;
@@ -1069,14 +1092,15 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
     return red[0] + red[1] + red[2] + red[3];
 }
 
-// Block rows: embedding of [anchor, mask, ...] and their RMS statistics.
+// Rows of the pass: row j embeds ids[j] for j < n_ids and the mask token
+// otherwise (a draft block is [anchor, mask, ...]); also their RMS statistics.
 // 16-byte accesses; every thread's loads are issued before any use.
 template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_t* anchor, int mask_id, int V,
+__global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_t* ids, int n_ids, int mask_id, int V,
                                                     int H, float eps, T* x, float* rstd, unsigned long long* best) {
     __shared__ float red[4];
     const int j = blockIdx.x;
-    const int tok = j == 0 ? min(max(anchor[0], 0), V - 1) : mask_id;  // out-of-range anchors are clamped
+    const int tok = j < n_ids ? min(max(ids[j], 0), V - 1) : mask_id;  // out-of-range ids are clamped
     const Frag<T>* src = reinterpret_cast<const Frag<T>*>(embed + (long long)tok * H);
     Frag<T>* dst = reinterpret_cast<Frag<T>*>(x + (long long)j * H);
     const int n8 = H / 8;  // H is a multiple of 32
@@ -1354,11 +1378,31 @@ static KVPages make_pages(const DevCtx& c) {
 
 #define WS(type, field) reinterpret_cast<type>(c.ws + c.lay.field)
 
+// One pass of the decoder stack over `rows` rows at positions C..C+rows-1.
+//  draft  (causal == false): rows = the block [anchor, mask, ...]; every row
+//          attends to the C cached context keys and to all block keys (held in
+//          workspace, never written to the cache).
+//  causal (causal == true):  rows = `n_ids` given tokens; each layer writes
+//          their K/V into the cache at C.. first, then row j attends to cache
+//          keys 0..C+j.  The context splits sit at fixed absolute key
+//          positions, so a row's result does not depend on how many rows
+//          share the pass.
+struct PassArgs {
+    int C;
+    const int32_t* ids;
+    int n_ids;
+    int rows;
+    bool causal;
+    float* logits;
+    int32_t* tokens;
+    void* const* cap;  // causal: 5 capture buffers (feature layers) or null
+    long long cap_ld;
+};
+
 template <typename T>
-static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, float* logits, int32_t* tokens,
-                                hipStream_t s) {
+static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     const Dims& d = c.dm;
-    const int H = d.H, B = d.B, nq = d.nq, nkv = d.nkv, D = d.d, F = d.F;
+    const int H = d.H, B = pa.rows, nq = d.nq, nkv = d.nkv, D = d.d, F = d.F, C = pa.C;
     T* x = WS(T*, x);
     T* q = WS(T*, q);
     T* kblk = WS(T*, kblk);
@@ -1374,13 +1418,22 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
     const float eps = (float)d.eps;
     hipError_t e;
 
-    hipLaunchKernelGGL((embed_kernel<T>), dim3(B), dim3(256), 0, s, (const T*)c.embed, anchor, d.mask_id, d.V, H, eps, x,
-                       rstd, best);
+    hipLaunchKernelGGL((embed_kernel<T>), dim3(B), dim3(256), 0, s, (const T*)c.embed, pa.ids, pa.n_ids, d.mask_id, d.V,
+                       H, eps, x, rstd, best);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    int kps, ns;
-    attn_split_plan(C, nkv, c.num_cus, &kps, &ns);
+    int kps, ns, nparts;
+    if (pa.causal) {
+        kps = causal_split_keys(d.max_ctx);
+        ns = (C + B + kps - 1) / kps;
+        nparts = ns;
+    } else {
+        attn_split_plan(C, nkv, c.num_cus, &kps, &ns);
+        nparts = ns + 1;  // + the block's own keys
+    }
     const int group = nq / nkv;
+    int32_t sel[5];
+    feature_layers(d.Lt, sel);
 
     for (int l = 0; l < d.Ld; ++l) {
         OpQKV<T> qkv;
@@ -1399,8 +1452,10 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
         qkv.cosT = cosT;
         qkv.sinT = sinT;
         qkv.qout = q;
-        qkv.kout = kblk;
-        qkv.vTout = vblkT;
+        qkv.kout = pa.causal ? nullptr : kblk;
+        qkv.vTout = pa.causal ? nullptr : vblkT;
+        qkv.kv = make_pages<T>(c);
+        qkv.layer = l;
         c.tracer->begin(DFLASH_TRACE_QKV, s);
         if ((e = run_skinny<T>(c, qkv, B, H, qkv.tq + 2 * qkv.tk, s)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_QKV, s);
@@ -1411,24 +1466,25 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
         aa.vblkT = vblkT;
         aa.kv = make_pages<T>(c);
         aa.layer = l;
-        aa.C = C;
+        aa.C = pa.causal ? C + B : C;
         aa.B = B;
         aa.nq = nq;
         aa.nkv = nkv;
         aa.group = group;
         aa.kps = kps;
         aa.n_splits = ns;
+        aa.causal_base = pa.causal ? C : -1;
         aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
         aa.part_o = WS(float*, attn_o);
         aa.part_ml = WS(float*, attn_ml);
         c.tracer->begin(DFLASH_TRACE_ATTN, s);
-        const dim3 agrid(ns + 1, nkv), ablk(256);
+        const dim3 agrid(nparts, nkv), ablk(256);
         if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1>), agrid, ablk, 0, s, aa);
         else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2>), agrid, ablk, 0, s, aa);
         else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1>), agrid, ablk, 0, s, aa);
         else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2>), agrid, ablk, 0, s, aa);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(512), 0, s, aa.part_o, aa.part_ml, ns + 1, nq,
+        hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(512), 0, s, aa.part_o, aa.part_ml, nparts, nq,
                            D, B, obuf);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_ATTN, s);
@@ -1469,6 +1525,12 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
         dn.ss_part = ss;
         dn.rstd_out = rstd;
         dn.eps = eps;
+        if (pa.cap)
+            for (int i = 0; i < 5; ++i)
+                if (sel[i] == l && pa.cap[i]) {  // layer l's output is a captured feature layer
+                    dn.cap = (T*)pa.cap[i];
+                    dn.cap_ld = pa.cap_ld;
+                }
         c.tracer->begin(DFLASH_TRACE_DOWN, s);
         if ((e = run_skinny<T>(c, dn, B, F, (H + 31) / 32, s)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_DOWN, s);
@@ -1480,10 +1542,10 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
     lm.V = d.V;
     lm.K = H;
     lm.M = B;
-    lm.logits = logits;
+    lm.logits = pa.logits;
     lm.best = best;
     lm.wg_cnt = counters + 1;
-    lm.tokens = tokens;
+    lm.tokens = pa.tokens;
     c.tracer->begin(DFLASH_TRACE_LM_HEAD, s);
     if ((e = run_skinny<T>(c, lm, B, H, (d.V + 31) / 32, s)) != hipSuccess) return e;
     c.tracer->end(DFLASH_TRACE_LM_HEAD, s);
@@ -1492,10 +1554,19 @@ static hipError_t draft_block_t(const DevCtx& c, int C, const int32_t* anchor, f
 
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits, int32_t* tokens,
                               hipStream_t s) {
+    PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0};
     c.tracer->begin(DFLASH_TRACE_DRAFT, s);
-    hipError_t e = c.dm.dtype == DFLASH_F32 ? draft_block_t<float>(c, C, anchor, logits, tokens, s)
-                                            : draft_block_t<bf16_t>(c, C, anchor, logits, tokens, s);
+    hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_DRAFT, s);
+    return e;
+}
+
+hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits, int32_t* argmax,
+                                 void* const* capture, long long capture_ld, hipStream_t s) {
+    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld};
+    c.tracer->begin(DFLASH_TRACE_TARGET, s);
+    hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
+    if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_TARGET, s);
     return e;
 }
 

@@ -1,0 +1,113 @@
+"""Greedy and DFlash speculative generation over libdflash contexts.
+
+Orchestration only: every step of the model runs in libdflash calls; torch
+holds the device buffers and moves a few token ids between them.
+
+A *target* is a ``DFlash`` context whose decoder stack is the target model
+(its ``draft_layers`` field set to the target's layer count) used through
+``target_forward``; a *draft* is a ``DFlash`` context holding the draft model
+and its fusion weights.
+"""
+from __future__ import annotations
+
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import DFlash, feature_layers
+
+ROWS = 16  # rows per target call: the largest block libdflash verifies at once
+
+
+class _Capture:
+    """Device buffers for the five captured target layers of one call."""
+
+    def __init__(self, target: DFlash):
+        s = target.shape
+        self.sel = feature_layers(s.target_layers)
+        self.slabs = [torch.empty(ROWS, s.hidden, dtype=target.dtype, device=target.device) for _ in range(5)]
+        self.n_layers = s.target_layers
+
+    def views(self, M: int):
+        return [t[:M] for t in self.slabs]
+
+    def layer_list(self, M: int):
+        lst: List[Optional[torch.Tensor]] = [None] * self.n_layers
+        for i, l in enumerate(self.sel):
+            lst[l] = self.slabs[i][:M]
+        return lst
+
+
+def prefill(target: DFlash, prompt: torch.Tensor, draft: Optional[DFlash] = None) -> torch.Tensor:
+    """Run the prompt (device int32[P]) through the target in calls of up to 16
+    rows; with a draft, fuse and inject every call's captured features as its
+    context.  Returns the first generated token as device int32[1]."""
+    cap = _Capture(target)
+    am = torch.empty(ROWS, dtype=torch.int32, device=target.device)
+    fused = None
+    if draft is not None:
+        fused = torch.empty(ROWS, draft.shape.hidden, dtype=draft.dtype, device=draft.device)
+    P = prompt.shape[0]
+    M = 0
+    for r0 in range(0, P, ROWS):
+        M = min(ROWS, P - r0)
+        target.target_forward(prompt[r0:r0 + M], argmax=am[:M], capture=cap.views(M) if draft is not None else None)
+        if draft is not None:
+            f = draft.fuse_context(cap.layer_list(M), out=fused[:M])
+            draft.inject_kv(f, r0)
+    return am[M - 1:M].clone()
+
+
+def greedy_generate(target: DFlash, prompt: torch.Tensor, n_new: int) -> torch.Tensor:
+    """Plain greedy decoding: one target row per call.  Device int32[n_new]."""
+    out = torch.empty(n_new, dtype=torch.int32, device=target.device)
+    out[0:1].copy_(prefill(target, prompt))
+    for i in range(1, n_new):
+        target.target_forward(out[i - 1:i], argmax=out[i:i + 1])
+    return out
+
+
+def spec_generate(target: DFlash, draft: DFlash, prompt: torch.Tensor, n_new: int,
+                  drafts_fn: Optional[Callable[[int], Sequence[int]]] = None) -> Tuple[List[int], List[int]]:
+    """DFlash speculative decoding with greedy block verification.
+
+    Per step at context length C with anchor a (the last emitted token, at C):
+    draft the block [a, mask, ...] (or take drafts_fn(C) -> B-1 ids), verify
+    [a, d_1..d_{B-1}] with one causal target call, accept the k leading drafts
+    that equal the target's tokens, emit them and the target's next token
+    (bonus); fuse and inject all B verified rows into the draft, then keep
+    C + k + 1 positions in both caches.  Returns (tokens, k of every step)."""
+    B = draft.shape.block
+    dev = target.device
+    first = prefill(target, prompt, draft)
+    cap = _Capture(target)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+    vin = torch.empty(B, dtype=torch.int32, device=dev)
+    g = torch.empty(B, dtype=torch.int32, device=dev)
+    res = torch.empty(2, dtype=torch.int32, device=dev)
+    fused = torch.empty(B, draft.shape.hidden, dtype=draft.dtype, device=dev)
+    anchor = first.clone()
+    out = [int(first.item())]
+    ks: List[int] = []
+    C = prompt.shape[0]
+    while len(out) < n_new:
+        if drafts_fn is None:
+            draft.draft_block(anchor, tokens=tok)
+        else:
+            tok[1:].copy_(torch.tensor(list(drafts_fn(C)), dtype=torch.int32))
+        vin[0:1].copy_(anchor)
+        vin[1:].copy_(tok[1:])
+        target.target_forward(vin, argmax=g, capture=cap.views(B))
+        draft.verify_accept(vin, g, out=res)
+        f = draft.fuse_context(cap.layer_list(B), out=fused)
+        draft.inject_kv(f, C)
+        host = torch.cat([res, vin]).cpu()
+        k, bonus = int(host[0]), int(host[1])
+        target.rollback(C + k + 1)
+        draft.rollback(C + k + 1)
+        out.extend(int(t) for t in host[3:3 + k])
+        out.append(bonus)
+        ks.append(k)
+        anchor.copy_(res[1:2])
+        C += k + 1
+    return out[:n_new], ks

@@ -75,7 +75,9 @@ typedef struct {
 
 /* Device pointers to the weights (borrowed for the context's lifetime).
  * Unused entries may be NULL: a context used only for fuse/inject needs
- * fc, fc_norm, wk and wv; the draft additionally needs the rest. */
+ * fc, fc_norm, wk and wv; the draft additionally needs the rest.  A context
+ * used only as a causal model (dflash_target_forward) may leave fc and fc_norm
+ * NULL; dflash_fuse_context then fails with STATE. */
 typedef struct {
     const void* fc;          /* [H, 5H] context fusion Linear (no bias) */
     const void* fc_norm;     /* [H] RMSNorm gain after the fusion */
@@ -184,6 +186,32 @@ dflash_status dflash_verify_accept(dflash_ctx* ctx, const int32_t* draft, const 
  * as context.  Host metadata only; pages past new_len become free. */
 dflash_status dflash_rollback(dflash_ctx* ctx, int32_t new_len);
 
+/* Causal forward of the context's decoder stack used as the target (verifier)
+ * model ([A] §1.1 autoregressive generation, §1.2 parallel verification of a
+ * drafted block; [C] greedy verification is lossless): rows tokens[0..M-1] at
+ * positions C..C+M-1 (C = current length) are embedded, and in every layer
+ * their rotated K and V are appended to the context's paged KV cache before row
+ * j attends to keys 0..C+j (causal).  Then the final RMSNorm, the LM head and
+ * a per-row argmax (ties: lowest id).  Afterwards length = C + M; a caller
+ * that accepts only a prefix rolls back with dflash_rollback.
+ * Batch invariant: row j's results are bit-identical whatever M and whatever
+ * rows share the call (attention splits sit at fixed key positions; every
+ * reduction has a fixed order), so verifying a block of M rows gives exactly
+ * the tokens of M one-row calls.
+ * tokens: device int32[M], 1 <= M <= 16 (ids outside [0, V) are clamped).
+ * argmax_out: device int32[M], argmax_out[j] = greedy token for position C+j+1.
+ * logits_out: device fp32 [M, V] or NULL.
+ * capture: NULL, or a host array of DFLASH_NUM_FEATURES device pointers (entries
+ *   may be NULL); entry i receives the output rows of target layer
+ *   dflash_feature_layers(target_layers)[i] (the residual stream after that
+ *   layer), [M, H] with row stride capture_ld elements: the hidden states that
+ *   dflash_fuse_context of a draft context takes.
+ * Requires every layer's weights, final_norm, embed and lm_head (INVAL), and
+ * C + M <= max_ctx (CAPACITY; nothing written). */
+dflash_status dflash_target_forward(dflash_ctx* ctx, const int32_t* tokens, int32_t M,
+                                    float* logits_out, int32_t* argmax_out,
+                                    void* const* capture, int64_t capture_ld, void* stream);
+
 /* Load already-rotated K and V for positions [pos0, pos0+M) of every layer
  * (restoring a saved cache, or K/V computed elsewhere).  k, v: device
  * [Ld, M, nkv, d] contiguous.  Same pos0/capacity rules as dflash_inject_kv. */
@@ -206,7 +234,8 @@ typedef enum {
     DFLASH_TRACE_ATTN = 6,     /* split-KV attention + merge, every layer */
     DFLASH_TRACE_DRAFT = 7,    /* the whole dflash_draft_block call */
     DFLASH_TRACE_FUSE = 8,     /* fusion GEMM of dflash_fuse_context (without its RMSNorm) */
-    DFLASH_TRACE_INJECT = 9    /* injection of dflash_inject_kv */
+    DFLASH_TRACE_INJECT = 9,   /* injection of dflash_inject_kv */
+    DFLASH_TRACE_TARGET = 10   /* the whole dflash_target_forward call */
 } dflash_trace_class;
 
 /* Tracing aid: while enabled, every launch of the given kernel class is

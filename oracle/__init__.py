@@ -55,7 +55,7 @@ def lib():
         L.orc_inject_rows.argtypes = [vp, vp, i64, vp, i32, i64, vp, vp]
         L.orc_draft_block.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp, vp]
         L.orc_accept.argtypes = [vp, vp, i32, vp, vp]
-        L.orc_target_forward.argtypes = [vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp]
+        L.orc_target_forward.argtypes = [vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp, vp]
         for f in ("orc_fuse_rows", "orc_inject_rows", "orc_draft_block", "orc_target_forward"):
             getattr(L, f).restype = C.c_int
         _lib = L
@@ -235,7 +235,7 @@ class TargetCache:
 
 
 def target_forward(model: Model, cache: TargetCache, tokens: Sequence[int], pos0: int,
-                   capture: Optional[Sequence[int]] = None):
+                   capture: Optional[Sequence[int]] = None, want_logits: bool = False):
     s = model.shape
     t = np.ascontiguousarray(tokens, dtype=np.int32)
     n = len(t)
@@ -243,9 +243,81 @@ def target_forward(model: Model, cache: TargetCache, tokens: Sequence[int], pos0
     gap = np.empty(n, dtype=np.float64)
     cap_a = np.ascontiguousarray(capture, dtype=np.int32) if capture is not None else None
     hid = np.empty((5, n, s.hidden), dtype=np.float64) if capture is not None else None
+    logits = np.empty((n, s.vocab), dtype=np.float32) if want_logits else None
     rc = lib().orc_target_forward(model.ref, t.ctypes.data, n, pos0, _dptr(cache.k), _dptr(cache.v),
                                   cache.cap, cap_a.ctypes.data if cap_a is not None else None,
                                   hid.ctypes.data if hid is not None else None,
+                                  logits.ctypes.data if logits is not None else None,
                                   am.ctypes.data, gap.ctypes.data)
     assert rc == 0
-    return {"argmax": am, "gap": gap, "hidden": hid}
+    return {"argmax": am, "gap": gap, "hidden": hid, "logits": logits}
+
+
+# ---------------------------------------------------------------- generation loops
+
+def greedy_generate(target: Model, prompt: Sequence[int], n_new: int, cap: Optional[int] = None):
+    """Plain greedy decoding of the causal target ([A] §1.1): the prompt in one
+    forward, then one token per forward.  Returns (tokens [n_new], gaps [n_new])
+    where gaps[i] is the top-2 logit gap of the step that chose tokens[i]."""
+    P = len(prompt)
+    cache = TargetCache(target, cap or P + n_new + 1)
+    r = target_forward(target, cache, prompt, 0)
+    toks, gaps = [int(r["argmax"][-1])], [float(r["gap"][-1])]
+    for i in range(1, n_new):
+        r = target_forward(target, cache, [toks[-1]], P + i - 1)
+        toks.append(int(r["argmax"][0]))
+        gaps.append(float(r["gap"][0]))
+    return np.array(toks, dtype=np.int32), np.array(gaps)
+
+
+def spec_generate(target: Model, draft: Model, prompt: Sequence[int], n_new: int, drafts_fn=None):
+    """DFlash speculative decoding with greedy block verification ([A] §2.2,
+    §8.2; [B] 技术内幕; [C]):
+      - the target runs over the prompt, capturing its five feature layers;
+        the draft fuses them and injects them as context K/V;
+      - each step drafts B-1 tokens from [anchor, mask ...] at C (or takes
+        them from drafts_fn(C) -> B-1 ids, to force a pattern), the target
+        verifies [anchor, d_1..d_{B-1}] causally, k leading drafts are
+        accepted and the target's token after them is the bonus;
+      - all B verified rows are fused and injected, then both caches keep
+        C + k + 1 positions; the bonus is the next anchor.
+    Returns (tokens [n_new], list of k per step)."""
+    s = target.shape
+    B, H = s.block, s.hidden
+    P = len(prompt)
+    cap = P + n_new + B
+    sel = feature_layers(s.target_layers)
+    NKs = (draft.n_layers, cap, s.n_kv_heads, s.head_dim)
+    store = torch.float32 if s.dtype == "fp32" else torch.bfloat16
+    ctx_k = torch.zeros(NKs, dtype=store)
+    ctx_v = torch.zeros(NKs, dtype=store)
+    cache = TargetCache(target, cap)
+
+    def add_context(hidden, pos0):
+        slabs = [to_storage(hidden[i], s.dtype) for i in range(5)]
+        n = slabs[0].shape[0]
+        fused = to_storage(fuse_rows(draft, slabs, range(n)), s.dtype)
+        k, v = inject_rows(draft, fused, range(n), pos0)
+        ctx_k[:, pos0:pos0 + n] = to_storage(k, s.dtype).reshape(draft.n_layers, n, s.n_kv_heads, s.head_dim)
+        ctx_v[:, pos0:pos0 + n] = to_storage(v, s.dtype).reshape(draft.n_layers, n, s.n_kv_heads, s.head_dim)
+
+    r = target_forward(target, cache, prompt, 0, capture=sel)
+    add_context(r["hidden"], 0)
+    anchor = int(r["argmax"][-1])
+    out, ks = [anchor], []
+    C = P
+    while len(out) < n_new:
+        if drafts_fn is None:
+            d = draft_block(draft, ctx_k, ctx_v, C, anchor, want_logits=False)["tokens"]
+        else:
+            d = np.concatenate([[anchor], np.asarray(drafts_fn(C), dtype=np.int32)])
+        vin = np.concatenate([[anchor], d[1:]]).astype(np.int32)
+        r = target_forward(target, cache, vin, C, capture=sel)
+        k, bonus = accept(d, r["argmax"])
+        add_context(r["hidden"], C)   # all B verified rows; only C..C+k are kept
+        out.extend(int(t) for t in d[1:k + 1])
+        out.append(int(bonus))
+        ks.append(k)
+        anchor = int(bonus)
+        C += k + 1
+    return np.array(out[:n_new], dtype=np.int32), ks

@@ -400,7 +400,7 @@ void orc_accept(const int32_t* d, const int32_t* g, int32_t B, int32_t* k, int32
 int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int64_t pos0,
                        double* cache_k, double* cache_v, int64_t cap,
                        const int32_t* capture, double* hidden_out,
-                       int32_t* argmax_out, double* gap_out)
+                       float* logits_out, int32_t* argmax_out, double* gap_out)
 {
     const int32_t H = m->hidden, dt = m->dtype;
     const int64_t NK = (int64_t)m->n_kv_heads * m->head_dim;
@@ -423,7 +423,7 @@ int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int
                 if (capture[s] == l)
                     memcpy(hidden_out + (int64_t)s * n * H, x, sizeof(double) * (size_t)n * H);
     }
-    lm_head_argmax(m, x, n, NULL, argmax_out, gap_out);
+    lm_head_argmax(m, x, n, logits_out, argmax_out, gap_out);
     free(x); free(pos);
     return 0;
 }

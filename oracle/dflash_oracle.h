@@ -93,11 +93,12 @@ void orc_accept(const int32_t* d, const int32_t* g, int32_t B, int32_t* k, int32
 /* Causal (target) forward of n tokens at positions pos0.. with a dense KV cache
  * cache_k/cache_v: [n_layers][cap][nkv*d] doubles holding positions 0..pos0-1 on
  * entry and 0..pos0+n-1 on return.  capture: 5 layer ids (0-based) whose output
- * rows go to hidden_out [5][n][H] (may be NULL).  argmax_out [n], gap_out [n]. */
+ * rows go to hidden_out [5][n][H] (may be NULL).  logits_out [n][V] fp32 (may be
+ * NULL), argmax_out [n], gap_out [n]. */
 int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int64_t pos0,
                        double* cache_k, double* cache_v, int64_t cap,
                        const int32_t* capture, double* hidden_out,
-                       int32_t* argmax_out, double* gap_out);
+                       float* logits_out, int32_t* argmax_out, double* gap_out);
 
 #ifdef __cplusplus
 }

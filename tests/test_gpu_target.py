@@ -1,0 +1,268 @@
+"""The causal target forward (the verify side of a speculative step) and the
+toy end-to-end greedy loop, through the C ABI, against the CPU oracle.
+
+* parity: logits, tokens, captured feature layers and the paged KV cache of a
+  chain of target calls of ragged row counts vs one oracle forward;
+* batch invariance: a row's results are bit-identical whether it is verified
+  alone or inside a block (the property that makes speculative output equal
+  greedy output bit for bit);
+* the toy workload (target hidden 1024, 8 layers, 16/4 heads x 64, FFN 2816,
+  vocab 32000; 3-layer draft; 2048-token prompt, 512 tokens): speculative
+  decoding == greedy decoding, with DFlash drafts and with forced all-right,
+  all-wrong and random-prefix drafts; GPU greedy vs oracle greedy.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dflash_inputs as di
+from tests.gpu_helpers import (assert_logits, assert_rows_close, assert_tokens, bf16_logit_tol, dev,
+                               drift_ulps)
+
+pytestmark = pytest.mark.gpu
+
+T_BF16 = di.Shape("t_bf16", "bf16", hidden=512, target_layers=8, draft_layers=8, n_q_heads=8,
+                  n_kv_heads=2, head_dim=128, ffn=1376, vocab=4000, ctx=300, seed=31)
+T_BF16_D64 = T_BF16.replace(name="t_bf16_d64", n_q_heads=16, n_kv_heads=4, head_dim=64, seed=32)
+T_FP32_G5 = di.Shape("t_fp32_g5", "fp32", hidden=320, target_layers=8, draft_layers=8, n_q_heads=10,
+                     n_kv_heads=2, head_dim=64, ffn=688, vocab=1024, ctx=300, seed=33)
+TOY = di.SHAPES["toy_e2e"]
+
+
+@pytest.fixture(scope="module")
+def dl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_diffusion_drafter_context_amd as m
+    m.lib()
+    return m
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def target_ctx(dl, s, w, max_ctx, page_seed=7):
+    return dl.DFlash(s.replace(draft_layers=s.target_layers), dev(w), max_ctx=max_ctx, page_seed=page_seed)
+
+
+def run_chunks(dl, ctx, s, toks, chunks, sel_capture=True):
+    """Target calls over toks in the given row counts; returns argmax, logits, captures."""
+    am, lg, caps = [], [], [[] for _ in range(5)]
+    pos = 0
+    for M in chunks:
+        cap = [torch.empty(M, s.hidden, dtype=s.torch_dtype, device="cuda") for _ in range(5)]
+        t = torch.from_numpy(np.asarray(toks[pos:pos + M], dtype=np.int32)).cuda()
+        a, l = ctx.target_forward(t, want_logits=True, capture=cap if sel_capture else None)
+        am.append(a)
+        lg.append(l)
+        for i in range(5):
+            caps[i].append(cap[i])
+        pos += M
+    sync()
+    return (torch.cat(am).cpu().numpy(), torch.cat(lg).cpu().numpy(),
+            [torch.cat(c).float().cpu().numpy() for c in caps])
+
+
+def oracle_noise_floor(orc, m, toks, ref, sel):
+    """How far the oracle itself moves when it accumulates dot products in fp32
+    instead of fp64 (same definition, same bf16 rounding points): the largest
+    logit change, and per captured layer the largest row change in bf16 ulps.
+    Layer after layer, bf16 rounding turns accumulation-order differences into
+    whole-ulp differences, so two correct implementations drift by about this."""
+    orc.set_fp32_accumulation(True)
+    try:
+        alt_cache = orc.TargetCache(m, len(toks))
+        alt = orc.target_forward(m, alt_cache, toks, 0, capture=sel, want_logits=True)
+    finally:
+        orc.set_fp32_accumulation(False)
+    lg = float(np.abs(alt["logits"].astype(np.float64) - ref["logits"].astype(np.float64)).max())
+    n = alt_cache.k.shape[0] * alt_cache.k.shape[1]
+    kv = max(drift_ulps(alt_cache.k.reshape(n, -1), ref["cache"].k.reshape(n, -1)),
+             drift_ulps(alt_cache.v.reshape(n, -1), ref["cache"].v.reshape(n, -1)))
+    return lg, [drift_ulps(alt["hidden"][i], ref["hidden"][i]) for i in range(5)], kv
+
+
+# ------------------------------------------------------------------ parity
+
+@pytest.mark.parametrize("shape", [T_BF16, T_BF16_D64, T_FP32_G5])
+def test_target_forward_matches_oracle(dl, orc, shape):
+    """300 tokens in calls of 16, 5, 1, 16, ... rows (splits of 256 keys are
+    crossed; the page table is shuffled)."""
+    s = shape
+    w = di.toy_target_weights(s)
+    toks = di.uniform_int(s.ctx, 0, s.vocab - 1, s.seed, "prompt").numpy()
+    chunks, n = [], 0
+    for M in [16, 5, 1, 16, 16, 3, 16, 7, 16, 16, 2, 16, 11] * 4:
+        M = min(M, s.ctx - n)
+        if M <= 0:
+            break
+        chunks.append(M)
+        n += M
+    assert n == s.ctx
+    ctx = target_ctx(dl, s, w, max_ctx=s.ctx + 64)
+    am, lg, caps = run_chunks(dl, ctx, s, toks, chunks)
+    assert ctx.length == s.ctx
+
+    m = orc.Model(s, w, n_layers=s.target_layers)
+    sel = orc.feature_layers(s.target_layers)
+    cache = orc.TargetCache(m, s.ctx)
+    ref = orc.target_forward(m, cache, toks, 0, capture=sel, want_logits=True)
+    ref["cache"] = cache
+    noise, hid_ulps, kv_ulps = (oracle_noise_floor(orc, m, toks, ref, sel) if s.dtype == "bf16"
+                                else (None, [0.0] * 5, 0.0))
+    assert_logits(lg, ref["logits"], s.dtype, noise)
+    assert_tokens(am, ref["argmax"], ref["gap"], lg, ref["logits"], s.dtype, noise)
+    for i in range(5):
+        assert_rows_close(caps[i], ref["hidden"][i], s.dtype, f"captured layer {sel[i]}",
+                          ulps=max(2.0, 2.0 * hid_ulps[i]))
+    gk, gv = ctx.read_kv(0, s.ctx)
+    sync()
+    L, NK = s.target_layers, s.n_kv_heads * s.head_dim
+    tol = max(2.0, 2.0 * kv_ulps)
+    assert_rows_close(gk.float().cpu().numpy().reshape(L * s.ctx, NK), cache.k.reshape(L * s.ctx, NK), s.dtype, "K",
+                      ulps=tol)
+    assert_rows_close(gv.float().cpu().numpy().reshape(L * s.ctx, NK), cache.v.reshape(L * s.ctx, NK), s.dtype, "V",
+                      ulps=tol)
+
+
+# ------------------------------------------------------------------ batch invariance
+
+@pytest.mark.parametrize("shape", [T_BF16, T_FP32_G5])
+@pytest.mark.parametrize("C", [0, 37, 250, 256, 600])
+def test_target_forward_is_batch_invariant(dl, shape, C):
+    s = shape
+    w = di.toy_target_weights(s)
+    ctx = target_ctx(dl, s, w, max_ctx=C + 64)
+    toks = di.uniform_int(C + 16, 0, s.vocab - 1, s.seed + C, "binv").numpy()
+    if C:
+        run_chunks(dl, ctx, s, toks[:C], [16] * (C // 16) + ([C % 16] if C % 16 else []), sel_capture=False)
+    results = []
+    for split in ([16], [1] * 16, [7, 9], [3, 13]):
+        ctx.rollback(C)
+        am, lg, caps = run_chunks(dl, ctx, s, toks[C:], split)
+        k, v = ctx.read_kv(C, 16)
+        sync()
+        results.append((am, lg, caps, k.cpu(), v.cpu()))
+    a0 = results[0]
+    for r in results[1:]:
+        assert np.array_equal(r[0], a0[0])
+        assert np.array_equal(r[1], a0[1])
+        for i in range(5):
+            assert np.array_equal(r[2][i], a0[2][i])
+        assert torch.equal(r[3], a0[3]) and torch.equal(r[4], a0[4])
+
+
+def test_target_forward_errors(dl):
+    s = T_FP32_G5
+    ctx = target_ctx(dl, s, di.toy_target_weights(s), max_ctx=40)
+    t = torch.zeros(17, dtype=torch.int32, device="cuda")
+    with pytest.raises(dl.DFlashError):
+        ctx.target_forward(t)                     # more than 16 rows
+    for _ in range(2):
+        ctx.target_forward(t[:16])
+    with pytest.raises(dl.DFlashError):
+        ctx.target_forward(t[:16])                # 48 > max_ctx: nothing written
+    assert ctx.length == 32
+    with pytest.raises(dl.DFlashError):           # no fusion weights in a target context
+        ctx.fuse_context([torch.zeros(4, s.hidden, device="cuda")] * s.target_layers)
+    sync()
+
+
+# ------------------------------------------------------------------ toy end-to-end
+
+@pytest.fixture(scope="module")
+def toy(dl):
+    s = TOY
+    tw = dev(di.toy_target_weights(s))
+    dw = dev(di.draft_weights(s))
+    prompt = di.toy_prompt(s).cuda()
+    n_new = di.TOY_GENERATE
+    cap = prompt.shape[0] + n_new + 2 * s.block
+
+    def fresh():
+        tgt = dl.DFlash(s.replace(draft_layers=s.target_layers), tw, max_ctx=cap, page_seed=11)
+        drf = dl.DFlash(s, dw, max_ctx=cap, page_seed=12)
+        return tgt, drf
+
+    from block_diffusion_drafter_context_amd import spec
+    tgt, _ = fresh()
+    greedy = spec.greedy_generate(tgt, prompt, n_new).cpu().numpy()
+    return {"fresh": fresh, "prompt": prompt, "n_new": n_new, "greedy": greedy, "spec": spec}
+
+
+@pytest.mark.parametrize("mode", ["dflash", "perfect", "null", "prefix"])
+def test_toy_spec_equals_greedy(toy, mode):
+    """Greedy block verification is lossless: the speculative loop emits the
+    GPU's own greedy tokens bit for bit, whatever the drafts."""
+    greedy, P, V = toy["greedy"], toy["prompt"].shape[0], TOY.vocab
+    rng = np.random.default_rng(9)
+
+    def truth(C):
+        return [int(greedy[p - P]) if p - P < len(greedy) else 0 for p in range(C + 1, C + 16)]
+
+    fn = {"dflash": None,
+          "perfect": truth,
+          "null": lambda C: [(t + 1) % V for t in truth(C)],
+          "prefix": lambda C: [t if j < r else (t + 1) % V
+                               for r in [int(rng.integers(0, 16))] for j, t in enumerate(truth(C))]}[mode]
+    tgt, drf = toy["fresh"]()
+    out, ks = toy["spec"].spec_generate(tgt, drf, toy["prompt"], toy["n_new"], drafts_fn=fn)
+    print(f"[toy {mode}] steps {len(ks)} mean k {np.mean(ks):.3f} tokens/step {len(out) / max(len(ks), 1):.2f}",
+          flush=True)
+    first_bad = next((i for i in range(len(out)) if out[i] != greedy[i]), None)
+    assert first_bad is None, f"spec diverges from greedy at generated token {first_bad}"
+    if mode == "perfect":
+        assert all(k == 15 for k in ks[:-1])
+    if mode == "null":
+        assert ks == [0] * (toy["n_new"] - 1)
+
+
+@pytest.fixture(scope="module")
+def toy_oracle(orc):
+    """The oracle's greedy tokens (one token per forward), plus one teacher-forced
+    forward over prompt + those tokens in fp64 and in fp32 accumulation: its
+    logits at the generated positions and their drift (the bf16 noise floor)."""
+    s = TOY
+    m = orc.Model(s, di.toy_target_weights(s), n_layers=s.target_layers)
+    prompt = di.toy_prompt(s).numpy()
+    toks, gaps = orc.greedy_generate(m, prompt, di.TOY_GENERATE)
+    P = len(prompt)
+    seq = np.concatenate([prompt, toks[:-1]]).astype(np.int32)
+    ref = orc.target_forward(m, orc.TargetCache(m, len(seq)), seq, 0, want_logits=True)
+    assert np.array_equal(ref["argmax"][P - 1:], toks)  # the oracle is batch invariant
+    orc.set_fp32_accumulation(True)
+    try:
+        alt = orc.target_forward(m, orc.TargetCache(m, len(seq)), seq, 0, want_logits=True)
+    finally:
+        orc.set_fp32_accumulation(False)
+    logits = ref["logits"][P - 1:].copy()
+    noise = float(np.abs(alt["logits"][P - 1:].astype(np.float64) - logits).max())
+    del ref, alt
+    return prompt, toks, gaps, logits, noise
+
+
+def test_toy_greedy_matches_oracle(dl, toy, toy_oracle):
+    """The GPU target, teacher-forced on the oracle's greedy sequence, picks the
+    oracle's token at every generated position except near-ties (oracle top-2
+    gap inside the bf16 logit band, with the GPU's token inside the band of the
+    oracle's maximum); the free-running GPU greedy sequence equals the oracle's
+    up to its first near-tie."""
+    prompt, otoks, ogaps, ologits, noise = toy_oracle
+    band = bf16_logit_tol(noise)
+    P, n = len(prompt), len(otoks)
+    seq = np.concatenate([prompt, otoks[:-1]]).astype(np.int32)
+    tgt, _ = toy["fresh"]()
+    am = torch.empty(len(seq), dtype=torch.int32, device="cuda")
+    seq_d = torch.from_numpy(seq).cuda()
+    for r0 in range(0, len(seq), 16):
+        M = min(16, len(seq) - r0)
+        tgt.target_forward(seq_d[r0:r0 + M], argmax=am[r0:r0 + M])
+    sync()
+    pred = am.cpu().numpy()[P - 1:]
+    nex = assert_tokens(pred, otoks, ogaps, ref_logits=ologits, dtype="bf16", noise_floor=noise)
+    print(f"[toy oracle] noise floor {noise:.4f}; teacher-forced near-tie mismatches {nex} of {n}", flush=True)
+    g = toy["greedy"]
+    first = next((i for i in range(n) if g[i] != otoks[i]), n)
+    print(f"[toy oracle] free-running greedy agrees for the first {first} of {n} tokens", flush=True)
+    assert first == n or ogaps[first] < band, f"free-running greedy diverges at {first} (gap {ogaps[first]:.3g})"

@@ -408,3 +408,46 @@ def test_target_prefill_equals_decode(orc):
     assert np.array_equal(a["argmax"], np.array(outs))
     assert np.array_equal(a["hidden"], np.stack(hids, axis=1))
     assert np.array_equal(c1.k, c2.k)
+
+
+TOYLET = di.Shape("toylet", "fp32", hidden=64, target_layers=8, draft_layers=2, n_q_heads=4,
+                  n_kv_heads=2, head_dim=16, ffn=96, vocab=128, ctx=20, seed=21)
+
+
+@pytest.fixture(scope="module")
+def toylet(orc):
+    s = TOYLET
+    tm = orc.Model(s, di.toy_target_weights(s), n_layers=s.target_layers)
+    dw = di.draft_weights(s)
+    dm = orc.Model(s, dw)
+    prompt = di.uniform_int(s.ctx, 0, s.vocab - 1, s.seed, "prompt").numpy()
+    greedy, _ = orc.greedy_generate(tm, prompt, 40)
+    return tm, dm, prompt, greedy
+
+
+@pytest.mark.parametrize("mode", ["dflash", "perfect", "null", "prefix"])
+def test_spec_decode_is_lossless(orc, toylet, mode):
+    """Greedy block verification emits exactly the target's greedy tokens
+    whatever the drafts are ([C]: lossless greedy verification): drafts from
+    the DFlash draft model, all correct (k = 15 every block), all wrong
+    (k = 0), and correct up to a random length."""
+    tm, dm, prompt, greedy = toylet
+    P, V = len(prompt), TOYLET.vocab
+    rng = np.random.default_rng(5)
+
+    def truth(C):  # greedy tokens at positions C+1..C+15 (past the end: anything)
+        return [int(greedy[p - P]) if p - P < len(greedy) else 0 for p in range(C + 1, C + 16)]
+
+    fn = {"dflash": None,
+          "perfect": truth,
+          "null": lambda C: [(t + 1) % V for t in truth(C)],
+          "prefix": lambda C: [t if j < r else (t + 1) % V
+                               for r in [int(rng.integers(0, 16))] for j, t in enumerate(truth(C))]}[mode]
+    out, ks = orc.spec_generate(tm, dm, prompt, len(greedy), drafts_fn=fn)
+    assert np.array_equal(out, greedy)
+    if mode == "perfect":
+        assert ks[:-1] == [15] * (len(ks) - 1) and len(ks) == math.ceil((len(greedy) - 1) / 16)
+    if mode == "null":
+        assert ks == [0] * (len(greedy) - 1)
+    if mode == "prefix":
+        assert len(set(ks)) > 3
