@@ -23,12 +23,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// round-to-nearest-even fp32 -> bf16 (NaN becomes a quiet NaN)
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (bf16_t)0x7FC0;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// round-to-nearest-even fp32 -> bf16 (the hardware conversion, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// two values in one conversion: a in the low half, b in the high half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elem;
@@ -71,9 +73,7 @@ template <> struct Frag<bf16_t> {
         return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
     }
     __device__ __forceinline__ void set8(const float* f) {
-        uint32_t w[4];
-        for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
-        v = make_uint4(w[0], w[1], w[2], w[3]);
+        v = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
     }
 };
 template <> struct Frag<float> {

@@ -37,6 +37,11 @@ dflash_status validate_config(const dflash_config* c, Dims* o, std::string* err)
     if (c->max_ctx < 0 || c->max_ctx > (1 << 24)) return fail(DFLASH_ERR_INVAL, "max_ctx must be in [0, 2^24]");
     if (c->max_rows < 1 || c->max_rows > (1 << 20)) return fail(DFLASH_ERR_INVAL, "max_rows must be in [1, 2^20]");
     if (!(c->rope_base > 1.0) || !(c->eps >= 0.0)) return fail(DFLASH_ERR_INVAL, "rope_base must be > 1 and eps >= 0");
+    {   // every attention split must touch at most kMaxSplitPages pages
+        const long long kps_max = ((long long)c->max_ctx + kMaxSplits - 1) / kMaxSplits + 2LL * kAttnChunk;
+        if (std::max<long long>(kps_max, causal_split_keys(c->max_ctx)) / c->page_size + 2 > kMaxSplitPages)
+            return fail(DFLASH_ERR_UNSUPPORTED, "max_ctx too large for this page_size");
+    }
     const long long nqd = (long long)c->n_q_heads * c->head_dim;
     if (nqd % 32) return fail(DFLASH_ERR_UNSUPPORTED, "n_q_heads*head_dim must be a multiple of 32");
     if ((long long)c->vocab * c->hidden > (1LL << 40)) return fail(DFLASH_ERR_INVAL, "vocab*hidden too large");
@@ -86,7 +91,8 @@ Layout compute_layout(const Dims& d, int num_cus) {
     L.rstd = take(16 * 4);
     const int blk = 16 * kSkinnyNT;
     L.max_ss_tiles = (d.H + blk - 1) / blk;
-    L.ss_part = take((size_t)L.max_ss_tiles * 16 * 4);
+    L.ss_stride = (L.max_ss_tiles + 15) / 16 * 16;
+    L.ss_part = take((size_t)L.ss_stride * 16 * 4);
     // 4 waves per CU: measured best for every skinny-GEMM shape of the draft
     // pass (fewer concurrent weight streams keep DRAM pages open longer)
     L.nwaves = std::max(num_cus, 1) * 4;
@@ -142,17 +148,23 @@ std::vector<int32_t> make_page_table(int n_pages, uint64_t seed) {
     return p;
 }
 
-void attn_split_plan(int C, int nkv, int num_cus, int* kps, int* ns) {
+void attn_split_plan(int C, int nkv, int num_cus, int page, int* kps, int* ns) {
     if (C <= 0) {
         *kps = kAttnChunk;
         *ns = 0;
         return;
     }
-    // one round of workgroups over all kv heads: kAttnWGPerCU per CU
-    long long target = std::max(1LL, (long long)kAttnWGPerCU * num_cus / std::max(nkv, 1));
+    // about three workgroups per CU over all kv heads, and at least three
+    // chunks per split (a split's fixed cost -- Q loads, first-chunk latency,
+    // partial write and merge read -- is then amortised); measured best at 4K
+    // and 36K keys on MI355X
+    long long target = std::max(1LL, 3LL * num_cus / std::max(nkv, 1));
     long long per = (C + target - 1) / target;
     per = ((per + kAttnChunk - 1) / kAttnChunk) * kAttnChunk;
-    per = std::max<long long>(per, kAttnChunk);
+    per = std::max<long long>(per, 3 * kAttnChunk);
+    // a split touches at most kMaxSplitPages pages (their ids are staged in LDS)
+    const long long per_cap = std::max<long long>(kAttnChunk, ((long long)(kMaxSplitPages - 2) * page) / kAttnChunk * kAttnChunk);
+    per = std::min(per, per_cap);
     long long n = (C + per - 1) / per;
     while (n > kMaxSplits) {
         per += kAttnChunk;

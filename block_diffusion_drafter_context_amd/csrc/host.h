@@ -21,6 +21,7 @@ constexpr int kAttnChunk = 64;           // keys per attention step
 constexpr int kAttnStages = 2;           // attention chunks resident in LDS per workgroup
 constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU
 constexpr int kMaxSplits = 256;          // context splits of the split-KV attention
+constexpr int kMaxSplitPages = 1040;     // KV pages one attention split may touch
 constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
 
 struct Dims {
@@ -55,6 +56,7 @@ struct Layout {
     int nwaves;           // skinny-GEMM waves per launch
     int max_tiles;        // largest tile count of any skinny GEMM
     int max_ss_tiles;     // tiles of an N = H skinny GEMM (row sum-of-squares partials)
+    int ss_stride;        // row stride of the partials ([16 rows][ss_stride], zero past the tiles)
     int n_rope_pos;       // positions covered by the rotary table
 };
 
@@ -73,7 +75,7 @@ void feature_layers(int target_layers, int32_t out[5]);
 
 // Attention split plan for a context of C keys: keys per split (multiple of
 // kAttnChunk) and number of context splits (the block keys get one more).
-void attn_split_plan(int C, int nkv, int num_cus, int* keys_per_split, int* n_splits);
+void attn_split_plan(int C, int nkv, int num_cus, int page, int* keys_per_split, int* n_splits);
 
 // Keys per split of the causal forward: fixed for a context (it depends on
 // max_ctx only), so split boundaries sit at the same absolute positions in

@@ -51,23 +51,68 @@ struct NoState {};
 constexpr int kP = 4;  // chunks per pipelined load group
 
 // Activation prologues ------------------------------------------------------
-// Each provides Raw (what is loaded for one chunk), prep(row) (per-wave
-// constant), load(raw, row, k) (issue loads only) and finish(frag, raw, prep)
-// (arithmetic at use time), so a prefetched group's loads stay in flight while
-// the previous group is computed.
+// Each provides Raw (what is loaded for one chunk), a per-wave constant
+// (pre_issue(pre, lane) issues its loads at wave start, pre_finish(pre, lane)
+// turns them into the value at first use), load(raw, row, k) (issue loads
+// only) and finish(frag, raw, prep) (arithmetic at use time), so a prefetched
+// group's loads stay in flight while the previous group is computed.
 
-// u = round(x * rstd[row] * gain[k])  (RMSNorm applied on load)
+constexpr int kSSPerLane = 40;  // row-statistics partials one lane sums (H <= 4 * 40 * 32 = 5120)
+
+// u = round(x * rstd[row] * gain[k])  (RMSNorm applied on load).  rstd comes
+// either from rstd[] or, when ss is set, from the per-32-column-tile row sums
+// of squares the producing GEMM wrote ([16 rows][ss_stride], zero past the
+// last tile): lane (row j, group g) sums the g-th quarter of row j's tiles in
+// order (16-byte loads), then the four quarters are added (a fixed order).
 template <typename T>
 struct NormA {
     const T* x;
     int ld;
     const float* rstd;
     const T* gain;
+    const float* ss = nullptr;
+    int ss_tiles = 0;
+    int ss_stride = 0;
+    int n_cols = 0;  // row length the sums of squares cover
+    float eps = 0.f;
     struct Raw {
         Frag<T> x, g;
         __device__ __forceinline__ void zero() { x.zero(); g.zero(); }
     };
-    __device__ __forceinline__ float prep(int row) const { return rstd[row]; }
+    struct Pre {
+        float v[kSSPerLane];
+    };
+    // tiles per quarter, a multiple of 4 (so 4 * quarter <= ss_stride)
+    __device__ __forceinline__ int quarter() const { return ((ss_tiles + 3) / 4 + 3) / 4 * 4; }
+    __device__ __forceinline__ void pre_issue(Pre& p, int lane) const {
+        const int j = lane & 15, g = lane >> 4;
+        if (!ss) {
+            p.v[0] = rstd[j];
+            return;
+        }
+        const int q = quarter();
+        const float* src = ss + (long long)j * ss_stride + g * q;
+#pragma unroll
+        for (int i = 0; i < kSSPerLane / 4; ++i)
+            if (4 * i < q) {
+                const float4 f = *reinterpret_cast<const float4*>(src + 4 * i);
+                p.v[4 * i] = f.x;
+                p.v[4 * i + 1] = f.y;
+                p.v[4 * i + 2] = f.z;
+                p.v[4 * i + 3] = f.w;
+            }
+    }
+    __device__ __forceinline__ float pre_finish(const Pre& p, int lane) const {
+        if (!ss) return p.v[0];
+        const int q = quarter();
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSSPerLane; ++i)
+            if (i < q) sum += p.v[i];
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        return 1.0f / sqrtf(sum / (float)n_cols + eps);
+    }
     __device__ __forceinline__ void load(Raw& r, int row, int k) const {
         r.x.load(x + (long long)row * ld + k);
         r.g.load(gain + k);
@@ -80,22 +125,29 @@ struct NormA {
     }
 };
 
+struct NoPre {
+    struct Pre {};
+    __device__ __forceinline__ void pre_issue(Pre&, int) const {}
+    __device__ __forceinline__ float pre_finish(const Pre&, int) const { return 0.f; }
+};
+
 template <typename T>
-struct PlainA {
+struct PlainA : NoPre {
     const T* x;
     long long ld;
+    PlainA() = default;
+    __host__ __device__ PlainA(const T* x_, long long ld_) : x(x_), ld(ld_) {}
     struct Raw {
         Frag<T> x;
         __device__ __forceinline__ void zero() { x.zero(); }
     };
-    __device__ __forceinline__ float prep(int) const { return 0.f; }
     __device__ __forceinline__ void load(Raw& r, int row, int k) const { r.x.load(x + row * ld + k); }
     __device__ __forceinline__ void finish(Frag<T>& f, const Raw& r, float) const { f = r.x; }
 };
 
 // five hidden-state slabs read as one concatenated row (never materialised)
 template <typename T>
-struct SlabA {
+struct SlabA : NoPre {
     const T* slab[5];
     long long ld;
     int H;
@@ -103,7 +155,6 @@ struct SlabA {
         Frag<T> x;
         __device__ __forceinline__ void zero() { x.zero(); }
     };
-    __device__ __forceinline__ float prep(int) const { return 0.f; }
     __device__ __forceinline__ void load(Raw& r, int row, int k) const {
         const int s = k / H;
         r.x.load(slab[s] + row * ld + (k - s * H));
@@ -126,7 +177,8 @@ __device__ __forceinline__ const T* sw_stream(const T* base, int col_block, int 
 // the current group is computed.
 template <typename T, class AL>
 __device__ __forceinline__ void skinny_segment(const AL& al, const T* s0, const T* s1, int ch0, int ch1, int K,
-                                               int lane, int row, int grp, bool row_ok, float pre, f32x4_t acc[2]) {
+                                               int lane, int row, int grp, bool row_ok, const typename AL::Pre& pr,
+                                               float& pre, bool& have_pre, f32x4_t acc[2]) {
     using Raw = typename AL::Raw;
     const int arow = row_ok ? row : 0;
     const T* w1s = s1 ? s1 : s0;
@@ -163,6 +215,10 @@ __device__ __forceinline__ void skinny_segment(const AL& al, const T* s0, const 
     for (int c = ch0; c < ch1; c += 2 * kP) {
         load_group(c + kP, gb);
         __builtin_amdgcn_sched_barrier(0);
+        if (!have_pre) {  // first use: its loads went out before any weight load
+            pre = al.pre_finish(pr, lane);
+            have_pre = true;
+        }
         compute(c, ga);
         __builtin_amdgcn_sched_barrier(0);
         load_group(c + 2 * kP, ga);
@@ -178,7 +234,10 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
     const int wave = blockIdx.x * kSkinnyWavesPerWG + (threadIdx.x >> 6);
     const int row = lane & 15, grp = lane >> 4;
     const bool row_ok = row < c.M;
-    const float pre = row_ok ? op.a.prep(row) : 0.f;
+    typename decltype(op.a)::Pre pr;
+    op.a.pre_issue(pr, lane);
+    float pre = 0.f;
+    bool have_pre = false;
     typename Op::State st;
     op.wave_begin(st);
 
@@ -194,7 +253,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
         const int ch0 = (int)(i - tbeg), ch1 = (int)(seg_end - tbeg);
         f32x4_t acc[2] = {zero4(), zero4()};
         skinny_segment<T>(op.a, op.b_rows(tile, 0, c.nchunks), op.b_rows(tile, 1, c.nchunks), ch0, ch1, c.K, lane, row,
-                          grp, row_ok, pre, acc);
+                          grp, row_ok, pr, pre, have_pre, acc);
         i = seg_end;
         if (!(ch0 == 0 && ch1 == c.nchunks)) {
             // partial tile: publish, and let the last contributor finish it
@@ -226,15 +285,17 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
             if (lane == 0) atomicExch(&c.tile_cnt[tile], 0u);
         }
         op.epilogue(tile, acc, lane, st);
-        if (Op::kDoneHook) {
-            wait_vmem();
-            unsigned old = 0;
-            if (lane == 0) old = atomicAdd(c.done_cnt, 1u);
-            old = __shfl(old, 0, 64);
-            if (old == (unsigned)(c.ntiles - 1)) {
-                compiler_fence();
-                op.done_hook(lane, c.ntiles);
-                if (lane == 0) atomicExch(c.done_cnt, 0u);
+        if constexpr (Op::kDoneHook) {
+            if (op.done_wanted()) {
+                wait_vmem();
+                unsigned old = 0;
+                if (lane == 0) old = atomicAdd(c.done_cnt, 1u);
+                old = __shfl(old, 0, 64);
+                if (old == (unsigned)(c.ntiles - 1)) {
+                    compiler_fence();
+                    op.done_hook(lane, c.ntiles);
+                    if (lane == 0) atomicExch(c.done_cnt, 0u);
+                }
             }
         }
     }
@@ -273,6 +334,15 @@ struct KVPages {
         const int p = pos / page;
         slot = pos - p * page;
         return reinterpret_cast<T*>(base + (2LL * l + 1) * layer_kv_bytes) + (long long)table[p] * page_elems();
+    }
+    // the same, for an already looked-up physical page
+    template <typename T>
+    __device__ __forceinline__ T* kpage_phys(int l, int phys) const {
+        return reinterpret_cast<T*>(base + (2LL * l) * layer_kv_bytes) + (long long)phys * page_elems();
+    }
+    template <typename T>
+    __device__ __forceinline__ T* vpage_phys(int l, int phys) const {
+        return reinterpret_cast<T*>(base + (2LL * l + 1) * layer_kv_bytes) + (long long)phys * page_elems();
     }
 };
 
@@ -368,7 +438,8 @@ struct OpResid {
     const T* w;
     int N, K, M;
     T* x;
-    float* ss_part;
+    float* ss_part;          // [16 rows][ss_stride] per-tile row sums of squares
+    int ss_stride;
     float* rstd_out;
     float eps;
     T* cap = nullptr;        // optional copy of the updated rows (stride cap_ld)
@@ -399,23 +470,25 @@ struct OpResid {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const float s = group16_sum(sq[ii]);
-            if ((lane & 15) == 0) st_agent(ss_part + tile * 16 + 4 * (lane >> 4) + ii, s);
+            if ((lane & 15) == 0) st_agent(ss_part + (long long)(4 * (lane >> 4) + ii) * ss_stride + tile, s);
         }
     }
+    __device__ __forceinline__ bool done_wanted() const { return rstd_out != nullptr; }
     __device__ __forceinline__ void done_hook(int lane, int ntiles) const {
         // lane handles row j = lane & 15 over tiles t = g, g+4, ... (g = lane >> 4)
         const int j = lane & 15, g = lane >> 4;
         float s = 0.f;
         int t = g;
         for (; t + 12 < ntiles; t += 16) {  // four independent loads in flight
-            const float a0 = ld_agent(ss_part + t * 16 + j), a1 = ld_agent(ss_part + (t + 4) * 16 + j);
-            const float a2 = ld_agent(ss_part + (t + 8) * 16 + j), a3 = ld_agent(ss_part + (t + 12) * 16 + j);
+            const float* r = ss_part + (long long)j * ss_stride;
+            const float a0 = ld_agent(r + t), a1 = ld_agent(r + t + 4);
+            const float a2 = ld_agent(r + t + 8), a3 = ld_agent(r + t + 12);
             s += a0;
             s += a1;
             s += a2;
             s += a3;
         }
-        for (; t < ntiles; t += 4) s += ld_agent(ss_part + t * 16 + j);
+        for (; t < ntiles; t += 4) s += ld_agent(ss_part + (long long)j * ss_stride + t);
         s += __shfl_xor(s, 16, 64);
         s += __shfl_xor(s, 32, 64);
         if (lane < 16) rstd_out[j] = 1.0f / sqrtf(s / (float)N + eps);
@@ -729,26 +802,39 @@ struct HeadAcc {
 template <typename T, int D, class VF>
 __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], int nvalid, float scale_log2, int grp,
                                            VF&& vfrag) {
-    float mx = h.m;
-    float p[4][4];
-    const bool full = nvalid >= 64;
+    // raw scores, masked; the running max is kept in scaled log2 units (the
+    // scale is positive, so the max commutes with it)
+    float sr[4][4];
+    float mr = -INFINITY;
+    if (__all(nvalid >= 64)) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int kk = kb * 16 + 4 * grp + ii;
-            p[kb][ii] = (full || kk < nvalid) ? s[kb][ii] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, p[kb][ii]);
-        }
-    mx = cross4_max(mx);
+            for (int ii = 0; ii < 4; ++ii) {
+                sr[kb][ii] = s[kb][ii];
+                mr = fmaxf(mr, sr[kb][ii]);
+            }
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int kk = kb * 16 + 4 * grp + ii;
+                sr[kb][ii] = kk < nvalid ? s[kb][ii] : -INFINITY;
+                mr = fmaxf(mr, sr[kb][ii]);
+            }
+    }
+    mr = cross4_max(mr);
+    const float mx = fmaxf(h.m, mr * scale_log2);
     const float mref = mx == -INFINITY ? 0.f : mx;  // all keys masked so far: exp2(-inf) = 0
-    const float alpha = exp2f(h.m - mref);
+    const float alpha = __builtin_amdgcn_exp2f(h.m - mref);
+    float p[4][4];
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const float e = exp2f(p[kb][ii] - mref);
+            const float e = __builtin_amdgcn_exp2f(fmaf(sr[kb][ii], scale_log2, -mref));
             p[kb][ii] = e;
             ps += e;
         }
@@ -774,11 +860,17 @@ __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], in
             pf_lo.set8(pl);
         }
         pf.set8(pv);
+        // all V fragments of this 32-key step first, then independent MFMA
+        // chains (one accumulator per 16 dims) so the matrix unit never waits
+        // on its own previous result
+        Frag<T> vf[D / 16];
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-            const Frag<T> vf = vfrag(t, db);
-            mma(h.o[db], vf, pf);
-            if (kSplitP) mma(h.o[db], vf, pf_lo);
+        for (int db = 0; db < D / 16; ++db) vf[db] = vfrag(t, db);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) mma(h.o[db], vf[db], pf);
+        if (kSplitP) {
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) mma(h.o[db], vf[db], pf_lo);
         }
     }
 }
@@ -836,7 +928,7 @@ __device__ __forceinline__ Frag<T> lds_frag(const char* base, int row, int ncol,
 // from LDS.  Scores are formed transposed, S^T = K Q^T, so the probabilities
 // land in the B-operand layout of O^T += V^T P^T and never leave registers.
 template <typename T, int D, int HPW>
-__global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs a) {
     constexpr int CH = kAttnChunk;                  // keys per chunk (64)
     constexpr int KCOL = D * (int)sizeof(T) / 16;   // 16-byte columns of a K row
     constexpr int VCOL = CH * (int)sizeof(T) / 16;  // 16-byte columns of a V^T row
@@ -844,6 +936,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
     constexpr int STAGE = (CH * KCOL + D * VCOL) * 16;   // bytes per stage
     constexpr int NS = kAttnStages;  // chunks in LDS: one computed while the next streams in
     __shared__ __attribute__((aligned(16))) char lds[NS * STAGE];
+    __shared__ int s_pages[kMaxSplitPages];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = blockIdx.y, split = blockIdx.x;
@@ -889,29 +982,49 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
         const int kbeg = split * a.kps;
         const int kend = min(a.C, kbeg + a.kps);
         const int nch = (kend - kbeg + CH - 1) / CH;
-        // issue the direct loads of chunk c into stage st
+        // physical pages of the split, looked up once (a table load per chunk
+        // would put a dependent round trip in front of every chunk's loads)
+        const int pg0 = kbeg / a.kv.page;
+        const int npg = (kend - 1) / a.kv.page - pg0 + 1;  // <= kMaxSplitPages (host-checked)
+        for (int i = threadIdx.x; i < npg; i += blockDim.x) s_pages[i] = a.kv.table[pg0 + i];
+        // Waves 0-1 bring in the chunk's K rows, waves 2-3 its V^T rows (the two
+        // halves of a stage are the same size).  Per-lane byte offsets of the NI
+        // 16-byte pieces are fixed for the whole split; only the chunk base moves.
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        const bool kwave = wu < 2;
+        int off[NI], krow[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int inst = wu * NI + j;
+            const int P = inst * 64 + lane;  // 16-byte piece of the stage
+            if (kwave) {
+                const int r = P / KCOL, pc = P % KCOL;
+                krow[j] = r;
+                off[j] = (pc ^ (r % KCOL)) * 16;
+            } else {
+                const int Q = P - CH * KCOL;
+                const int dim = Q / VCOL, pc = Q % VCOL;
+                krow[j] = 0;
+                off[j] = dim * a.kv.page * (int)sizeof(T) + (pc ^ (dim % VCOL)) * 16;
+            }
+        }
+        __syncthreads();
+        // issue the direct loads of chunk c into stage st (no global load on this
+        // path: the page id comes from LDS, so earlier chunks stay in flight)
         auto issue = [&](int c, int st) {
             const int key0 = kbeg + c * CH;
-            int slot0;
-            const T* kp = a.kv.kpage<T>(a.layer, key0, slot0) + ((long long)g * a.kv.page + slot0) * D;
-            const T* vp = a.kv.vpage<T>(a.layer, key0, slot0) + (long long)g * D * a.kv.page + slot0;
+            const int lp = key0 / a.kv.page;
+            const int slot0 = key0 - lp * a.kv.page;
+            const int phys = __builtin_amdgcn_readfirstlane(s_pages[lp - pg0]);
             const int rmax = kend - 1 - key0;  // last written key row of this chunk
+            const char* cbase = kwave
+                ? reinterpret_cast<const char*>(a.kv.kpage_phys<T>(a.layer, phys) + ((long long)g * a.kv.page + slot0) * D)
+                : reinterpret_cast<const char*>(a.kv.vpage_phys<T>(a.layer, phys) + (long long)g * D * a.kv.page + slot0);
             char* base = lds + st * STAGE;
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-                const int inst = w * NI + j;
-                const int P = inst * 64 + lane;  // 16-byte piece of the stage
-                const char* src;
-                if (P < CH * KCOL) {
-                    const int r = P / KCOL, pc = P % KCOL;
-                    const int c16 = pc ^ (r % KCOL);
-                    src = reinterpret_cast<const char*>(kp + (long long)min(r, rmax) * D) + c16 * 16;
-                } else {
-                    const int Q = P - CH * KCOL;
-                    const int dim = Q / VCOL, pc = Q % VCOL;
-                    const int c16 = pc ^ (dim % VCOL);
-                    src = reinterpret_cast<const char*>(vp + (long long)dim * a.kv.page) + c16 * 16;
-                }
+                const int inst = wu * NI + j;
+                const char* src = cbase + (kwave ? min(krow[j], rmax) * D * (int)sizeof(T) : 0) + off[j];
                 __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(base + inst * 1024), 16, 0, 0);
             }
         };
@@ -951,14 +1064,17 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a) {
                 if (w + 4 * hh >= a.group) break;
                 f32x4_t sc[4];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    sc[kb] = zero4();
-                    const int r = kb * 16 + col;
+                for (int kb = 0; kb < 4; ++kb) sc[kb] = zero4();
+                // per 32-dim slice: the four 16-key K fragments, then four
+                // independent MFMAs (one accumulator per 16 keys)
 #pragma unroll
-                    for (int kc = 0; kc < D / 32; ++kc) {
-                        const Frag<T> kf = lds_frag<T>(kl, r, KCOL, (kc * 32 + grp * 8) * (int)sizeof(T) / 16);
-                        mma(sc[kb], kf, qf[hh][kc]);
-                    }
+                for (int kc = 0; kc < D / 32; ++kc) {
+                    Frag<T> kf[4];
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+                        kf[kb] = lds_frag<T>(kl, kb * 16 + col, KCOL, (kc * 32 + grp * 8) * (int)sizeof(T) / 16);
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) mma(sc[kb], kf[kb], qf[hh][kc]);
                 }
                 softmax_pv<T, D>(acc[hh], sc, nvis, a.scale_log2, grp, [&](int t, int db) {
                     Frag<T> vf = lds_frag<T>(vl, 16 * db + col, VCOL, (32 * t + 8 * grp) * (int)sizeof(T) / 16);
@@ -1428,16 +1544,33 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         ns = (C + B + kps - 1) / kps;
         nparts = ns;
     } else {
-        attn_split_plan(C, nkv, c.num_cus, &kps, &ns);
+        attn_split_plan(C, nkv, c.num_cus, d.page, &kps, &ns);
         nparts = ns + 1;  // + the block's own keys
     }
     const int group = nq / nkv;
     int32_t sel[5];
     feature_layers(d.Lt, sel);
+    // RMSNorm statistics of the residual after O / down: each consumer wave sums
+    // the producer's per-tile sums of squares itself (no completion chain in
+    // the producer) when a row's tiles fit one lane set; else the producer's
+    // last tile computes rstd.
+    const int ss_tiles = (H + 16 * kSkinnyNT - 1) / (16 * kSkinnyNT);
+    const bool lazy_stats = ss_tiles <= 4 * kSSPerLane;
+    auto norm_in = [&](const void* gain, bool after_resid) {
+        NormA<T> na{x, H, rstd, (const T*)gain};
+        if (after_resid && lazy_stats) {
+            na.ss = ss;
+            na.ss_tiles = ss_tiles;
+            na.ss_stride = c.lay.ss_stride;
+            na.n_cols = H;
+            na.eps = eps;
+        }
+        return na;
+    };
 
     for (int l = 0; l < d.Ld; ++l) {
         OpQKV<T> qkv;
-        qkv.a = NormA<T>{x, H, rstd, (const T*)c.attn_norm[l]};
+        qkv.a = norm_in(c.attn_norm[l], l > 0);
         qkv.wq = (const T*)c.sw_wq[l];
         qkv.wk = (const T*)c.sw_wk[l];
         qkv.wv = (const T*)c.sw_wv[l];
@@ -1497,14 +1630,15 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         op.M = B;
         op.x = x;
         op.ss_part = ss;
-        op.rstd_out = rstd;
+        op.ss_stride = c.lay.ss_stride;
+        op.rstd_out = lazy_stats ? nullptr : rstd;
         op.eps = eps;
         c.tracer->begin(DFLASH_TRACE_O_PROJ, s);
         if ((e = run_skinny<T>(c, op, B, nq * D, (H + 31) / 32, s)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_O_PROJ, s);
 
         OpSwiGLU<T> sw;
-        sw.a = NormA<T>{x, H, rstd, (const T*)c.mlp_norm[l]};
+        sw.a = norm_in(c.mlp_norm[l], true);
         sw.wg = (const T*)c.sw_wg[l];
         sw.wu = (const T*)c.sw_wu[l];
         sw.F = F;
@@ -1523,7 +1657,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         dn.M = B;
         dn.x = x;
         dn.ss_part = ss;
-        dn.rstd_out = rstd;
+        dn.ss_stride = c.lay.ss_stride;
+        dn.rstd_out = lazy_stats ? nullptr : rstd;
         dn.eps = eps;
         if (pa.cap)
             for (int i = 0; i < 5; ++i)
@@ -1537,7 +1672,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     }
 
     OpLMHead<T> lm;
-    lm.a = NormA<T>{x, H, rstd, (const T*)c.final_norm};
+    lm.a = norm_in(c.final_norm, d.Ld > 0);
     lm.w = (const T*)c.sw_lm;
     lm.V = d.V;
     lm.K = H;
