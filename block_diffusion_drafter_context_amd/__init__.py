@@ -186,8 +186,11 @@ class DFlash:
 
     def __del__(self):
         h = getattr(self, "h", None)
-        if h:
-            lib().dflash_destroy(h)
+        if h and _lib is not None:
+            try:
+                _lib.dflash_destroy(h)
+            except Exception:  # interpreter shutdown: the library may already be gone
+                pass
             self.h = None
 
     def _check(self, st: int, what: str):

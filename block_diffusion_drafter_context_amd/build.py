@@ -27,10 +27,15 @@ def build(verbose: bool = False) -> str:
         subprocess.check_call(cmd)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
+    # a kernel whose host stub was not emitted would only fail at load time
+    undef = subprocess.run(["nm", "-u", tmp], capture_output=True, text=True).stdout
+    missing = [l.split()[-1] for l in undef.splitlines() if "dflash" in l]
+    if missing:
+        raise RuntimeError(f"libdflash.so has undefined library symbols: {missing[:4]}")
     os.replace(tmp, LIB)
     return LIB
 

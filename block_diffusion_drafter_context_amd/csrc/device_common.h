@@ -160,6 +160,19 @@ __device__ __forceinline__ float group16_max(float v) {
     return v;
 }
 // reduce across the 4 lane groups (lanes l, l^16, l^32, l^48)
+// Workgroup barrier for pipelines that feed LDS with direct global->LDS loads.
+// __syncthreads() also fences memory, which drains every outstanding global
+// load (vmcnt(0)) and with it the prefetched stages; here the caller has
+// already waited (vmcnt) for exactly the loads the next step needs.  This
+// wave's LDS reads are complete (lgkmcnt(0)) before it arrives, so a stage
+// refilled after the barrier is no longer being read; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float cross4_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 16, 64));
     v = fmaxf(v, __shfl_xor(v, 32, 64));

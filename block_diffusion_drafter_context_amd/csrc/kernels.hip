@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dflash {
 
@@ -903,17 +904,26 @@ __device__ __forceinline__ void mask_vfrag(Frag<float>& f, int t, int grp, int n
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// XOR key of the 16-byte columns of LDS tile row `row` (rows of `ncol`
+// columns).  A 16-byte read serves 16 lanes per pass from 256 bytes of banks;
+// the 16 consecutive rows those lanes read must land in 16 different 16-byte
+// bank groups: rows of >= 256 bytes key on row % ncol, 128-byte rows (two per
+// 256 bytes) on the row bits above that.
+__host__ __device__ __forceinline__ int lds_key(int row, int ncol) {
+    return ncol >= 16 ? row % ncol : (row >> 1) % ncol;
+}
+
 // Fragment read from an LDS tile of rows of `ncol` 16-byte columns whose
-// columns are XOR-swizzled by row; c16 = first logical 16-byte column.
+// columns are XOR-swizzled by lds_key; c16 = first logical 16-byte column.
 __device__ __forceinline__ Frag<bf16_t> lds_frag_t(const char* base, int row, int ncol, int c16, bf16_t*) {
     Frag<bf16_t> f;
-    f.v = *reinterpret_cast<const uint4*>(base + (row * ncol + (c16 ^ (row % ncol))) * 16);
+    f.v = *reinterpret_cast<const uint4*>(base + (row * ncol + (c16 ^ lds_key(row, ncol))) * 16);
     return f;
 }
 __device__ __forceinline__ Frag<float> lds_frag_t(const char* base, int row, int ncol, int c16, float*) {
     Frag<float> f;
-    f.a = *reinterpret_cast<const float4*>(base + (row * ncol + (c16 ^ (row % ncol))) * 16);
-    f.b = *reinterpret_cast<const float4*>(base + (row * ncol + ((c16 + 1) ^ (row % ncol))) * 16);
+    f.a = *reinterpret_cast<const float4*>(base + (row * ncol + (c16 ^ lds_key(row, ncol))) * 16);
+    f.b = *reinterpret_cast<const float4*>(base + (row * ncol + ((c16 + 1) ^ lds_key(row, ncol))) * 16);
     return f;
 }
 template <typename T>
@@ -1000,12 +1010,12 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
             if (kwave) {
                 const int r = P / KCOL, pc = P % KCOL;
                 krow[j] = r;
-                off[j] = (pc ^ (r % KCOL)) * 16;
+                off[j] = (pc ^ lds_key(r, KCOL)) * 16;
             } else {
                 const int Q = P - CH * KCOL;
                 const int dim = Q / VCOL, pc = Q % VCOL;
                 krow[j] = 0;
-                off[j] = dim * a.kv.page * (int)sizeof(T) + (pc ^ (dim % VCOL)) * 16;
+                off[j] = dim * a.kv.page * (int)sizeof(T) + (pc ^ lds_key(dim, VCOL)) * 16;
             }
         }
         __syncthreads();
@@ -1053,7 +1063,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
                 else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
                 else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            __syncthreads();
+            stage_barrier();  // every wave's pieces of chunk c are in LDS
             const char* kl = lds + (NS == 2 ? (c & 1) : (c % NS)) * STAGE;
             const char* vl = kl + CH * KCOL * 16;
             const int nvalid = kend - (kbeg + c * CH);
@@ -1082,7 +1092,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
                     return vf;
                 });
             }
-            __syncthreads();  // stage (c % NS) is overwritten by chunk c + NS
+            stage_barrier();  // stage (c % NS) is overwritten by chunk c + NS
         }
     } else {
         if (!kEarlyQ) load_q();
@@ -1476,6 +1486,260 @@ __global__ __launch_bounds__(256) void big_gemm_kernel(Op op, int M, int N, int 
 }
 
 // ============================================================================
+// large-M bf16 GEMM (prefill-side fusion and injection): C = A . B^T
+// ============================================================================
+//
+// A [M][K] and B [N][K] are both K-contiguous.  One workgroup (4 waves, 2 x 2)
+// computes a 256 x BN tile of C, each wave 128 x BN/2 as blocks of the
+// 32x32x16 bf16 MFMA (acc lane l: column l % 32, rows 8*(i/4) + 4*(l/32) + i%4).
+// K advances in steps of 32 through an NS-stage LDS ring filled by direct
+// global->LDS 16-byte loads issued NS-1 steps ahead.  In LDS an operand tile
+// is lines of 128 bytes, each line two 64-byte rows; the eight 16-byte slots
+// of line L are XOR-permuted by L % 8 so the fragment reads of eight
+// consecutive rows hit eight different slots (no bank conflicts).  Tiles are
+// handed out so that each XCD works on a contiguous range of an M-fastest
+// grouped order (its concurrent workgroups share A and B panels in its L2).
+
+constexpr int kGBM = 256;
+
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// LDS byte offset of (row, 16-byte column c) of an operand tile whose rows
+// hold BK (32 or 64) elements.  The LDS serves a 16-lane quarter of a 16-byte
+// read per pass from 64 four-byte banks (256 bytes): the sixteen rows such a
+// quarter reads at one column must fall in sixteen different 16-byte bank
+// groups, so the slot permutation keys on the row bits above the 256-byte
+// interleave.
+template <int BK>
+__device__ __forceinline__ int gtile_off(int row, int c) {
+    if constexpr (BK == 32) {  // two 64-byte rows per 128-byte line
+        const int line = row >> 1, slot = ((row & 1) << 2) | c;
+        return line * 128 + ((slot ^ ((line >> 1) & 7)) << 4);
+    } else {                   // one 128-byte row per line
+        return row * 128 + ((c ^ ((row >> 1) & 7)) << 4);
+    }
+}
+// inverse: the (row, 16-byte column) a piece P (16-byte index of the tile) holds
+template <int BK>
+__device__ __forceinline__ void gtile_piece(int P, int& row, int& c) {
+    const int line = P >> 3;
+    const int slot = (P & 7) ^ ((line >> 1) & 7);
+    if constexpr (BK == 32) {
+        row = 2 * line + (slot >> 2);
+        c = slot & 3;
+    } else {
+        row = line;
+        c = slot;
+    }
+}
+
+// Op::kBN: tile width (128 or 256); Op::kNS: LDS stages; Op::kWM: waves along
+// M (2 or 4; 2 waves along N).  Each wave owns a (256/kWM) x (BN/2) block:
+// MI = 8/kWM row blocks and NJ = BN/64 column blocks of 32.
+template <class Op>
+__global__ __launch_bounds__(128 * Op::kWM) void tile_gemm_kernel(Op op, int M, int N, int K, int tiles_m, int tiles_n,
+                                                                  int per_xcd) {
+    constexpr int BN = Op::kBN, NS = Op::kNS, WM = Op::kWM, BK = Op::kBK;
+    constexpr int THREADS = 128 * WM, MI = 8 / WM, NJ = BN / 64;
+    constexpr int ABYTES = kGBM * BK * 2, BBYTES = BN * BK * 2, STAGE = ABYTES + BBYTES;
+    constexpr int APIECES = kGBM * BK / 8 / THREADS, BPIECES = BN * BK / 8 / THREADS;  // 16-byte pieces per thread per stage
+    constexpr int LOADS = APIECES + BPIECES;
+    __shared__ __attribute__((aligned(16))) char lds[NS * STAGE];
+    const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
+    const int t = xcd * per_xcd + r;
+    if (r >= per_xcd || t >= tiles_m * tiles_n) return;
+    constexpr int GM = Op::kGM;
+    const int grp = t / (GM * tiles_n);
+    const int gm0 = grp * GM, gsz = min(GM, tiles_m - gm0);
+    const int idx = t - grp * GM * tiles_n;
+    const int m0 = (gm0 + idx % gsz) * kGBM, n0 = (idx / gsz) * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid >> 1, wn = wid & 1;
+    constexpr int WROWS = kGBM / WM;
+
+    // this thread's 16-byte pieces per stage: piece P = j*THREADS + tid lands
+    // at LDS byte 16*P of its operand; (row, column) inverts the slot
+    // permutation.  Rows past M / N re-read the last row (never stored).
+    long long arow[APIECES];
+    int acol[APIECES];
+#pragma unroll
+    for (int j = 0; j < APIECES; ++j) {
+        int row, c;
+        gtile_piece<BK>(j * THREADS + tid, row, c);
+        arow[j] = op.a_row(min(m0 + row, M - 1));
+        acol[j] = 8 * c;
+    }
+    const bf16_t* brow[BPIECES];
+#pragma unroll
+    for (int j = 0; j < BPIECES; ++j) {
+        int row, c;
+        gtile_piece<BK>(j * THREADS + tid, row, c);
+        brow[j] = op.b_row(min(n0 + row, N - 1), K) + 8 * c;
+    }
+    const int nk = K / BK;
+    // (the builtin takes an untyped source pointer: typed const pointers are cast)
+    auto issue = [&](int ks, int st) {
+        const int k0 = ks * BK;
+        char* base = lds + st * STAGE;
+#pragma unroll
+        for (int j = 0; j < APIECES; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(op.a_at(arow[j], k0) + acol[j]),
+                                             (lds_void_t*)(base + (j * THREADS + wid * 64) * 16), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < BPIECES; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(brow[j] + k0),
+                                             (lds_void_t*)(base + ABYTES + (j * THREADS + wid * 64) * 16), 16, 0, 0);
+    };
+
+    f32x16_t acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int frow = lane & 31, fcol = lane >> 5;
+    for (int st = 0; st < NS - 1; ++st)
+        if (st < nk) issue(st, st);
+    for (int ks = 0; ks < nk; ++ks) {
+        // this thread's pieces of step ks have landed when at most the later
+        // steps' loads are still in flight
+        const int later = min(NS - 2, nk - 1 - ks);
+        if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        stage_barrier();  // all pieces of step ks are in LDS; step ks-1 is no longer read
+        if (ks + NS - 1 < nk) issue(ks + NS - 1, (ks + NS - 1) % NS);
+        const char* As = lds + (ks % NS) * STAGE;
+        const char* Bs = As + ABYTES;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8v_t af[MI], bfr[NJ];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                af[i] = *reinterpret_cast<const bf16x8v_t*>(As + gtile_off<BK>(wm * WROWS + i * 32 + frow, kk * 2 + fcol));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8v_t*>(Bs + gtile_off<BK>(wn * (BN / 2) + j * 32 + frow, kk * 2 + fcol));
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    op.template epilogue<MI, NJ>(acc, m0 + wm * WROWS, n0 + wn * (BN / 2), lane, M, N);
+}
+
+// Fusion: Y[m][n] = round(sum_k concat(slabs)[m][k] W_fc[n][k]); the row RMSNorm
+// follows in rmsnorm_rows_kernel.
+struct TileFuseOp {
+    static constexpr int kBN = 256, kNS = 2, kWM = 4, kBK = 64, kGM = 8;
+    const bf16_t* slab[5];
+    long long ld;
+    int H;
+    const bf16_t* w;  // [H][5H]
+    bf16_t* out;      // [M][H]
+    __device__ __forceinline__ long long a_row(int m) const { return (long long)m * ld; }
+    // a K step never crosses a slab (H is a multiple of 32)
+    __device__ __forceinline__ const bf16_t* a_at(long long row, int k0) const {
+        const int s = k0 / H;
+        return slab[s] + row + (k0 - s * H);
+    }
+    __device__ __forceinline__ const bf16_t* b_row(int n, int K) const { return w + (long long)n * K; }
+    template <int MI, int NJ>
+    __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[MI][NJ], int mb, int nb, int lane, int M, int N) const {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int n = nb + j * 32 + (lane & 31);
+                if (n >= N) continue;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = mb + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (m < M) out[(long long)m * H + n] = f32_to_bf16(acc[i][j][e]);
+                }
+            }
+    }
+};
+
+// Injection: for every draft layer, K = RoPE(c W_k^T) and V = c W_v^T into the
+// paged cache.  Column n = ((layer * 2 + kind) * nkv + head) * d + dim in the
+// weights' own row order; a wave's 128 columns hold whole heads, so the rotary
+// partners (dim, dim + d/2) sit in the same lane, d/64 column blocks apart.
+struct TileInjectOp {
+    static constexpr int kBN = 256, kNS = 4, kWM = 4, kBK = 32, kGM = 8;  // 256-wide tiles: each wave holds whole heads
+    const bf16_t* a;  // fused rows [M][ld]
+    long long ld;
+    const bf16_t* wk[DFLASH_MAX_LAYERS];
+    const bf16_t* wv[DFLASH_MAX_LAYERS];
+    int nkv, d, pos0;
+    const float* cosT;
+    const float* sinT;
+    KVPages kv;
+    __device__ __forceinline__ long long a_row(int m) const { return (long long)m * ld; }
+    __device__ __forceinline__ const bf16_t* a_at(long long row, int k0) const { return a + row + k0; }
+    __device__ __forceinline__ const bf16_t* b_row(int n, int K) const {
+        const int nk = nkv * d;
+        const int l = n / (2 * nk), kind = (n / nk) & 1, rr = n % nk;
+        return (kind == 0 ? wk[l] : wv[l]) + (long long)rr * K;
+    }
+    template <int PO, int MI>  // PO: rotary partner distance in 32-column blocks (d / 64)
+    __device__ __forceinline__ void epi(const f32x16_t (&acc)[MI][4], int mb, int nb, int lane, int M) const {
+        const int nk = nkv * d;
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            // column blocks j0 (dims < d/2 of a head) and j1 = j0 + PO (their partners)
+            const int j0 = PO == 2 ? pr : 2 * pr, j1 = j0 + PO;
+            const int n = nb + j0 * 32 + (lane & 31);
+            const int l = n / (2 * nk), kind = (n / nk) & 1;
+            const int rr = n % nk, h = rr / d, dim = rr % d;  // dim < d/2
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = mb + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (m >= M) continue;
+                    const int pos = pos0 + m;
+                    const float x0 = acc[i][j0][e], x1 = acc[i][j1][e];
+                    int slot;
+                    if (kind == 0) {
+                        const long long tt = (long long)pos * (d / 2) + dim;
+                        const float cs = cosT[tt], sn = sinT[tt];
+                        bf16_t* pg = kv.kpage<bf16_t>(l, pos, slot) + ((long long)h * kv.page + slot) * d;
+                        pg[dim] = f32_to_bf16(x0 * cs - x1 * sn);
+                        pg[dim + d / 2] = f32_to_bf16(x0 * sn + x1 * cs);
+                    } else {
+                        bf16_t* pg = kv.vpage<bf16_t>(l, pos, slot) + (long long)h * d * kv.page + vslot(slot);
+                        pg[(long long)dim * kv.page] = f32_to_bf16(x0);
+                        pg[(long long)(dim + d / 2) * kv.page] = f32_to_bf16(x1);
+                    }
+                }
+        }
+    }
+    template <int MI, int NJ>  // NJ 4: a wave holds 128 columns (whole heads)
+    __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[MI][NJ], int mb, int nb, int lane, int M, int N) const {
+        static_assert(NJ == 4, "injection tiles must give each wave whole heads");
+        if (nb >= N) return;
+        if (d == 128) epi<2, MI>(acc, mb, nb, lane, M);
+        else epi<1, MI>(acc, mb, nb, lane, M);
+    }
+};
+
+template <class Op>
+static hipError_t run_tile_gemm(const Op& op, int M, int N, int K, hipStream_t s) {
+    const int tm = (M + kGBM - 1) / kGBM, tn = (N + Op::kBN - 1) / Op::kBN;
+    const int per_xcd = (tm * tn + 7) / 8;
+    hipLaunchKernelGGL((tile_gemm_kernel<Op>), dim3(8 * per_xcd), dim3(128 * Op::kWM), 0, s, op, M, N, K, tm, tn, per_xcd);
+    return hipGetLastError();
+}
+
+// ============================================================================
 // launchers
 // ============================================================================
 
@@ -1724,6 +1988,16 @@ static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long 
         c.tracer->begin(DFLASH_TRACE_FUSE, s);
         if ((e = run_skinny<T>(c, op, M, 5 * H, (H + 31) / 32, s)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_FUSE, s);
+    } else if constexpr (sizeof(T) == 2) {
+        TileFuseOp op;
+        for (int i = 0; i < 5; ++i) op.slab[i] = (const bf16_t*)slabs[i];
+        op.ld = ld;
+        op.H = H;
+        op.w = (const bf16_t*)c.fc;
+        op.out = (bf16_t*)out;
+        c.tracer->begin(DFLASH_TRACE_FUSE, s);
+        if ((e = run_tile_gemm(op, M, H, 5 * H, s)) != hipSuccess) return e;
+        c.tracer->end(DFLASH_TRACE_FUSE, s);
     } else {
         BigFuseOp<T> op;
         op.a = sa;
@@ -1768,6 +2042,25 @@ static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int
         op.kv = make_pages<T>(c);
         c.tracer->begin(DFLASH_TRACE_INJECT, s);
         hipError_t e = run_skinny<T>(c, op, M, d.H, d.Ld * 2 * d.nkv * d.d / 32, s);
+        if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_INJECT, s);
+        return e;
+    }
+    if constexpr (sizeof(T) == 2) {
+        TileInjectOp op;
+        op.a = (const bf16_t*)fused;
+        op.ld = ld;
+        for (int l = 0; l < d.Ld; ++l) {
+            op.wk[l] = (const bf16_t*)c.wk[l];
+            op.wv[l] = (const bf16_t*)c.wv[l];
+        }
+        op.nkv = d.nkv;
+        op.d = d.d;
+        op.pos0 = pos0;
+        op.cosT = cosT;
+        op.sinT = sinT;
+        op.kv = make_pages<bf16_t>(c);
+        c.tracer->begin(DFLASH_TRACE_INJECT, s);
+        hipError_t e = run_tile_gemm(op, M, d.Ld * 2 * d.nkv * d.d, d.H, s);
         if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_INJECT, s);
         return e;
     }
