@@ -71,6 +71,7 @@ def main():
     ap.add_argument("--long-ctx", type=int, default=36864, help="second context length measured (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-side fusion/injection GEMM timing")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="after timing, copy this many GiB device-to-device (plain copy kernel for counter scaling)")
     args = ap.parse_args()
@@ -111,7 +112,20 @@ def main():
     step_hidden = [di.target_hidden(s, l, 16, tag="step").cuda() if l in sel else None
                    for l in range(s.target_layers)]
     u, r, last = di.target_coins(s)
-    u_d, r_d = u.cuda(), r.cuda()
+    # the synthetic target argmax of a block, as three device ops per step:
+    # g[j] = (d[j+1] + r'[j]) mod V with r'[j] = 0 where the target agrees
+    # (u[j+1] < p) and r[j+1] otherwise, and g[B-1] = last
+    B = s.block
+    sel_idx = torch.tensor(list(range(1, B)) + [0], dtype=torch.int64, device="cuda")
+    keep = torch.tensor([1] * (B - 1) + [0], dtype=torch.int32, device="cuda")
+    add = torch.tensor([0 if float(u[j]) < di.SYNTH_AGREE_P else int(r[j]) for j in range(1, B)] + [last],
+                       dtype=torch.int32, device="cuda")
+    g_buf = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def synthetic_target(tokens):
+        torch.index_select(tokens, 0, sel_idx, out=g_buf)
+        g_buf.mul_(keep).add_(add)
+        return g_buf.remainder_(s.vocab)
     fused_buf = torch.empty(16, s.hidden, dtype=s.torch_dtype, device="cuda")
     tok_buf = torch.empty(s.block, dtype=torch.int32, device="cuda")
     res_buf = torch.empty(2, dtype=torch.int32, device="cuda")
@@ -123,7 +137,7 @@ def main():
 
         def step():
             tokens, _ = ctx.draft_block(anchor, tokens=tok_buf)
-            g = di.synthetic_target_argmax(tokens, u_d, r_d, last, s.vocab)
+            g = synthetic_target(tokens)
             ctx.verify_accept(tokens, g, out=res_buf)
             fused = ctx.fuse_context(step_hidden, out=fused_buf)
             ctx.inject_kv(fused, C0)
@@ -245,6 +259,62 @@ def main():
                            "draft_pass_hbm_frac": round(ab2["draft"] / (dr_us * 1e-6) / HBM_PEAK, 4)}
         log(f"[bench] long ctx: {json.dumps(out['long_ctx'])}")
         del ctx2
+
+    # ---- prefill side: fusion and injection of 32768 context rows (27B-class shape)
+    if not args.no_prefill:
+        if "ctx" in locals():
+            del ctx
+        torch.cuda.empty_cache()
+        ps = di.SHAPES["fusion_prefill_32k"]
+        Mp = ps.ctx
+        wp = {k: v.cuda() for k, v in di.draft_weights(ps, need_draft=False, need_lm=False).items()}
+        pctx = dl.DFlash(ps, wp, max_ctx=Mp + 64, max_rows=Mp)
+        psel = dl.feature_layers(ps.target_layers)
+        gen = torch.Generator(device="cuda").manual_seed(ps.seed)
+        slabs = {l: torch.randn(Mp, ps.hidden, generator=gen, device="cuda").to(torch.bfloat16) for l in psel}
+        hid = [slabs.get(l) for l in range(ps.target_layers)]
+        fused = torch.empty(Mp, ps.hidden, dtype=torch.bfloat16, device="cuda")
+
+        def time_ms(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        fuse_ms = time_ms(lambda: pctx.fuse_context(hid, out=fused))
+        # the GEMM alone (without its row RMSNorm), from the library's own event trace
+        dl.lib().dflash_trace_enable(pctx.h, 8, 8)
+        for _ in range(5):
+            pctx.fuse_context(hid, out=fused)
+        import ctypes as C_
+        tms, tn = C_.c_double(), C_.c_int32()
+        dl.lib().dflash_trace_read(pctx.h, C_.byref(tms), C_.byref(tn))
+        dl.lib().dflash_trace_enable(pctx.h, 0, 0)
+        gemm_ms = tms.value / max(tn.value, 1)
+
+        def inject():
+            pctx.rollback(0)
+            pctx.inject_kv(fused, 0)
+
+        inject_ms = time_ms(inject)
+        fl_fuse = 2.0 * Mp * 5 * ps.hidden * ps.hidden
+        n_inj = ps.draft_layers * 2 * ps.n_kv_heads * ps.head_dim
+        fl_inj = 2.0 * Mp * ps.hidden * n_inj
+        out["prefill"] = {
+            "workload": "fusion_prefill_32k", "rows": Mp, "hidden": ps.hidden, "concat_k": 5 * ps.hidden,
+            "fuse_gemm_ms": round(gemm_ms, 3), "fuse_gemm_tflops": round(fl_fuse / (gemm_ms * 1e-3) / 1e12, 1),
+            "fuse_gemm_mfma_frac": round(fl_fuse / (gemm_ms * 1e-3) / BF16_PEAK, 4),
+            "fuse_with_norm_ms": round(fuse_ms, 3),
+            "inject_ms": round(inject_ms, 3), "inject_tflops": round(fl_inj / (inject_ms * 1e-3) / 1e12, 1),
+            "inject_mfma_frac": round(fl_inj / (inject_ms * 1e-3) / BF16_PEAK, 4)}
+        log(f"[bench] prefill: {json.dumps(out['prefill'])}")
+        del pctx, slabs, hid, fused, wp
+        torch.cuda.empty_cache()
 
     # ---- CPU oracle baseline: one full step of the oracle on a bounded sample
     if not args.no_cpu_baseline:

@@ -256,6 +256,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
         skinny_segment<T>(op.a, op.b_rows(tile, 0, c.nchunks), op.b_rows(tile, 1, c.nchunks), ch0, ch1, c.K, lane, row,
                           grp, row_ok, pr, pre, have_pre, acc);
         i = seg_end;
+        op.prefetch(tile, lane, st);  // epilogue inputs, in flight during the exchange below
         if (!(ch0 == 0 && ch1 == c.nchunks)) {
             // partial tile: publish, and let the last contributor finish it
             const int slot = tile == first_tile ? 0 : 1;
@@ -382,6 +383,7 @@ struct OpQKV {
         return sw_stream(W, (h * d + 16 * i + blk * (d / 2)) / 16, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
@@ -433,7 +435,9 @@ struct OpQKV {
 // last finished tile turns them into rstd (fixed summation order).
 template <typename T>
 struct OpResid {
-    using State = NoState;
+    struct State {
+        float xv[2][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
+    };
     static constexpr bool kDoneHook = true;
     PlainA<T> a;
     const T* w;
@@ -451,7 +455,18 @@ struct OpResid {
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+    __device__ __forceinline__ void prefetch(int tile, int lane, State& st) const {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int n = min(32 * tile + 16 * b + (lane & 15), N - 1);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int j = min(4 * (lane >> 4) + ii, M - 1);
+                st.xv[b][ii] = Elem<T>::to_f32(x[(long long)j * N + n]);
+            }
+        }
+    }
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State& st) const {
         float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -462,7 +477,7 @@ struct OpResid {
                 const int j = 4 * (lane >> 4) + ii;
                 if (j >= M) continue;
                 T* p = x + (long long)j * N + n;
-                const float xn = Elem<T>::round(Elem<T>::to_f32(*p) + Elem<T>::round(acc[b][ii]));
+                const float xn = Elem<T>::round(st.xv[b][ii] + Elem<T>::round(acc[b][ii]));
                 *p = Elem<T>::from_f32(xn);
                 if (cap) cap[(long long)j * cap_ld + n] = Elem<T>::from_f32(xn);
                 sq[ii] += xn * xn;
@@ -510,6 +525,7 @@ struct OpSwiGLU {
         return sw_stream(blk == 0 ? wg : wu, tile, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
@@ -560,6 +576,7 @@ struct OpLMHead {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) { s.v[ii] = -INFINITY; s.idx[ii] = 0x7FFFFFFF; }
     }
+    __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State& s) const {
 #pragma unroll
@@ -642,6 +659,7 @@ struct OpFuse {
         return n0 < H ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
@@ -688,6 +706,7 @@ struct OpInject {
         return sw_stream(kind == 0 ? wk[l] : wv[l], (h * d + 16 * i + blk * (d / 2)) / 16, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
@@ -1637,15 +1656,17 @@ __global__ __launch_bounds__(128 * Op::kWM) void tile_gemm_kernel(Op op, int M, 
 
 // Fusion: Y[m][n] = round(sum_k concat(slabs)[m][k] W_fc[n][k]); the row RMSNorm
 // follows in rmsnorm_rows_kernel.
-struct TileFuseOp {
-    static constexpr int kBN = 256, kNS = 2, kWM = 4, kBK = 64, kGM = 8;
+// BK 64 (2 LDS stages) needs H % 64 == 0; BK 32 (4 stages) covers H % 32 == 0
+template <int BK>
+struct TileFuseOpT {
+    static constexpr int kBN = 256, kNS = BK == 64 ? 2 : 4, kWM = 4, kBK = BK, kGM = 4;
     const bf16_t* slab[5];
     long long ld;
     int H;
     const bf16_t* w;  // [H][5H]
     bf16_t* out;      // [M][H]
     __device__ __forceinline__ long long a_row(int m) const { return (long long)m * ld; }
-    // a K step never crosses a slab (H is a multiple of 32)
+    // a K step never crosses a slab (H is a multiple of BK)
     __device__ __forceinline__ const bf16_t* a_at(long long row, int k0) const {
         const int s = k0 / H;
         return slab[s] + row + (k0 - s * H);
@@ -1672,8 +1693,10 @@ struct TileFuseOp {
 // paged cache.  Column n = ((layer * 2 + kind) * nkv + head) * d + dim in the
 // weights' own row order; a wave's 128 columns hold whole heads, so the rotary
 // partners (dim, dim + d/2) sit in the same lane, d/64 column blocks apart.
-struct TileInjectOp {
-    static constexpr int kBN = 256, kNS = 4, kWM = 4, kBK = 32, kGM = 8;  // 256-wide tiles: each wave holds whole heads
+template <int BK>
+struct TileInjectOpT {
+    // 256-wide tiles: each wave holds whole heads
+    static constexpr int kBN = 256, kNS = BK == 64 ? 2 : 4, kWM = 4, kBK = BK, kGM = 4;
     const bf16_t* a;  // fused rows [M][ld]
     long long ld;
     const bf16_t* wk[DFLASH_MAX_LAYERS];
@@ -1989,14 +2012,16 @@ static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long 
         if ((e = run_skinny<T>(c, op, M, 5 * H, (H + 31) / 32, s)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_FUSE, s);
     } else if constexpr (sizeof(T) == 2) {
-        TileFuseOp op;
-        for (int i = 0; i < 5; ++i) op.slab[i] = (const bf16_t*)slabs[i];
-        op.ld = ld;
-        op.H = H;
-        op.w = (const bf16_t*)c.fc;
-        op.out = (bf16_t*)out;
+        auto go = [&](auto op) {
+            for (int i = 0; i < 5; ++i) op.slab[i] = (const bf16_t*)slabs[i];
+            op.ld = ld;
+            op.H = H;
+            op.w = (const bf16_t*)c.fc;
+            op.out = (bf16_t*)out;
+            return run_tile_gemm(op, M, H, 5 * H, s);
+        };
         c.tracer->begin(DFLASH_TRACE_FUSE, s);
-        if ((e = run_tile_gemm(op, M, H, 5 * H, s)) != hipSuccess) return e;
+        if ((e = H % 64 == 0 ? go(TileFuseOpT<64>{}) : go(TileFuseOpT<32>{})) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_FUSE, s);
     } else {
         BigFuseOp<T> op;
@@ -2046,21 +2071,23 @@ static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int
         return e;
     }
     if constexpr (sizeof(T) == 2) {
-        TileInjectOp op;
-        op.a = (const bf16_t*)fused;
-        op.ld = ld;
-        for (int l = 0; l < d.Ld; ++l) {
-            op.wk[l] = (const bf16_t*)c.wk[l];
-            op.wv[l] = (const bf16_t*)c.wv[l];
-        }
-        op.nkv = d.nkv;
-        op.d = d.d;
-        op.pos0 = pos0;
-        op.cosT = cosT;
-        op.sinT = sinT;
-        op.kv = make_pages<bf16_t>(c);
+        auto go = [&](auto op) {
+            op.a = (const bf16_t*)fused;
+            op.ld = ld;
+            for (int l = 0; l < d.Ld; ++l) {
+                op.wk[l] = (const bf16_t*)c.wk[l];
+                op.wv[l] = (const bf16_t*)c.wv[l];
+            }
+            op.nkv = d.nkv;
+            op.d = d.d;
+            op.pos0 = pos0;
+            op.cosT = cosT;
+            op.sinT = sinT;
+            op.kv = make_pages<bf16_t>(c);
+            return run_tile_gemm(op, M, d.Ld * 2 * d.nkv * d.d, d.H, s);
+        };
         c.tracer->begin(DFLASH_TRACE_INJECT, s);
-        hipError_t e = run_tile_gemm(op, M, d.Ld * 2 * d.nkv * d.d, d.H, s);
+        hipError_t e = d.H % 64 == 0 ? go(TileInjectOpT<64>{}) : go(TileInjectOpT<32>{});
         if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_INJECT, s);
         return e;
     }
