@@ -9,6 +9,10 @@ import dflash_inputs as di
 MID_BF16 = di.Shape("mid_bf16", "bf16", hidden=512, target_layers=12, draft_layers=2, n_q_heads=8,
                     n_kv_heads=2, head_dim=128, ffn=1376, vocab=4000, ctx=300, seed=21)
 MID_BF16_D64 = MID_BF16.replace(name="mid_bf16_d64", n_q_heads=8, n_kv_heads=4, head_dim=64, seed=22)
+# hidden 352 is a multiple of 32 but not of 64: the prefill GEMMs take their
+# 32-deep K-step path and a partial 256-column tile
+MID_BF16_H352 = di.Shape("mid_bf16_h352", "bf16", hidden=352, target_layers=10, draft_layers=2, n_q_heads=4,
+                         n_kv_heads=2, head_dim=64, ffn=704, vocab=1008, ctx=300, seed=24)
 MID_FP32_G5 = di.Shape("mid_fp32_g5", "fp32", hidden=320, target_layers=9, draft_layers=1, n_q_heads=10,
                        n_kv_heads=2, head_dim=64, ffn=688, vocab=1024, ctx=100, seed=23)
 

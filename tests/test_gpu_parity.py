@@ -5,8 +5,8 @@ import pytest
 import torch
 
 import dflash_inputs as di
-from tests.gpu_helpers import (MID_BF16, MID_BF16_D64, MID_FP32_G5, assert_logits, assert_rows_close,
-                               assert_tokens, dev)
+from tests.gpu_helpers import (MID_BF16, MID_BF16_D64, MID_BF16_H352, MID_FP32_G5, assert_logits,
+                               assert_rows_close, assert_tokens, dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,8 @@ def test_accept_matches_oracle(dl, orc, B):
 # ------------------------------------------------------------------ fusion
 
 @pytest.mark.parametrize("shape,M", [(TINY, 1), (TINY, 3), (TINY, 16), (TINY, 17), (TINY, 128), (TINY, 130),
-                                     (MID_BF16, 1), (MID_BF16, 16), (MID_BF16, 100), (MID_FP32_G5, 40)])
+                                     (MID_BF16, 1), (MID_BF16, 16), (MID_BF16, 100), (MID_BF16, 300),
+                                     (MID_BF16_H352, 17), (MID_BF16_H352, 300), (MID_FP32_G5, 40)])
 def test_fuse_matches_oracle(dl, orc, shape, M):
     w = di.draft_weights(shape, gains="random", need_draft=False, need_lm=False)
     ctx = dl.DFlash(shape, dev(w), max_ctx=64, max_rows=max(M, 16))
@@ -78,16 +79,17 @@ def test_fuse_strided_rows(dl, orc):
 
 # ------------------------------------------------------------------ injection
 
-@pytest.mark.parametrize("shape", [TINY, MID_BF16, MID_BF16_D64])
+@pytest.mark.parametrize("shape", [TINY, MID_BF16, MID_BF16_D64, MID_BF16_H352])
 def test_inject_matches_oracle(dl, orc, shape):
-    """Three injections (large-M, 16-row and ragged) into a shuffled page table,
-    then every position read back and compared with the oracle."""
+    """Injections of 300 rows (prefill GEMM), 16 and 5 rows (skinny), 270 rows at
+    the unaligned position 321 (crossing a page boundary) and 1 row, into a
+    shuffled page table; every position read back and compared with the oracle."""
     w = di.draft_weights(shape, gains="random", need_draft=False, need_lm=False)
     ctx = dl.DFlash(shape, dev(w), max_ctx=1024, max_rows=600, page_seed=99)
     m = orc.Model(shape, w)
     pos = 0
     ks, vs = [], []
-    for M in (300, 16, 5, 1):
+    for M in (300, 16, 5, 270, 1):
         fused = di.fused_context(shape, M, tag=f"fused{pos}")
         ctx.inject_kv(fused.cuda(), pos)
         k, v = orc.inject_rows(m, fused, range(M), pos)
