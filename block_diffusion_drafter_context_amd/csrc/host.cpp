@@ -96,7 +96,7 @@ Layout compute_layout(const Dims& d, int num_cus) {
     // 4 waves per CU: measured best for every skinny-GEMM shape of the draft
     // pass (fewer concurrent weight streams keep DRAM pages open longer)
     L.nwaves = std::max(num_cus, 1) * 4;
-    L.partial = take((size_t)L.nwaves * 2 * kSkinnyNT * 256 * 4);
+    L.partial = take((size_t)L.nwaves * 2 * kSkinnyMaxNT * 256 * 4);
     // tiles of every skinny GEMM: qkv, o, gate/up, down, lm head, fuse, inject
     long long t = 0;
     const long long nqd = (long long)d.nq * d.d, nkd = (long long)d.nkv * d.d;

@@ -16,7 +16,8 @@ namespace dflash {
 // Launch geometry shared by host and device code.
 constexpr int kWaveSize = 64;
 constexpr int kSkinnyWavesPerWG = 4;     // skinny (M <= 16) GEMM: 256-thread workgroups
-constexpr int kSkinnyNT = 2;             // 16-column blocks per skinny tile
+constexpr int kSkinnyNT = 2;             // 16-column blocks per skinny tile (most ops)
+constexpr int kSkinnyMaxNT = 4;          // the widest skinny tile (LM head)
 constexpr int kAttnChunk = 64;           // keys per attention step
 constexpr int kAttnStages = 2;           // attention chunks resident in LDS per workgroup
 constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU

@@ -176,16 +176,18 @@ __device__ __forceinline__ const T* sw_stream(const T* base, int col_block, int 
 // are masked to zero at use), and the loop is unrolled twice over two register
 // sets (ping-pong, no copies), so the next group's loads stay in flight while
 // the current group is computed.
-template <typename T, class AL>
-__device__ __forceinline__ void skinny_segment(const AL& al, const T* s0, const T* s1, int ch0, int ch1, int K,
+template <typename T, int NT, class AL>
+__device__ __forceinline__ void skinny_segment(const AL& al, const T* const (&sb)[NT], int ch0, int ch1, int K,
                                                int lane, int row, int grp, bool row_ok, const typename AL::Pre& pr,
-                                               float& pre, bool& have_pre, f32x4_t acc[2]) {
+                                               float& pre, bool& have_pre, f32x4_t (&acc)[NT]) {
     using Raw = typename AL::Raw;
     const int arow = row_ok ? row : 0;
-    const T* w1s = s1 ? s1 : s0;
+    const T* ws[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) ws[b] = sb[b] ? sb[b] : sb[0];  // blocks past N re-read block 0 (never stored)
     const int klast = K - 8;  // last valid 8-element group of an activation row
     struct Group {
-        Frag<T> w0[kP], w1[kP];
+        Frag<T> w[NT][kP];
         Raw a[kP];
     };
     auto load_group = [&](int c, Group& g) {
@@ -193,8 +195,8 @@ __device__ __forceinline__ void skinny_segment(const AL& al, const T* s0, const 
         for (int p = 0; p < kP; ++p) {
             const int ch = min(c + p, ch1 - 1);
             const int k = min(ch * 32 + grp * 8, klast);
-            g.w0[p].load_sw(s0 + (long long)ch * 512, lane);
-            g.w1[p].load_sw(w1s + (long long)ch * 512, lane);
+#pragma unroll
+            for (int b = 0; b < NT; ++b) g.w[b][p].load_sw(ws[b] + (long long)ch * 512, lane);
             al.load(g.a[p], arow, k);
         }
     };
@@ -205,8 +207,8 @@ __device__ __forceinline__ void skinny_segment(const AL& al, const T* s0, const 
             al.finish(a, g.a[p], pre);
             const bool ok = row_ok && (c + p < ch1) && ((c + p) * 32 + grp * 8 < K);
             a.mask(ok ? 0xFFFFFFFFu : 0u);
-            mma(acc[0], a, g.w0[p]);
-            mma(acc[1], a, g.w1[p]);
+#pragma unroll
+            for (int b = 0; b < NT; ++b) mma(acc[b], a, g.w[b][p]);
         }
     };
     // sched_barrier(0) keeps the compiler from sinking a group's loads next to
@@ -231,6 +233,7 @@ __device__ __forceinline__ void skinny_segment(const AL& al, const T* s0, const 
 
 template <typename T, class Op>
 __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
+    constexpr int NT = Op::kNT;  // 16-column blocks per tile
     const int lane = threadIdx.x & 63;
     const int wave = blockIdx.x * kSkinnyWavesPerWG + (threadIdx.x >> 6);
     const int row = lane & 15, grp = lane >> 4;
@@ -252,17 +255,22 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
         const long long tbeg = (long long)tile * c.nchunks;
         const long long seg_end = end < tbeg + c.nchunks ? end : tbeg + c.nchunks;
         const int ch0 = (int)(i - tbeg), ch1 = (int)(seg_end - tbeg);
-        f32x4_t acc[2] = {zero4(), zero4()};
-        skinny_segment<T>(op.a, op.b_rows(tile, 0, c.nchunks), op.b_rows(tile, 1, c.nchunks), ch0, ch1, c.K, lane, row,
-                          grp, row_ok, pr, pre, have_pre, acc);
+        f32x4_t acc[NT];
+        const T* sb[NT];
+#pragma unroll
+        for (int b = 0; b < NT; ++b) {
+            acc[b] = zero4();
+            sb[b] = op.b_rows(tile, b, c.nchunks);
+        }
+        skinny_segment<T, NT>(op.a, sb, ch0, ch1, c.K, lane, row, grp, row_ok, pr, pre, have_pre, acc);
         i = seg_end;
         op.prefetch(tile, lane, st);  // epilogue inputs, in flight during the exchange below
         if (!(ch0 == 0 && ch1 == c.nchunks)) {
             // partial tile: publish, and let the last contributor finish it
             const int slot = tile == first_tile ? 0 : 1;
-            float* mine = c.partial + ((long long)wave * 2 + slot) * (kSkinnyNT * 256);
+            float* mine = c.partial + ((long long)wave * 2 + slot) * (kSkinnyMaxNT * 256);
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NT; ++b)
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) st_agent(mine + b * 256 + ii * 64 + lane, acc[b][ii]);
             wait_vmem();
@@ -273,16 +281,16 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
             old = __shfl(old, 0, 64);
             if (old != (unsigned)(w_last - w_first)) continue;
             compiler_fence();
-            acc[0] = zero4();
-            acc[1] = zero4();
+#pragma unroll
+            for (int b = 0; b < NT; ++b) acc[b] = zero4();
             for (int w = w_first; w <= w_last; ++w) {
                 const int ft = (int)(((long long)w * c.per_wave) / c.nchunks);
-                const float* src = c.partial + ((long long)w * 2 + (ft == tile ? 0 : 1)) * (kSkinnyNT * 256);
-                float v[8];
+                const float* src = c.partial + ((long long)w * 2 + (ft == tile ? 0 : 1)) * (kSkinnyMaxNT * 256);
+                float v[4 * NT];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = ld_agent(src + (q >> 2) * 256 + (q & 3) * 64 + lane);
+                for (int q = 0; q < 4 * NT; ++q) v[q] = ld_agent(src + (q >> 2) * 256 + (q & 3) * 64 + lane);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) acc[q >> 2][q & 3] += v[q];
+                for (int q = 0; q < 4 * NT; ++q) acc[q >> 2][q & 3] += v[q];
             }
             if (lane == 0) atomicExch(&c.tile_cnt[tile], 0u);
         }
@@ -353,6 +361,7 @@ struct KVPages {
 // (16i, 16i + d/2) of one head so each rotary pair sits in one lane.
 template <typename T>
 struct OpQKV {
+    static constexpr int kNT = 2;  // 16-column blocks per tile
     using State = NoState;
     static constexpr bool kDoneHook = false;
     NormA<T> a;
@@ -386,7 +395,7 @@ struct OpQKV {
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
         int kind, h, i;
         decode(tile, kind, h, i);
         const int dim = 16 * i + (lane & 15), half = d / 2;
@@ -435,6 +444,7 @@ struct OpQKV {
 // last finished tile turns them into rstd (fixed summation order).
 template <typename T>
 struct OpResid {
+    static constexpr int kNT = 2;  // 16-column blocks per tile
     struct State {
         float xv[2][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
     };
@@ -466,7 +476,7 @@ struct OpResid {
             }
         }
     }
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State& st) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State& st) const {
         float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -514,6 +524,7 @@ struct OpResid {
 // h = round(silu(u . Wg^T) * (u . Wu^T)); tile t pairs column block t of Wg and Wu.
 template <typename T>
 struct OpSwiGLU {
+    static constexpr int kNT = 2;  // 16-column blocks per tile
     using State = NoState;
     static constexpr bool kDoneHook = false;
     NormA<T> a;
@@ -528,7 +539,7 @@ struct OpSwiGLU {
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
         const int n = 16 * tile + (lane & 15);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -556,6 +567,7 @@ __device__ __forceinline__ float unordered_bits(uint32_t k) {
 // workgroup writes the tokens.
 template <typename T>
 struct OpLMHead {
+    static constexpr int kNT = 4;  // 64-column tiles: one activation load feeds four weight blocks
     struct State {
         float v[4];
         int idx[4];
@@ -569,7 +581,7 @@ struct OpLMHead {
     unsigned* wg_cnt;              // workgroup completion counter
     int32_t* tokens;               // [M]
     __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
-        const int n0 = 32 * tile + 16 * blk;
+        const int n0 = 16 * kNT * tile + 16 * blk;
         return n0 < V ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State& s) const {
@@ -578,10 +590,10 @@ struct OpLMHead {
     }
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State& s) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State& s) const {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = 32 * tile + 16 * b + (lane & 15);
+        for (int b = 0; b < kNT; ++b) {
+            const int n = 16 * kNT * tile + 16 * b + (lane & 15);
             if (n >= V) continue;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
@@ -648,6 +660,7 @@ struct OpLMHead {
 // y = round(W_fc . concat(slabs)) for M <= 16 rows (RMSNorm follows separately).
 template <typename T>
 struct OpFuse {
+    static constexpr int kNT = 2;  // 16-column blocks per tile
     using State = NoState;
     static constexpr bool kDoneHook = false;
     SlabA<T> a;
@@ -662,7 +675,7 @@ struct OpFuse {
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             const int n = 32 * tile + 16 * b + (lane & 15);
@@ -681,6 +694,7 @@ struct OpFuse {
 // pair i of blocks (16i, 16i + d/2).
 template <typename T>
 struct OpInject {
+    static constexpr int kNT = 2;  // 16-column blocks per tile
     using State = NoState;
     static constexpr bool kDoneHook = false;
     PlainA<T> a;
@@ -709,7 +723,7 @@ struct OpInject {
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t acc[2], int lane, State&) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
         int l, kind, h, i;
         decode(tile, l, kind, h, i);
         const int dim = 16 * i + (lane & 15), half = d / 2;
@@ -1841,7 +1855,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     // the producer's per-tile sums of squares itself (no completion chain in
     // the producer) when a row's tiles fit one lane set; else the producer's
     // last tile computes rstd.
-    const int ss_tiles = (H + 16 * kSkinnyNT - 1) / (16 * kSkinnyNT);
+    const int ss_tiles = (H + 16 * OpResid<T>::kNT - 1) / (16 * OpResid<T>::kNT);
     const bool lazy_stats = ss_tiles <= 4 * kSSPerLane;
     auto norm_in = [&](const void* gain, bool after_resid) {
         NormA<T> na{x, H, rstd, (const T*)gain};
@@ -1969,7 +1983,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     lm.wg_cnt = counters + 1;
     lm.tokens = pa.tokens;
     c.tracer->begin(DFLASH_TRACE_LM_HEAD, s);
-    if ((e = run_skinny<T>(c, lm, B, H, (d.V + 31) / 32, s)) != hipSuccess) return e;
+    if ((e = run_skinny<T>(c, lm, B, H, (d.V + 16 * OpLMHead<T>::kNT - 1) / (16 * OpLMHead<T>::kNT), s)) != hipSuccess)
+        return e;
     c.tracer->end(DFLASH_TRACE_LM_HEAD, s);
     return hipSuccess;
 }
