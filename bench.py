@@ -72,6 +72,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-side fusion/injection GEMM timing")
+    ap.add_argument("--kv-rotate", type=int, default=4,
+                    help="independent contexts (KV caches, anchors) the 4K steps rotate through, so the 256 MB "
+                         "Infinity Cache cannot hold one context's KV between its steps")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="after timing, copy this many GiB device-to-device (plain copy kernel for counter scaling)")
     args = ap.parse_args()
@@ -152,34 +155,45 @@ def main():
 
         return step, stats
 
-    def timed(ctx, C0, steps, warmup, trace_cls=None):
-        step, stats = make_step(ctx, C0)
-        for _ in range(warmup):
-            step()
+    def timed(ctxs, C0, steps, warmup, trace_cls=None):
+        """Steps rotate through the contexts in ctxs (a list, or one context)."""
+        if not isinstance(ctxs, list):
+            ctxs = [ctxs]
+        made = [make_step(c, C0) for c in ctxs]
+        for i in range(warmup):
+            made[i % len(made)][0]()
         torch.cuda.synchronize()
         if trace_cls is not None:
-            st = dl.lib().dflash_trace_enable(ctx.h, trace_cls, steps * 8)
-            assert st == 0
-        stats["k"] = stats["n"] = 0
+            for c in ctxs:
+                st = dl.lib().dflash_trace_enable(c.h, trace_cls, steps * 8)
+                assert st == 0
+        for _, st_ in made:
+            st_["k"] = st_["n"] = 0
         t = time.perf_counter()
-        for _ in range(steps):
-            step()
+        for i in range(steps):
+            made[i % len(made)][0]()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t
+        stats = {"k": sum(m[1]["k"] for m in made), "n": sum(m[1]["n"] for m in made)}
         trace = None
         if trace_cls is not None:
             import ctypes as C_
-            ms, n = C_.c_double(), C_.c_int32()
-            dl.lib().dflash_trace_read(ctx.h, C_.byref(ms), C_.byref(n))
-            trace = (ms.value, n.value)
-            dl.lib().dflash_trace_enable(ctx.h, 0, 0)
+            tot_ms, tot_n = 0.0, 0
+            for c in ctxs:
+                ms, n = C_.c_double(), C_.c_int32()
+                dl.lib().dflash_trace_read(c.h, C_.byref(ms), C_.byref(n))
+                tot_ms += ms.value
+                tot_n += n.value
+                dl.lib().dflash_trace_enable(c.h, 0, 0)
+            trace = (tot_ms, tot_n)
         return dt, stats, trace
 
     # ---- headline: context C, LM head traced live over the timed region
     t0 = time.time()
-    ctx = prepare(C, "ctx")
-    log(f"[bench] prefill fuse+inject of {C} rows done in {time.time() - t0:.1f}s")
-    dt, stats, tr = timed(ctx, C, args.steps, args.warmup, trace_cls=1)
+    ctxs = [prepare(C, f"ctx{i}" if i else "ctx") for i in range(max(args.kv_rotate, 1))]
+    ctx = ctxs[0]
+    log(f"[bench] {len(ctxs)} contexts, prefill fuse+inject of {C} rows each, done in {time.time() - t0:.1f}s")
+    dt, stats, tr = timed(ctxs, C, args.steps, args.warmup, trace_cls=1)
     ab = alg_bytes(s, C)
     bps = args.steps / dt
     lm_ms = tr[0] / max(tr[1], 1)
@@ -202,7 +216,8 @@ def main():
         "config": {"workload": args.workload, "hidden": s.hidden, "target_layers": s.target_layers,
                    "draft_layers": s.draft_layers, "heads": f"{s.n_q_heads}/{s.n_kv_heads}x{s.head_dim}",
                    "ffn": s.ffn, "vocab": s.vocab, "ctx": C, "block": s.block,
-                   "step": "draft_block+verify_accept+fuse(16)+inject(16)+rollback"},
+                   "step": "draft_block+verify_accept+fuse(16)+inject(16)+rollback",
+                   "kv_contexts_rotated": len(ctxs)},
         "drafted_tok_per_s": round(15 * bps, 1),
         "hbm_frac_step": round(ab["step"] * bps / HBM_PEAK, 4),
         "alg_bytes_per_step": ab["step"],
@@ -235,7 +250,7 @@ def main():
                      "inject16": (9, ab["inject16"])}
         bd = {}
         for name, (cls, byts) in per_layer.items():
-            _, _, tr2 = timed(ctx, C, 30, 2, trace_cls=cls)
+            _, _, tr2 = timed(ctxs, C, 32, 4, trace_cls=cls)
             us = tr2[0] / max(tr2[1], 1) * 1e3
             bd[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
         out["breakdown_ctx"] = bd
@@ -244,6 +259,7 @@ def main():
     # ---- long context
     if args.long_ctx:
         del ctx
+        ctxs.clear()
         torch.cuda.empty_cache()
         t0 = time.time()
         ctx2 = prepare(args.long_ctx, "long")
@@ -264,6 +280,7 @@ def main():
     if not args.no_prefill:
         if "ctx" in locals():
             del ctx
+        ctxs.clear()
         torch.cuda.empty_cache()
         ps = di.SHAPES["fusion_prefill_32k"]
         Mp = ps.ctx
