@@ -237,6 +237,30 @@ def main():
         out["copy_calibration_bytes"] = n
         del src, dst
 
+    def draft_percentiles(ctxs_, C0, n=200):
+        """p10 / p50 / p90 of single draft-pass durations (HIP events), in us;
+        steps rotate through the contexts as in the timed region."""
+        import ctypes as C_
+        if not isinstance(ctxs_, list):
+            ctxs_ = [ctxs_]
+        made = [make_step(c, C0)[0] for c in ctxs_]
+        for c in ctxs_:
+            assert dl.lib().dflash_trace_enable(c.h, 7, n) == 0
+        for i in range(n):
+            made[i % len(made)]()
+        v = []
+        for c in ctxs_:
+            buf = (C_.c_float * n)()
+            cnt = C_.c_int32()
+            assert dl.lib().dflash_trace_read_each(c.h, buf, n, C_.byref(cnt)) == 0
+            dl.lib().dflash_trace_enable(c.h, 0, 0)
+            v.extend(buf[:cnt.value])
+        v = np.array(v, dtype=np.float64) * 1e3
+        return [round(float(np.percentile(v, q)), 1) for q in (10, 50, 90)]
+
+    out["draft_pass_us_p10_p50_p90"] = draft_percentiles(ctxs, C)
+    log(f"[bench] draft pass p10/p50/p90 {out['draft_pass_us_p10_p50_p90']} us")
+
     # ---- per-kernel-class breakdown (separate short traced runs, not the timed region)
     if not args.no_breakdown:
         per_layer = {"qkv": (4, (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * s.hidden * s.elem_bytes),
@@ -268,7 +292,9 @@ def main():
         ab2 = alg_bytes(s, args.long_ctx)
         bps2 = args.steps / dt2
         dr_us = tr2[0] / max(tr2[1], 1) * 1e3
+        pct = draft_percentiles(ctx2, args.long_ctx)
         out["long_ctx"] = {"ctx": args.long_ctx, "blocks_per_s": round(bps2, 2),
+                           "draft_pass_us_p10_p50_p90": pct,
                            "drafted_tok_per_s": round(15 * bps2, 1),
                            "hbm_frac_step": round(ab2["step"] * bps2 / HBM_PEAK, 4),
                            "draft_pass_us": round(dr_us, 1),

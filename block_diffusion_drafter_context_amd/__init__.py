@@ -100,6 +100,12 @@ def lib():
         L.dflash_read_kv.argtypes = [vp, i32, i32, vp, vp, vp]
         L.dflash_target_forward.restype = st
         L.dflash_target_forward.argtypes = [vp, vp, i32, vp, vp, vp, i64, vp]
+        L.dflash_trace_enable.restype = st
+        L.dflash_trace_enable.argtypes = [vp, i32, i32]
+        L.dflash_trace_read.restype = st
+        L.dflash_trace_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i32)]
+        L.dflash_trace_read_each.restype = st
+        L.dflash_trace_read_each.argtypes = [vp, C.POINTER(C.c_float), i32, C.POINTER(i32)]
         _lib = L
     return _lib
 

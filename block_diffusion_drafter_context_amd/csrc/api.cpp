@@ -392,4 +392,17 @@ dflash_status dflash_trace_read(dflash_ctx* c, double* total_ms, int32_t* launch
     return DFLASH_OK;
 }
 
+dflash_status dflash_trace_read_each(dflash_ctx* c, float* durations_ms, int32_t capacity, int32_t* launches) {
+    if (!c || !durations_ms || !launches || capacity < 0) return DFLASH_ERR_INVAL;
+    const int n = std::min(c->tracer.n, capacity);
+    for (int i = 0; i < n; ++i) {
+        hipError_t e = hipEventSynchronize(c->events[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
+        e = hipEventElapsedTime(&durations_ms[i], c->events[2 * i], c->events[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(c, e, "hipEventElapsedTime");
+    }
+    *launches = n;
+    return DFLASH_OK;
+}
+
 }  // extern "C"

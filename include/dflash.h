@@ -249,6 +249,11 @@ dflash_status dflash_trace_enable(dflash_ctx* ctx, int32_t kernel_class, int32_t
  * timed launches and their count.  Host pointers. */
 dflash_status dflash_trace_read(dflash_ctx* ctx, double* total_ms, int32_t* launches);
 
+/* The same records one by one: durations_ms (host float[capacity]) receives the
+ * duration of each timed launch in launch order, *launches the number written
+ * (at most capacity). */
+dflash_status dflash_trace_read_each(dflash_ctx* ctx, float* durations_ms, int32_t capacity, int32_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

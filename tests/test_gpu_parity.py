@@ -240,3 +240,27 @@ def test_error_paths(dl):
     assert ctx.length == 10
     with pytest.raises(dl.DFlashError):
         ctx.read_kv(5, 6)
+
+
+def test_trace_records(dl):
+    """Per-launch trace durations: one record per draft call, all positive, and
+    their sum equals the summed total; capacity bounds the count."""
+    import ctypes as C
+    s = TINY
+    ctx = dl.DFlash(s, dev(di.draft_weights(s)), max_ctx=200)
+    k, v = di.context_kv(s, 100)
+    ctx.load_kv(k.cuda(), v.cuda())
+    a = torch.tensor([3], dtype=torch.int32, device="cuda")
+    L = dl.lib()
+    assert L.dflash_trace_enable(ctx.h, 7, 8) == 0
+    for _ in range(5):
+        ctx.draft_block(a)
+    buf = (C.c_float * 8)()
+    n = C.c_int32()
+    assert L.dflash_trace_read_each(ctx.h, buf, 8, C.byref(n)) == 0
+    assert n.value == 5 and all(x > 0 for x in buf[:5])
+    tot, m = C.c_double(), C.c_int32()
+    assert L.dflash_trace_read(ctx.h, C.byref(tot), C.byref(m)) == 0
+    assert m.value == 5 and abs(tot.value - sum(buf[:5])) <= 1e-3 * tot.value + 1e-6
+    assert L.dflash_trace_read_each(ctx.h, buf, 2, C.byref(n)) == 0 and n.value == 2
+    assert L.dflash_trace_enable(ctx.h, 0, 0) == 0
