@@ -283,14 +283,26 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
             compiler_fence();
 #pragma unroll
             for (int b = 0; b < NT; ++b) acc[b] = zero4();
-            for (int w = w_first; w <= w_last; ++w) {
-                const int ft = (int)(((long long)w * c.per_wave) / c.nchunks);
-                const float* src = c.partial + ((long long)w * 2 + (ft == tile ? 0 : 1)) * (kSkinnyMaxNT * 256);
-                float v[4 * NT];
+            // the contributors' partials are loaded a batch at a time (one
+            // round trip per batch, not per contributor), then summed in
+            // contributor order
+            constexpr int FB = 16 / NT;
+            for (int w0 = w_first; w0 <= w_last; w0 += FB) {
+                float v[FB][4 * NT];
 #pragma unroll
-                for (int q = 0; q < 4 * NT; ++q) v[q] = ld_agent(src + (q >> 2) * 256 + (q & 3) * 64 + lane);
+                for (int u = 0; u < FB; ++u) {
+                    const int w = min(w0 + u, w_last);
+                    const int ft = (int)(((long long)w * c.per_wave) / c.nchunks);
+                    const float* src = c.partial + ((long long)w * 2 + (ft == tile ? 0 : 1)) * (kSkinnyMaxNT * 256);
 #pragma unroll
-                for (int q = 0; q < 4 * NT; ++q) acc[q >> 2][q & 3] += v[q];
+                    for (int q = 0; q < 4 * NT; ++q) v[u][q] = ld_agent(src + (q >> 2) * 256 + (q & 3) * 64 + lane);
+                }
+#pragma unroll
+                for (int u = 0; u < FB; ++u)
+                    if (w0 + u <= w_last) {
+#pragma unroll
+                        for (int q = 0; q < 4 * NT; ++q) acc[q >> 2][q & 3] += v[u][q];
+                    }
             }
             if (lane == 0) atomicExch(&c.tile_cnt[tile], 0u);
         }
