@@ -1661,20 +1661,37 @@ __global__ __launch_bounds__(128 * Op::kWM) void tile_gemm_kernel(Op op, int M, 
         if (ks + NS - 1 < nk) issue(ks + NS - 1, (ks + NS - 1) % NS);
         const char* As = lds + (ks % NS) * STAGE;
         const char* Bs = As + ABYTES;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            bf16x8v_t af[MI], bfr[NJ];
+        // fragments of K slice kk+1 are read while the MFMAs of slice kk run
+        bf16x8v_t af[2][MI], bfr[2][NJ];
+        auto load_frags = [&](int kk, int b) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                af[i] = *reinterpret_cast<const bf16x8v_t*>(As + gtile_off<BK>(wm * WROWS + i * 32 + frow, kk * 2 + fcol));
+                af[b][i] = *reinterpret_cast<const bf16x8v_t*>(As + gtile_off<BK>(wm * WROWS + i * 32 + frow, kk * 2 + fcol));
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8v_t*>(Bs + gtile_off<BK>(wn * (BN / 2) + j * 32 + frow, kk * 2 + fcol));
+                bfr[b][j] = *reinterpret_cast<const bf16x8v_t*>(Bs + gtile_off<BK>(wn * (BN / 2) + j * 32 + frow, kk * 2 + fcol));
+        };
+        load_frags(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int b = kk & 1;
+            if (kk + 1 < BK / 16) load_frags(kk + 1, b ^ 1);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][i], bfr[b][j], acc[i][j], 0, 0, 0);
+            // order: one MFMA, one LDS read, ... then the remaining MFMAs
+            if (kk + 1 < BK / 16) {
+#pragma unroll
+                for (int r = 0; r < MI + NJ; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - (MI + NJ), 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);
+            }
         }
     }
     op.template epilogue<MI, NJ>(acc, m0 + wm * WROWS, n0 + wn * (BN / 2), lane, M, N);
