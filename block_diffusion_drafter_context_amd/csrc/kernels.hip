@@ -19,9 +19,14 @@
 //  * attn_split_kernel<T>  -- split-KV attention of the B block queries of one
 //    kv-head group over [injected context keys ; block keys], MFMA for both
 //    products, online softmax in fp32.  attn_merge_kernel combines the splits.
-//  * big_gemm_kernel<T, Op> -- MFMA tiled GEMM for M > 16 rows (prefill-side
-//    fusion and injection), epilogue staged through LDS.
-//  * small kernels: embedding rows, row RMSNorm, acceptance scan, KV copy.
+//    In causal mode the same kernels run a target model's forward over the
+//    rows being verified (per-row key limit, cache writes, feature capture).
+//  * tile_gemm_kernel<Op>  -- bf16 MFMA GEMM for M > 16 rows (prefill-side
+//    fusion and injection): 256 x 256 tiles, 32x32x16 MFMA, K steps staged
+//    through LDS by direct global->LDS loads.  big_gemm_kernel<T, Op> is the
+//    fp32 form, epilogue staged through LDS.
+//  * small kernels: embedding rows, row RMSNorm, acceptance scan, KV copy,
+//    one-time weight reorder.
 #include "device_common.h"
 #include "kernels.h"
 
