@@ -72,6 +72,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-side fusion/injection GEMM timing")
+    ap.add_argument("--no-27b", action="store_true", help="skip the 27B-class draft pass at 36K context")
     ap.add_argument("--kv-rotate", type=int, default=4,
                     help="independent contexts (KV caches, anchors) the 4K steps rotate through, so the 256 MB "
                          "Infinity Cache cannot hold one context's KV between its steps")
@@ -259,6 +260,12 @@ def main():
         return [round(float(np.percentile(v, q)), 1) for q in (10, 50, 90)]
 
     out["draft_pass_us_p10_p50_p90"] = draft_percentiles(ctxs, C)
+    p50 = out["draft_pass_us_p10_p50_p90"][1]
+    # the draft call alone: blocks/s = 1 / median pass; 15 drafted tokens or 16 block positions per block
+    out["draft_pass_blocks_per_s"] = round(1e6 / p50, 1)
+    out["draft_pass_drafted_tok_per_s"] = round(15e6 / p50, 1)
+    out["draft_pass_block_positions_per_s"] = round(16e6 / p50, 1)
+    out["draft_pass_hbm_frac_p50"] = round(alg_bytes(s, C)["draft"] / (p50 * 1e-6) / HBM_PEAK, 4)
     log(f"[bench] draft pass p10/p50/p90 {out['draft_pass_us_p10_p50_p90']} us")
 
     # ---- per-kernel-class breakdown (separate short traced runs, not the timed region)
@@ -295,12 +302,56 @@ def main():
         pct = draft_percentiles(ctx2, args.long_ctx)
         out["long_ctx"] = {"ctx": args.long_ctx, "blocks_per_s": round(bps2, 2),
                            "draft_pass_us_p10_p50_p90": pct,
+                           "draft_pass_blocks_per_s": round(1e6 / pct[1], 1),
+                           "draft_pass_hbm_frac_p50": round(ab2["draft"] / (pct[1] * 1e-6) / HBM_PEAK, 4),
                            "drafted_tok_per_s": round(15 * bps2, 1),
                            "hbm_frac_step": round(ab2["step"] * bps2 / HBM_PEAK, 4),
                            "draft_pass_us": round(dr_us, 1),
                            "draft_pass_hbm_frac": round(ab2["draft"] / (dr_us * 1e-6) / HBM_PEAK, 4)}
         log(f"[bench] long ctx: {json.dumps(out['long_ctx'])}")
         del ctx2
+
+    # ---- 27B-class draft pass at 36864 tokens of injected context (the draft call alone)
+    if not args.no_27b:
+        if "ctx" in locals():
+            del ctx
+        ctxs.clear()
+        torch.cuda.empty_cache()
+        import ctypes as C_
+        s3 = di.SHAPES["dense27b_36k"]
+        t0 = time.time()
+        w3 = {k: v.cuda() for k, v in di.draft_weights(s3).items()}
+        ctx3 = dl.DFlash(s3, w3, max_ctx=s3.ctx + 64)
+        k3, v3 = di.context_kv(s3, s3.ctx)
+        ctx3.load_kv(k3.cuda(), v3.cuda())
+        del k3, v3
+        a3 = torch.tensor([di.anchor_token(s3)], dtype=torch.int32, device="cuda")
+        t3 = torch.empty(s3.block, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] 27B-class context of {s3.ctx} tokens ready in {time.time() - t0:.1f}s")
+        for _ in range(args.warmup):
+            ctx3.draft_block(a3, tokens=t3)
+        torch.cuda.synchronize()
+        n3 = args.steps
+        assert dl.lib().dflash_trace_enable(ctx3.h, 7, n3) == 0
+        for _ in range(n3):
+            ctx3.draft_block(a3, tokens=t3)
+        buf = (C_.c_float * n3)()
+        cnt = C_.c_int32()
+        assert dl.lib().dflash_trace_read_each(ctx3.h, buf, n3, C_.byref(cnt)) == 0
+        dl.lib().dflash_trace_enable(ctx3.h, 0, 0)
+        v = np.array(buf[:cnt.value], dtype=np.float64) * 1e3
+        pct3 = [round(float(np.percentile(v, q)), 1) for q in (10, 50, 90)]
+        ab3 = alg_bytes(s3, s3.ctx)["draft"]
+        out["dense27b_36k"] = {"workload": "dense27b_36k", "hidden": s3.hidden, "ffn": s3.ffn, "heads": "40/8x128",
+                               "ctx": s3.ctx, "draft_pass_us_p10_p50_p90": pct3,
+                               "draft_pass_blocks_per_s": round(1e6 / pct3[1], 1),
+                               "draft_pass_drafted_tok_per_s": round(15e6 / pct3[1], 1),
+                               "alg_bytes_per_pass": ab3,
+                               "draft_pass_hbm_frac_p50": round(ab3 / (pct3[1] * 1e-6) / HBM_PEAK, 4)}
+        log(f"[bench] 27B-class @36K: {json.dumps(out['dense27b_36k'])}")
+        del ctx3, w3
+        torch.cuda.empty_cache()
 
     # ---- prefill side: fusion and injection of 32768 context rows (27B-class shape)
     if not args.no_prefill:
