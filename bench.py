@@ -268,6 +268,25 @@ def main():
     out["draft_pass_hbm_frac_p50"] = round(alg_bytes(s, C)["draft"] / (p50 * 1e-6) / HBM_PEAK, 4)
     log(f"[bench] draft pass p10/p50/p90 {out['draft_pass_us_p10_p50_p90']} us")
 
+    # ---- the chip's practical streaming-read rate, next to the 8 TB/s spec
+    probe_buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+    probe_sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        probe_bytes = dl.hbm_read_probe(probe_buf, probe_sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dl.hbm_read_probe(probe_buf, probe_sink)
+    e1.record()
+    torch.cuda.synchronize()
+    probe_gbps = probe_bytes / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    out["hbm_read_ceiling"] = {"GBps": round(probe_gbps, 1), "frac_of_peak": round(probe_gbps * 1e9 / HBM_PEAK, 4),
+                               "bytes": probe_bytes, "lm_head_frac_of_ceiling": round(lm_ach / 1e9 / probe_gbps, 4),
+                               "kernel": "read_probe_kernel: 16-byte non-temporal loads, 4 waves per CU, one contiguous "
+                                         "range per wave, 16 KB in flight per wave"}
+    log(f"[bench] streaming-read ceiling {json.dumps(out['hbm_read_ceiling'])}")
+    del probe_buf, probe_sink
+
     # ---- per-kernel-class breakdown (separate short traced runs, not the timed region)
     if not args.no_breakdown:
         per_layer = {"qkv": (4, (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim * s.hidden * s.elem_bytes),

@@ -104,6 +104,8 @@ def lib():
         L.dflash_trace_enable.argtypes = [vp, i32, i32]
         L.dflash_trace_read.restype = st
         L.dflash_trace_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i32)]
+        L.dflash_hbm_read_probe.restype = st
+        L.dflash_hbm_read_probe.argtypes = [vp, i64, vp, C.POINTER(i64), vp]
         L.dflash_trace_read_each.restype = st
         L.dflash_trace_read_each.argtypes = [vp, C.POINTER(C.c_float), i32, C.POINTER(i32)]
         _lib = L
@@ -128,6 +130,17 @@ def make_config(shape, max_ctx: int, max_rows: int = 16, page_seed: int = 0) -> 
     c.page_size, c.max_ctx, c.max_rows = shape.page_size, max_ctx, max_rows
     c.rope_base, c.eps, c.page_seed = shape.rope_base, shape.eps, page_seed
     return c
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
+    """One launch of the library's streaming-read kernel over the device tensor
+    buf (a measurement aid); returns the bytes it reads."""
+    n = C.c_int64()
+    st = lib().dflash_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), C.byref(n),
+                                     _stream(stream))
+    if st:
+        raise DFlashError(st, "hbm_read_probe")
+    return n.value
 
 
 def workspace_size(cfg: Config):

@@ -405,4 +405,17 @@ dflash_status dflash_trace_read_each(dflash_ctx* c, float* durations_ms, int32_t
     return DFLASH_OK;
 }
 
+dflash_status dflash_hbm_read_probe(const void* buf, int64_t bytes, void* sink, int64_t* read_bytes, void* stream) {
+    if (!buf || !sink || !read_bytes || bytes < 0 || (reinterpret_cast<uintptr_t>(buf) & 15)) return DFLASH_ERR_INVAL;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return DFLASH_ERR_HIP;
+    long long rb = 0;
+    const hipError_t e = dflash::launch_read_probe(buf, bytes, cus, static_cast<unsigned*>(sink), &rb,
+                                                   static_cast<hipStream_t>(stream));
+    *read_bytes = rb;
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 }  // extern "C"

@@ -61,6 +61,9 @@ struct DevCtx {
 
 // Write the swizzled copy of a row-major [N][K] matrix (N % 16 == 0, K % 8 == 0).
 hipError_t launch_swizzle(int dtype, const void* W, int N, int K, void* out, hipStream_t s);
+// reads the largest whole-round prefix of buf; *read_bytes receives its size
+hipError_t launch_read_probe(const void* buf, long long bytes, int num_cus, unsigned* sink, long long* read_bytes,
+                             hipStream_t s);
 
 // One draft block over the first C context positions.
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits,

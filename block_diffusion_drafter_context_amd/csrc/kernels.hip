@@ -1399,6 +1399,35 @@ __global__ __launch_bounds__(64) void swizzle_kernel(const T* W, int N, int K, T
     }
 }
 
+// Streaming-read probe: every wave reads one contiguous range with 16-byte
+// non-temporal loads, 16 KB in flight, and folds the data into one word so
+// the loads are not removed (written only if it hits a fixed value).
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* __restrict__ p, long long per_wave, unsigned* sink) {
+    constexpr int U = 16;
+    const int lane = threadIdx.x & 63;
+    const long long wave = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const u32x4_t* base = p + wave * per_wave;
+    unsigned acc = 0;
+    for (long long i = 0; i < per_wave; i += 64 * U) {
+        u32x4_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(base + i + u * 64 + lane);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+hipError_t launch_read_probe(const void* buf, long long bytes, int num_cus, unsigned* sink, long long* read_bytes, hipStream_t s) {
+    const long long waves = 4LL * num_cus;
+    const long long per_wave = (bytes / 16 / waves) / (64 * 16) * (64 * 16);  // 16-byte units, whole rounds
+    *read_bytes = per_wave * waves * 16;
+    if (per_wave <= 0) return hipSuccess;
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)num_cus), dim3(256), 0, s, reinterpret_cast<const u32x4_t*>(buf),
+                       per_wave, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_swizzle(int dtype, const void* W, int N, int K, void* out, hipStream_t s) {
     const dim3 grid((K + 31) / 32, N / 16);
     if (dtype == DFLASH_F32)

@@ -254,6 +254,17 @@ dflash_status dflash_trace_read(dflash_ctx* ctx, double* total_ms, int32_t* laun
  * (at most capacity). */
 dflash_status dflash_trace_read_each(dflash_ctx* ctx, float* durations_ms, int32_t capacity, int32_t* launches);
 
+/* Measurement aid, not part of the method: one launch of a plain streaming-read
+ * kernel over the device buffer buf (bytes long, 16-byte aligned) on the given
+ * stream, so a caller can time the chip's practical HBM read rate next to the
+ * draft kernels' roofline figures.  Every wave of 4 per CU reads one contiguous
+ * range with 16-byte non-temporal loads.  *read_bytes (host) receives the bytes
+ * actually read: the largest prefix that divides evenly into the waves' rounds
+ * (0 if bytes is below 4 MB per 256 CUs; then nothing is launched).  sink is a
+ * device word the kernel may write (never read back).  INVAL on null pointers,
+ * a negative size or a misaligned buffer. */
+dflash_status dflash_hbm_read_probe(const void* buf, int64_t bytes, void* sink, int64_t* read_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

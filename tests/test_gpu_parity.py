@@ -264,3 +264,17 @@ def test_trace_records(dl):
     assert m.value == 5 and abs(tot.value - sum(buf[:5])) <= 1e-3 * tot.value + 1e-6
     assert L.dflash_trace_read_each(ctx.h, buf, 2, C.byref(n)) == 0 and n.value == 2
     assert L.dflash_trace_enable(ctx.h, 0, 0) == 0
+
+
+def test_hbm_read_probe(dl):
+    """The streaming-read measurement aid reads the whole-round prefix of its
+    buffer and rejects a misaligned one."""
+    buf = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    n = dl.hbm_read_probe(buf, sink)
+    sync()
+    assert 0 < n <= buf.numel() and n % (16 * 64 * 16) == 0
+    assert dl.hbm_read_probe(buf[:1024], sink) == 0  # too small for one round per wave: nothing launched
+    with pytest.raises(dl.DFlashError) as e:
+        dl.hbm_read_probe(buf[1:], sink)
+    assert e.value.status == -1
