@@ -73,6 +73,7 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-side fusion/injection GEMM timing")
     ap.add_argument("--no-27b", action="store_true", help="skip the 27B-class draft pass at 36K context")
+    ap.add_argument("--no-toy", action="store_true", help="skip the toy end-to-end speculative loop")
     ap.add_argument("--kv-rotate", type=int, default=4,
                     help="independent contexts (KV caches, anchors) the 4K steps rotate through, so the 256 MB "
                          "Infinity Cache cannot hold one context's KV between its steps")
@@ -371,6 +372,61 @@ def main():
         log(f"[bench] 27B-class @36K: {json.dumps(out['dense27b_36k'])}")
         del ctx3, w3
         torch.cuda.empty_cache()
+
+    # ---- toy end-to-end greedy speculative loop against plain greedy decoding
+    if not args.no_toy:
+        from block_diffusion_drafter_context_amd import spec
+        st = di.SHAPES["toy_e2e"]
+        tw = {k: v.cuda() for k, v in di.toy_target_weights(st).items()}
+        dw = {k: v.cuda() for k, v in di.draft_weights(st).items()}
+        prompt = di.toy_prompt(st).cuda()
+        n_new = di.TOY_GENERATE
+        cap = prompt.shape[0] + n_new + 2 * st.block
+
+        def fresh():
+            return (dl.DFlash(st.replace(draft_layers=st.target_layers), tw, max_ctx=cap),
+                    dl.DFlash(st, dw, max_ctx=cap))
+
+        def wall(fn):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            r = fn()
+            torch.cuda.synchronize()
+            return r, time.perf_counter() - t
+
+        tgt, _ = fresh()
+        spec.greedy_generate(tgt, prompt, 8)  # warm-up of every kernel shape
+        tgt, _ = fresh()
+        _, t_pre = wall(lambda: spec.prefill(tgt, prompt))
+        tgt, drf = fresh()
+        _, t_pre_s = wall(lambda: spec.prefill(tgt, prompt, drf))
+        tgt, _ = fresh()
+        greedy, t_g = wall(lambda: spec.greedy_generate(tgt, prompt, n_new).cpu().tolist())
+        tgt, drf = fresh()
+        (sp, ks), t_s = wall(lambda: spec.spec_generate(tgt, drf, prompt, n_new))
+        P = prompt.shape[0]
+
+        def truth(C0):
+            return [int(greedy[p - P]) if p - P < len(greedy) else 0 for p in range(C0 + 1, C0 + st.block)]
+
+        tgt, drf = fresh()
+        (spp, ksp), t_p = wall(lambda: spec.spec_generate(tgt, drf, prompt, n_new, drafts_fn=truth))
+        out["toy_e2e"] = {
+            "workload": "toy_e2e", "prompt": P, "generated": n_new,
+            "note": "wall times include the prompt prefill (16-row target calls, plus fuse/inject for the draft in "
+                    "the speculative loops); decode rates subtract the matching prefill time. The draft is "
+                    "random-init, so its blocks are rarely accepted; the target-drafts run feeds the target's own "
+                    "greedy tokens as drafts (every block accepted)",
+            "prefill_s": round(t_pre, 4), "prefill_with_draft_s": round(t_pre_s, 4),
+            "greedy_s": round(t_g, 4), "greedy_decode_tok_per_s": round(n_new / max(t_g - t_pre, 1e-9), 1),
+            "spec_s": round(t_s, 4), "spec_steps": len(ks), "spec_mean_accept_k": round(float(np.mean(ks)), 3),
+            "spec_tokens_per_step": round(len(sp) / max(len(ks), 1), 3), "spec_equals_greedy": sp == greedy,
+            "spec_decode_tok_per_s": round(n_new / max(t_s - t_pre_s, 1e-9), 1),
+            "target_drafts_s": round(t_p, 4), "target_drafts_steps": len(ksp),
+            "target_drafts_equals_greedy": spp == greedy,
+            "target_drafts_decode_tok_per_s": round(n_new / max(t_p - t_pre_s, 1e-9), 1)}
+        log(f"[bench] toy end to end: {json.dumps(out['toy_e2e'])}")
+        del tw, dw
 
     # ---- prefill side: fusion and injection of 32768 context rows (27B-class shape)
     if not args.no_prefill:
