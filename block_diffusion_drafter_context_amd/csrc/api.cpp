@@ -406,7 +406,9 @@ dflash_status dflash_trace_read_each(dflash_ctx* c, float* durations_ms, int32_t
 }
 
 dflash_status dflash_hbm_read_probe(const void* buf, int64_t bytes, void* sink, int64_t* read_bytes, void* stream) {
-    if (!buf || !sink || !read_bytes || bytes < 0 || (reinterpret_cast<uintptr_t>(buf) & 15)) return DFLASH_ERR_INVAL;
+    if (!buf || !sink || !read_bytes || bytes < 0 || (reinterpret_cast<uintptr_t>(buf) & 15) ||
+        (reinterpret_cast<uintptr_t>(sink) & 3))
+        return DFLASH_ERR_INVAL;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)

@@ -261,8 +261,8 @@ dflash_status dflash_trace_read_each(dflash_ctx* ctx, float* durations_ms, int32
  * range with 16-byte non-temporal loads.  *read_bytes (host) receives the bytes
  * actually read: the largest prefix that divides evenly into the waves' rounds
  * (0 if bytes is below 4 MB per 256 CUs; then nothing is launched).  sink is a
- * device word the kernel may write (never read back).  INVAL on null pointers,
- * a negative size or a misaligned buffer. */
+ * 4-byte-aligned device word the kernel may write (never read back).  INVAL on
+ * null pointers, a negative size or a misaligned buffer or sink. */
 dflash_status dflash_hbm_read_probe(const void* buf, int64_t bytes, void* sink, int64_t* read_bytes, void* stream);
 
 #ifdef __cplusplus
