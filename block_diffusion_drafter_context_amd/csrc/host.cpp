@@ -154,11 +154,13 @@ void attn_split_plan(int C, int nkv, int num_cus, int page, int* kps, int* ns) {
         *ns = 0;
         return;
     }
-    // about three workgroups per CU over all kv heads, and at least three
-    // chunks per split (a split's fixed cost -- Q loads, first-chunk latency,
-    // partial write and merge read -- is then amortised); measured best at 4K
-    // and 36K keys on MI355X
-    long long target = std::max(1LL, 3LL * num_cus / std::max(nkv, 1));
+    // the splits plus the block's own part fill one round of resident
+    // attention workgroups (kAttnWGPerCU per CU, over all kv heads), and every
+    // split has at least three chunks (a split's fixed cost -- Q loads,
+    // first-chunk latency, partial write and merge read -- is then amortised).
+    // On MI355X at 36K keys one round beats 1.5 rounds (3 workgroups per CU) by
+    // about 36 us per draft pass; at 4K the three-chunk minimum decides.
+    long long target = std::max(1LL, (long long)kAttnWGPerCU * num_cus / std::max(nkv, 1) - 1);
     long long per = (C + target - 1) / target;
     per = ((per + kAttnChunk - 1) / kAttnChunk) * kAttnChunk;
     per = std::max<long long>(per, 3 * kAttnChunk);
