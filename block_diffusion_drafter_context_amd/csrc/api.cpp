@@ -200,7 +200,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
         (e = hipMemsetAsync(x.ws + L.tile_cnt, 0, (size_t)L.max_tiles * 4, s)) != hipSuccess ||
         (e = hipMemsetAsync(x.ws + L.counters, 0, 64 * 4, s)) != hipSuccess ||
         (e = hipMemsetAsync(x.ws + L.best, 0, 16 * 8, s)) != hipSuccess ||
-        (e = hipMemsetAsync(x.ws + L.ss_part, 0, (size_t)L.ss_stride * 16 * 4, s)) != hipSuccess ||
+        (e = hipMemsetAsync(x.ws + L.ss_part, 0, (size_t)L.ss_stride * 16 * 4 * 2, s)) != hipSuccess ||
         (e = hipStreamSynchronize(s)) != hipSuccess) {
         delete c;
         return DFLASH_ERR_HIP;

@@ -92,7 +92,7 @@ Layout compute_layout(const Dims& d, int num_cus) {
     const int blk = 16 * kSkinnyNT;
     L.max_ss_tiles = (d.H + blk - 1) / blk;
     L.ss_stride = (L.max_ss_tiles + 15) / 16 * 16;
-    L.ss_part = take((size_t)L.ss_stride * 16 * 4);
+    L.ss_part = take((size_t)L.ss_stride * 16 * 4 * 2);  // two buffers (see the draft pass)
     // 4 waves per CU: measured best for every skinny-GEMM shape of the draft
     // pass (fewer concurrent weight streams keep DRAM pages open longer)
     L.nwaves = std::max(num_cus, 1) * 4;

@@ -329,6 +329,148 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
     op.wave_end(st, lane);
 }
 
+// Workgroup-local split-K.  Every workgroup owns `tpw` consecutive whole
+// tiles, and its W waves split each tile's K range evenly (cpw chunks each).
+// Each wave streams the (tile, K group) sequence of all its tiles as one
+// ping-pong pipeline of KP-chunk load groups and parks a tile's partial sum in
+// LDS when the tile's last group is done.  After the stream, the W partials
+// of each tile are added in wave order by one wave, which runs the epilogue.
+// No partial leaves the CU, so the launch has no device-scope exchange.  The
+// steady-state loop issues its loads unconditionally and holds no other
+// memory access, so each group waits only for its own loads (global stores or
+// loads on a branch would make the compiler wait for every load in flight).
+// The split depends on N and K alone (batch invariant), and the order of the
+// sums is fixed (deterministic).
+struct WGCommon {
+    int M;          // valid rows (<= 16)
+    int K;          // reduction length (multiple of 8)
+    int nchunks;    // ceil(K / 32)
+    int ntiles;
+    int tpw;        // tiles per workgroup
+    int cpw;        // chunks of a tile per wave (a multiple of KP)
+    float* clear;   // cleared at launch (clear_n floats), or null
+    int clear_n;
+};
+
+template <typename T, class Op, int W, int MINWG, int KP>
+__global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommon c) {
+    constexpr int NT = Op::kNT;  // 16-column blocks per tile
+    extern __shared__ f32x4_t wg_red[];  // [tile][wave][block][lane]: one 16-byte access per lane
+    using AL = decltype(op.a);
+    using Raw = typename AL::Raw;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row = lane & 15, grp = lane >> 4;
+    const bool row_ok = row < c.M;
+    typename AL::Pre pr;
+    op.a.pre_issue(pr, lane);
+    typename Op::State st;
+    op.wave_begin(st);
+
+    const int t0 = blockIdx.x * c.tpw;
+    const int nt = min(c.tpw, c.ntiles - t0);
+    const int ch0 = wv * c.cpw;
+    const int ch1 = min(ch0 + c.cpw, c.nchunks);
+    const int chl = (ch1 > ch0 ? ch1 : c.nchunks) - 1;  // last chunk a load touches (a wave past K re-reads it, masked)
+    const int gpt = c.cpw / KP;                          // load groups per tile
+    const int total = nt * gpt;
+    const int arow = row_ok ? row : 0;
+    const int klast = c.K - 8;  // last valid 8-element group of an activation row
+
+    struct Group {
+        Frag<T> w[NT][KP];
+        Raw a[KP];
+    };
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[b] = zero4();
+
+    auto load_group = [&](int n, Group& g) {
+        const int ti = n / gpt;
+        const int tile = t0 + ti;
+        const int cb = ch0 + (n - ti * gpt) * KP;
+        const T* ws[NT];
+#pragma unroll
+        for (int b = 0; b < NT; ++b) {
+            const T* q = op.b_rows(tile, b, c.nchunks);
+            ws[b] = q ? q : op.b_rows(tile, 0, c.nchunks);  // blocks past N re-read block 0 (never stored)
+        }
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            const int ch = min(cb + p, chl);
+            const int k = min(ch * 32 + grp * 8, klast);
+#pragma unroll
+            for (int b = 0; b < NT; ++b) g.w[b][p].load_sw(ws[b] + (long long)ch * 512, lane);
+            op.a.load(g.a[p], arow, k);
+        }
+    };
+    float pre = 0.f;
+    auto compute = [&](int n, const Group& g) {
+        const int ti = n / gpt;
+        const int cb = ch0 + (n - ti * gpt) * KP;
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            Frag<T> a;
+            op.a.finish(a, g.a[p], pre);
+            const bool ok = row_ok && (cb + p < ch1) && ((cb + p) * 32 + grp * 8 < c.K);
+            a.mask(ok ? 0xFFFFFFFFu : 0u);
+#pragma unroll
+            for (int b = 0; b < NT; ++b) mma(acc[b], a, g.w[b][p]);
+        }
+        if (n - ti * gpt == gpt - 1) {  // the tile's last group: park its partial (LDS only)
+#pragma unroll
+            for (int b = 0; b < NT; ++b) {
+                wg_red[((ti * W + wv) * NT + b) * 64 + lane] = acc[b];
+                acc[b] = zero4();
+            }
+        }
+    };
+
+    Group ga, gb;
+    load_group(0, ga);
+    load_group(min(1, total - 1), gb);
+    __builtin_amdgcn_sched_barrier(0);
+    pre = op.a.pre_finish(pr, lane);  // its loads went out before any weight load
+    int n = 0;
+    for (; n + 3 < total; n += 2) {  // groups n, n+1 in flight; n+2, n+3 exist
+        compute(n, ga);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(n + 2, ga);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(n + 1, gb);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(n + 3, gb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // the last 1, 2 or 3 groups (n and n+1 already loaded)
+    compute(n, ga);
+    if (n + 2 < total) {
+        load_group(n + 2, ga);
+        compute(n + 1, gb);
+        compute(n + 2, ga);
+    } else if (n + 1 < total) {
+        compute(n + 1, gb);
+    }
+
+    if (c.clear)
+        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < c.clear_n; i += gridDim.x * blockDim.x) c.clear[i] = 0.f;
+    for (int i = wv; i < nt; i += W) op.prefetch(t0 + i, lane, st);  // epilogue inputs, in flight during the barrier
+    __syncthreads();
+    for (int i = wv; i < nt; i += W) {
+        f32x4_t sum[NT];
+#pragma unroll
+        for (int b = 0; b < NT; ++b) sum[b] = zero4();
+        for (int q = 0; q < W; ++q)
+#pragma unroll
+            for (int b = 0; b < NT; ++b) {
+                const f32x4_t v = wg_red[((i * W + q) * NT + b) * 64 + lane];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) sum[b][ii] += v[ii];
+            }
+        op.epilogue(t0 + i, sum, lane, st);
+    }
+    op.wave_end(st, lane);
+}
+
 // Ops ------------------------------------------------------------------------
 
 // V pages store the positions of every 32-slot group in the order
@@ -457,35 +599,38 @@ struct OpQKV {
 };
 
 // x += round(A . W^T) (residual add, both rounded), then the row statistics
-// of the new x for the next RMSNorm: per-tile partial sums of squares, and the
-// last finished tile turns them into rstd (fixed summation order).
-template <typename T>
+// of the new x for the next RMSNorm: per-32-column row sums of squares.  With
+// 32-column tiles (NT_ = 2) a tile stores its sums, and the last finished tile
+// can turn them into rstd (fixed summation order); with 16-column tiles the two
+// tiles of a 32-column slot add their sums into the slot, cleared beforehand
+// (two addends in either order give the same fp32 sum).
+template <typename T, int NT_ = 2>
 struct OpResid {
-    static constexpr int kNT = 2;  // 16-column blocks per tile
+    static constexpr int kNT = NT_;  // 16-column blocks per tile
     struct State {
-        float xv[2][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
+        float xv[NT_][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
     };
-    static constexpr bool kDoneHook = true;
+    static constexpr bool kDoneHook = NT_ == 2;
     PlainA<T> a;
     const T* w;
     int N, K, M;
     T* x;
-    float* ss_part;          // [16 rows][ss_stride] per-tile row sums of squares
+    float* ss_part;          // [16 rows][ss_stride] per-32-column row sums of squares
     int ss_stride;
     float* rstd_out;
     float eps;
     T* cap = nullptr;        // optional copy of the updated rows (stride cap_ld)
     long long cap_ld = 0;
     __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
-        const int n0 = 32 * tile + 16 * blk;
+        const int n0 = 16 * NT_ * tile + 16 * blk;
         return n0 < N ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void prefetch(int tile, int lane, State& st) const {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = min(32 * tile + 16 * b + (lane & 15), N - 1);
+        for (int b = 0; b < NT_; ++b) {
+            const int n = min(16 * NT_ * tile + 16 * b + (lane & 15), N - 1);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int j = min(4 * (lane >> 4) + ii, M - 1);
@@ -496,8 +641,8 @@ struct OpResid {
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State& st) const {
         float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int n = 32 * tile + 16 * b + (lane & 15);
+        for (int b = 0; b < NT_; ++b) {
+            const int n = 16 * NT_ * tile + 16 * b + (lane & 15);
             if (n >= N) continue;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
@@ -513,10 +658,14 @@ struct OpResid {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const float s = group16_sum(sq[ii]);
-            if ((lane & 15) == 0) st_agent(ss_part + (long long)(4 * (lane >> 4) + ii) * ss_stride + tile, s);
+            float* slot = ss_part + (long long)(4 * (lane >> 4) + ii) * ss_stride + (NT_ == 2 ? tile : tile >> 1);
+            if ((lane & 15) == 0) {
+                if constexpr (NT_ == 2) st_agent(slot, s);
+                else __hip_atomic_fetch_add(slot, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
-    __device__ __forceinline__ bool done_wanted() const { return rstd_out != nullptr; }
+    __device__ __forceinline__ bool done_wanted() const { return NT_ == 2 && rstd_out != nullptr; }
     __device__ __forceinline__ void done_hook(int lane, int ntiles) const {
         // lane handles row j = lane & 15 over tiles t = g, g+4, ... (g = lane >> 4)
         const int j = lane & 15, g = lane >> 4;
@@ -787,6 +936,57 @@ static hipError_t run_skinny(const DevCtx& c, const Op& op, int M, int K, int nt
     const int grid = (int)((waves + kSkinnyWavesPerWG - 1) / kSkinnyWavesPerWG);
     hipLaunchKernelGGL((skinny_kernel<T, Op>), dim3(grid), dim3(64 * kSkinnyWavesPerWG), 0, s, op, sc);
     return hipGetLastError();
+}
+
+// Workgroup-local split-K plan: one workgroup per CU, each owning
+// ceil(ntiles / CUs) consecutive tiles (measured: two workgroups on some CUs
+// and eight waves per tile were both slower).  A load group carries 8 KB of
+// weights per wave (KP chunks x NT 16-column blocks).
+static int wg_tiles_per_cu(int ntiles, int cus) { return std::max(1, (ntiles + cus - 1) / cus); }
+
+// Whether the plan suits the launch: at most one tile per CU (e.g. 192 tiles
+// of the 8B-shape QKV measured 18.0 us against 21.3 on stream-K), or several
+// that keep the CUs evenly busy (>= 70 % of tile slots used).  Otherwise the
+// stream-K kernel, which splits work evenly at any size, is the faster one
+// (e.g. 320 tiles on 256 CUs).
+static bool wg_plan_balanced(int ntiles, int cus) {
+    cus = std::max(cus, 1);
+    return ntiles <= cus || (long long)ntiles * 10 >= 7LL * cus * wg_tiles_per_cu(ntiles, cus);
+}
+
+template <typename T, class Op>
+static hipError_t run_skinny_wg(const DevCtx& c, const Op& op, int M, int K, int ntiles, hipStream_t s,
+                                float* clear = nullptr, int clear_n = 0) {
+    constexpr int NT = Op::kNT;
+    constexpr int KP = NT == 1 && sizeof(T) == 2 ? 8 : 4;
+    constexpr int W = 4;
+    WGCommon wc;
+    wc.M = M;
+    wc.K = K;
+    wc.nchunks = (K + 31) / 32;
+    wc.ntiles = ntiles;
+    wc.tpw = wg_tiles_per_cu(ntiles, std::max(c.num_cus, 1));
+    const int grid = (ntiles + wc.tpw - 1) / wc.tpw;
+    wc.cpw = ((wc.nchunks + W - 1) / W + KP - 1) / KP * KP;
+    wc.clear = clear;
+    wc.clear_n = clear_n;
+    const size_t lds = (size_t)wc.tpw * W * NT * 64 * sizeof(f32x4_t);
+    // The occupancy hint of two workgroups per CU caps the kernel at 256
+    // architectural VGPRs (it needs < 190, no spills).  Built without it, the
+    // compiler also allocated AGPRs and the results were wrong; that build is
+    // not used.
+    hipLaunchKernelGGL((skinny_wg_kernel<T, Op, W, 2, KP>), dim3(grid), dim3(64 * W), lds, s, op, wc);
+    return hipGetLastError();
+}
+
+// The layer projections of a pass: bf16 on the workgroup-local kernel when its
+// plan is balanced, else (and for the small fp32 workload) stream-K.
+template <typename T, class Op>
+static hipError_t run_layer_gemm(const DevCtx& c, const Op& op, int M, int K, int ntiles, hipStream_t s) {
+    if constexpr (sizeof(T) == 2) {
+        if (wg_plan_balanced(ntiles, c.num_cus)) return run_skinny_wg<T>(c, op, M, K, ntiles, s);
+    }
+    return run_skinny<T>(c, op, M, K, ntiles, s);
 }
 
 // ============================================================================
@@ -1273,9 +1473,11 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 // 16-byte accesses; every thread's loads are issued before any use.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_t* ids, int n_ids, int mask_id, int V,
-                                                    int H, float eps, T* x, float* rstd, unsigned long long* best) {
+                                                    int H, float eps, T* x, float* rstd, unsigned long long* best,
+                                                    float* clear, int clear_n) {
     __shared__ float red[4];
     const int j = blockIdx.x;
+    for (int i = j * 256 + threadIdx.x; i < clear_n; i += gridDim.x * 256) clear[i] = 0.f;
     const int tok = j < n_ids ? min(max(ids[j], 0), V - 1) : mask_id;  // out-of-range ids are clamped
     const Frag<T>* src = reinterpret_cast<const Frag<T>*>(embed + (long long)tok * H);
     Frag<T>* dst = reinterpret_cast<Frag<T>*>(x + (long long)j * H);
@@ -1890,7 +2092,12 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     T* obuf = WS(T*, obuf);
     T* hbuf = WS(T*, hbuf);
     float* rstd = WS(float*, rstd);
-    float* ss = WS(float*, ss_part);
+    // two buffers of per-32-column row sums of squares: the O projection
+    // writes ss0 (read by gate/up) and clears ss1; the down projection writes
+    // ss1 (read by the next QKV or the LM head) and clears ss0
+    float* ss0 = WS(float*, ss_part);
+    float* ss1 = ss0 + 16LL * c.lay.ss_stride;
+    const int ss_n = 16 * c.lay.ss_stride;
     unsigned long long* best = WS(unsigned long long*, best);
     unsigned* counters = WS(unsigned*, counters);
     const float* cosT = WS(const float*, rope_cos);
@@ -1899,7 +2106,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     hipError_t e;
 
     hipLaunchKernelGGL((embed_kernel<T>), dim3(B), dim3(256), 0, s, (const T*)c.embed, pa.ids, pa.n_ids, d.mask_id, d.V,
-                       H, eps, x, rstd, best);
+                       H, eps, x, rstd, best, ss0, ss_n);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     int kps, ns, nparts;
@@ -1920,7 +2127,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     // last tile computes rstd.
     const int ss_tiles = (H + 16 * OpResid<T>::kNT - 1) / (16 * OpResid<T>::kNT);
     const bool lazy_stats = ss_tiles <= 4 * kSSPerLane;
-    auto norm_in = [&](const void* gain, bool after_resid) {
+    const bool resid_wg = sizeof(T) == 2 && lazy_stats && wg_plan_balanced(H / 16, c.num_cus);
+    auto norm_in = [&](const void* gain, bool after_resid, const float* ss) {
         NormA<T> na{x, H, rstd, (const T*)gain};
         if (after_resid && lazy_stats) {
             na.ss = ss;
@@ -1934,7 +2142,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
 
     for (int l = 0; l < d.Ld; ++l) {
         OpQKV<T> qkv;
-        qkv.a = norm_in(c.attn_norm[l], l > 0);
+        qkv.a = norm_in(c.attn_norm[l], l > 0, ss1);
         qkv.wq = (const T*)c.sw_wq[l];
         qkv.wk = (const T*)c.sw_wk[l];
         qkv.wv = (const T*)c.sw_wv[l];
@@ -1954,7 +2162,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         qkv.kv = make_pages<T>(c);
         qkv.layer = l;
         c.tracer->begin(DFLASH_TRACE_QKV, s);
-        if ((e = run_skinny<T>(c, qkv, B, H, qkv.tq + 2 * qkv.tk, s)) != hipSuccess) return e;
+        if ((e = run_layer_gemm<T>(c, qkv, B, H, qkv.tq + 2 * qkv.tk, s)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_QKV, s);
 
         AttnArgs aa;
@@ -1986,23 +2194,43 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_ATTN, s);
 
-        OpResid<T> op;
-        op.a = PlainA<T>{obuf, (long long)nq * D};
-        op.w = (const T*)c.sw_wo[l];
-        op.N = H;
-        op.K = nq * D;
-        op.M = B;
-        op.x = x;
-        op.ss_part = ss;
-        op.ss_stride = c.lay.ss_stride;
-        op.rstd_out = lazy_stats ? nullptr : rstd;
-        op.eps = eps;
+        auto resid_op = [&](auto& op, const void* w, int K, const T* a, float* ss_out) {
+            op.a = PlainA<T>{a, (long long)K};
+            op.w = (const T*)w;
+            op.N = H;
+            op.K = K;
+            op.M = B;
+            op.x = x;
+            op.ss_part = ss_out;
+            op.ss_stride = c.lay.ss_stride;
+            op.rstd_out = lazy_stats ? nullptr : rstd;
+            op.eps = eps;
+        };
+        // bf16 with lazy statistics and a balanced plan: 16-column tiles on the
+        // workgroup-local kernel, whose sums of squares add into cleared
+        // 32-column slots; else 32-column stream-K tiles, which store their
+        // sums (and a completion chain without lazy statistics).  O and down
+        // have the same N, so both take the same branch.
+        auto run_resid = [&](const void* w, int K, const T* a, float* ss_out, float* ss_clear, T* cap) {
+            if (resid_wg) {
+                OpResid<T, 1> op;
+                resid_op(op, w, K, a, ss_out);
+                op.cap = cap;
+                op.cap_ld = pa.cap_ld;
+                return run_skinny_wg<T>(c, op, B, K, H / 16, s, ss_clear, ss_n);
+            }
+            OpResid<T, 2> op;  // 32-column tiles: each stores its sums (no clearing needed)
+            resid_op(op, w, K, a, ss_out);
+            op.cap = cap;
+            op.cap_ld = pa.cap_ld;
+            return run_skinny<T>(c, op, B, K, (H + 31) / 32, s);
+        };
         c.tracer->begin(DFLASH_TRACE_O_PROJ, s);
-        if ((e = run_skinny<T>(c, op, B, nq * D, (H + 31) / 32, s)) != hipSuccess) return e;
+        if ((e = run_resid(c.sw_wo[l], nq * D, obuf, ss0, ss1, nullptr)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_O_PROJ, s);
 
         OpSwiGLU<T> sw;
-        sw.a = norm_in(c.mlp_norm[l], true);
+        sw.a = norm_in(c.mlp_norm[l], true, ss0);
         sw.wg = (const T*)c.sw_wg[l];
         sw.wu = (const T*)c.sw_wu[l];
         sw.F = F;
@@ -2010,33 +2238,20 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         sw.M = B;
         sw.h = hbuf;
         c.tracer->begin(DFLASH_TRACE_GATE_UP, s);
-        if ((e = run_skinny<T>(c, sw, B, H, F / 16, s)) != hipSuccess) return e;
+        if ((e = run_layer_gemm<T>(c, sw, B, H, F / 16, s)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_GATE_UP, s);
 
-        OpResid<T> dn;
-        dn.a = PlainA<T>{hbuf, (long long)F};
-        dn.w = (const T*)c.sw_wd[l];
-        dn.N = H;
-        dn.K = F;
-        dn.M = B;
-        dn.x = x;
-        dn.ss_part = ss;
-        dn.ss_stride = c.lay.ss_stride;
-        dn.rstd_out = lazy_stats ? nullptr : rstd;
-        dn.eps = eps;
+        T* cap = nullptr;
         if (pa.cap)
             for (int i = 0; i < 5; ++i)
-                if (sel[i] == l && pa.cap[i]) {  // layer l's output is a captured feature layer
-                    dn.cap = (T*)pa.cap[i];
-                    dn.cap_ld = pa.cap_ld;
-                }
+                if (sel[i] == l && pa.cap[i]) cap = (T*)pa.cap[i];  // layer l's output is a captured feature layer
         c.tracer->begin(DFLASH_TRACE_DOWN, s);
-        if ((e = run_skinny<T>(c, dn, B, F, (H + 31) / 32, s)) != hipSuccess) return e;
+        if ((e = run_resid(c.sw_wd[l], F, hbuf, ss1, ss0, cap)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_DOWN, s);
     }
 
     OpLMHead<T> lm;
-    lm.a = norm_in(c.final_norm, d.Ld > 0);
+    lm.a = norm_in(c.final_norm, d.Ld > 0, ss1);
     lm.w = (const T*)c.sw_lm;
     lm.V = d.V;
     lm.K = H;
