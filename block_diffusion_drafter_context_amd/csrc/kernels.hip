@@ -332,13 +332,15 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
 // Workgroup-local split-K.  Every workgroup owns `tpw` consecutive whole
 // tiles, and its W waves split each tile's K range evenly (cpw chunks each).
 // Each wave streams the (tile, K group) sequence of all its tiles as one
-// ping-pong pipeline of KP-chunk load groups and parks a tile's partial sum in
+// pipeline of KP-chunk load groups, DEPTH of them in flight, and parks a tile's partial sum in
 // LDS when the tile's last group is done.  After the stream, the W partials
 // of each tile are added in wave order by one wave, which runs the epilogue.
 // No partial leaves the CU, so the launch has no device-scope exchange.  The
 // steady-state loop issues its loads unconditionally and holds no other
 // memory access, so each group waits only for its own loads (global stores or
 // loads on a branch would make the compiler wait for every load in flight).
+// The epilogue's own inputs (residual rows, rotary tables) are loaded at the
+// start, ahead of the weights.
 // The split depends on N and K alone (batch invariant), and the order of the
 // sums is fixed (deterministic).
 struct WGCommon {
@@ -352,7 +354,7 @@ struct WGCommon {
     int clear_n;
 };
 
-template <typename T, class Op, int W, int MINWG, int KP>
+template <typename T, class Op, int W, int MINWG, int KP, int DEPTH>
 __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommon c) {
     constexpr int NT = Op::kNT;  // 16-column blocks per tile
     extern __shared__ f32x4_t wg_red[];  // [tile][wave][block][lane]: one 16-byte access per lane
@@ -368,6 +370,9 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommo
 
     const int t0 = blockIdx.x * c.tpw;
     const int nt = min(c.tpw, c.ntiles - t0);
+    // epilogue inputs of the wave's first tile (it finishes tiles wv, wv + W,
+    // ...): issued before the weights, they arrive with the first group
+    if (wv < nt) op.prefetch(t0 + wv, lane, st);
     const int ch0 = wv * c.cpw;
     const int ch1 = min(ch0 + c.cpw, c.nchunks);
     const int chl = (ch1 > ch0 ? ch1 : c.nchunks) - 1;  // last chunk a load touches (a wave past K re-reads it, masked)
@@ -425,37 +430,37 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommo
         }
     };
 
-    Group ga, gb;
-    load_group(0, ga);
-    load_group(min(1, total - 1), gb);
+    // DEPTH groups in flight: group n lives in ring slot n % DEPTH
+    Group g[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_group(min(d, total - 1), g[d]);
     __builtin_amdgcn_sched_barrier(0);
     pre = op.a.pre_finish(pr, lane);  // its loads went out before any weight load
     int n = 0;
-    for (; n + 3 < total; n += 2) {  // groups n, n+1 in flight; n+2, n+3 exist
-        compute(n, ga);
-        __builtin_amdgcn_sched_barrier(0);
-        load_group(n + 2, ga);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(n + 1, gb);
-        __builtin_amdgcn_sched_barrier(0);
-        load_group(n + 3, gb);
-        __builtin_amdgcn_sched_barrier(0);
+    for (; n + 2 * DEPTH - 1 < total; n += DEPTH) {  // every group loaded here exists
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            compute(n + d, g[d]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_group(n + d + DEPTH, g[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    // the last 1, 2 or 3 groups (n and n+1 already loaded)
-    compute(n, ga);
-    if (n + 2 < total) {
-        load_group(n + 2, ga);
-        compute(n + 1, gb);
-        compute(n + 2, ga);
-    } else if (n + 1 < total) {
-        compute(n + 1, gb);
+    // the last DEPTH .. 2 DEPTH - 1 groups (groups n .. n + DEPTH - 1 already loaded)
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        if (n + d < total) compute(n + d, g[d]);
+        if (n + d + DEPTH < total) load_group(n + d + DEPTH, g[d]);
     }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (n + DEPTH + d < total) compute(n + DEPTH + d, g[d]);
 
     if (c.clear)
         for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < c.clear_n; i += gridDim.x * blockDim.x) c.clear[i] = 0.f;
-    for (int i = wv; i < nt; i += W) op.prefetch(t0 + i, lane, st);  // epilogue inputs, in flight during the barrier
     __syncthreads();
     for (int i = wv; i < nt; i += W) {
+        if (i != wv) op.prefetch(t0 + i, lane, st);  // a later tile's inputs (more than W tiles per workgroup)
         f32x4_t sum[NT];
 #pragma unroll
         for (int b = 0; b < NT; ++b) sum[b] = zero4();
@@ -521,7 +526,10 @@ struct KVPages {
 template <typename T>
 struct OpQKV {
     static constexpr int kNT = 2;  // 16-column blocks per tile
-    using State = NoState;
+    static constexpr int kWGDepth = 2;  // load groups in flight
+    struct State {
+        float cs[4], sn[4];  // rotary cos/sin of the lane's rows, loaded ahead of the exchange
+    };
     static constexpr bool kDoneHook = false;
     NormA<T> a;
     const T* wq;
@@ -551,10 +559,21 @@ struct OpQKV {
         return sw_stream(W, (h * d + 16 * i + blk * (d / 2)) / 16, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
-    __device__ __forceinline__ void prefetch(int, int, State&) const {}
+    __device__ __forceinline__ void prefetch(int tile, int lane, State& st) const {
+        int kind, h, i;
+        decode(tile, kind, h, i);
+        const int dim = 16 * i + (lane & 15), half = d / 2;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int j = min(4 * (lane >> 4) + ii, M - 1);
+            const long long t = (long long)(pos0 + j) * half + dim;
+            st.cs[ii] = cosT[t];
+            st.sn[ii] = sinT[t];
+        }
+    }
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State& st) const {
         int kind, h, i;
         decode(tile, kind, h, i);
         const int dim = 16 * i + (lane & 15), half = d / 2;
@@ -564,8 +583,7 @@ struct OpQKV {
             if (j >= M) continue;
             float x0 = acc[0][ii], x1 = acc[1][ii];
             if (kind != 2) {
-                const long long t = (long long)(pos0 + j) * half + dim;
-                const float cs = cosT[t], sn = sinT[t];
+                const float cs = st.cs[ii], sn = st.sn[ii];
                 const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
                 x0 = r0;
                 x1 = r1;
@@ -607,6 +625,7 @@ struct OpQKV {
 template <typename T, int NT_ = 2>
 struct OpResid {
     static constexpr int kNT = NT_;  // 16-column blocks per tile
+    static constexpr int kWGDepth = 2;  // load groups in flight (a third measured no faster)
     struct State {
         float xv[NT_][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
     };
@@ -691,6 +710,7 @@ struct OpResid {
 template <typename T>
 struct OpSwiGLU {
     static constexpr int kNT = 2;  // 16-column blocks per tile
+    static constexpr int kWGDepth = 2;  // load groups in flight (a third measured no faster)
     using State = NoState;
     static constexpr bool kDoneHook = false;
     NormA<T> a;
@@ -942,6 +962,7 @@ static hipError_t run_skinny(const DevCtx& c, const Op& op, int M, int K, int nt
 // ceil(ntiles / CUs) consecutive tiles (measured: two workgroups on some CUs
 // and eight waves per tile were both slower).  A load group carries 8 KB of
 // weights per wave (KP chunks x NT 16-column blocks).
+
 static int wg_tiles_per_cu(int ntiles, int cus) { return std::max(1, (ntiles + cus - 1) / cus); }
 
 // Whether the plan suits the launch: at most one tile per CU (e.g. 192 tiles
@@ -975,7 +996,7 @@ static hipError_t run_skinny_wg(const DevCtx& c, const Op& op, int M, int K, int
     // architectural VGPRs (it needs < 190, no spills).  Built without it, the
     // compiler also allocated AGPRs and the results were wrong; that build is
     // not used.
-    hipLaunchKernelGGL((skinny_wg_kernel<T, Op, W, 2, KP>), dim3(grid), dim3(64 * W), lds, s, op, wc);
+    hipLaunchKernelGGL((skinny_wg_kernel<T, Op, W, 2, KP, Op::kWGDepth>), dim3(grid), dim3(64 * W), lds, s, op, wc);
     return hipGetLastError();
 }
 
