@@ -224,7 +224,7 @@ def main():
         "hbm_frac_step": round(ab["step"] * bps / HBM_PEAK, 4),
         "alg_bytes_per_step": ab["step"],
         "mean_accept_k": stats["k"] / max(stats["n"], 1),
-        "roofline": {"bound": "hbm", "kernel": "skinny_kernel<OpLMHead> (LM head + argmax)",
+        "roofline": {"bound": "hbm", "kernel": "skinny_wg_kernel<OpLMHeadWG> (LM head + argmax)",
                      "achieved": round(lm_ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(lm_ach / HBM_PEAK, 4), "traffic": profiled_traffic(args.workload),
                      "alg_bytes_per_launch": ab["lm_head"], "avg_launch_us": round(lm_ms * 1e3, 2)},

@@ -421,11 +421,32 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommo
 #pragma unroll
             for (int b = 0; b < NT; ++b) mma(acc[b], a, g.w[b][p]);
         }
-        if (n - ti * gpt == gpt - 1) {  // the tile's last group: park its partial (LDS only)
+        if (n - ti * gpt == gpt - 1) {  // the tile's last group
+            if constexpr (Op::kInLoop) {
+                // all waves finish the tile together, wave wv taking rows
+                // 4 g + wv: partials in a double buffer, summed in wave order
+                const int buf = ti & 1;
 #pragma unroll
-            for (int b = 0; b < NT; ++b) {
-                wg_red[((ti * W + wv) * NT + b) * 64 + lane] = acc[b];
-                acc[b] = zero4();
+                for (int b = 0; b < NT; ++b) {
+                    wg_red[((buf * W + wv) * NT + b) * 64 + lane] = acc[b];
+                    acc[b] = zero4();
+                }
+                stage_barrier();
+                const float* red = reinterpret_cast<const float*>(wg_red);
+                float v[NT];
+#pragma unroll
+                for (int b = 0; b < NT; ++b) {
+                    v[b] = 0.f;
+#pragma unroll
+                    for (int q = 0; q < W; ++q) v[b] += red[(((buf * W + q) * NT + b) * 64 + lane) * 4 + wv];
+                }
+                op.finish_rows(t0 + ti, v, lane, wv, st);
+            } else {  // park the partial (LDS only) for the epilogue after the stream
+#pragma unroll
+                for (int b = 0; b < NT; ++b) {
+                    wg_red[((ti * W + wv) * NT + b) * 64 + lane] = acc[b];
+                    acc[b] = zero4();
+                }
             }
         }
     };
@@ -458,20 +479,22 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommo
 
     if (c.clear)
         for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < c.clear_n; i += gridDim.x * blockDim.x) c.clear[i] = 0.f;
-    __syncthreads();
-    for (int i = wv; i < nt; i += W) {
-        if (i != wv) op.prefetch(t0 + i, lane, st);  // a later tile's inputs (more than W tiles per workgroup)
-        f32x4_t sum[NT];
-#pragma unroll
-        for (int b = 0; b < NT; ++b) sum[b] = zero4();
-        for (int q = 0; q < W; ++q)
-#pragma unroll
-            for (int b = 0; b < NT; ++b) {
-                const f32x4_t v = wg_red[((i * W + q) * NT + b) * 64 + lane];
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) sum[b][ii] += v[ii];
-            }
-        op.epilogue(t0 + i, sum, lane, st);
+    if constexpr (!Op::kInLoop) {
+        __syncthreads();
+        for (int i = wv; i < nt; i += W) {
+            if (i != wv) op.prefetch(t0 + i, lane, st);  // a later tile's inputs (more than W tiles per workgroup)
+            f32x4_t sum[NT];
+    #pragma unroll
+            for (int b = 0; b < NT; ++b) sum[b] = zero4();
+            for (int q = 0; q < W; ++q)
+    #pragma unroll
+                for (int b = 0; b < NT; ++b) {
+                    const f32x4_t v = wg_red[((i * W + q) * NT + b) * 64 + lane];
+    #pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) sum[b][ii] += v[ii];
+                }
+            op.epilogue(t0 + i, sum, lane, st);
+        }
     }
     op.wave_end(st, lane);
 }
@@ -526,6 +549,7 @@ struct KVPages {
 template <typename T>
 struct OpQKV {
     static constexpr int kNT = 2;  // 16-column blocks per tile
+    static constexpr bool kInLoop = false;
     static constexpr int kWGDepth = 2;  // load groups in flight
     struct State {
         float cs[4], sn[4];  // rotary cos/sin of the lane's rows, loaded ahead of the exchange
@@ -625,6 +649,7 @@ struct OpQKV {
 template <typename T, int NT_ = 2>
 struct OpResid {
     static constexpr int kNT = NT_;  // 16-column blocks per tile
+    static constexpr bool kInLoop = false;
     static constexpr int kWGDepth = 2;  // load groups in flight (a third measured no faster)
     struct State {
         float xv[NT_][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
@@ -710,6 +735,7 @@ struct OpResid {
 template <typename T>
 struct OpSwiGLU {
     static constexpr int kNT = 2;  // 16-column blocks per tile
+    static constexpr bool kInLoop = false;
     static constexpr int kWGDepth = 2;  // load groups in flight (a third measured no faster)
     using State = NoState;
     static constexpr bool kDoneHook = false;
@@ -829,6 +855,94 @@ struct OpLMHead {
         }
         __syncthreads();
         if (__float_as_uint(sv[0][0]) == 1u) {
+            compiler_fence();
+            if (threadIdx.x < 16) {
+                const int j = threadIdx.x;
+                if (j < M) {
+                    const unsigned long long key = atomicOr(best + j, 0ull);
+                    tokens[j] = (int32_t)(0xFFFFFFFFu - (unsigned)(key & 0xFFFFFFFFull));
+                }
+                atomicExch(best + j, 0ull);
+            }
+            if (threadIdx.x == 0) atomicExch(wg_cnt, 0u);
+        }
+    }
+};
+
+// LM head with a fused argmax on the workgroup-local kernel: 32-column tiles,
+// finished inside the stream by all four waves (wave wv owns rows 4 g + wv of
+// every tile, so each of the 16 rows has one owner per workgroup).  The fp32
+// logits go out through a range-checked buffer store that drops rows >= M,
+// columns >= V and everything when no logits buffer is given, so the stream's
+// instruction sequence has no branch around a memory access.  Per row the
+// owner keeps (value, lowest id), reduces it over its 16 lanes and publishes a
+// packed (value, ~id) key with a 64-bit atomic max (order independent); the
+// last workgroup writes the tokens.
+template <typename T>
+struct OpLMHeadWG {
+    static constexpr int kNT = 2;
+    static constexpr bool kInLoop = true;
+    static constexpr int kWGDepth = 2;
+    struct State {
+        float v;
+        int idx;
+        __amdgpu_buffer_rsrc_t out;
+    };
+    NormA<T> a;
+    const T* w;
+    int V, K, M;
+    float* logits;                 // [M, V] or null
+    unsigned long long* best;      // [16] packed keys, zero on entry
+    unsigned* wg_cnt;              // workgroup completion counter
+    int32_t* tokens;               // [M]
+    __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
+        const int n0 = 32 * tile + 16 * blk;
+        return n0 < V ? sw_stream(w, n0 / 16, nch) : nullptr;
+    }
+    __device__ __forceinline__ void wave_begin(State& s) const {
+        s.v = -INFINITY;
+        s.idx = 0x7FFFFFFF;
+        // 0x00020000: the gfx9 buffer descriptor's format word (raw 32-bit data)
+        s.out = __builtin_amdgcn_make_buffer_rsrc(logits, 0, logits ? (int)((long long)M * V * 4) : 0, 0x00020000);
+    }
+    __device__ __forceinline__ void prefetch(int, int, State&) const {}
+    __device__ __forceinline__ void finish_rows(int tile, const float (&v)[kNT], int lane, int wv, State& s) const {
+        const int row = 4 * (lane >> 4) + wv;
+#pragma unroll
+        for (int b = 0; b < kNT; ++b) {
+            const int n = 32 * tile + 16 * b + (lane & 15);
+            const bool ok = n < V;
+            const int off = ok && row < M ? (row * V + n) * 4 : 0x7FFFFFF0;  // out of range: dropped
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[b]), s.out, off, 0, 0);
+            if (ok && (v[b] > s.v || (v[b] == s.v && n < s.idx))) {
+                s.v = v[b];
+                s.idx = n;
+            }
+        }
+    }
+    __device__ void wave_end(State& s, int lane) const {
+        __shared__ unsigned last;
+        float v = s.v;
+        int id = s.idx;
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+            const float ov = __shfl_xor(v, m, 64);
+            const int oi = __shfl_xor(id, m, 64);
+            if (ov > v || (ov == v && oi < id)) {
+                v = ov;
+                id = oi;
+            }
+        }
+        const int row = 4 * (lane >> 4) + (threadIdx.x >> 6);
+        if ((lane & 15) == 0 && row < M && id != 0x7FFFFFFF) {
+            const unsigned long long key = ((unsigned long long)ordered_bits(v) << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)id);
+            atomicMax(best + row, key);
+        }
+        wait_vmem();
+        __syncthreads();
+        if (threadIdx.x == 0) last = atomicAdd(wg_cnt, 1u) == gridDim.x - 1 ? 1u : 0u;
+        __syncthreads();
+        if (last) {
             compiler_fence();
             if (threadIdx.x < 16) {
                 const int j = threadIdx.x;
@@ -991,7 +1105,7 @@ static hipError_t run_skinny_wg(const DevCtx& c, const Op& op, int M, int K, int
     wc.cpw = ((wc.nchunks + W - 1) / W + KP - 1) / KP * KP;
     wc.clear = clear;
     wc.clear_n = clear_n;
-    const size_t lds = (size_t)wc.tpw * W * NT * 64 * sizeof(f32x4_t);
+    const size_t lds = (size_t)(Op::kInLoop ? 2 : wc.tpw) * W * NT * 64 * sizeof(f32x4_t);
     // The occupancy hint of two workgroups per CU caps the kernel at 256
     // architectural VGPRs (it needs < 190, no spills).  Built without it, the
     // compiler also allocated AGPRs and the results were wrong; that build is
@@ -2271,19 +2385,39 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         c.tracer->end(DFLASH_TRACE_DOWN, s);
     }
 
-    OpLMHead<T> lm;
-    lm.a = norm_in(c.final_norm, d.Ld > 0, ss1);
-    lm.w = (const T*)c.sw_lm;
-    lm.V = d.V;
-    lm.K = H;
-    lm.M = B;
-    lm.logits = pa.logits;
-    lm.best = best;
-    lm.wg_cnt = counters + 1;
-    lm.tokens = pa.tokens;
     c.tracer->begin(DFLASH_TRACE_LM_HEAD, s);
-    if ((e = run_skinny<T>(c, lm, B, H, (d.V + 16 * OpLMHead<T>::kNT - 1) / (16 * OpLMHead<T>::kNT), s)) != hipSuccess)
-        return e;
+    const int lm_tiles_wg = (d.V + 31) / 32;
+    bool lm_done = false;
+    if constexpr (sizeof(T) == 2) {
+        if (d.V % 16 == 0 && wg_plan_balanced(lm_tiles_wg, c.num_cus)) {
+            OpLMHeadWG<T> lm;
+            lm.a = norm_in(c.final_norm, d.Ld > 0, ss1);
+            lm.w = (const T*)c.sw_lm;
+            lm.V = d.V;
+            lm.K = H;
+            lm.M = B;
+            lm.logits = pa.logits;
+            lm.best = best;
+            lm.wg_cnt = counters + 1;
+            lm.tokens = pa.tokens;
+            if ((e = run_skinny_wg<T>(c, lm, B, H, lm_tiles_wg, s)) != hipSuccess) return e;
+            lm_done = true;
+        }
+    }
+    if (!lm_done) {
+        OpLMHead<T> lm;
+        lm.a = norm_in(c.final_norm, d.Ld > 0, ss1);
+        lm.w = (const T*)c.sw_lm;
+        lm.V = d.V;
+        lm.K = H;
+        lm.M = B;
+        lm.logits = pa.logits;
+        lm.best = best;
+        lm.wg_cnt = counters + 1;
+        lm.tokens = pa.tokens;
+        if ((e = run_skinny<T>(c, lm, B, H, (d.V + 16 * OpLMHead<T>::kNT - 1) / (16 * OpLMHead<T>::kNT), s)) != hipSuccess)
+            return e;
+    }
     c.tracer->end(DFLASH_TRACE_LM_HEAD, s);
     return hipSuccess;
 }
