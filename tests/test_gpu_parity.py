@@ -153,6 +153,23 @@ def test_draft_short_block(dl, orc, B):
     assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype, ref["noise"])
 
 
+@pytest.mark.parametrize("B", [16, 5])
+def test_draft_lm_head_partial_tile(dl, orc, B):
+    """Vocabulary 1008 ends in half a 32-column LM-head tile; a short block
+    leaves rows the logits buffer does not have.  Tokens must not depend on
+    whether logits are requested."""
+    s = MID_BF16_H352.replace(block=B)
+    w = di.draft_weights(s, gains="random")
+    tok, lg, ref, ctx = _draft_pair(dl, orc, s, 300, anchor=5, w=w)
+    assert lg.shape == (B, s.vocab)
+    assert_logits(lg, ref["logits"], s.dtype, ref["noise"])
+    assert_tokens(tok, ref["tokens"], ref["gap"], lg, ref["logits"], s.dtype, ref["noise"])
+    a = torch.tensor([5], dtype=torch.int32, device="cuda")
+    t_off, _ = ctx.draft_block(a, want_logits=False)
+    sync()
+    assert torch.equal(t_off.cpu(), torch.as_tensor(np.asarray(tok)).to(t_off.dtype))
+
+
 def test_draft_deterministic_and_logits_optional(dl, orc):
     s = MID_BF16
     w = di.draft_weights(s)
