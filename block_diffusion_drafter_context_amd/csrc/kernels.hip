@@ -7,10 +7,13 @@
 //  [B] "从 ICML 论文到你的显卡：llama.cpp 吞下 DFlash…" (arex-research.com), 技术内幕.
 //
 // Kernels:
-//  * skinny_kernel<T, Op>  -- the weight-streaming GEMM for M <= 16 rows.  Every
-//    projection of the draft pass (QKV+RoPE, O+residual, gate/up+SwiGLU,
-//    down+residual, LM head+argmax) and the per-step fusion/injection of 16
-//    verified rows run through it.  Work is split "stream-K" style: the
+//  * skinny_wg_kernel<T, Op>  -- the weight-streaming GEMM for M <= 16 rows of a
+//    bf16 pass: QKV+RoPE, O+residual, gate/up+SwiGLU, down+residual and the LM
+//    head+argmax.  Each workgroup owns whole output tiles and its 4 waves split
+//    a tile's K range; the partial sums meet in LDS (no device-scope exchange).
+//  * skinny_kernel<T, Op>  -- the stream-K form of the same GEMM: the per-step
+//    fusion/injection of 16 verified rows, fp32 passes, and projections whose
+//    tiles would fill the CUs unevenly on the kernel above.  Work is split "stream-K" style: the
 //    (column tile x 32-wide K chunk) space is cut into equal contiguous ranges,
 //    one per wave, so every wave streams the same number of weight bytes; a tile
 //    split between waves is finished by the last contributor, which sums the
