@@ -335,9 +335,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
 // Workgroup-local split-K.  Every workgroup owns `tpw` consecutive whole
 // tiles, and its W waves split each tile's K range evenly (cpw chunks each).
 // Each wave streams the (tile, K group) sequence of all its tiles as one
-// pipeline of KP-chunk load groups, DEPTH of them in flight, and parks a tile's partial sum in
-// LDS when the tile's last group is done.  After the stream, the W partials
-// of each tile are added in wave order by one wave, which runs the epilogue.
+// pipeline of KP-chunk load groups, DEPTH of them in flight, and parks a
+// tile's partial sum in LDS when the tile's last group is done.  After the
+// stream, the W partials of each tile are added in wave order by one wave,
+// which runs the epilogue.  Ops with kInLoop (the LM head, too many tiles to
+// park) instead finish each tile inside the stream: all W waves meet at an
+// LDS-only barrier and each adds the partials of a quarter of the rows.
 // No partial leaves the CU, so the launch has no device-scope exchange.  The
 // steady-state loop issues its loads unconditionally and holds no other
 // memory access, so each group waits only for its own loads (global stores or
@@ -353,7 +356,7 @@ struct WGCommon {
     int ntiles;
     int tpw;        // tiles per workgroup
     int cpw;        // chunks of a tile per wave (a multiple of KP)
-    float* clear;   // cleared at launch (clear_n floats), or null
+    float* clear;   // cleared by the launch after its stream (clear_n floats), or null
     int clear_n;
 };
 
