@@ -889,7 +889,7 @@ struct OpLMHead {
 // last workgroup writes the tokens.
 template <typename T>
 struct OpLMHeadWG {
-    static constexpr int kNT = 2;
+    static constexpr int kNT = 4;
     static constexpr bool kInLoop = true;
     static constexpr int kWGDepth = 2;
     struct State {
@@ -905,7 +905,7 @@ struct OpLMHeadWG {
     unsigned* wg_cnt;              // workgroup completion counter
     int32_t* tokens;               // [M]
     __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
-        const int n0 = 32 * tile + 16 * blk;
+        const int n0 = 16 * kNT * tile + 16 * blk;
         return n0 < V ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State& s) const {
@@ -919,7 +919,7 @@ struct OpLMHeadWG {
         const int row = 4 * (lane >> 4) + wv;
 #pragma unroll
         for (int b = 0; b < kNT; ++b) {
-            const int n = 32 * tile + 16 * b + (lane & 15);
+            const int n = 16 * kNT * tile + 16 * b + (lane & 15);
             const bool ok = n < V;
             const int off = ok && row < M ? (row * V + n) * 4 : 0x7FFFFFF0;  // out of range: dropped
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[b]), s.out, off, 0, 0);
@@ -2395,7 +2395,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     }
 
     c.tracer->begin(DFLASH_TRACE_LM_HEAD, s);
-    const int lm_tiles_wg = (d.V + 31) / 32;
+    const int lm_tiles_wg = (d.V + 16 * OpLMHeadWG<T>::kNT - 1) / (16 * OpLMHeadWG<T>::kNT);
     bool lm_done = false;
     if constexpr (sizeof(T) == 2) {
         if (d.V % 16 == 0 && wg_plan_balanced(lm_tiles_wg, c.num_cus)) {
