@@ -889,7 +889,7 @@ struct OpLMHead {
 // last workgroup writes the tokens.
 template <typename T>
 struct OpLMHeadWG {
-    static constexpr int kNT = 4;
+    static constexpr int kNT = 8;
     static constexpr bool kInLoop = true;
     static constexpr int kWGDepth = 2;
     struct State {
@@ -1102,7 +1102,7 @@ template <typename T, class Op>
 static hipError_t run_skinny_wg(const DevCtx& c, const Op& op, int M, int K, int ntiles, hipStream_t s,
                                 float* clear = nullptr, int clear_n = 0) {
     constexpr int NT = Op::kNT;
-    constexpr int KP = NT == 1 && sizeof(T) == 2 ? 8 : 4;
+    constexpr int KP = NT == 1 && sizeof(T) == 2 ? 8 : (NT >= 8 ? 2 : 4);
     constexpr int W = 4;
     WGCommon wc;
     wc.M = M;
