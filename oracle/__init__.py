@@ -54,9 +54,12 @@ def lib():
         L.orc_fuse_rows.argtypes = [vp, vp, i64, vp, i32, vp]
         L.orc_inject_rows.argtypes = [vp, vp, i64, vp, i32, i64, vp, vp]
         L.orc_draft_block.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp, vp]
+        L.orc_draft_layer.argtypes = [vp, i32, vp, vp, i64, vp, vp]
+        L.orc_lm_head.argtypes = [vp, vp, i32, vp, vp, vp]
         L.orc_accept.argtypes = [vp, vp, i32, vp, vp]
         L.orc_target_forward.argtypes = [vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp, vp]
-        for f in ("orc_fuse_rows", "orc_inject_rows", "orc_draft_block", "orc_target_forward"):
+        for f in ("orc_fuse_rows", "orc_inject_rows", "orc_draft_block", "orc_target_forward", "orc_draft_layer",
+                  "orc_lm_head"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -212,6 +215,36 @@ def draft_block(model: Model, ctx_k: Optional[torch.Tensor], ctx_v: Optional[tor
                                trace.ctypes.data if trace is not None else None)
     assert rc == 0
     return {"logits": logits, "tokens": tokens, "gap": gap, "trace": trace}
+
+
+def draft_layer(model: Model, layer: int, ctx_k: Optional[torch.Tensor], ctx_v: Optional[torch.Tensor],
+                C_len: int, x_in: np.ndarray) -> np.ndarray:
+    """One draft layer alone: x_in [B, H] (storage values, e.g. another
+    implementation's input to that layer); ctx_k / ctx_v: storage tensors
+    [>=C, nkv, d] of that layer (or None when C == 0).  Returns [B, H]."""
+    s = model.shape
+    x_in = np.ascontiguousarray(x_in, dtype=np.float64)
+    assert x_in.shape == (s.block, s.hidden)
+    if C_len > 0:
+        ctx_k, ctx_v = ctx_k.contiguous(), ctx_v.contiguous()
+    out = np.empty_like(x_in)
+    rc = lib().orc_draft_layer(model.ref, layer, _ptr(ctx_k) if C_len > 0 else None,
+                               _ptr(ctx_v) if C_len > 0 else None, C_len, _dptr(x_in), _dptr(out))
+    assert rc == 0
+    return out
+
+
+def lm_head(model: Model, x: np.ndarray):
+    """Final RMSNorm + LM head + argmax of rows x [R, H] (storage values)."""
+    s = model.shape
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    R = x.shape[0]
+    logits = np.empty((R, s.vocab), dtype=np.float32)
+    tokens = np.empty(R, dtype=np.int32)
+    gap = np.empty(R, dtype=np.float64)
+    rc = lib().orc_lm_head(model.ref, _dptr(x), R, logits.ctypes.data, tokens.ctypes.data, gap.ctypes.data)
+    assert rc == 0
+    return {"logits": logits, "tokens": tokens, "gap": gap}
 
 
 def accept(drafts: Sequence[int], target: Sequence[int]):

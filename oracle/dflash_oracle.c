@@ -375,6 +375,41 @@ int orc_draft_block(const orc_model* m, const void* const* ctx_k, const void* co
     return 0;
 }
 
+/* The same draft layer on its own: layer l over block rows x_in[B][H]
+ * (storage values) at positions C..C+B-1, attending without a mask to the C
+ * injected context keys of that layer (ctx_k, ctx_v: [C][nkv][d] storage) and
+ * to the block's own keys ([A] §2.2 draft_inference; one repetition of the
+ * per-layer step of orc_draft_block).  x_out[B][H] receives the residual
+ * stream after the layer.  Used to compare a layer given identical inputs. */
+int orc_draft_layer(const orc_model* m, int32_t l, const void* ctx_k, const void* ctx_v, int64_t C,
+                    const double* x_in, double* x_out)
+{
+    const int32_t H = m->hidden, B = m->block;
+    const int64_t NK = (int64_t)m->n_kv_heads * m->head_dim;
+    if (m->head_dim > 256 || l < 0 || l >= m->n_layers) return -1;
+    double* kb = (double*)malloc(sizeof(double) * (size_t)B * NK);
+    double* vb = (double*)malloc(sizeof(double) * (size_t)B * NK);
+    int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)B);
+    if (!kb || !vb || !pos) { free(kb); free(vb); free(pos); return -1; }
+    memcpy(x_out, x_in, sizeof(double) * (size_t)B * H);
+    for (int32_t j = 0; j < B; ++j) pos[j] = C + j;
+    kv_src ks = { C > 0 ? ctx_k : NULL, C, kb, B };
+    kv_src vs = { C > 0 ? ctx_v : NULL, C, vb, B };
+    decoder_layer(m, l, x_out, B, pos, &ks, &vs, kb, vb, 0, 0);
+    free(kb); free(vb); free(pos);
+    return 0;
+}
+
+/* The draft's output head on its own: final RMSNorm, shared LM head ([A]
+ * §3.3), fp32 logits, argmax (ties: lowest id) and top-2 gap of R rows x[R][H]
+ * (storage values). */
+int orc_lm_head(const orc_model* m, const double* x, int32_t R, float* logits, int32_t* tokens, double* gap)
+{
+    if (R < 1) return -1;
+    lm_head_argmax(m, x, R, logits, tokens, gap);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* greedy verification                                                 */
 /* ------------------------------------------------------------------ */

@@ -87,6 +87,16 @@ int orc_draft_block(const orc_model* m, const void* const* ctx_k, const void* co
                     int64_t C, int32_t anchor, float* logits, int32_t* tokens, double* gap,
                     double* trace);
 
+/* one draft layer l alone: x_out[B][H] = layer l of the block rows x_in[B][H] at
+ * positions C.., over the C context keys ctx_k/ctx_v ([C][nkv][d] storage) and
+ * the block's own keys (no mask) */
+int orc_draft_layer(const orc_model* m, int32_t l, const void* ctx_k, const void* ctx_v, int64_t C,
+                    const double* x_in, double* x_out);
+
+/* final RMSNorm + LM head + argmax of R rows x[R][H]: logits [R][V] fp32 (may be
+ * NULL), tokens [R], gap [R] top-2 gap (may be NULL) */
+int orc_lm_head(const orc_model* m, const double* x, int32_t R, float* logits, int32_t* tokens, double* gap);
+
 /* greedy block verification: d[1..B-1] drafts, g[0..B-1] target argmax */
 void orc_accept(const int32_t* d, const int32_t* g, int32_t B, int32_t* k, int32_t* bonus);
 

@@ -451,3 +451,98 @@ def test_spec_decode_is_lossless(orc, toylet, mode):
         assert ks == [0] * (len(greedy) - 1)
     if mode == "prefix":
         assert len(set(ks)) > 3
+
+
+# ---------------------------------------------------------------- causal target vs an independent formulation
+
+CAUSAL = di.Shape("causal", "fp32", hidden=64, target_layers=8, draft_layers=8, n_q_heads=4,
+                  n_kv_heads=2, head_dim=16, ffn=96, vocab=128, ctx=24, seed=41)
+
+
+@pytest.mark.parametrize("chunks", [[24], [7, 1, 16], [1] * 8 + [16]])
+def test_target_forward_brute_force(orc, chunks):
+    """The oracle's causal forward ([A] §1.1 autoregressive generation, §1.2
+    verification of a block in one causal pass) against torch's attention with
+    an explicit lower-triangular mask over the whole sequence: logits, argmax
+    and the five captured layers (the residual stream right AFTER each selected
+    layer).  The oracle runs the sequence as one prefill, or as calls of 1 and
+    16 rows appended to its cache, so a row that misses its own key or a
+    capture taken before the layer fails here."""
+    s = CAUSAL
+    w = di.toy_target_weights(s)
+    m = orc.Model(s, w, n_layers=s.target_layers)
+    toks = di.uniform_int(s.ctx, 0, s.vocab - 1, s.seed, "causal").numpy()
+    sel = orc.feature_layers(s.target_layers)
+    cache = orc.TargetCache(m, s.ctx)
+    lg, am, hid, pos = [], [], [], 0
+    for n in chunks:
+        r = orc.target_forward(m, cache, toks[pos:pos + n], pos, capture=sel, want_logits=True)
+        lg.append(r["logits"])
+        am.append(r["argmax"])
+        hid.append(r["hidden"])
+        pos += n
+    assert pos == s.ctx
+    lg, am, hid = np.concatenate(lg), np.concatenate(am), np.concatenate(hid, axis=1)
+    ref_lg, ref_hid = torch_ref.target_forward(s, w, toks, s.target_layers)
+    ref_lg, ref_hid = ref_lg.numpy(), ref_hid.numpy()
+    np.testing.assert_allclose(lg, ref_lg, rtol=1e-5, atol=1e-6)
+    assert np.array_equal(am, ref_lg.argmax(axis=1))
+    for i, l in enumerate(sel):
+        np.testing.assert_allclose(hid[i], ref_hid[l], rtol=1e-5, atol=1e-6, err_msg=f"captured layer {l}")
+
+
+def test_target_first_row_sees_only_itself(orc):
+    """Row 0 of a prefill attends to its own key alone, so its output does not
+    depend on the tokens after it; row j depends on token j (its own key)."""
+    s = CAUSAL
+    w = di.toy_target_weights(s)
+    m = orc.Model(s, w, n_layers=s.target_layers)
+    toks = di.uniform_int(6, 0, s.vocab - 1, s.seed, "own").numpy()
+    alt = toks.copy()
+    alt[3] = (alt[3] + 1) % s.vocab
+    a = orc.target_forward(m, orc.TargetCache(m, 6), toks, 0, want_logits=True)["logits"]
+    b = orc.target_forward(m, orc.TargetCache(m, 6), alt, 0, want_logits=True)["logits"]
+    assert np.array_equal(a[:3], b[:3])
+    assert np.abs(a[3] - b[3]).max() > 1e-4 and np.abs(a[5] - b[5]).max() > 1e-4
+
+
+# ---------------------------------------------------------------- fusion storage rounding (bf16)
+
+def test_fuse_rounds_linear_output_before_norm(orc):
+    """bf16 storage contract of the fusion ([A] §2.2 rms_norm(linear(concat))):
+    the Linear's output is stored (rounded to bf16) and the RMSNorm reads the
+    stored values.  Written here with torch's own matmul, bf16 conversion and
+    rms_norm; leaving out the rounding between the two changes about a quarter
+    of the bf16 outputs."""
+    s = MICRO.replace(dtype="bf16")
+    H = s.hidden
+    w = di.draft_weights(s, gains="random", need_draft=False, need_lm=False)
+    slabs = [di.target_hidden(s, l, 32) for l in range(5)]
+    out = orc.fuse_rows(orc.Model(s, w), slabs, range(32))
+    x = torch.cat([t.double() for t in slabs], dim=1)
+    y = (x @ w["fc"].double().T).to(torch.bfloat16).double()
+    ref = F.rms_norm(y, (H,), weight=w["fc_norm"].double(), eps=s.eps).to(torch.bfloat16).double().numpy()
+    # torch converts float64 -> float32 -> bfloat16, which can differ from a
+    # direct rounding only at exact bf16 halfway points of the float32 value
+    assert (out != ref).mean() < 2e-3
+
+
+# ---------------------------------------------------------------- per-layer entry points
+
+def test_draft_layers_compose_to_the_block(orc):
+    """Chaining the one-layer entry and the LM-head entry reproduces the full
+    draft block exactly (they expose the block's own steps)."""
+    s = MICRO
+    m, w = micro_model(orc)
+    C = 24
+    k, v = _ctx(s, C)
+    full = orc.draft_block(m, k, v, C, 9, want_trace=True)
+    x = full["trace"][0]
+    for l in range(s.draft_layers):
+        x = orc.draft_layer(m, l, k[l], v[l], C, x)
+        assert np.array_equal(x, full["trace"][l + 1])
+    head = orc.lm_head(m, x)
+    assert np.array_equal(head["logits"], full["logits"]) and np.array_equal(head["tokens"], full["tokens"])
+    m0 = orc.Model(s, w)
+    x0 = orc.draft_block(m0, None, None, 0, 9, want_trace=True)["trace"]
+    assert np.array_equal(orc.draft_layer(m0, 0, None, None, 0, x0[0]), x0[1])

@@ -79,3 +79,41 @@ def inject(shape, w, fused, pos0):
         ks.append(_r32(k))
         vs.append(_r32(v))
     return torch.stack(ks), torch.stack(vs)
+
+
+def target_forward(shape, w, tokens, n_layers):
+    """fp32-storage causal forward of `tokens` from position 0 (a prefill of
+    the whole sequence at once): the autoregressive model of [A] §1.1, written
+    with an explicit lower-triangular visibility mask (key j is visible to
+    query i iff j <= i, the query's own key included).  Returns (logits [n, V],
+    hidden [n_layers, n, H]) where hidden[l] is the residual stream right after
+    decoder layer l (before any final norm)."""
+    H, d = shape.hidden, shape.head_dim
+    nq, nkv = shape.n_q_heads, shape.n_kv_heads
+    eps = shape.eps
+    g = lambda k: w[k].to(torch.float64)
+    n = len(tokens)
+    x = g("embed")[torch.as_tensor(list(tokens), dtype=torch.long)]
+    pos = torch.arange(n)
+    visible = torch.ones(n, n, dtype=torch.bool).tril()
+    outs = []
+    for l in range(n_layers):
+        u = _r32(F.rms_norm(x, (H,), weight=g(f"attn_norm.{l}"), eps=eps))
+        q = (u @ g(f"wq.{l}").T).view(n, nq, d).transpose(0, 1)
+        k = (u @ g(f"wk.{l}").T).view(n, nkv, d).transpose(0, 1)
+        v = _r32((u @ g(f"wv.{l}").T).view(n, nkv, d).transpose(0, 1))
+        q = _r32(rope_complex(q, pos, shape.rope_base))
+        k = _r32(rope_complex(k, pos, shape.rope_base))
+        rep = nq // nkv
+        k = k.repeat_interleave(rep, dim=0)
+        v = v.repeat_interleave(rep, dim=0)
+        o = F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=visible,
+                                           scale=1.0 / math.sqrt(d))[0]
+        o = _r32(o.transpose(0, 1).reshape(n, nq * d))
+        x = _r32(x + _r32(o @ g(f"wo.{l}").T))
+        u = _r32(F.rms_norm(x, (H,), weight=g(f"mlp_norm.{l}"), eps=eps))
+        h = _r32(F.silu(u @ g(f"wg.{l}").T) * (u @ g(f"wu.{l}").T))
+        x = _r32(x + _r32(h @ g(f"wd.{l}").T))
+        outs.append(x.clone())
+    z = _r32(F.rms_norm(x, (H,), weight=g("final_norm"), eps=eps))
+    return _r32(z @ g("lm_head").T), torch.stack(outs)
