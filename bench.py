@@ -45,6 +45,37 @@ def alg_bytes(s, C):
             "fuse16": fuse16, "inject16": inject16, "step": draft + fuse16 + inject16}
 
 
+def cpu_identity():
+    """Model name, sockets, physical cores and logical CPUs of the host (from
+    lscpu, else /proc/cpuinfo); fields that cannot be read are left out."""
+    import subprocess
+    info = {}
+    try:
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        kv = dict(l.split(":", 1) for l in txt.splitlines() if ":" in l)
+        kv = {a.strip(): b.strip() for a, b in kv.items()}
+        if "Model name" in kv:
+            info["cpu_model"] = kv["Model name"]
+        if "Socket(s)" in kv:
+            info["sockets"] = int(kv["Socket(s)"])
+            if "Core(s) per socket" in kv:
+                info["physical_cores"] = int(kv["Core(s) per socket"]) * info["sockets"]
+        if "CPU(s)" in kv:
+            info["logical_cpus"] = int(kv["CPU(s)"])
+    except Exception:
+        pass
+    if "cpu_model" not in info and os.path.exists("/proc/cpuinfo"):
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except Exception:
+        pass
+    return info
+
+
 def profiled_traffic(workload):
     """HBM bytes per LM-head launch from the committed counter passes, or None
     when they were taken on another workload or on different kernel sources."""
@@ -340,11 +371,13 @@ def main():
         import ctypes as C_
         s3 = di.SHAPES["dense27b_36k"]
         t0 = time.time()
-        w3 = {k: v.cuda() for k, v in di.draft_weights(s3).items()}
+        w3_cpu = di.draft_weights(s3)
+        w3 = {k: v.cuda() for k, v in w3_cpu.items()}
         ctx3 = dl.DFlash(s3, w3, max_ctx=s3.ctx + 64)
         k3, v3 = di.context_kv(s3, s3.ctx)
         ctx3.load_kv(k3.cuda(), v3.cuda())
-        del k3, v3
+        if args.no_cpu_baseline:
+            del w3_cpu, k3, v3
         a3 = torch.tensor([di.anchor_token(s3)], dtype=torch.int32, device="cuda")
         t3 = torch.empty(s3.block, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
@@ -501,24 +534,78 @@ def main():
         m = orc.Model(s, w_cpu)
         k, v = di.context_kv(s, C)
         hid16 = [di.target_hidden(s, l, 16, tag="step") for l in sel]
-        anchor = di.anchor_token(s)
-        n_cpu = 0
-        t = time.perf_counter()
-        while n_cpu < 30 and (n_cpu == 0 or time.perf_counter() - t < 10.0):
-            ref = orc.draft_block(m, k, v, C, anchor, want_logits=False)
-            g = di.synthetic_target_argmax(ref["tokens"], u.numpy(), r.numpy(), last, s.vocab)
-            _, anchor = orc.accept(ref["tokens"], g)
-            f16 = orc.fuse_rows(m, hid16, range(16))
-            orc.inject_rows(m, orc.to_storage(f16, s.dtype), range(16), C)
-            n_cpu += 1
-        cpu_s = (time.perf_counter() - t) / n_cpu
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+        def oracle_steps(n_max, budget_s):
+            anchor = di.anchor_token(s)
+            n_cpu = 0
+            t = time.perf_counter()
+            while n_cpu < n_max and (n_cpu == 0 or time.perf_counter() - t < budget_s):
+                ref = orc.draft_block(m, k, v, C, anchor, want_logits=False)
+                g = di.synthetic_target_argmax(ref["tokens"], u.numpy(), r.numpy(), last, s.vocab)
+                _, anchor = orc.accept(ref["tokens"], g)
+                f16 = orc.fuse_rows(m, hid16, range(16))
+                orc.inject_rows(m, orc.to_storage(f16, s.dtype), range(16), C)
+                n_cpu += 1
+            return n_cpu, (time.perf_counter() - t) / n_cpu
+
+        threads = orc.get_threads()
+        n_cpu, cpu_s = oracle_steps(30, 10.0)
+        host = cpu_identity()
         out["cpu_baseline"] = {"value": round(1.0 / cpu_s, 5), "unit": "draft blocks/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"{n_cpu} full steps (draft block at C={C} + accept + fuse/inject of 16 rows, "
                                          f"anchor from each step's bonus), fp64 oracle, {cpu_s * n_cpu:.1f}s in all, "
-                                         f"{cpu_s:.2f}s per step"}
-        log(f"[bench] cpu oracle: {n_cpu} steps, {cpu_s:.2f}s per step with {threads} threads")
+                                         f"{cpu_s:.2f}s per step, {threads} OpenMP threads",
+                               **host}
+        log(f"[bench] cpu oracle: {n_cpu} steps, {cpu_s:.2f}s per step with {threads} threads; host {host}")
+        # the same step on one thread
+        orc.set_threads(1)
+        n1, s1 = oracle_steps(1, 0.0)
+        orc.set_threads(threads)
+        out["cpu_baseline"]["single_thread"] = {"value": round(1.0 / s1, 5), "unit": "draft blocks/s",
+                                                "sample": f"{n1} full step on 1 thread, {s1:.2f}s"}
+        log(f"[bench] cpu oracle, 1 thread: {s1:.2f}s per step")
+        other = {}
+        # the 8B shape at 36864 tokens of context: one draft block
+        if args.long_ctx:
+            kl, vl = di.context_kv(s, args.long_ctx)
+            t = time.perf_counter()
+            orc.draft_block(m, kl, vl, args.long_ctx, di.anchor_token(s), want_logits=False)
+            dt_ = time.perf_counter() - t
+            other[f"{args.workload}@{args.long_ctx}"] = {"value": round(1.0 / dt_, 5), "unit": "draft blocks/s",
+                                                         "sample": f"1 draft block at C={args.long_ctx}, {dt_:.2f}s"}
+            del kl, vl
+        # the 27B-class draft block at 36864 tokens
+        if "w3_cpu" in locals():
+            m3 = orc.Model(s3, w3_cpu)
+            t = time.perf_counter()
+            orc.draft_block(m3, k3, v3, s3.ctx, di.anchor_token(s3), want_logits=False)
+            dt_ = time.perf_counter() - t
+            other["dense27b_36k"] = {"value": round(1.0 / dt_, 5), "unit": "draft blocks/s",
+                                     "sample": f"1 draft block at C={s3.ctx}, {dt_:.2f}s"}
+            del m3, w3_cpu, k3, v3
+        # prefill fusion + injection of 32768 rows, timed on a 16-row subset and
+        # scaled linearly in rows (each row's fusion and injection is independent)
+        if not args.no_prefill:
+            ps = di.SHAPES["fusion_prefill_32k"]
+            wp_cpu = di.draft_weights(ps, need_draft=False, need_lm=False)
+            mp = orc.Model(ps, wp_cpu)
+            psel = dl.feature_layers(ps.target_layers)
+            rows = 16
+            slabs = [di.target_hidden(ps, l, rows, tag="cpu") for l in psel]
+            t = time.perf_counter()
+            fz = orc.fuse_rows(mp, slabs, range(rows))
+            orc.inject_rows(mp, orc.to_storage(fz, ps.dtype), range(rows), 0)
+            dt_ = time.perf_counter() - t
+            full_s = dt_ * ps.ctx / rows
+            fl = 2.0 * ps.ctx * ps.hidden * (5 * ps.hidden + ps.draft_layers * 2 * ps.n_kv_heads * ps.head_dim)
+            other["fusion_prefill_32k"] = {"value": round(full_s, 1), "unit": "s per 32768-row fuse+inject",
+                                           "tflops": round(fl / full_s / 1e12, 5),
+                                           "sample": f"fuse+inject of {rows} of {ps.ctx} rows in {dt_:.2f}s, "
+                                                     f"scaled by {ps.ctx // rows} (extrapolated, not measured whole)"}
+            del mp, wp_cpu
+        out["cpu_baseline"]["other_configs"] = other
+        log(f"[bench] cpu oracle, other configs: {json.dumps(other)}")
 
     print(json.dumps(out), flush=True)
 

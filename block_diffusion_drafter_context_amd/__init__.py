@@ -90,6 +90,8 @@ def lib():
         L.dflash_inject_kv.argtypes = [vp, vp, i64, i32, i32, vp]
         L.dflash_draft_block.restype = st
         L.dflash_draft_block.argtypes = [vp, vp, vp, vp, vp]
+        L.dflash_draft_block_ex.restype = st
+        L.dflash_draft_block_ex.argtypes = [vp, vp, vp, vp, vp, i64, vp]
         L.dflash_verify_accept.restype = st
         L.dflash_verify_accept.argtypes = [vp, vp, vp, vp, vp]
         L.dflash_rollback.restype = st
@@ -239,15 +241,22 @@ class DFlash:
                                            _stream(stream)), "inject_kv")
 
     def draft_block(self, anchor: torch.Tensor, tokens: Optional[torch.Tensor] = None, want_logits: bool = False,
-                    logits: Optional[torch.Tensor] = None, stream=None):
-        """anchor: device int32[1].  Returns (tokens int32[B], logits fp32[B, V] or None)."""
+                    logits: Optional[torch.Tensor] = None, layers_out: Optional[torch.Tensor] = None, stream=None):
+        """anchor: device int32[1].  Returns (tokens int32[B], logits fp32[B, V] or None).
+        layers_out: optional device tensor [Ld, B, H] (context dtype) that receives
+        the residual stream after every draft layer."""
         B, V = self.shape.block, self.shape.vocab
         if tokens is None:
             tokens = torch.empty(B, dtype=torch.int32, device=self.device)
         if want_logits and logits is None:
             logits = torch.empty(B, V, dtype=torch.float32, device=self.device)
-        self._check(lib().dflash_draft_block(self.h, anchor.data_ptr(), _p(logits), tokens.data_ptr(),
-                                             _stream(stream)), "draft_block")
+        if layers_out is None:
+            st = lib().dflash_draft_block(self.h, anchor.data_ptr(), _p(logits), tokens.data_ptr(), _stream(stream))
+        else:
+            assert layers_out.shape[:2] == (self.shape.draft_layers, B) and layers_out.stride(0) == B * layers_out.stride(1)
+            st = lib().dflash_draft_block_ex(self.h, anchor.data_ptr(), _p(logits), tokens.data_ptr(),
+                                             layers_out.data_ptr(), layers_out.stride(1), _stream(stream))
+        self._check(st, "draft_block")
         return tokens, logits
 
     def verify_accept(self, draft: torch.Tensor, target: torch.Tensor, out: Optional[torch.Tensor] = None,

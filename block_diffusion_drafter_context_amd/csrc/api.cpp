@@ -264,6 +264,11 @@ dflash_status dflash_inject_kv(dflash_ctx* c, const void* fused, int64_t ld, int
 
 dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* anchor, float* logits_out, int32_t* tokens_out,
                                  void* stream) {
+    return dflash_draft_block_ex(c, anchor, logits_out, tokens_out, nullptr, 0, stream);
+}
+
+dflash_status dflash_draft_block_ex(dflash_ctx* c, const int32_t* anchor, float* logits_out, int32_t* tokens_out,
+                                    void* layer_out, int64_t layer_ld, void* stream) {
     if (!c) return DFLASH_ERR_INVAL;
     const DevCtx& x = c->dev;
     if (!anchor || !tokens_out) return fail(c, DFLASH_ERR_INVAL, "null anchor or tokens_out");
@@ -272,9 +277,12 @@ dflash_status dflash_draft_block(dflash_ctx* c, const int32_t* anchor, float* lo
         if (!x.attn_norm[l] || !x.wq[l] || !x.wo[l] || !x.mlp_norm[l] || !x.wg[l] || !x.wu[l] || !x.wd[l])
             return fail(c, DFLASH_ERR_INVAL, "draft needs every layer's weights");
     if (logits_out && !aligned(logits_out, 4)) return fail(c, DFLASH_ERR_INVAL, "logits_out misaligned");
+    if (layer_out && (layer_ld < x.dm.H || !aligned(layer_out, x.dm.elem)))
+        return fail(c, DFLASH_ERR_INVAL, "layer_out misaligned or layer_ld < H");
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
-    hipError_t e = launch_draft_block(x, c->length, anchor, logits_out, tokens_out, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_draft_block(x, c->length, anchor, logits_out, tokens_out, layer_out, layer_ld,
+                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(c, e, "draft launch");
     return DFLASH_OK;
 }
@@ -311,8 +319,13 @@ dflash_status dflash_target_forward(dflash_ctx* c, const int32_t* tokens, int32_
     if (logits_out && !aligned(logits_out, 4)) return fail(c, DFLASH_ERR_INVAL, "logits_out misaligned");
     if (capture) {
         if (capture_ld < d.H) return fail(c, DFLASH_ERR_INVAL, "capture_ld must be >= H");
-        for (int i = 0; i < DFLASH_NUM_FEATURES; ++i)
+        int32_t sel[DFLASH_NUM_FEATURES];
+        feature_layers(d.Lt, sel);
+        for (int i = 0; i < DFLASH_NUM_FEATURES; ++i) {
             if (capture[i] && !aligned(capture[i], d.elem)) return fail(c, DFLASH_ERR_INVAL, "capture buffer misaligned");
+            if (capture[i] && sel[i] >= d.Ld)
+                return fail(c, DFLASH_ERR_INVAL, "capture requested for a layer beyond the context's draft_layers");
+        }
     }
     if ((long long)c->length + M > d.max_ctx) return fail(c, DFLASH_ERR_CAPACITY, "forward would exceed max_ctx");
     dflash_status st = check_device(c);

@@ -66,8 +66,9 @@ hipError_t launch_read_probe(const void* buf, long long bytes, int num_cus, unsi
                              hipStream_t s);
 
 // One draft block over the first C context positions.
+// layer_out: optional [Ld][B][layer_ld] copy of the residual stream after every layer.
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits,
-                              int32_t* tokens, hipStream_t s);
+                              int32_t* tokens, void* layer_out, long long layer_ld, hipStream_t s);
 // Causal forward of M <= 16 tokens at positions C..C+M-1 (K/V appended to the cache).
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits,
                                  int32_t* argmax, void* const* capture, long long capture_ld, hipStream_t s);

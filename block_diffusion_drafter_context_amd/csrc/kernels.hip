@@ -2223,6 +2223,8 @@ struct PassArgs {
     int32_t* tokens;
     void* const* cap;  // causal: 5 capture buffers (feature layers) or null
     long long cap_ld;
+    void* layer_out;   // draft: [Ld][rows][layer_ld] residual after every layer, or null
+    long long layer_ld;
 };
 
 template <typename T>
@@ -2355,22 +2357,23 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         // 32-column slots; else 32-column stream-K tiles, which store their
         // sums (and a completion chain without lazy statistics).  O and down
         // have the same N, so both take the same branch.
-        auto run_resid = [&](const void* w, int K, const T* a, float* ss_out, float* ss_clear, T* cap) {
+        auto run_resid = [&](const void* w, int K, const T* a, float* ss_out, float* ss_clear, T* cap,
+                             long long cap_ld) {
             if (resid_wg) {
                 OpResid<T, 1> op;
                 resid_op(op, w, K, a, ss_out);
                 op.cap = cap;
-                op.cap_ld = pa.cap_ld;
+                op.cap_ld = cap_ld;
                 return run_skinny_wg<T>(c, op, B, K, H / 16, s, ss_clear, ss_n);
             }
             OpResid<T, 2> op;  // 32-column tiles: each stores its sums (no clearing needed)
             resid_op(op, w, K, a, ss_out);
             op.cap = cap;
-            op.cap_ld = pa.cap_ld;
+            op.cap_ld = cap_ld;
             return run_skinny<T>(c, op, B, K, (H + 31) / 32, s);
         };
         c.tracer->begin(DFLASH_TRACE_O_PROJ, s);
-        if ((e = run_resid(c.sw_wo[l], nq * D, obuf, ss0, ss1, nullptr)) != hipSuccess) return e;
+        if ((e = run_resid(c.sw_wo[l], nq * D, obuf, ss0, ss1, nullptr, 0)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_O_PROJ, s);
 
         OpSwiGLU<T> sw;
@@ -2386,11 +2389,16 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         c.tracer->end(DFLASH_TRACE_GATE_UP, s);
 
         T* cap = nullptr;
+        long long cap_ld = pa.cap_ld;
         if (pa.cap)
             for (int i = 0; i < 5; ++i)
                 if (sel[i] == l && pa.cap[i]) cap = (T*)pa.cap[i];  // layer l's output is a captured feature layer
+        if (pa.layer_out) {
+            cap = (T*)pa.layer_out + (long long)l * B * pa.layer_ld;
+            cap_ld = pa.layer_ld;
+        }
         c.tracer->begin(DFLASH_TRACE_DOWN, s);
-        if ((e = run_resid(c.sw_wd[l], F, hbuf, ss1, ss0, cap)) != hipSuccess) return e;
+        if ((e = run_resid(c.sw_wd[l], F, hbuf, ss1, ss0, cap, cap_ld)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_DOWN, s);
     }
 
@@ -2432,8 +2440,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
 }
 
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits, int32_t* tokens,
-                              hipStream_t s) {
-    PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0};
+                              void* layer_out, long long layer_ld, hipStream_t s) {
+    PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0, layer_out, layer_ld};
     c.tracer->begin(DFLASH_TRACE_DRAFT, s);
     hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_DRAFT, s);
@@ -2442,7 +2450,7 @@ hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, flo
 
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits, int32_t* argmax,
                                  void* const* capture, long long capture_ld, hipStream_t s) {
-    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld};
+    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, nullptr, 0};
     c.tracer->begin(DFLASH_TRACE_TARGET, s);
     hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_TARGET, s);

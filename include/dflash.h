@@ -171,6 +171,16 @@ dflash_status dflash_inject_kv(dflash_ctx* ctx, const void* fused, int64_t ld,
 dflash_status dflash_draft_block(dflash_ctx* ctx, const int32_t* anchor, float* logits_out,
                                  int32_t* tokens_out, void* stream);
 
+/* dflash_draft_block, and in the same launches the residual stream after every
+ * draft layer: layer_out (device, [Ld][B][layer_ld] in the context dtype, or
+ * NULL) receives row j of layer l's output at layer_out[(l*B + j)*layer_ld].
+ * An inspection aid: a caller (a test) can feed layer l's input to another
+ * implementation of that one layer.  layer_ld >= H and keeps rows aligned to
+ * the element size (INVAL otherwise); tokens and logits are those of
+ * dflash_draft_block. */
+dflash_status dflash_draft_block_ex(dflash_ctx* ctx, const int32_t* anchor, float* logits_out,
+                                    int32_t* tokens_out, void* layer_out, int64_t layer_ld, void* stream);
+
 /* Greedy block verification ([B] 技术内幕; [A] §1.2, §8.2 linear verification):
  *   k = number of leading j in 1..B-1 with draft[j] == target[j-1],  bonus = target[k].
  * draft: device int32[B] (as written by dflash_draft_block); target: device
@@ -183,7 +193,10 @@ dflash_status dflash_verify_accept(dflash_ctx* ctx, const int32_t* draft, const 
 /* Roll the draft KV cache back to new_len tokens (0 <= new_len <= length, INVAL
  * otherwise): after injecting the B verified rows of a step at C, the caller
  * rolls back to C + k + 1 so only the anchor and the accepted drafts remain
- * as context.  Host metadata only; pages past new_len become free. */
+ * as context.  Host metadata only: positions from new_len on stop being
+ * context and are overwritten by the next injection.  The page table is fixed
+ * at creation (logical page i always maps to the same physical page), so no
+ * page is released or reassigned. */
 dflash_status dflash_rollback(dflash_ctx* ctx, int32_t new_len);
 
 /* Causal forward of the context's decoder stack used as the target (verifier)
@@ -205,7 +218,8 @@ dflash_status dflash_rollback(dflash_ctx* ctx, int32_t new_len);
  *   may be NULL); entry i receives the output rows of target layer
  *   dflash_feature_layers(target_layers)[i] (the residual stream after that
  *   layer), [M, H] with row stride capture_ld elements: the hidden states that
- *   dflash_fuse_context of a draft context takes.
+ *   dflash_fuse_context of a draft context takes.  A non-NULL entry whose layer
+ *   is not below draft_layers (the depth of this context's stack) is INVAL.
  * Requires every layer's weights, final_norm, embed and lm_head (INVAL), and
  * C + M <= max_ctx (CAPACITY; nothing written). */
 dflash_status dflash_target_forward(dflash_ctx* ctx, const int32_t* tokens, int32_t M,

@@ -45,6 +45,8 @@ def lib():
         L = C.CDLL(_LIB)
         vp, i32, i64, dp = C.c_void_p, C.c_int32, C.c_int64, C.POINTER(C.c_double)
         L.orc_set_fp32_accumulation.argtypes = [i32]
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_get_threads.restype = i32
         L.orc_round_bf16.restype = C.c_double
         L.orc_round_bf16.argtypes = [C.c_double]
         L.orc_round_array_bf16.argtypes = [vp, i64, vp]
@@ -118,6 +120,15 @@ class Model:
     @property
     def ref(self):
         return C.byref(self.s)
+
+
+def set_threads(n: int):
+    """OpenMP threads of the oracle's loops (results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
 
 
 def set_fp32_accumulation(on: bool):

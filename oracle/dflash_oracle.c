@@ -24,6 +24,7 @@
 #include "dflash_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -87,6 +88,11 @@ void orc_feature_layers(int32_t L, int32_t out[5])
 {
     for (int i = 0; i < 5; ++i) out[i] = (6 + i * (L - 3)) / 4; /* floor(1 + i(L-3)/4 + 1/2) */
 }
+
+/* OpenMP threads of the parallel loops (results do not depend on it: only
+ * independent outputs are split).  For timing the oracle on fewer cores. */
+void orc_set_threads(int32_t n) { if (n > 0) omp_set_num_threads(n); }
+int32_t orc_get_threads(void) { return omp_get_max_threads(); }
 
 /* Accumulator precision of dot products: fp64 (the oracle's definition) unless
  * the fp32 variant is selected.  The fp32 variant exists only to measure how far

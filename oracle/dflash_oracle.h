@@ -56,6 +56,10 @@ typedef struct {
  * Used only to measure the rounding noise between correct implementations. */
 void orc_set_fp32_accumulation(int32_t on);
 
+/* OpenMP threads of the oracle's parallel loops (results are thread-count independent) */
+void orc_set_threads(int32_t n);
+int32_t orc_get_threads(void);
+
 /* storage rounding */
 double orc_round_bf16(double v);
 double orc_round(double v, int32_t dtype);

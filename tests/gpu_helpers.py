@@ -88,3 +88,43 @@ def assert_tokens(got, ref, gap, logits=None, ref_logits=None, dtype="bf16", noi
             short = float(ref_logits[j].max()) - float(ref_logits[j][got[j]])
             assert short < tol, f"row {j}: gpu token {got[j]} is {short:.3g} below the oracle max"
     return len(mism)
+
+
+def check_layers(orc, model, w, shape, ctx_k, ctx_v, C, anchor, layers, logits, tokens):
+    """Parity at the stated bar, one launch group at a time: each draft layer's
+    GPU input (the embedding rows, then the GPU's own previous layer output)
+    goes through the oracle's one-layer step, and the GPU's output of that layer
+    must be within 2 bf16 ulps of the row maximum (fp32: 1e-4 relative); the
+    GPU's final residual goes through the oracle's LM head, and the GPU logits
+    must be within 2e-2 absolute (fp32: 1e-4 relative), tokens exact except
+    where the oracle's top-2 gap is below 1e-3.  Returns the largest logit
+    difference and the largest per-layer difference in ulps of the row max."""
+    L, B, H = shape.draft_layers, shape.block, shape.hidden
+    gl = layers.float().cpu().numpy().astype(np.float64).reshape(L, B, H)
+    ids = [anchor] + [shape.mask_id] * (B - 1)
+    x_in = w["embed"][ids].double().numpy()
+    worst_ulps = 0.0
+    for l in range(L):
+        kl = ctx_k[l] if C > 0 else None
+        vl = ctx_v[l] if C > 0 else None
+        ref = orc.draft_layer(model, l, kl, vl, C, x_in)
+        if shape.dtype == "bf16":
+            worst_ulps = max(worst_ulps, float((np.abs(gl[l] - ref).max(axis=1)
+                                                / bf16_ulp(np.abs(ref).max(axis=1))).max()))
+        assert_rows_close(gl[l], ref, shape.dtype, f"draft layer {l} given the GPU's input")
+        x_in = gl[l]
+    head = orc.lm_head(model, gl[L - 1])
+    lg = np.asarray(logits, dtype=np.float64)
+    ref_lg = head["logits"].astype(np.float64)
+    if shape.dtype == "fp32":
+        rel = np.abs(lg - ref_lg).max(axis=1) / np.abs(ref_lg).max(axis=1)
+        assert rel.max() <= 1e-4, f"LM head logits relative error {rel.max():.3g}"
+        err = float(rel.max())
+    else:
+        err = float(np.abs(lg - ref_lg).max())
+        assert err <= 2e-2, f"LM head logits absolute error {err:.3g} given the GPU's final residual"
+    tok = np.asarray(tokens)
+    for j in np.flatnonzero(tok != head["tokens"]):
+        assert head["gap"][j] < 1e-3, (f"row {j}: gpu token {tok[j]} vs oracle {head['tokens'][j]} "
+                                       f"(oracle top-2 gap {head['gap'][j]:.3g}) given the GPU's final residual")
+    return err, worst_ulps

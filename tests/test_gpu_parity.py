@@ -6,7 +6,7 @@ import torch
 
 import dflash_inputs as di
 from tests.gpu_helpers import (MID_BF16, MID_BF16_D64, MID_BF16_H352, MID_FP32_G5, assert_logits,
-                               assert_rows_close, assert_tokens, dev)
+                               assert_rows_close, assert_tokens, check_layers, dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,9 +125,12 @@ def _draft_pair(dl, orc, shape, C, anchor, page_seed=3, w=None):
         k, v = di.context_kv(shape, C)
         ctx.load_kv(k.cuda(), v.cuda())
     a = torch.tensor([anchor], dtype=torch.int32, device="cuda")
-    tokens, logits = ctx.draft_block(a, want_logits=True)
+    layers = torch.empty(shape.draft_layers, shape.block, shape.hidden, dtype=shape.torch_dtype, device="cuda")
+    tokens, logits = ctx.draft_block(a, want_logits=True, layers_out=layers)
     sync()
     m = orc.Model(shape, w)
+    # the stated bar layer by layer on identical inputs, then the end-to-end comparison
+    check_layers(orc, m, w, shape, k, v, C, anchor, layers, logits.cpu().numpy(), tokens.cpu().numpy())
     ref = orc.draft_block(m, k, v, C, anchor)
     ref["noise"] = orc.draft_noise_floor(m, k, v, C, anchor, ref["logits"]) if shape.dtype == "bf16" else None
     return tokens.cpu().numpy(), logits.cpu().numpy(), ref, ctx
@@ -168,6 +171,25 @@ def test_draft_lm_head_partial_tile(dl, orc, B):
     t_off, _ = ctx.draft_block(a, want_logits=False)
     sync()
     assert torch.equal(t_off.cpu(), torch.as_tensor(np.asarray(tok)).to(t_off.dtype))
+
+
+def test_layer_capture_changes_nothing(dl):
+    """The per-layer copy is an extra store in the down projection's epilogue:
+    tokens and logits are bit-identical with and without it."""
+    s = MID_BF16
+    ctx = dl.DFlash(s, dev(di.draft_weights(s)), max_ctx=600)
+    k, v = di.context_kv(s, 400)
+    ctx.load_kv(k.cuda(), v.cuda())
+    a = torch.tensor([9], dtype=torch.int32, device="cuda")
+    t1, l1 = ctx.draft_block(a, want_logits=True)
+    t1, l1 = t1.clone(), l1.clone()
+    layers = torch.empty(s.draft_layers, s.block, s.hidden, dtype=s.torch_dtype, device="cuda")
+    t2, l2 = ctx.draft_block(a, want_logits=True, layers_out=layers)
+    sync()
+    assert torch.equal(t1, t2) and torch.equal(l1, l2)
+    st = dl.lib().dflash_draft_block_ex(ctx.h, a.data_ptr(), None, t2.data_ptr(), layers.data_ptr(), s.hidden - 1,
+                                        None)
+    assert st == -1  # layer_ld below H: refused before anything is enqueued
 
 
 def test_draft_deterministic_and_logits_optional(dl, orc):

@@ -167,6 +167,16 @@ def test_target_forward_errors(dl):
     with pytest.raises(dl.DFlashError):           # no fusion weights in a target context
         ctx.fuse_context([torch.zeros(4, s.hidden, device="cuda")] * s.target_layers)
     sync()
+    # a capture of a feature layer the stack does not have is refused, nothing enqueued
+    short = dl.DFlash(s.replace(draft_layers=4), dev(di.toy_target_weights(s)), max_ctx=40)
+    sel = dl.feature_layers(s.target_layers)
+    cap = [torch.empty(2, s.hidden, dtype=s.torch_dtype, device="cuda") if l >= 4 else None for l in sel]
+    with pytest.raises(dl.DFlashError) as e:
+        short.target_forward(t[:2], capture=cap)
+    assert e.value.status == -1 and short.length == 0
+    short.target_forward(t[:2], capture=[c if l < 4 else None for c, l in zip(cap, sel)])
+    sync()
+    assert short.length == 2
 
 
 # ------------------------------------------------------------------ toy end-to-end
