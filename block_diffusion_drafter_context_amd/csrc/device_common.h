@@ -173,6 +173,21 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Wait states after a run of MFMAs, before control flow can branch away.
+// hipcc for gfx950 (ROCm 7.2) pads a read of an MFMA result with the wait
+// states the hardware needs (8 for a 16x16x32 bf16 result read by a VALU or
+// v_accvgpr_read in straight-line code), but on a path that enters a join
+// block through a taken branch it can leave them out when the join block has
+// another predecessor whose path is longer: the read then sees the accumulator
+// from before the MFMA.  16 explicit wait states cover every MFMA used here,
+// so no path leaving the MFMA run depends on the compiler's padding.  (A
+// compile-only reproducer is csrc/repro/mfma_join_hazard.hip.)
+__device__ __forceinline__ void mfma_settle() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7" ::);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float cross4_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 16, 64));
     v = fmaxf(v, __shfl_xor(v, 32, 64));

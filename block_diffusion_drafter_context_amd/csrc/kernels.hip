@@ -218,6 +218,7 @@ __device__ __forceinline__ void skinny_segment(const AL& al, const T* const (&sb
 #pragma unroll
             for (int b = 0; b < NT; ++b) mma(acc[b], a, g.w[b][p]);
         }
+        mfma_settle();
     };
     // sched_barrier(0) keeps the compiler from sinking a group's loads next to
     // their uses (it otherwise trades the overlap for registers)
@@ -424,6 +425,7 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommo
 #pragma unroll
             for (int b = 0; b < NT; ++b) mma(acc[b], a, g.w[b][p]);
         }
+        mfma_settle();
         if (n - ti * gpt == gpt - 1) {  // the tile's last group
             if constexpr (Op::kInLoop) {
                 // all waves finish the tile together, wave wv taking rows
@@ -1116,9 +1118,11 @@ static hipError_t run_skinny_wg(const DevCtx& c, const Op& op, int M, int K, int
     wc.clear_n = clear_n;
     const size_t lds = (size_t)(Op::kInLoop ? 2 : wc.tpw) * W * NT * 64 * sizeof(f32x4_t);
     // The occupancy hint of two workgroups per CU caps the kernel at 256
-    // architectural VGPRs (it needs < 190, no spills).  Built without it, the
-    // compiler also allocated AGPRs and the results were wrong; that build is
-    // not used.
+    // architectural VGPRs (it needs < 190, no spills); it measured at least as
+    // fast as one workgroup per CU, which also allocates AGPRs.  (The AGPR
+    // build once gave wrong results: its accumulator copies were read right
+    // after a taken branch without the MFMA wait states; mfma_settle() now
+    // pads every group.)
     hipLaunchKernelGGL((skinny_wg_kernel<T, Op, W, 2, KP, Op::kWGDepth>), dim3(grid), dim3(64 * W), lds, s, op, wc);
     return hipGetLastError();
 }
