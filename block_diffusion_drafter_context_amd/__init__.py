@@ -86,6 +86,8 @@ def lib():
         L.dflash_length.argtypes = [vp]
         L.dflash_fuse_context.restype = st
         L.dflash_fuse_context.argtypes = [vp, vp, i64, i32, vp, vp]
+        L.dflash_fuse_context_static.restype = st
+        L.dflash_fuse_context_static.argtypes = [vp, vp, i64, i32, vp, vp]
         L.dflash_inject_kv.restype = st
         L.dflash_inject_kv.argtypes = [vp, vp, i64, i32, i32, vp]
         L.dflash_draft_block.restype = st
@@ -233,6 +235,17 @@ class DFlash:
             out = torch.empty(M, self.shape.hidden, dtype=self.dtype, device=self.device)
         arr = (C.c_void_p * len(layer_hidden))(*[_p(t) for t in layer_hidden])
         self._check(lib().dflash_fuse_context(self.h, arr, ld, M, out.data_ptr(), _stream(stream)), "fuse_context")
+        return out
+
+    def fuse_context_static(self, layer_hidden: Sequence[Optional[torch.Tensor]], out: torch.Tensor, stream=None):
+        """fuse_context for M <= 16 rows without context scratch (the library's
+        static per-GPU array); out is caller-allocated [M, H]."""
+        assert len(layer_hidden) == self.cfg.target_layers
+        ref = next(t for t in layer_hidden if t is not None)
+        M, ld = ref.shape[0], ref.stride(0)
+        arr = (C.c_void_p * len(layer_hidden))(*[_p(t) for t in layer_hidden])
+        self._check(lib().dflash_fuse_context_static(self.h, arr, ld, M, out.data_ptr(), _stream(stream)),
+                    "fuse_context_static")
         return out
 
     def inject_kv(self, fused: torch.Tensor, pos0: Optional[int] = None, stream=None):

@@ -118,6 +118,9 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
     Layout L = compute_layout(d, cus);
     if (ws_bytes < L.total || kv_bytes < L.kv_total) return DFLASH_ERR_CAPACITY;
 
+    // the static scratch of dflash_fuse_context_static: its address on this device
+    if (static_scratch_init(dev) != hipSuccess) return DFLASH_ERR_HIP;
+
     dflash_ctx* c = new (std::nothrow) dflash_ctx();
     if (!c) return DFLASH_ERR_CAPACITY;
     c->cfg = *cfg;
@@ -243,6 +246,32 @@ dflash_status dflash_fuse_context(dflash_ctx* c, const void* const* layer_hidden
     if (st != DFLASH_OK) return st;
     hipError_t e = launch_fuse(c->dev, slabs, ld, M, fused_out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(c, e, "fuse launch");
+    return DFLASH_OK;
+}
+
+dflash_status dflash_fuse_context_static(dflash_ctx* c, const void* const* layer_hidden, int64_t ld, int32_t M,
+                                         void* fused_out, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!layer_hidden || !fused_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (!c->dev.fc) return fail(c, DFLASH_ERR_STATE, "context was created without fusion weights");
+    if (M < 1 || M > DFLASH_MAX_BLOCK)
+        return fail(c, DFLASH_ERR_CAPACITY, "M must be in [1, 16]: the static scratch holds one 16-row fusion");
+    if (!static_scratch_fits(c->dev))
+        return fail(c, DFLASH_ERR_UNSUPPORTED, "hidden size or CU count beyond the static scratch");
+    if (ld < d.H || ld % (16 / d.elem)) return fail(c, DFLASH_ERR_INVAL, "ld must be >= H and keep rows 16-byte aligned");
+    int32_t sel[5];
+    feature_layers(d.Lt, sel);
+    const void* slabs[5];
+    for (int i = 0; i < 5; ++i) {
+        slabs[i] = layer_hidden[sel[i]];
+        if (!slabs[i] || !aligned(slabs[i], 16)) return fail(c, DFLASH_ERR_INVAL, "selected layer pointer null or misaligned");
+    }
+    if (!aligned(fused_out, 16)) return fail(c, DFLASH_ERR_INVAL, "fused_out misaligned");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_fuse_static(c->dev, c->device, slabs, ld, M, fused_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "static fuse launch");
     return DFLASH_OK;
 }
 

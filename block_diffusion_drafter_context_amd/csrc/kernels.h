@@ -75,6 +75,14 @@ hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, 
 // Context fusion of M rows (selected slabs given in ascending layer order).
 hipError_t launch_fuse(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out,
                        hipStream_t s);
+// The same for M <= 16 rows with the stream-K scratch in the library's static
+// per-GPU array (static_scratch_init(device) must have run for that device).
+hipError_t launch_fuse_static(const DevCtx& c, int device, const void* const slabs[5], long long ld, int M,
+                              void* out, hipStream_t s);
+// Look up (once per device, with that device current) the static scratch's address.
+hipError_t static_scratch_init(int device);
+// Whether a context's 16-row fusion fits the static scratch.
+bool static_scratch_fits(const DevCtx& c);
 // KV injection of M rows of fused features at positions pos0...
 hipError_t launch_inject(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s);
 // Greedy acceptance.

@@ -36,6 +36,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace dflash {
@@ -1061,8 +1062,17 @@ struct OpInject {
     }
 };
 
+// Where a stream-K launch keeps its partial tiles and tile counters: the
+// context workspace, or the library's static scratch (see fuse_static below).
+struct SkinnyScratch {
+    float* partial;
+    unsigned* tile_cnt;
+    unsigned* done_cnt;
+};
+
 template <typename T, class Op>
-static hipError_t run_skinny(const DevCtx& c, const Op& op, int M, int K, int ntiles, hipStream_t s) {
+static hipError_t run_skinny(const DevCtx& c, const Op& op, int M, int K, int ntiles, hipStream_t s,
+                             const SkinnyScratch* sx = nullptr) {
     SkinnyCommon sc;
     sc.M = M;
     sc.K = K;
@@ -1075,9 +1085,9 @@ static hipError_t run_skinny(const DevCtx& c, const Op& op, int M, int K, int nt
     if (per < kP) per = kP;
     sc.per_wave = (int)per;
     const long long waves = (total + per - 1) / per;
-    sc.partial = reinterpret_cast<float*>(c.ws + c.lay.partial);
-    sc.tile_cnt = reinterpret_cast<unsigned*>(c.ws + c.lay.tile_cnt);
-    sc.done_cnt = reinterpret_cast<unsigned*>(c.ws + c.lay.counters);
+    sc.partial = sx ? sx->partial : reinterpret_cast<float*>(c.ws + c.lay.partial);
+    sc.tile_cnt = sx ? sx->tile_cnt : reinterpret_cast<unsigned*>(c.ws + c.lay.tile_cnt);
+    sc.done_cnt = sx ? sx->done_cnt : reinterpret_cast<unsigned*>(c.ws + c.lay.counters);
     const int grid = (int)((waves + kSkinnyWavesPerWG - 1) / kSkinnyWavesPerWG);
     hipLaunchKernelGGL((skinny_kernel<T, Op>), dim3(grid), dim3(64 * kSkinnyWavesPerWG), 0, s, op, sc);
     return hipGetLastError();
@@ -2462,7 +2472,8 @@ hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, 
 }
 
 template <typename T>
-static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out, hipStream_t s) {
+static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out, hipStream_t s,
+                         const SkinnyScratch* sx = nullptr) {
     const int H = c.dm.H;
     SlabA<T> sa;
     for (int i = 0; i < 5; ++i) sa.slab[i] = (const T*)slabs[i];
@@ -2478,7 +2489,7 @@ static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long 
         op.M = M;
         op.out = (T*)out;
         c.tracer->begin(DFLASH_TRACE_FUSE, s);
-        if ((e = run_skinny<T>(c, op, M, 5 * H, (H + 31) / 32, s)) != hipSuccess) return e;
+        if ((e = run_skinny<T>(c, op, M, 5 * H, (H + 31) / 32, s, sx)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_FUSE, s);
     } else if constexpr (sizeof(T) == 2) {
         auto go = [&](auto op) {
@@ -2512,6 +2523,67 @@ static hipError_t fuse_t(const DevCtx& c, const void* const slabs[5], long long 
 hipError_t launch_fuse(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out, hipStream_t s) {
     if (c.dm.dtype == DFLASH_F32) return fuse_t<float>(c, slabs, ld, M, out, s);
     return fuse_t<bf16_t>(c, slabs, ld, M, out, s);
+}
+
+// ---- allocation-free 16-row fusion -----------------------------------------
+// The stream-K partial tiles ([waves][2][kSkinnyMaxNT][256] fp32, 4 waves per
+// CU, at most 256 CUs: 8 MiB) and the tile counters (at most
+// kStaticScratchTiles) of dflash_fuse_context_static live in this file-scope
+// array, one copy per GPU, held until the process ends.  Host code never uses
+// the array's name as an address: dflash_create looks up each device's copy
+// with hipGetSymbolAddress (with that device current) and the launcher takes
+// that pointer.
+constexpr size_t kStaticScratchPartial = (size_t)256 * kSkinnyWavesPerWG * 2 * kSkinnyMaxNT * 256 * 4;
+constexpr int kStaticScratchTiles = 4096;
+constexpr size_t kStaticScratchBytes = kStaticScratchPartial + (size_t)kStaticScratchTiles * 4 + 256;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxScratchDevices];
+
+hipError_t static_scratch_init(int device) {
+    if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device]) return hipSuccess;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+    return hipSuccess;
+}
+
+bool static_scratch_fits(const DevCtx& c) {
+    return c.lay.nwaves <= 256 * kSkinnyWavesPerWG && (c.dm.H + 31) / 32 <= kStaticScratchTiles;
+}
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(unsigned* p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_fuse_static(const DevCtx& c, int device, const void* const slabs[5], long long ld, int M, void* out,
+                              hipStream_t s) {
+    if (M > 16 || !static_scratch_fits(c)) return hipErrorInvalidValue;
+    char* base = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (device >= 0 && device < kMaxScratchDevices) base = static_cast<char*>(g_scratch_ptr[device]);
+    }
+    if (!base) return hipErrorNotInitialized;
+    SkinnyScratch sx;
+    sx.partial = reinterpret_cast<float*>(base);
+    sx.tile_cnt = reinterpret_cast<unsigned*>(base + kStaticScratchPartial);
+    sx.done_cnt = sx.tile_cnt + kStaticScratchTiles;  // not used by the fusion's epilogue
+    // the counters of the previous call on this GPU are zero after a complete
+    // launch; cleared here (a kernel, so the call can be captured) in case one
+    // was cut short
+    const int ntiles = (c.dm.H + 31) / 32;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((ntiles + 255) / 256), dim3(256), 0, s, sx.tile_cnt, ntiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (c.dm.dtype == DFLASH_F32) return fuse_t<float>(c, slabs, ld, M, out, s, &sx);
+    return fuse_t<bf16_t>(c, slabs, ld, M, out, s, &sx);
 }
 
 template <typename T>

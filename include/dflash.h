@@ -150,6 +150,20 @@ int32_t dflash_length(const dflash_ctx* ctx);
 dflash_status dflash_fuse_context(dflash_ctx* ctx, const void* const* layer_hidden, int64_t ld,
                                   int32_t M, void* fused_out, void* stream);
 
+/* dflash_fuse_context for M <= 16 rows (the per-step fusion of the verified
+ * rows) that allocates nothing and uses no context scratch: for callers that
+ * cannot allocate device memory or change its layout per call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * stream-K partial sums and tile counters live in a static array of
+ * 8 MiB + 16 KiB per GPU inside the library (held until the process ends;
+ * its address is looked up by dflash_create).  Arguments and results are those
+ * of dflash_fuse_context, bit for bit.  CAPACITY if M > 16, UNSUPPORTED if the
+ * context's hidden size needs more than 4096 32-column tiles.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (two streams,
+ * two contexts) race; serialise them. */
+dflash_status dflash_fuse_context_static(dflash_ctx* ctx, const void* const* layer_hidden, int64_t ld,
+                                         int32_t M, void* fused_out, void* stream);
+
 /* KV injection ([A] §2.2 kv_injection, §5.2; [B] KV Injection): for every draft
  * layer l and row i < M,
  *   K_l[pos0+i] = RoPE(W_k^l . fused[i], pos0+i),  V_l[pos0+i] = W_v^l . fused[i]
