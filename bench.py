@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-side fusion/injection GEMM timing")
     ap.add_argument("--no-27b", action="store_true", help="skip the 27B-class draft pass at 36K context")
     ap.add_argument("--no-toy", action="store_true", help="skip the toy end-to-end speculative loop")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the target verify pass at the Qwen3-8B target shape (36 layers)")
     ap.add_argument("--kv-rotate", type=int, default=4,
                     help="independent contexts (KV caches, anchors) the 4K steps rotate through, so the 256 MB "
                          "Infinity Cache cannot hold one context's KV between its steps")
@@ -404,6 +406,62 @@ def main():
                                "draft_pass_hbm_frac_p50": round(ab3 / (pct3[1] * 1e-6) / HBM_PEAK, 4)}
         log(f"[bench] 27B-class @36K: {json.dumps(out['dense27b_36k'])}")
         del ctx3, w3
+        torch.cuda.empty_cache()
+
+    # ---- the verify side at the Qwen3-8B target shape: a causal forward of 16
+    # rows through 36 layers over a 4096-token paged target cache (random
+    # device-side weights and cache: an HBM-bound pass, values do not matter)
+    if not args.no_verify:
+        if "ctx" in locals():
+            del ctx
+        ctxs.clear()
+        torch.cuda.empty_cache()
+        import ctypes as C_
+        sv = s.replace(name="qwen3_8b_target", draft_layers=36)
+        Lv, Cv = sv.draft_layers, s.ctx
+        gen = torch.Generator(device="cuda").manual_seed(sv.seed)
+        t0 = time.time()
+
+        def rnd(*shape, std=sv.w_std):
+            return (torch.randn(*shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+        H_, nq_, nkv_, d_, F_ = sv.hidden, sv.n_q_heads, sv.n_kv_heads, sv.head_dim, sv.ffn
+        wv = {"final_norm": torch.ones(H_, dtype=torch.bfloat16, device="cuda"),
+              "embed": rnd(sv.vocab, H_), "lm_head": rnd(sv.vocab, H_)}
+        for l in range(Lv):
+            wv[f"attn_norm.{l}"] = torch.ones(H_, dtype=torch.bfloat16, device="cuda")
+            wv[f"mlp_norm.{l}"] = torch.ones(H_, dtype=torch.bfloat16, device="cuda")
+            wv[f"wq.{l}"], wv[f"wk.{l}"], wv[f"wv.{l}"] = rnd(nq_ * d_, H_), rnd(nkv_ * d_, H_), rnd(nkv_ * d_, H_)
+            wv[f"wo.{l}"], wv[f"wg.{l}"], wv[f"wu.{l}"], wv[f"wd.{l}"] = rnd(H_, nq_ * d_), rnd(F_, H_), rnd(F_, H_), rnd(H_, F_)
+        ctxv = dl.DFlash(sv, wv, max_ctx=Cv + 64)
+        kv_std = sv.w_std * float(np.sqrt(H_))
+        ctxv.load_kv(rnd(Lv, Cv, nkv_, d_, std=kv_std), rnd(Lv, Cv, nkv_, d_, std=kv_std))
+        vt = torch.randint(0, sv.vocab, (16,), generator=gen, device="cuda", dtype=torch.int64).to(torch.int32)
+        va = torch.empty(16, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        log(f"[bench] 8B-shape target (36 layers) with {Cv} cached tokens ready in {time.time() - t0:.1f}s")
+        for _ in range(args.warmup):
+            ctxv.target_forward(vt, argmax=va)
+            ctxv.rollback(Cv)
+        torch.cuda.synchronize()
+        nv = max(20, args.steps // 4)
+        assert dl.lib().dflash_trace_enable(ctxv.h, 10, nv) == 0
+        for _ in range(nv):
+            ctxv.target_forward(vt, argmax=va)
+            ctxv.rollback(Cv)
+        buf = (C_.c_float * nv)()
+        cnt = C_.c_int32()
+        assert dl.lib().dflash_trace_read_each(ctxv.h, buf, nv, C_.byref(cnt)) == 0
+        dl.lib().dflash_trace_enable(ctxv.h, 0, 0)
+        vus = np.array(buf[:cnt.value], dtype=np.float64) * 1e3
+        layer_w = (H_ * nq_ * d_ + 2 * H_ * nkv_ * d_ + nq_ * d_ * H_ + 3 * H_ * F_) * 2
+        vbytes = Lv * layer_w + sv.vocab * H_ * 2 + Lv * Cv * 2 * nkv_ * d_ * 2 + Lv * 16 * 2 * nkv_ * d_ * 2
+        pv = [round(float(np.percentile(vus, q)), 1) for q in (10, 50, 90)]
+        out["target_verify"] = {"workload": "qwen3_8b target, 36 layers, 16 rows over 4096 cached tokens",
+                                "us_p10_p50_p90": pv, "alg_bytes_per_pass": vbytes,
+                                "hbm_frac_p50": round(vbytes / (pv[1] * 1e-6) / HBM_PEAK, 4),
+                                "verified_rows_per_s": round(16e6 / pv[1], 1)}
+        log(f"[bench] target verify: {json.dumps(out['target_verify'])}")
+        del ctxv, wv
         torch.cuda.empty_cache()
 
     # ---- toy end-to-end greedy speculative loop against plain greedy decoding

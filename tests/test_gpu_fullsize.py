@@ -129,3 +129,55 @@ def test_prefill_fuse_inject_32k_sampled(dl, orc):
         gk, gv = ctx.read_kv(r, 1)
         assert_rows_close(gk.float().cpu().numpy().reshape(L, -1), rk[:, i], s.dtype, f"K pos {r}")
         assert_rows_close(gv.float().cpu().numpy().reshape(L, -1), rv[:, i], s.dtype, f"V pos {r}")
+
+
+@pytest.mark.timeout(1500)
+def test_qwen3_8b_target_verify_4k(dl, orc):
+    """The verify side of a step at the Qwen3-8B target shape ([A] §1.2
+    parallel verification; [B] 技术内幕): a causal forward of 16 rows through 36
+    target layers (hidden 4096, 32/8 heads x 128, FFN 12288, vocab 151936)
+    over a 4096-token paged target KV cache of seeded values, capturing the
+    five feature layers the draft fuses.  The oracle's dense cache holds the
+    same bytes (no oracle prefill).  Logits, tokens and captured layers are
+    compared with the oracle's causal forward under the bf16 band that its
+    own fp32-vs-fp64 drift sets over 36 layers."""
+    from tests.gpu_helpers import bf16_logit_tol, drift_ulps
+    s = di.SHAPES["qwen3_8b_4k"].replace(name="qwen3_8b_target", draft_layers=36)
+    C, M = 4096, 16
+    w = di.toy_target_weights(s)
+    ctx = dl.DFlash(s, dev(w), max_ctx=C + 64, page_seed=23)
+    k, v = di.context_kv(s, C, tag="target_kv")
+    ctx.load_kv(k.cuda(), v.cuda())
+    toks = di.uniform_int(M, 0, s.vocab, s.seed, "verify_rows")
+    sel = orc.feature_layers(s.target_layers)
+    cap = [torch.empty(M, s.hidden, dtype=s.torch_dtype, device="cuda") for _ in range(5)]
+    am, lg = ctx.target_forward(toks.cuda(), want_logits=True, capture=cap)
+    torch.cuda.synchronize()
+    assert ctx.length == C + M
+    print(f"[fullsize] target verify 36 layers, C={C}, {M} rows: gpu done", flush=True)
+    m = orc.Model(s, w, n_layers=36)
+    NK = s.n_kv_heads * s.head_dim
+
+    def run_oracle():
+        cache = orc.TargetCache(m, C + M)
+        cache.k[:, :C] = k.reshape(36, C, NK).double().numpy()
+        cache.v[:, :C] = v.reshape(36, C, NK).double().numpy()
+        return orc.target_forward(m, cache, toks.numpy(), C, capture=sel, want_logits=True)
+
+    ref = run_oracle()
+    orc.set_fp32_accumulation(True)
+    try:
+        alt = run_oracle()
+    finally:
+        orc.set_fp32_accumulation(False)
+    noise = float(np.abs(alt["logits"].astype(np.float64) - ref["logits"].astype(np.float64)).max())
+    lg = lg.cpu().numpy()
+    err = float(np.abs(lg - ref["logits"]).max())
+    print(f"[fullsize] target verify: max|dlogit| {err:.3g}, oracle fp32-vs-fp64 drift {noise:.3g}", flush=True)
+    assert_logits(lg, ref["logits"], s.dtype, noise)
+    n_ex = assert_tokens(am.cpu().numpy(), ref["argmax"], ref["gap"], lg, ref["logits"], s.dtype, noise)
+    print(f"[fullsize] target verify: exempt near-tie token mismatches {n_ex}/{M}", flush=True)
+    for i in range(5):
+        ulps = drift_ulps(alt["hidden"][i], ref["hidden"][i])
+        assert_rows_close(cap[i].float().cpu().numpy(), ref["hidden"][i], s.dtype, f"captured layer {sel[i]}",
+                          ulps=max(2.0, 2.0 * ulps))
