@@ -158,58 +158,56 @@ def main():
     keep = torch.tensor([1] * (B - 1) + [0], dtype=torch.int32, device="cuda")
     add = torch.tensor([0 if float(u[j]) < di.SYNTH_AGREE_P else int(r[j]) for j in range(1, B)] + [last],
                        dtype=torch.int32, device="cuda")
-    g_buf = torch.empty(B, dtype=torch.int32, device="cuda")
 
-    def synthetic_target(tokens):
+    def synthetic_target(tokens, g_buf):
         torch.index_select(tokens, 0, sel_idx, out=g_buf)
         g_buf.mul_(keep).add_(add)
         return g_buf.remainder_(s.vocab)
-    fused_buf = torch.empty(16, s.hidden, dtype=s.torch_dtype, device="cuda")
-    tok_buf = torch.empty(s.block, dtype=torch.int32, device="cuda")
-    res_buf = torch.empty(2, dtype=torch.int32, device="cuda")
-    res_host = torch.empty(2, dtype=torch.int32).pin_memory()
 
     def make_step(ctx, C0):
+        """One device-resident step on ctx (its length lives on the device):
+        draft -> synthetic target -> accept -> fuse the 16 verified rows ->
+        inject them at the length -> keep the anchor and the k accepted rows ->
+        back to C0 (every step sees the same context) -> the bonus token is the
+        next anchor.  No host read anywhere, so steps are enqueued back to back
+        and the step can be captured in a HIP graph (static buffers)."""
         anchor = torch.tensor([di.anchor_token(s)], dtype=torch.int32, device="cuda")
-        stats = {"k": 0, "n": 0}
+        tok = torch.empty(B, dtype=torch.int32, device="cuda")
+        g = torch.empty(B, dtype=torch.int32, device="cuda")
+        res = torch.empty(2, dtype=torch.int32, device="cuda")
+        fused = torch.empty(16, s.hidden, dtype=s.torch_dtype, device="cuda")
 
         def step():
-            tokens, _ = ctx.draft_block(anchor, tokens=tok_buf)
-            g = synthetic_target(tokens)
-            ctx.verify_accept(tokens, g, out=res_buf)
-            fused = ctx.fuse_context(step_hidden, out=fused_buf)
-            ctx.inject_kv(fused, C0)
-            res_host.copy_(res_buf, non_blocking=True)
-            torch.cuda.current_stream().synchronize()
-            k = int(res_host[0])
-            ctx.rollback(C0 + k + 1)
-            ctx.rollback(C0)
-            anchor.copy_(res_buf[1:2])
-            stats["k"] += k
-            stats["n"] += 1
+            ctx.draft_block(anchor, tokens=tok)
+            synthetic_target(tok, g)
+            ctx.verify_accept(tok, g, out=res)
+            ctx.fuse_context(step_hidden, out=fused)
+            ctx.inject_kv(fused, -1)
+            ctx.keep_accepted(res)
+            ctx.set_length_async(C0)
+            anchor.copy_(res[1:2])
 
-        return step, stats
+        step.res = res
+        return step
 
     def timed(ctxs, C0, steps, warmup, trace_cls=None):
-        """Steps rotate through the contexts in ctxs (a list, or one context)."""
+        """Eager device-resident steps rotating through the contexts in ctxs
+        (a list, or one context); no host synchronisation inside the loop."""
         if not isinstance(ctxs, list):
             ctxs = [ctxs]
         made = [make_step(c, C0) for c in ctxs]
         for i in range(warmup):
-            made[i % len(made)][0]()
+            made[i % len(made)]()
         torch.cuda.synchronize()
         if trace_cls is not None:
             for c in ctxs:
                 st = dl.lib().dflash_trace_enable(c.h, trace_cls, steps * 8)
                 assert st == 0
-        for _, st_ in made:
-            st_["k"] = st_["n"] = 0
         t = time.perf_counter()
         for i in range(steps):
-            made[i % len(made)][0]()
+            made[i % len(made)]()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t
-        stats = {"k": sum(m[1]["k"] for m in made), "n": sum(m[1]["n"] for m in made)}
         trace = None
         if trace_cls is not None:
             import ctypes as C_
@@ -221,14 +219,50 @@ def main():
                 tot_n += n.value
                 dl.lib().dflash_trace_enable(c.h, 0, 0)
             trace = (tot_ms, tot_n)
-        return dt, stats, trace
+        return dt, trace
+
+    def accept_stats(ctxs, C0, n=32):
+        """Mean accepted k over n steps (host reads after each step; untimed)."""
+        made = [make_step(c, C0) for c in ctxs]
+        ks = []
+        for i in range(n):
+            m = made[i % len(made)]
+            m()
+            ks.append(int(m.res[0].item()))
+        return float(np.mean(ks))
+
+    def graph_timed(ctxs, C0, steps, warmup):
+        """The same step captured once per context in a HIP graph and replayed."""
+        made = [make_step(c, C0) for c in ctxs]
+        for m in made:  # every kernel loaded before capture
+            m()
+        torch.cuda.synchronize()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for m in made:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cs):
+                m()
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
 
     # ---- headline: context C, LM head traced live over the timed region
     t0 = time.time()
     ctxs = [prepare(C, f"ctx{i}" if i else "ctx") for i in range(max(args.kv_rotate, 1))]
+    for c_ in ctxs:
+        c_.enable_device_length()
     ctx = ctxs[0]
     log(f"[bench] {len(ctxs)} contexts, prefill fuse+inject of {C} rows each, done in {time.time() - t0:.1f}s")
-    dt, stats, tr = timed(ctxs, C, args.steps, args.warmup, trace_cls=1)
+    dt, tr = timed(ctxs, C, args.steps, args.warmup, trace_cls=1)
     ab = alg_bytes(s, C)
     bps = args.steps / dt
     lm_ms = tr[0] / max(tr[1], 1)
@@ -251,12 +285,13 @@ def main():
         "config": {"workload": args.workload, "hidden": s.hidden, "target_layers": s.target_layers,
                    "draft_layers": s.draft_layers, "heads": f"{s.n_q_heads}/{s.n_kv_heads}x{s.head_dim}",
                    "ffn": s.ffn, "vocab": s.vocab, "ctx": C, "block": s.block,
-                   "step": "draft_block+verify_accept+fuse(16)+inject(16)+rollback",
+                   "step": "device-resident: draft_block+synthetic target+verify_accept+fuse(16)+inject(16)"
+                           "+keep_accepted+rewind, no host read",
                    "kv_contexts_rotated": len(ctxs)},
         "drafted_tok_per_s": round(15 * bps, 1),
         "hbm_frac_step": round(ab["step"] * bps / HBM_PEAK, 4),
         "alg_bytes_per_step": ab["step"],
-        "mean_accept_k": stats["k"] / max(stats["n"], 1),
+        "mean_accept_k": None,
         "roofline": {"bound": "hbm", "kernel": "skinny_wg_kernel<OpLMHeadWG> (LM head + argmax)",
                      "achieved": round(lm_ach / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(lm_ach / HBM_PEAK, 4), "traffic": profiled_traffic(args.workload),
@@ -278,7 +313,7 @@ def main():
         import ctypes as C_
         if not isinstance(ctxs_, list):
             ctxs_ = [ctxs_]
-        made = [make_step(c, C0)[0] for c in ctxs_]
+        made = [make_step(c, C0) for c in ctxs_]
         for c in ctxs_:
             assert dl.lib().dflash_trace_enable(c.h, 7, n) == 0
         for i in range(n):
@@ -301,6 +336,12 @@ def main():
     out["draft_pass_block_positions_per_s"] = round(16e6 / p50, 1)
     out["draft_pass_hbm_frac_p50"] = round(alg_bytes(s, C)["draft"] / (p50 * 1e-6) / HBM_PEAK, 4)
     log(f"[bench] draft pass p10/p50/p90 {out['draft_pass_us_p10_p50_p90']} us")
+    out["mean_accept_k"] = round(accept_stats(ctxs, C), 4)
+    # the same step captured in a HIP graph per context and replayed
+    dtg = graph_timed(ctxs, C, args.steps, args.warmup)
+    out["graph_step"] = {"blocks_per_s": round(args.steps / dtg, 2), "us_per_step": round(dtg / args.steps * 1e6, 1),
+                         "hbm_frac_step": round(ab["step"] * args.steps / dtg / HBM_PEAK, 4)}
+    log(f"[bench] graph-replayed step: {json.dumps(out['graph_step'])}")
 
     # ---- the chip's practical streaming-read rate, next to the 8 TB/s spec
     probe_buf = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
@@ -334,7 +375,7 @@ def main():
                      "inject16": (9, ab["inject16"])}
         bd = {}
         for name, (cls, byts) in per_layer.items():
-            _, _, tr2 = timed(ctxs, C, 32, 4, trace_cls=cls)
+            _, tr2 = timed(ctxs, C, 32, 4, trace_cls=cls)
             us = tr2[0] / max(tr2[1], 1) * 1e3
             bd[name] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1)}
         out["breakdown_ctx"] = bd
@@ -347,8 +388,9 @@ def main():
         torch.cuda.empty_cache()
         t0 = time.time()
         ctx2 = prepare(args.long_ctx, "long")
+        ctx2.enable_device_length()
         log(f"[bench] prefill of {args.long_ctx} rows done in {time.time() - t0:.1f}s")
-        dt2, _, tr2 = timed(ctx2, args.long_ctx, args.steps, args.warmup, trace_cls=7)
+        dt2, tr2 = timed(ctx2, args.long_ctx, args.steps, args.warmup, trace_cls=7)
         ab2 = alg_bytes(s, args.long_ctx)
         bps2 = args.steps / dt2
         dr_us = tr2[0] / max(tr2[1], 1) * 1e3

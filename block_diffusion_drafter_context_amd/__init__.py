@@ -96,6 +96,14 @@ def lib():
         L.dflash_draft_block_ex.argtypes = [vp, vp, vp, vp, vp, i64, vp]
         L.dflash_verify_accept.restype = st
         L.dflash_verify_accept.argtypes = [vp, vp, vp, vp, vp]
+        L.dflash_device_length_enable.restype = st
+        L.dflash_device_length_enable.argtypes = [vp, vp]
+        L.dflash_keep_accepted.restype = st
+        L.dflash_keep_accepted.argtypes = [vp, vp, vp]
+        L.dflash_set_length_async.restype = st
+        L.dflash_set_length_async.argtypes = [vp, i32, vp]
+        L.dflash_read_device_length.restype = st
+        L.dflash_read_device_length.argtypes = [vp, vp, vp]
         L.dflash_rollback.restype = st
         L.dflash_rollback.argtypes = [vp, i32]
         L.dflash_load_kv.restype = st
@@ -249,6 +257,7 @@ class DFlash:
         return out
 
     def inject_kv(self, fused: torch.Tensor, pos0: Optional[int] = None, stream=None):
+        """pos0: the current length (default); -1 with the device-resident length."""
         pos0 = self.length if pos0 is None else pos0
         self._check(lib().dflash_inject_kv(self.h, fused.data_ptr(), fused.stride(0), fused.shape[0], pos0,
                                            _stream(stream)), "inject_kv")
@@ -301,6 +310,24 @@ class DFlash:
         self._check(lib().dflash_target_forward(self.h, tokens.data_ptr(), M, _p(logits), argmax.data_ptr(), cap, ld,
                                                 _stream(stream)), "target_forward")
         return argmax, logits
+
+    # ---- device-resident length (a step without host round trips; capturable)
+    def enable_device_length(self, stream=None):
+        self._check(lib().dflash_device_length_enable(self.h, _stream(stream)), "device_length_enable")
+
+    def keep_accepted(self, result: torch.Tensor, stream=None):
+        """length += result[0] + 1 on the device (result: a verify_accept output)."""
+        self._check(lib().dflash_keep_accepted(self.h, result.data_ptr(), _stream(stream)), "keep_accepted")
+
+    def set_length_async(self, new_len: int, stream=None):
+        self._check(lib().dflash_set_length_async(self.h, new_len, _stream(stream)), "set_length_async")
+
+    def read_device_length(self, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """Device int32[2]: {length, capacity-error flag}."""
+        if out is None:
+            out = torch.empty(2, dtype=torch.int32, device=self.device)
+        self._check(lib().dflash_read_device_length(self.h, out.data_ptr(), _stream(stream)), "read_device_length")
+        return out
 
     def rollback(self, new_len: int):
         self._check(lib().dflash_rollback(self.h, new_len), "rollback")

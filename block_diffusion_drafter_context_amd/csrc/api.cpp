@@ -22,6 +22,7 @@ struct dflash_ctx {
     std::vector<hipEvent_t> events;
     dflash_config cfg;
     int32_t length = 0;
+    bool dev_len = false;  // the length lives in the workspace's device word (host length unused)
     int device = 0;
     std::string err;
 };
@@ -224,7 +225,55 @@ dflash_status dflash_destroy(dflash_ctx* c) {
     return DFLASH_OK;
 }
 
-int32_t dflash_length(const dflash_ctx* c) { return c ? c->length : -1; }
+int32_t dflash_length(const dflash_ctx* c) { return c && !c->dev_len ? c->length : -1; }
+
+static int* len_word(dflash_ctx* c) { return reinterpret_cast<int*>(c->dev.ws + c->dev.lay.len_dev); }
+
+dflash_status dflash_device_length_enable(dflash_ctx* c, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (c->dev_len) return fail(c, DFLASH_ERR_STATE, "the length already lives on the device");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_len_set(len_word(c), c->length, s);
+    if (e == hipSuccess) e = launch_len_set(len_word(c) + 1, 0, s);  // capacity-error flag
+    if (e != hipSuccess) return hip_fail(c, e, "length word");
+    c->dev_len = true;
+    return DFLASH_OK;
+}
+
+dflash_status dflash_keep_accepted(dflash_ctx* c, const int32_t* result, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (!c->dev_len) return fail(c, DFLASH_ERR_STATE, "needs the device-resident length");
+    if (!result) return fail(c, DFLASH_ERR_INVAL, "null result");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_len_keep(len_word(c), result, c->dev.dm.max_ctx, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "keep accepted");
+    return DFLASH_OK;
+}
+
+dflash_status dflash_set_length_async(dflash_ctx* c, int32_t new_len, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (!c->dev_len) return fail(c, DFLASH_ERR_STATE, "needs the device-resident length");
+    if (new_len < 0 || new_len > c->dev.dm.max_ctx) return fail(c, DFLASH_ERR_INVAL, "new_len must be in [0, max_ctx]");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_len_set(len_word(c), new_len, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "set length");
+    return DFLASH_OK;
+}
+
+dflash_status dflash_read_device_length(dflash_ctx* c, int32_t* out, void* stream) {
+    if (!c || !out) return DFLASH_ERR_INVAL;
+    if (!c->dev_len) return fail(c, DFLASH_ERR_STATE, "needs the device-resident length");
+    if (!aligned(out, 4)) return fail(c, DFLASH_ERR_INVAL, "out misaligned");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipError_t e = launch_len_read(len_word(c), out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "read length");
+    return DFLASH_OK;
+}
 
 dflash_status dflash_fuse_context(dflash_ctx* c, const void* const* layer_hidden, int64_t ld, int32_t M,
                                   void* fused_out, void* stream) {
@@ -280,6 +329,17 @@ dflash_status dflash_inject_kv(dflash_ctx* c, const void* fused, int64_t ld, int
     const Dims& d = c->dev.dm;
     if (!fused || !aligned(fused, 16)) return fail(c, DFLASH_ERR_INVAL, "fused null or misaligned");
     if (ld < d.H || ld % (16 / d.elem)) return fail(c, DFLASH_ERR_INVAL, "ld must be >= H and keep rows 16-byte aligned");
+    if (c->dev_len) {  // rows go to the device length; the length itself is unchanged
+        if (pos0 != -1) return fail(c, DFLASH_ERR_INVAL, "with the device-resident length pos0 must be -1");
+        if (M < 1 || M > DFLASH_MAX_BLOCK || M > d.max_rows)
+            return fail(c, DFLASH_ERR_CAPACITY, "with the device-resident length M must be in [1, 16]");
+        dflash_status st = check_device(c);
+        if (st != DFLASH_OK) return st;
+        hipError_t e = launch_inject(c->dev, fused, ld, M, 0, static_cast<hipStream_t>(stream), len_word(c),
+                                     len_word(c) + 1);
+        if (e != hipSuccess) return hip_fail(c, e, "inject launch");
+        return DFLASH_OK;
+    }
     if (M < 1 || M > d.max_rows) return fail(c, DFLASH_ERR_CAPACITY, "M must be in [1, max_rows]");
     if (pos0 != c->length) return fail(c, DFLASH_ERR_STATE, "pos0 must equal the current length");
     if ((long long)pos0 + M > d.max_ctx) return fail(c, DFLASH_ERR_CAPACITY, "injection would exceed max_ctx");
@@ -311,7 +371,7 @@ dflash_status dflash_draft_block_ex(dflash_ctx* c, const int32_t* anchor, float*
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
     hipError_t e = launch_draft_block(x, c->length, anchor, logits_out, tokens_out, layer_out, layer_ld,
-                                      static_cast<hipStream_t>(stream));
+                                      c->dev_len ? len_word(c) : nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(c, e, "draft launch");
     return DFLASH_OK;
 }
@@ -329,6 +389,7 @@ dflash_status dflash_verify_accept(dflash_ctx* c, const int32_t* draft, const in
 
 dflash_status dflash_rollback(dflash_ctx* c, int32_t new_len) {
     if (!c) return DFLASH_ERR_INVAL;
+    if (c->dev_len) return fail(c, DFLASH_ERR_STATE, "the length lives on the device: use dflash_set_length_async");
     if (new_len < 0 || new_len > c->length) return fail(c, DFLASH_ERR_INVAL, "new_len must be in [0, length]");
     c->length = new_len;
     return DFLASH_OK;
@@ -337,6 +398,7 @@ dflash_status dflash_rollback(dflash_ctx* c, int32_t new_len) {
 dflash_status dflash_target_forward(dflash_ctx* c, const int32_t* tokens, int32_t M, float* logits_out,
                                     int32_t* argmax_out, void* const* capture, int64_t capture_ld, void* stream) {
     if (!c) return DFLASH_ERR_INVAL;
+    if (c->dev_len) return fail(c, DFLASH_ERR_STATE, "not available with the device-resident length");
     const DevCtx& x = c->dev;
     const Dims& d = x.dm;
     if (!tokens || !argmax_out) return fail(c, DFLASH_ERR_INVAL, "null tokens or argmax_out");
@@ -368,6 +430,7 @@ dflash_status dflash_target_forward(dflash_ctx* c, const int32_t* tokens, int32_
 
 dflash_status dflash_load_kv(dflash_ctx* c, const void* k, const void* v, int32_t M, int32_t pos0, void* stream) {
     if (!c) return DFLASH_ERR_INVAL;
+    if (c->dev_len) return fail(c, DFLASH_ERR_STATE, "not available with the device-resident length");
     const Dims& d = c->dev.dm;
     if (!k || !v) return fail(c, DFLASH_ERR_INVAL, "null pointer");
     if (M < 1) return fail(c, DFLASH_ERR_INVAL, "M must be >= 1");
@@ -385,7 +448,8 @@ dflash_status dflash_load_kv(dflash_ctx* c, const void* k, const void* v, int32_
 dflash_status dflash_read_kv(dflash_ctx* c, int32_t pos0, int32_t M, void* k_out, void* v_out, void* stream) {
     if (!c) return DFLASH_ERR_INVAL;
     if (!k_out || !v_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
-    if (M < 1 || pos0 < 0 || (long long)pos0 + M > c->length)
+    const long long lim = c->dev_len ? c->dev.dm.max_ctx : c->length;  // device length: the capacity bounds it
+    if (M < 1 || pos0 < 0 || (long long)pos0 + M > lim)
         return fail(c, DFLASH_ERR_INVAL, "range must lie inside [0, length)");
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;

@@ -112,6 +112,7 @@ Layout compute_layout(const Dims& d, int num_cus) {
     const size_t parts = (size_t)(kMaxSplits + 1) * d.nq * 16;
     L.attn_o = take(parts * d.d * 4);
     L.attn_ml = take(parts * 2 * 4);
+    L.len_dev = take(2 * 4);
     const int e = d.elem;
     for (int l = 0; l < d.Ld; ++l) {
         L.sw_wq[l] = take(swizzled_bytes(nqd, d.H, e));

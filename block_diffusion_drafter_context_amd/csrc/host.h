@@ -51,6 +51,7 @@ struct Layout {
     size_t x, q, kblk, vblkT, obuf, hbuf;
     size_t rstd, ss_part, partial, tile_cnt, counters, best;
     size_t attn_o, attn_ml;
+    size_t len_dev;       // device-resident length: {length, capacity-error flag}
     size_t total;
     size_t kv_total;      // bytes of the KV pool
     size_t kv_layer_kv;   // bytes of one (layer, K-or-V) page array

@@ -67,8 +67,10 @@ hipError_t launch_read_probe(const void* buf, long long bytes, int num_cus, unsi
 
 // One draft block over the first C context positions.
 // layer_out: optional [Ld][B][layer_ld] copy of the residual stream after every layer.
+// len_dev: non-null when the context length lives on the device (C unused).
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits,
-                              int32_t* tokens, void* layer_out, long long layer_ld, hipStream_t s);
+                              int32_t* tokens, void* layer_out, long long layer_ld, const int* len_dev,
+                              hipStream_t s);
 // Causal forward of M <= 16 tokens at positions C..C+M-1 (K/V appended to the cache).
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits,
                                  int32_t* argmax, void* const* capture, long long capture_ld, hipStream_t s);
@@ -84,7 +86,13 @@ hipError_t static_scratch_init(int device);
 // Whether a context's 16-row fusion fits the static scratch.
 bool static_scratch_fits(const DevCtx& c);
 // KV injection of M rows of fused features at positions pos0...
-hipError_t launch_inject(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s);
+// len_dev non-null: rows go to *len_dev.. (M <= 16; err is set when they do not fit).
+hipError_t launch_inject(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s,
+                         const int* len_dev = nullptr, int* err = nullptr);
+// Device-resident length word: set, add k + 1 from an accept result {k, bonus}, copy {length, error} out.
+hipError_t launch_len_set(int* len, int value, hipStream_t s);
+hipError_t launch_len_keep(int* len, const int32_t* result, int max_ctx, hipStream_t s);
+hipError_t launch_len_read(const int* len, int32_t* out, hipStream_t s);
 // Greedy acceptance.
 hipError_t launch_accept(const DevCtx& c, const int32_t* draft, const int32_t* target, int32_t* out,
                          hipStream_t s);

@@ -565,9 +565,12 @@ struct OpQKV {
     static constexpr int kWGDepth = 2;  // load groups in flight
     struct State {
         float cs[4], sn[4];  // rotary cos/sin of the lane's rows, loaded ahead of the exchange
+        int pos0;            // position of row 0
     };
     static constexpr bool kDoneHook = false;
     NormA<T> a;
+    const int* len_dev = nullptr;  // device-resident length: row 0 sits at *len_dev (else at pos0)
+    int max_ctx = 0;               // the device length is clamped into [0, max_ctx] (rotary table bound)
     const T* wq;
     const T* wk;
     const T* wv;
@@ -594,7 +597,9 @@ struct OpQKV {
         const T* W = kind == 0 ? wq : (kind == 1 ? wk : wv);
         return sw_stream(W, (h * d + 16 * i + blk * (d / 2)) / 16, nch);
     }
-    __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void wave_begin(State& st) const {
+        st.pos0 = len_dev ? min(max(*len_dev, 0), max_ctx) : pos0;
+    }
     __device__ __forceinline__ void prefetch(int tile, int lane, State& st) const {
         int kind, h, i;
         decode(tile, kind, h, i);
@@ -602,7 +607,7 @@ struct OpQKV {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int j = min(4 * (lane >> 4) + ii, M - 1);
-            const long long t = (long long)(pos0 + j) * half + dim;
+            const long long t = (long long)(st.pos0 + j) * half + dim;
             st.cs[ii] = cosT[t];
             st.sn[ii] = sinT[t];
         }
@@ -631,11 +636,11 @@ struct OpQKV {
             } else if (!kout) {
                 int slot;
                 if (kind == 1) {
-                    T* pg = kv.kpage<T>(layer, pos0 + j, slot) + ((long long)h * kv.page + slot) * d;
+                    T* pg = kv.kpage<T>(layer, st.pos0 + j, slot) + ((long long)h * kv.page + slot) * d;
                     pg[dim] = Elem<T>::from_f32(x0);
                     pg[dim + half] = Elem<T>::from_f32(x1);
                 } else {
-                    T* pg = kv.vpage<T>(layer, pos0 + j, slot) + (long long)h * d * kv.page;
+                    T* pg = kv.vpage<T>(layer, st.pos0 + j, slot) + (long long)h * d * kv.page;
                     pg[(long long)dim * kv.page + vslot(slot)] = Elem<T>::from_f32(x0);
                     pg[(long long)(dim + half) * kv.page + vslot(slot)] = Elem<T>::from_f32(x1);
                 }
@@ -1007,12 +1012,18 @@ struct OpFuse {
 template <typename T>
 struct OpInject {
     static constexpr int kNT = 2;  // 16-column blocks per tile
-    using State = NoState;
+    struct State {
+        int pos0;  // position of row 0
+        bool ok;   // the rows fit the cache (else nothing is written)
+    };
     static constexpr bool kDoneHook = false;
     PlainA<T> a;
     const T* wk[DFLASH_MAX_LAYERS];
     const T* wv[DFLASH_MAX_LAYERS];
     int H, nkv, d, M, pos0;
+    const int* len_dev = nullptr;  // device-resident length: rows go to *len_dev.. (else pos0..)
+    int* err = nullptr;            // set to 1 when a device-length injection does not fit
+    int max_ctx = 0;
     const float* cosT;
     const float* sinT;
     KVPages kv;
@@ -1031,11 +1042,18 @@ struct OpInject {
         decode(tile, l, kind, h, i);
         return sw_stream(kind == 0 ? wk[l] : wv[l], (h * d + 16 * i + blk * (d / 2)) / 16, nch);
     }
-    __device__ __forceinline__ void wave_begin(State&) const {}
+    __device__ __forceinline__ void wave_begin(State& st) const {
+        st.pos0 = len_dev ? *len_dev : pos0;
+        st.ok = !len_dev || (st.pos0 >= 0 && st.pos0 + M <= max_ctx);
+    }
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
-    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
+    __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State& st) const {
+        if (!st.ok) {
+            if (tile == 0 && lane == 0) *err = 1;
+            return;
+        }
         int l, kind, h, i;
         decode(tile, l, kind, h, i);
         const int dim = 16 * i + (lane & 15), half = d / 2;
@@ -1043,7 +1061,7 @@ struct OpInject {
         for (int ii = 0; ii < 4; ++ii) {
             const int j = 4 * (lane >> 4) + ii;
             if (j >= M) continue;
-            const int pos = pos0 + j;
+            const int pos = st.pos0 + j;
             float x0 = acc[0][ii], x1 = acc[1][ii];
             int slot;
             if (kind == 0) {
@@ -1158,6 +1176,7 @@ struct AttnArgs {
     KVPages kv;
     int layer, C, B, nq, nkv, group, kps, n_splits;
     int causal_base;    // >= 0: causal, query row j sees keys 0..causal_base+j; -1: no mask
+    const int* len_dev; // non-null (draft only): the context length is *len_dev, not C
     float scale_log2;   // log2(e) / sqrt(d)
     float* part_o;      // [(n_splits+1)][nq][16][d]
     float* part_ml;     // [(n_splits+1)][nq][16][2]
@@ -1396,14 +1415,17 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
     };
 
     constexpr bool kEarlyQ = NS == 2;
+    // with a device-resident length the splits are planned for the capacity;
+    // those past the current length have no keys (their partial stays empty)
+    const int Cnow = a.len_dev ? min(*a.len_dev, a.C) : a.C;
     if (split < a.n_splits) {
         const int kbeg = split * a.kps;
-        const int kend = min(a.C, kbeg + a.kps);
-        const int nch = (kend - kbeg + CH - 1) / CH;
+        const int kend = min(Cnow, kbeg + a.kps);
+        const int nch = kend > kbeg ? (kend - kbeg + CH - 1) / CH : 0;
         // physical pages of the split, looked up once (a table load per chunk
         // would put a dependent round trip in front of every chunk's loads)
         const int pg0 = kbeg / a.kv.page;
-        const int npg = (kend - 1) / a.kv.page - pg0 + 1;  // <= kMaxSplitPages (host-checked)
+        const int npg = nch > 0 ? (kend - 1) / a.kv.page - pg0 + 1 : 0;  // <= kMaxSplitPages (host-checked)
         for (int i = threadIdx.x; i < npg; i += blockDim.x) s_pages[i] = a.kv.table[pg0 + i];
         // Waves 0-1 bring in the chunk's K rows, waves 2-3 its V^T rows (the two
         // halves of a stage are the same size).  Per-lane byte offsets of the NI
@@ -1448,7 +1470,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
         };
         // prologue: chunks 0 .. NS-2 in flight before anything else
         if constexpr (NS == 2) {
-            issue(0, 0);
+            if (nch > 0) issue(0, 0);
         } else {
             for (int c = 0; c < NS - 1; ++c)
                 if (c < nch) issue(c, c);
@@ -1719,6 +1741,32 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t* draft, const 
         out[0] = k;
         out[1] = target[k];
     }
+}
+
+// Device-resident length: set it, add the accepted rows (k + 1: the anchor
+// and the k accepted drafts, result = {k, bonus}), or copy it (with the
+// capacity-error word) to a caller buffer.
+__global__ void len_set_kernel(int* len, int value) {
+    if (threadIdx.x == 0) len[0] = value;
+}
+__global__ void len_keep_kernel(int* len, const int32_t* result, int max_ctx) {
+    if (threadIdx.x == 0) len[0] = min(len[0] + min(max(result[0], 0), DFLASH_MAX_BLOCK - 1) + 1, max_ctx);
+}
+__global__ void len_read_kernel(const int* len, int32_t* out) {
+    if (threadIdx.x < 2) out[threadIdx.x] = len[threadIdx.x];
+}
+
+hipError_t launch_len_set(int* len, int value, hipStream_t s) {
+    hipLaunchKernelGGL(len_set_kernel, dim3(1), dim3(64), 0, s, len, value);
+    return hipGetLastError();
+}
+hipError_t launch_len_keep(int* len, const int32_t* result, int max_ctx, hipStream_t s) {
+    hipLaunchKernelGGL(len_keep_kernel, dim3(1), dim3(64), 0, s, len, result, max_ctx);
+    return hipGetLastError();
+}
+hipError_t launch_len_read(const int* len, int32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(len_read_kernel, dim3(1), dim3(64), 0, s, len, out);
+    return hipGetLastError();
 }
 
 // dense [Ld][M][nkv][d] <-> pages
@@ -2239,6 +2287,7 @@ struct PassArgs {
     long long cap_ld;
     void* layer_out;   // draft: [Ld][rows][layer_ld] residual after every layer, or null
     long long layer_ld;
+    const int* len_dev;  // draft: the context length lives on the device (C unused), or null
 };
 
 template <typename T>
@@ -2275,7 +2324,9 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         ns = (C + B + kps - 1) / kps;
         nparts = ns;
     } else {
-        attn_split_plan(C, nkv, c.num_cus, d.page, &kps, &ns);
+        // a device-resident length is planned for the capacity (the splits
+        // past the current length stay empty)
+        attn_split_plan(pa.len_dev ? d.max_ctx : C, nkv, c.num_cus, d.page, &kps, &ns);
         nparts = ns + 1;  // + the block's own keys
     }
     const int group = nq / nkv;
@@ -2312,6 +2363,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         qkv.d = D;
         qkv.M = B;
         qkv.pos0 = C;
+        qkv.len_dev = pa.len_dev;
+        qkv.max_ctx = d.max_ctx;
         qkv.tq = nq * D / 32;
         qkv.tk = nkv * D / 32;
         qkv.cosT = cosT;
@@ -2331,7 +2384,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         aa.vblkT = vblkT;
         aa.kv = make_pages<T>(c);
         aa.layer = l;
-        aa.C = pa.causal ? C + B : C;
+        aa.C = pa.causal ? C + B : (pa.len_dev ? d.max_ctx : C);
+        aa.len_dev = pa.len_dev;
         aa.B = B;
         aa.nq = nq;
         aa.nkv = nkv;
@@ -2454,8 +2508,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
 }
 
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits, int32_t* tokens,
-                              void* layer_out, long long layer_ld, hipStream_t s) {
-    PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0, layer_out, layer_ld};
+                              void* layer_out, long long layer_ld, const int* len_dev, hipStream_t s) {
+    PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0, layer_out, layer_ld, len_dev};
     c.tracer->begin(DFLASH_TRACE_DRAFT, s);
     hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_DRAFT, s);
@@ -2464,7 +2518,7 @@ hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, flo
 
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits, int32_t* argmax,
                                  void* const* capture, long long capture_ld, hipStream_t s) {
-    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, nullptr, 0};
+    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, nullptr, 0, nullptr};
     c.tracer->begin(DFLASH_TRACE_TARGET, s);
     hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_TARGET, s);
@@ -2587,7 +2641,8 @@ hipError_t launch_fuse_static(const DevCtx& c, int device, const void* const sla
 }
 
 template <typename T>
-static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s) {
+static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s,
+                           const int* len_dev, int* err) {
     const Dims& d = c.dm;
     const float* cosT = WS(const float*, rope_cos);
     const float* sinT = WS(const float*, rope_sin);
@@ -2603,6 +2658,9 @@ static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int
         op.d = d.d;
         op.M = M;
         op.pos0 = pos0;
+        op.len_dev = len_dev;
+        op.err = err;
+        op.max_ctx = d.max_ctx;
         op.cosT = cosT;
         op.sinT = sinT;
         op.kv = make_pages<T>(c);
@@ -2611,6 +2669,7 @@ static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int
         if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_INJECT, s);
         return e;
     }
+    if (len_dev) return hipErrorInvalidValue;  // device-resident length: up to 16 rows per call
     if constexpr (sizeof(T) == 2) {
         auto go = [&](auto op) {
             op.a = (const bf16_t*)fused;
@@ -2654,9 +2713,10 @@ static hipError_t inject_t(const DevCtx& c, const void* fused, long long ld, int
     return e;
 }
 
-hipError_t launch_inject(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s) {
-    if (c.dm.dtype == DFLASH_F32) return inject_t<float>(c, fused, ld, M, pos0, s);
-    return inject_t<bf16_t>(c, fused, ld, M, pos0, s);
+hipError_t launch_inject(const DevCtx& c, const void* fused, long long ld, int M, int pos0, hipStream_t s,
+                         const int* len_dev, int* err) {
+    if (c.dm.dtype == DFLASH_F32) return inject_t<float>(c, fused, ld, M, pos0, s, len_dev, err);
+    return inject_t<bf16_t>(c, fused, ld, M, pos0, s, len_dev, err);
 }
 
 hipError_t launch_accept(const DevCtx& c, const int32_t* draft, const int32_t* target, int32_t* out, hipStream_t s) {

@@ -213,6 +213,33 @@ dflash_status dflash_verify_accept(dflash_ctx* ctx, const int32_t* draft, const 
  * page is released or reassigned. */
 dflash_status dflash_rollback(dflash_ctx* ctx, int32_t new_len);
 
+/* Device-resident length: a speculative step without a host round trip
+ * ([B] 技术内幕: keep the anchor and the accepted drafts; the next step drafts
+ * from there).  After dflash_device_length_enable the context's length lives
+ * in a device word (initialised from the host length) for the rest of the
+ * context's life, so a whole step -- draft, verification, fusion, injection,
+ * keeping the accepted rows -- is stream-ordered device work that can be
+ * captured in a HIP graph and replayed:
+ *  - dflash_draft_block reads the length from the device word; its attention
+ *    is planned for max_ctx (the splits past the length stay empty);
+ *  - dflash_inject_kv takes pos0 = -1 and M <= 16 and writes the rows at the
+ *    device length without changing it; rows that would pass max_ctx are not
+ *    written and the capacity-error word is set instead;
+ *  - dflash_keep_accepted adds k + 1 from a dflash_verify_accept result
+ *    {k, bonus} (device int32[2]): the anchor and the k accepted drafts of the
+ *    rows just injected stay context (k is clamped to [0, 15], the length to
+ *    max_ctx);
+ *  - dflash_set_length_async sets the length (0 <= new_len <= max_ctx);
+ *  - dflash_read_device_length copies {length, capacity-error} to a device
+ *    int32[2];
+ *  - dflash_rollback, dflash_target_forward and dflash_load_kv return STATE;
+ *    dflash_length returns -1; dflash_read_kv checks ranges against max_ctx.
+ * STATE if enabled twice, or if the other calls are used without it. */
+dflash_status dflash_device_length_enable(dflash_ctx* ctx, void* stream);
+dflash_status dflash_keep_accepted(dflash_ctx* ctx, const int32_t* result, void* stream);
+dflash_status dflash_set_length_async(dflash_ctx* ctx, int32_t new_len, void* stream);
+dflash_status dflash_read_device_length(dflash_ctx* ctx, int32_t* out, void* stream);
+
 /* Causal forward of the context's decoder stack used as the target (verifier)
  * model ([A] §1.1 autoregressive generation, §1.2 parallel verification of a
  * drafted block; [C] greedy verification is lossless): rows tokens[0..M-1] at
