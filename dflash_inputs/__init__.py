@@ -104,6 +104,19 @@ def uniform_int(n: int, lo: int, hi: int, seed: int, tag: str) -> torch.Tensor:
     return torch.randint(lo, hi, (n,), generator=_gen(seed, tag), dtype=torch.int64).to(torch.int32)
 
 
+def random_tree(n: int, seed: int, tag: str) -> np.ndarray:
+    """Parent array of a random rooted tree on n nodes in topological order:
+    parent[0] = -1, parent[j] uniform in [0, j)."""
+    u = uniform01(max(n, 1), seed, tag).numpy()
+    par = np.array([-1] + [int(u[j] * j) for j in range(1, n)], dtype=np.int32)
+    return par[:n]
+
+
+def chain_tree(n: int) -> np.ndarray:
+    """Parent array of a chain: node j's parent is j-1."""
+    return np.arange(-1, n - 1, dtype=np.int32)
+
+
 def uniform01(n: int, seed: int, tag: str) -> torch.Tensor:
     return torch.rand((n,), generator=_gen(seed, tag), dtype=torch.float64)
 

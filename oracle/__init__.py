@@ -60,8 +60,9 @@ def lib():
         L.orc_lm_head.argtypes = [vp, vp, i32, vp, vp, vp]
         L.orc_accept.argtypes = [vp, vp, i32, vp, vp]
         L.orc_target_forward.argtypes = [vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp, vp]
+        L.orc_target_forward_tree.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp, vp]
         for f in ("orc_fuse_rows", "orc_inject_rows", "orc_draft_block", "orc_target_forward", "orc_draft_layer",
-                  "orc_lm_head"):
+                  "orc_lm_head", "orc_target_forward_tree"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -279,7 +280,11 @@ class TargetCache:
 
 
 def target_forward(model: Model, cache: TargetCache, tokens: Sequence[int], pos0: int,
-                   capture: Optional[Sequence[int]] = None, want_logits: bool = False):
+                   capture: Optional[Sequence[int]] = None, want_logits: bool = False,
+                   parent: Optional[Sequence[int]] = None):
+    """Causal forward of `tokens` at pos0.. ([A] §1.1), or with `parent` the
+    tree verification of [A] §8.2: row j sits at pos0 + depth(j), its K/V at
+    cache slot pos0 + j, and it sees the cache before pos0 plus its ancestors."""
     s = model.shape
     t = np.ascontiguousarray(tokens, dtype=np.int32)
     n = len(t)
@@ -288,12 +293,17 @@ def target_forward(model: Model, cache: TargetCache, tokens: Sequence[int], pos0
     cap_a = np.ascontiguousarray(capture, dtype=np.int32) if capture is not None else None
     hid = np.empty((5, n, s.hidden), dtype=np.float64) if capture is not None else None
     logits = np.empty((n, s.vocab), dtype=np.float32) if want_logits else None
-    rc = lib().orc_target_forward(model.ref, t.ctypes.data, n, pos0, _dptr(cache.k), _dptr(cache.v),
-                                  cache.cap, cap_a.ctypes.data if cap_a is not None else None,
-                                  hid.ctypes.data if hid is not None else None,
-                                  logits.ctypes.data if logits is not None else None,
-                                  am.ctypes.data, gap.ctypes.data)
-    assert rc == 0
+    outs = (cache.cap, cap_a.ctypes.data if cap_a is not None else None,
+            hid.ctypes.data if hid is not None else None,
+            logits.ctypes.data if logits is not None else None, am.ctypes.data, gap.ctypes.data)
+    if parent is None:
+        rc = lib().orc_target_forward(model.ref, t.ctypes.data, n, pos0, _dptr(cache.k), _dptr(cache.v), *outs)
+    else:
+        par = np.ascontiguousarray(parent, dtype=np.int32)
+        assert par.shape == t.shape
+        rc = lib().orc_target_forward_tree(model.ref, t.ctypes.data, par.ctypes.data, n, pos0, _dptr(cache.k),
+                                           _dptr(cache.v), *outs)
+    assert rc == 0, "not a valid tree" if parent is not None else "capacity"
     return {"argmax": am, "gap": gap, "hidden": hid, "logits": logits}
 
 

@@ -237,14 +237,18 @@ static double kv_get(const kv_src* s, int32_t dtype, int64_t t, int64_t off, int
 }
 
 /* One pre-norm decoder layer over R rows held in x[R][H] (updated in place).
- * Rows sit at positions pos[r].  Keys visible to row r: the first n_vis(r) keys
- * of the concatenation [ksrc.st ; ksrc.db] (all of them when causal == 0).
+ * Rows sit at positions pos[r].  Keys visible to row r, among the concatenation
+ * [ksrc.st ; ksrc.db]:
+ *   causal == 0: all of them;
+ *   causal == 1, tree_vis NULL: keys 0 .. causal_base + r;
+ *   causal == 1, tree_vis given: keys 0 .. causal_base - 1, and key
+ *     causal_base + i (row i's own key) iff tree_vis[r * R + i] != 0.
  * kv_new_k/v receive the rows' own rotated K and V ([R][nkv*d], rounded) and
  * must already be appended at the end of ksrc.db/vsrc.db by the caller's layout:
  * this function fills them first, then attends. */
 static void decoder_layer(const orc_model* m, int32_t l, double* x, int32_t R, const int64_t* pos,
                           kv_src* ks, kv_src* vs, double* kv_new_k, double* kv_new_v,
-                          int causal, int64_t causal_base)
+                          int causal, int64_t causal_base, const unsigned char* tree_vis)
 {
     const int32_t H = m->hidden, dt = m->dtype, d = m->head_dim;
     const int32_t nq = m->n_q_heads, nkv = m->n_kv_heads, F = m->ffn;
@@ -280,23 +284,33 @@ static void decoder_layer(const orc_model* m, int32_t l, double* x, int32_t R, c
         for (int32_t r = 0; r < R; ++r)
             for (int32_t h = 0; h < nq; ++h) {
                 const int32_t g = h / group;            /* grouped-query: kv head of query head h */
-                const int64_t nvis = causal ? (causal_base + r + 1) : n_keys;
+                const int64_t nvis = !causal ? n_keys : (tree_vis ? causal_base + R : causal_base + r + 1);
+                /* a key hidden by the tree mask takes no part in the softmax */
+#define HIDDEN_KEY(j) (tree_vis && (j) >= causal_base && !tree_vis[(int64_t)r * R + ((j) - causal_base)])
                 const double* qh = q + r * NQ + (int64_t)h * d;
                 double mx = -INFINITY;
                 for (int64_t j = 0; j < nvis; ++j) {
+                    if (HIDDEN_KEY(j)) continue;
                     double s = 0.0;
                     for (int32_t i = 0; i < d; ++i) s += qh[i] * kv_get(ks, dt, j, (int64_t)g * d + i, NK);
                     sc[j] = s * scale;
                     if (sc[j] > mx) mx = sc[j];
                 }
                 double den = 0.0;
-                for (int64_t j = 0; j < nvis; ++j) { sc[j] = exp(sc[j] - mx); den += sc[j]; }
+                for (int64_t j = 0; j < nvis; ++j) {
+                    if (HIDDEN_KEY(j)) continue;
+                    sc[j] = exp(sc[j] - mx);
+                    den += sc[j];
+                }
                 double* oh = o + r * NQ + (int64_t)h * d;
                 /* o_i = sum_j p_j v_{j,i}: every o_i accumulates over keys in index order */
                 double acc[256];
                 for (int32_t i = 0; i < d; ++i) acc[i] = 0.0;
-                for (int64_t j = 0; j < nvis; ++j)
+                for (int64_t j = 0; j < nvis; ++j) {
+                    if (HIDDEN_KEY(j)) continue;
                     for (int32_t i = 0; i < d; ++i) acc[i] += sc[j] * kv_get(vs, dt, j, (int64_t)g * d + i, NK);
+                }
+#undef HIDDEN_KEY
                 for (int32_t i = 0; i < d; ++i) oh[i] = orc_round(acc[i] / den, dt);
             }
         free(sc);
@@ -373,7 +387,7 @@ int orc_draft_block(const orc_model* m, const void* const* ctx_k, const void* co
     for (int32_t l = 0; l < m->n_layers; ++l) {
         kv_src ks = { ctx_k ? ctx_k[l] : NULL, C, kb, B };
         kv_src vs = { ctx_v ? ctx_v[l] : NULL, C, vb, B };
-        decoder_layer(m, l, x, B, pos, &ks, &vs, kb, vb, 0, 0);
+        decoder_layer(m, l, x, B, pos, &ks, &vs, kb, vb, 0, 0, NULL);
         if (trace) memcpy(trace + (int64_t)(l + 1) * B * H, x, sizeof(double) * (size_t)B * H);
     }
     lm_head_argmax(m, x, B, logits, tokens, gap);
@@ -401,7 +415,7 @@ int orc_draft_layer(const orc_model* m, int32_t l, const void* ctx_k, const void
     for (int32_t j = 0; j < B; ++j) pos[j] = C + j;
     kv_src ks = { C > 0 ? ctx_k : NULL, C, kb, B };
     kv_src vs = { C > 0 ? ctx_v : NULL, C, vb, B };
-    decoder_layer(m, l, x_out, B, pos, &ks, &vs, kb, vb, 0, 0);
+    decoder_layer(m, l, x_out, B, pos, &ks, &vs, kb, vb, 0, 0, NULL);
     free(kb); free(vb); free(pos);
     return 0;
 }
@@ -436,6 +450,35 @@ void orc_accept(const int32_t* d, const int32_t* g, int32_t B, int32_t* k, int32
 /* causal target (toy end-to-end loop)                                 */
 /* ------------------------------------------------------------------ */
 
+/* Shared body of the causal and tree forwards: rows at positions pos[j], their
+ * K/V stored at cache slots pos0 + j, visibility as in decoder_layer. */
+static int target_rows(const orc_model* m, const int32_t* tokens, int32_t n, int64_t pos0, const int64_t* pos,
+                       const unsigned char* tree_vis, double* cache_k, double* cache_v, int64_t cap,
+                       const int32_t* capture, double* hidden_out,
+                       float* logits_out, int32_t* argmax_out, double* gap_out)
+{
+    const int32_t H = m->hidden, dt = m->dtype;
+    const int64_t NK = (int64_t)m->n_kv_heads * m->head_dim;
+    double* x = (double*)malloc(sizeof(double) * (size_t)n * H);
+    if (!x) return -1;
+    for (int32_t j = 0; j < n; ++j)
+        for (int32_t k = 0; k < H; ++k) x[(int64_t)j * H + k] = ld_elem(m->embed, dt, (int64_t)tokens[j] * H + k);
+    for (int32_t l = 0; l < m->n_layers; ++l) {
+        double* ck = cache_k + (int64_t)l * cap * NK;
+        double* cv = cache_v + (int64_t)l * cap * NK;
+        kv_src ks = { NULL, 0, ck, pos0 + n };
+        kv_src vs = { NULL, 0, cv, pos0 + n };
+        decoder_layer(m, l, x, n, pos, &ks, &vs, ck + pos0 * NK, cv + pos0 * NK, 1, pos0, tree_vis);
+        if (capture && hidden_out)
+            for (int s = 0; s < 5; ++s)
+                if (capture[s] == l)
+                    memcpy(hidden_out + (int64_t)s * n * H, x, sizeof(double) * (size_t)n * H);
+    }
+    lm_head_argmax(m, x, n, logits_out, argmax_out, gap_out);
+    free(x);
+    return 0;
+}
+
 /* Plain greedy autoregressive model forward ([A] §1.1): causal pre-norm
  * decoder with a dense KV cache; every row's argmax is reported. */
 int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int64_t pos0,
@@ -443,28 +486,44 @@ int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int
                        const int32_t* capture, double* hidden_out,
                        float* logits_out, int32_t* argmax_out, double* gap_out)
 {
-    const int32_t H = m->hidden, dt = m->dtype;
-    const int64_t NK = (int64_t)m->n_kv_heads * m->head_dim;
     if (pos0 + n > cap || m->head_dim > 256) return -1;
-    double* x = (double*)malloc(sizeof(double) * (size_t)n * H);
     int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
-    if (!x || !pos) return -1;
+    if (!pos) return -1;
+    for (int32_t j = 0; j < n; ++j) pos[j] = pos0 + j;
+    const int rc = target_rows(m, tokens, n, pos0, pos, NULL, cache_k, cache_v, cap, capture, hidden_out,
+                               logits_out, argmax_out, gap_out);
+    free(pos);
+    return rc;
+}
+
+/* Tree verification ([A] §8.2, DDTree: several branches checked in one target
+ * pass).  Row 0 is the root (parent[0] = -1); row j >= 1 has parent[j] in
+ * [0, j).  A row sits at position pos0 + depth(j) (its number of ancestors),
+ * its K/V go to cache slot pos0 + j, and it attends to the cache before pos0
+ * and to the slots of its ancestors and itself.  Every row therefore computes
+ * what a causal forward over its root-to-row path would compute.  -1 when the
+ * parent array is not such a tree. */
+int orc_target_forward_tree(const orc_model* m, const int32_t* tokens, const int32_t* parent, int32_t n,
+                            int64_t pos0, double* cache_k, double* cache_v, int64_t cap,
+                            const int32_t* capture, double* hidden_out,
+                            float* logits_out, int32_t* argmax_out, double* gap_out)
+{
+    if (n < 1 || pos0 + n > cap || m->head_dim > 256 || parent[0] != -1) return -1;
+    for (int32_t j = 1; j < n; ++j)
+        if (parent[j] < 0 || parent[j] >= j) return -1;
+    int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+    unsigned char* vis = (unsigned char*)calloc((size_t)n * n, 1);
+    if (!pos || !vis) { free(pos); free(vis); return -1; }
     for (int32_t j = 0; j < n; ++j) {
-        for (int32_t k = 0; k < H; ++k) x[(int64_t)j * H + k] = ld_elem(m->embed, dt, (int64_t)tokens[j] * H + k);
-        pos[j] = pos0 + j;
+        int64_t depth = 0;
+        for (int32_t u = j; u >= 0; u = parent[u]) {  /* walk up to the root */
+            vis[(int64_t)j * n + u] = 1;
+            if (u != j) ++depth;
+        }
+        pos[j] = pos0 + depth;
     }
-    for (int32_t l = 0; l < m->n_layers; ++l) {
-        double* ck = cache_k + (int64_t)l * cap * NK;
-        double* cv = cache_v + (int64_t)l * cap * NK;
-        kv_src ks = { NULL, 0, ck, pos0 + n };
-        kv_src vs = { NULL, 0, cv, pos0 + n };
-        decoder_layer(m, l, x, n, pos, &ks, &vs, ck + pos0 * NK, cv + pos0 * NK, 1, pos0);
-        if (capture && hidden_out)
-            for (int s = 0; s < 5; ++s)
-                if (capture[s] == l)
-                    memcpy(hidden_out + (int64_t)s * n * H, x, sizeof(double) * (size_t)n * H);
-    }
-    lm_head_argmax(m, x, n, logits_out, argmax_out, gap_out);
-    free(x); free(pos);
-    return 0;
+    const int rc = target_rows(m, tokens, n, pos0, pos, vis, cache_k, cache_v, cap, capture, hidden_out,
+                               logits_out, argmax_out, gap_out);
+    free(pos); free(vis);
+    return rc;
 }

@@ -113,6 +113,10 @@ int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int
                        double* cache_k, double* cache_v, int64_t cap,
                        const int32_t* capture, double* hidden_out,
                        float* logits_out, int32_t* argmax_out, double* gap_out);
+int orc_target_forward_tree(const orc_model* m, const int32_t* tokens, const int32_t* parent, int32_t n,
+                            int64_t pos0, double* cache_k, double* cache_v, int64_t cap,
+                            const int32_t* capture, double* hidden_out,
+                            float* logits_out, int32_t* argmax_out, double* gap_out);
 
 #ifdef __cplusplus
 }

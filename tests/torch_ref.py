@@ -81,21 +81,24 @@ def inject(shape, w, fused, pos0):
     return torch.stack(ks), torch.stack(vs)
 
 
-def target_forward(shape, w, tokens, n_layers):
+def target_forward(shape, w, tokens, n_layers, pos=None, visible=None):
     """fp32-storage causal forward of `tokens` from position 0 (a prefill of
     the whole sequence at once): the autoregressive model of [A] §1.1, written
     with an explicit lower-triangular visibility mask (key j is visible to
-    query i iff j <= i, the query's own key included).  Returns (logits [n, V],
-    hidden [n_layers, n, H]) where hidden[l] is the residual stream right after
-    decoder layer l (before any final norm)."""
+    query i iff j <= i, the query's own key included).  `pos` and `visible`
+    ([n, n] bool) replace the positions 0..n-1 and that mask when given.
+    Returns (logits [n, V], hidden [n_layers, n, H]) where hidden[l] is the
+    residual stream right after decoder layer l (before any final norm)."""
     H, d = shape.hidden, shape.head_dim
     nq, nkv = shape.n_q_heads, shape.n_kv_heads
     eps = shape.eps
     g = lambda k: w[k].to(torch.float64)
     n = len(tokens)
     x = g("embed")[torch.as_tensor(list(tokens), dtype=torch.long)]
-    pos = torch.arange(n)
-    visible = torch.ones(n, n, dtype=torch.bool).tril()
+    if pos is None:
+        pos = torch.arange(n)
+    if visible is None:
+        visible = torch.ones(n, n, dtype=torch.bool).tril()
     outs = []
     for l in range(n_layers):
         u = _r32(F.rms_norm(x, (H,), weight=g(f"attn_norm.{l}"), eps=eps))
@@ -117,3 +120,24 @@ def target_forward(shape, w, tokens, n_layers):
         outs.append(x.clone())
     z = _r32(F.rms_norm(x, (H,), weight=g("final_norm"), eps=eps))
     return _r32(z @ g("lm_head").T), torch.stack(outs)
+
+
+def tree_forward(shape, w, prefix, tree_tokens, parent, n_layers):
+    """[A] §8.2 tree verification written as one masked prefill: the prefix
+    (positions 0..P-1, causal) followed by the tree's rows, where row j sits
+    at position P + (its number of ancestors) and sees the whole prefix, its
+    ancestors and itself.  Ancestors are found by set closure over the parent
+    relation (not by walking up).  Returns (logits, hidden) of the tree rows."""
+    P, n = len(prefix), len(tree_tokens)
+    anc = torch.eye(n, dtype=torch.bool)
+    for j in range(1, n):
+        anc[j, parent[j]] = True
+    for _ in range(n):  # transitive closure: anc = anc OR anc.anc
+        anc = anc | ((anc.double() @ anc.double()) > 0)
+    vis = torch.zeros(P + n, P + n, dtype=torch.bool)
+    vis[:P, :P] = torch.ones(P, P, dtype=torch.bool).tril()
+    vis[P:, :P] = True
+    vis[P:, P:] = anc
+    pos = torch.cat([torch.arange(P), P + anc.sum(dim=1) - 1])
+    lg, hid = target_forward(shape, w, list(prefix) + list(tree_tokens), n_layers, pos=pos, visible=vis)
+    return lg[P:], hid[:, P:]
