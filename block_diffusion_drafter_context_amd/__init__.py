@@ -120,6 +120,18 @@ def lib():
         L.dflash_hbm_read_probe.argtypes = [vp, i64, vp, C.POINTER(i64), vp]
         L.dflash_trace_read_each.restype = st
         L.dflash_trace_read_each.argtypes = [vp, C.POINTER(C.c_float), i32, C.POINTER(i32)]
+        L.dflash_target_forward_ex.restype = st
+        L.dflash_target_forward_ex.argtypes = [vp, vp, vp, i32, vp, vp, vp, i64, vp]
+        L.dflash_target_forward_tree.restype = st
+        L.dflash_target_forward_tree.argtypes = [vp, vp, vp, i32, vp, vp, vp, i64, vp]
+        L.dflash_draft_topk.restype = st
+        L.dflash_draft_topk.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
+        L.dflash_build_tree.restype = st
+        L.dflash_build_tree.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+        L.dflash_tree_accept.restype = st
+        L.dflash_tree_accept.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+        L.dflash_tree_commit.restype = st
+        L.dflash_tree_commit.argtypes = [vp, i32, i32, vp, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -176,6 +188,17 @@ def _p(t: Optional[torch.Tensor]):
     if t is None:
         return None
     return t.data_ptr()
+
+
+def _capture_array(capture, hidden: int):
+    """A host array of 5 device pointers with their common row stride, or (None, 0)."""
+    if capture is None:
+        return None, 0
+    assert len(capture) == 5
+    live = [t for t in capture if t is not None]
+    ld = live[0].stride(0) if live else hidden
+    assert all(t.stride(0) == ld for t in live)
+    return (C.c_void_p * 5)(*[_p(t) for t in capture]), ld
 
 
 def _stream(stream=None):
@@ -291,25 +314,73 @@ class DFlash:
 
     def target_forward(self, tokens: torch.Tensor, argmax: Optional[torch.Tensor] = None, want_logits: bool = False,
                        logits: Optional[torch.Tensor] = None, capture: Optional[Sequence[Optional[torch.Tensor]]] = None,
-                       stream=None):
-        """Causal forward of tokens (device int32[M], M <= 16) at positions length..length+M-1.
+                       stream=None, parent: Optional[torch.Tensor] = None,
+                       layers_out: Optional[torch.Tensor] = None):
+        """Causal forward of tokens (device int32[M], M <= 16) at positions length..length+M-1,
+        or with parent (device int32[M]) the tree-masked forward of dflash_target_forward_tree.
         capture: 5 tensors [>= M, H] with one common row stride (or None entries).
+        layers_out: [Ld, M, H] device tensor receiving every layer's output (no capture then).
         Returns (argmax int32[M], logits fp32[M, V] or None)."""
         M, V = tokens.shape[0], self.shape.vocab
         if argmax is None:
             argmax = torch.empty(M, dtype=torch.int32, device=self.device)
         if want_logits and logits is None:
             logits = torch.empty(M, V, dtype=torch.float32, device=self.device)
-        cap, ld = None, 0
-        if capture is not None:
-            assert len(capture) == 5
-            live = [t for t in capture if t is not None]
-            ld = live[0].stride(0) if live else self.shape.hidden
-            assert all(t.stride(0) == ld for t in live)
-            cap = (C.c_void_p * 5)(*[_p(t) for t in capture])
-        self._check(lib().dflash_target_forward(self.h, tokens.data_ptr(), M, _p(logits), argmax.data_ptr(), cap, ld,
-                                                _stream(stream)), "target_forward")
+        cap, ld = _capture_array(capture, self.shape.hidden)
+        if layers_out is not None:
+            assert capture is None and layers_out.shape[:2] == (self.shape.draft_layers, M)
+            assert layers_out.stride(0) == M * layers_out.stride(1)
+            st = lib().dflash_target_forward_ex(self.h, tokens.data_ptr(), _p(parent), M, _p(logits),
+                                                argmax.data_ptr(), layers_out.data_ptr(), layers_out.stride(1),
+                                                _stream(stream))
+        elif parent is None:
+            st = lib().dflash_target_forward(self.h, tokens.data_ptr(), M, _p(logits), argmax.data_ptr(), cap, ld,
+                                             _stream(stream))
+        else:
+            st = lib().dflash_target_forward_tree(self.h, tokens.data_ptr(), parent.data_ptr(), M, _p(logits),
+                                                  argmax.data_ptr(), cap, ld, _stream(stream))
+        self._check(st, "target_forward")
         return argmax, logits
+
+    # ---- tree verification (DDTree)
+    def draft_topk(self, logits: torch.Tensor, K: int, ids: Optional[torch.Tensor] = None,
+                   logp: Optional[torch.Tensor] = None, stream=None):
+        """Top-K ids and log-probabilities of each row of logits (device fp32 [rows, >= V], rows <= 16)."""
+        rows = logits.shape[0]
+        if ids is None:
+            ids = torch.empty(rows, K, dtype=torch.int32, device=self.device)
+        if logp is None:
+            logp = torch.empty(rows, K, dtype=torch.float32, device=self.device)
+        self._check(lib().dflash_draft_topk(self.h, logits.data_ptr(), logits.stride(0), rows, K, ids.data_ptr(),
+                                            logp.data_ptr(), _stream(stream)), "draft_topk")
+        return ids, logp
+
+    def build_tree(self, anchor: torch.Tensor, ids: torch.Tensor, logp: torch.Tensor, budget: int,
+                   tokens: Optional[torch.Tensor] = None, parent: Optional[torch.Tensor] = None, stream=None):
+        """Best-first verification tree: (tokens, parent), device int32[budget + 1]."""
+        R, K = ids.shape
+        if tokens is None:
+            tokens = torch.empty(budget + 1, dtype=torch.int32, device=self.device)
+        if parent is None:
+            parent = torch.empty(budget + 1, dtype=torch.int32, device=self.device)
+        self._check(lib().dflash_build_tree(self.h, anchor.data_ptr(), ids.data_ptr(), logp.data_ptr(), R, K, budget,
+                                            tokens.data_ptr(), parent.data_ptr(), _stream(stream)), "build_tree")
+        return tokens, parent
+
+    def tree_accept(self, tokens: torch.Tensor, parent: torch.Tensor, target: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """Device int32[17]: {k, bonus, path[0..14]}."""
+        if out is None:
+            out = torch.empty(17, dtype=torch.int32, device=self.device)
+        self._check(lib().dflash_tree_accept(self.h, tokens.data_ptr(), parent.data_ptr(), target.data_ptr(),
+                                             tokens.shape[0], out.data_ptr(), _stream(stream)), "tree_accept")
+        return out
+
+    def tree_commit(self, pos0: int, M: int, result: torch.Tensor,
+                    capture: Optional[Sequence[Optional[torch.Tensor]]] = None, stream=None):
+        cap, ld = _capture_array(capture, self.shape.hidden)
+        self._check(lib().dflash_tree_commit(self.h, pos0, M, result.data_ptr(), cap, ld, _stream(stream)),
+                    "tree_commit")
 
     # ---- device-resident length (a step without host round trips; capturable)
     def enable_device_length(self, stream=None):

@@ -395,8 +395,13 @@ dflash_status dflash_rollback(dflash_ctx* c, int32_t new_len) {
     return DFLASH_OK;
 }
 
-dflash_status dflash_target_forward(dflash_ctx* c, const int32_t* tokens, int32_t M, float* logits_out,
-                                    int32_t* argmax_out, void* const* capture, int64_t capture_ld, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dflash_status target_forward(dflash_ctx* c, const int32_t* tokens, const int32_t* parent, int32_t M,
+                             float* logits_out, int32_t* argmax_out, void* const* capture, int64_t capture_ld,
+                             void* stream, void* layer_out = nullptr, int64_t layer_ld = 0) {
     if (!c) return DFLASH_ERR_INVAL;
     if (c->dev_len) return fail(c, DFLASH_ERR_STATE, "not available with the device-resident length");
     const DevCtx& x = c->dev;
@@ -418,13 +423,120 @@ dflash_status dflash_target_forward(dflash_ctx* c, const int32_t* tokens, int32_
                 return fail(c, DFLASH_ERR_INVAL, "capture requested for a layer beyond the context's draft_layers");
         }
     }
+    if (layer_out) {
+        if (capture) return fail(c, DFLASH_ERR_INVAL, "layer_out and capture are exclusive");
+        if (layer_ld < d.H || !aligned(layer_out, d.elem)) return fail(c, DFLASH_ERR_INVAL, "layer_ld must be >= H");
+    }
     if ((long long)c->length + M > d.max_ctx) return fail(c, DFLASH_ERR_CAPACITY, "forward would exceed max_ctx");
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
     hipError_t e = launch_causal_forward(x, c->length, tokens, M, logits_out, argmax_out, capture, capture_ld,
-                                         static_cast<hipStream_t>(stream));
+                                         static_cast<hipStream_t>(stream), parent, layer_out, layer_ld);
     if (e != hipSuccess) return hip_fail(c, e, "target forward launch");
     c->length += M;
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_target_forward(dflash_ctx* c, const int32_t* tokens, int32_t M, float* logits_out,
+                                    int32_t* argmax_out, void* const* capture, int64_t capture_ld, void* stream) {
+    return target_forward(c, tokens, nullptr, M, logits_out, argmax_out, capture, capture_ld, stream);
+}
+
+dflash_status dflash_target_forward_tree(dflash_ctx* c, const int32_t* tokens, const int32_t* parent, int32_t M,
+                                         float* logits_out, int32_t* argmax_out, void* const* capture,
+                                         int64_t capture_ld, void* stream) {
+    if (c && !parent) return fail(c, DFLASH_ERR_INVAL, "null parent");
+    return target_forward(c, tokens, parent, M, logits_out, argmax_out, capture, capture_ld, stream);
+}
+
+dflash_status dflash_target_forward_ex(dflash_ctx* c, const int32_t* tokens, const int32_t* parent, int32_t M,
+                                       float* logits_out, int32_t* argmax_out, void* layer_out, int64_t layer_ld,
+                                       void* stream) {
+    return target_forward(c, tokens, parent, M, logits_out, argmax_out, nullptr, 0, stream, layer_out, layer_ld);
+}
+
+dflash_status dflash_draft_topk(dflash_ctx* c, const float* logits, int64_t ld, int32_t rows, int32_t K,
+                                int32_t* ids_out, float* logp_out, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!logits || !ids_out || !logp_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (rows < 1 || rows > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "rows must be in [1, 16]");
+    if (K < 1 || K > DFLASH_TREE_MAX_K || K > d.V) return fail(c, DFLASH_ERR_INVAL, "K must be in [1, min(16, V)]");
+    if (ld < d.V) return fail(c, DFLASH_ERR_INVAL, "ld must be >= V");
+    if (!aligned(logits, 4)) return fail(c, DFLASH_ERR_INVAL, "logits misaligned");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    c->tracer.begin(DFLASH_TRACE_TREE, s);
+    hipError_t e = launch_topk(c->dev, logits, ld, rows, K, ids_out, logp_out, s);
+    if (e != hipSuccess) return hip_fail(c, e, "top-k launch");
+    c->tracer.end(DFLASH_TRACE_TREE, s);
+    return DFLASH_OK;
+}
+
+dflash_status dflash_build_tree(dflash_ctx* c, const int32_t* anchor, const int32_t* ids, const float* logp,
+                                int32_t depths, int32_t K, int32_t budget, int32_t* tokens_out, int32_t* parent_out,
+                                void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (!anchor || !ids || !logp || !tokens_out || !parent_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (depths < 1 || depths > DFLASH_MAX_BLOCK - 1) return fail(c, DFLASH_ERR_INVAL, "depths must be in [1, 15]");
+    if (K < 1 || K > DFLASH_TREE_MAX_K) return fail(c, DFLASH_ERR_INVAL, "K must be in [1, 16]");
+    if (budget < 0 || budget > DFLASH_MAX_BLOCK - 1) return fail(c, DFLASH_ERR_INVAL, "budget must be in [0, 15]");
+    long long nodes = 0, layer = 1;  // nodes of the full candidate tree (enough once it reaches the budget)
+    for (int i = 0; i < depths && nodes < budget; ++i) {
+        layer *= K;
+        nodes += layer;
+    }
+    if (nodes < budget) return fail(c, DFLASH_ERR_INVAL, "budget exceeds the candidate tree's size");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    c->tracer.begin(DFLASH_TRACE_TREE, s);
+    hipError_t e = launch_tree_build(anchor, c->dev.dm.V, ids, logp, depths, K, budget, tokens_out, parent_out, s);
+    if (e != hipSuccess) return hip_fail(c, e, "tree build launch");
+    c->tracer.end(DFLASH_TRACE_TREE, s);
+    return DFLASH_OK;
+}
+
+dflash_status dflash_tree_accept(dflash_ctx* c, const int32_t* tokens, const int32_t* parent, const int32_t* target,
+                                 int32_t M, int32_t* result_out, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    if (!tokens || !parent || !target || !result_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (M < 1 || M > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 16]");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    c->tracer.begin(DFLASH_TRACE_TREE, s);
+    hipError_t e = launch_tree_accept(tokens, parent, target, M, result_out, s);
+    if (e != hipSuccess) return hip_fail(c, e, "tree accept launch");
+    c->tracer.end(DFLASH_TRACE_TREE, s);
+    return DFLASH_OK;
+}
+
+dflash_status dflash_tree_commit(dflash_ctx* c, int32_t pos0, int32_t M, const int32_t* result, void* const* capture,
+                                 int64_t capture_ld, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!result) return fail(c, DFLASH_ERR_INVAL, "null result");
+    if (M < 1 || M > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 16]");
+    const long long lim = c->dev_len ? d.max_ctx : c->length;
+    if (pos0 < 0 || (long long)pos0 + M > lim) return fail(c, DFLASH_ERR_INVAL, "rows pos0..pos0+M-1 must be inside the context");
+    if (capture) {
+        if (capture_ld < d.H) return fail(c, DFLASH_ERR_INVAL, "capture_ld must be >= H");
+        for (int i = 0; i < DFLASH_NUM_FEATURES; ++i)
+            if (capture[i] && !aligned(capture[i], d.elem)) return fail(c, DFLASH_ERR_INVAL, "capture buffer misaligned");
+    }
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    c->tracer.begin(DFLASH_TRACE_TREE, s);
+    hipError_t e = launch_tree_commit(c->dev, pos0, M, result, capture, capture_ld, s);
+    if (e != hipSuccess) return hip_fail(c, e, "tree commit launch");
+    c->tracer.end(DFLASH_TRACE_TREE, s);
     return DFLASH_OK;
 }
 
@@ -460,7 +572,7 @@ dflash_status dflash_read_kv(dflash_ctx* c, int32_t pos0, int32_t M, void* k_out
 
 dflash_status dflash_trace_enable(dflash_ctx* c, int32_t kernel_class, int32_t max_launches) {
     if (!c) return DFLASH_ERR_INVAL;
-    if (kernel_class < DFLASH_TRACE_OFF || kernel_class > DFLASH_TRACE_TARGET || max_launches < 0 ||
+    if (kernel_class < DFLASH_TRACE_OFF || kernel_class > DFLASH_TRACE_TREE || max_launches < 0 ||
         max_launches > (1 << 20))
         return fail(c, DFLASH_ERR_INVAL, "bad trace class or launch count");
     hipError_t e = hipDeviceSynchronize();

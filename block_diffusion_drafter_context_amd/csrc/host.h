@@ -24,6 +24,8 @@ constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU
 constexpr int kMaxSplits = 256;          // context splits of the split-KV attention
 constexpr int kMaxSplitPages = 1040;     // KV pages one attention split may touch
 constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
+constexpr int kTopKMax = 16;             // candidates per draft position of a tree (the largest useful K)
+constexpr int kTopKSegs = 32;            // vocabulary segments of the top-K partial pass
 
 struct Dims {
     int dtype, H, Lt, Ld, nq, nkv, d, F, V, B, mask_id, page, max_ctx, max_rows, n_pages, elem;
@@ -52,6 +54,8 @@ struct Layout {
     size_t rstd, ss_part, partial, tile_cnt, counters, best;
     size_t attn_o, attn_ml;
     size_t len_dev;       // device-resident length: {length, capacity-error flag}
+    size_t tree_info;     // tree verification: per row {depth[16], ancestor mask[16]}
+    size_t topk_part;     // top-K partials: [16 rows][kTopKSegs] x (K values, K ids, max, sum)
     size_t total;
     size_t kv_total;      // bytes of the KV pool
     size_t kv_layer_kv;   // bytes of one (layer, K-or-V) page array

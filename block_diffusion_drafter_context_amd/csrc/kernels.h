@@ -72,8 +72,28 @@ hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, flo
                               int32_t* tokens, void* layer_out, long long layer_ld, const int* len_dev,
                               hipStream_t s);
 // Causal forward of M <= 16 tokens at positions C..C+M-1 (K/V appended to the cache).
+// tree_parent (device int32[M], or null): the rows form a tree; row j is placed
+// at C + depth(j) and sees the cache before C plus its ancestors (K/V still at C + j).
+// layer_out (or null): [Ld][M][layer_ld] residual after every layer, in place of capture.
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits,
-                                 int32_t* argmax, void* const* capture, long long capture_ld, hipStream_t s);
+                                 int32_t* argmax, void* const* capture, long long capture_ld, hipStream_t s,
+                                 const int32_t* tree_parent = nullptr, void* layer_out = nullptr,
+                                 long long layer_ld = 0);
+// Tree verification helpers (tree.hip).
+// Per row r < rows of logits [rows][ld]: the K <= 16 largest ids (ties: lower
+// id first) and their fp32 log-probabilities.
+hipError_t launch_topk(const DevCtx& c, const float* logits, long long ld, int rows, int K, int32_t* ids,
+                       float* logp, hipStream_t s);
+// Best-first candidate tree of `budget` nodes over R depths of K candidates.
+hipError_t launch_tree_build(const int32_t* anchor, int V, const int32_t* ids, const float* logp, int R, int K,
+                             int budget, int32_t* tokens, int32_t* parent, hipStream_t s);
+// Accepted path of a verified tree: out = {k, bonus, path[0..14]}.
+hipError_t launch_tree_accept(const int32_t* tokens, const int32_t* parent, const int32_t* target, int M,
+                              int32_t* out, hipStream_t s);
+// Move the accepted rows behind the root: KV slots pos0 + path[i] -> pos0 + 1 + i
+// in every layer, and rows path[i] -> 1 + i of each non-null capture buffer.
+hipError_t launch_tree_commit(const DevCtx& c, int pos0, int M, const int32_t* result, void* const* capture,
+                              long long capture_ld, hipStream_t s);
 // Context fusion of M rows (selected slabs given in ascending layer order).
 hipError_t launch_fuse(const DevCtx& c, const void* const slabs[5], long long ld, int M, void* out,
                        hipStream_t s);

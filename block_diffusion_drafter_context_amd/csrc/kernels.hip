@@ -32,6 +32,7 @@
 //    one-time weight reorder.
 #include "device_common.h"
 #include "kernels.h"
+#include "kv_pages.h"
 
 #include <math.h>
 
@@ -513,47 +514,6 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommo
 
 // Ops ------------------------------------------------------------------------
 
-// V pages store the positions of every 32-slot group in the order
-//   0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31
-// so that the 8 positions one lane feeds to a 32-key P.V matrix-core step
-// (4 from each 16-key half) are 8 consecutive elements.
-__host__ __device__ __forceinline__ int vslot(int slot) {
-    const int k = slot & 31;
-    const int pos = k < 16 ? 8 * (k >> 2) + (k & 3) : 8 * ((k - 16) >> 2) + 4 + (k & 3);
-    return (slot & ~31) | pos;
-}
-
-// Paged draft-KV addressing: per (layer, K|V) an array of pages; K pages are
-// [nkv][page][d] (key rows), V pages [nkv][d][page] (value columns, so the
-// attention's P.V operand reads runs of consecutive positions).
-struct KVPages {
-    char* base;
-    const int32_t* table;
-    long long layer_kv_bytes;  // bytes of one (layer, K|V) page array
-    int page, nkv, d, elem;
-    __device__ __forceinline__ long long page_elems() const { return (long long)nkv * page * d; }
-    template <typename T>
-    __device__ __forceinline__ T* kpage(int l, int pos, int& slot) const {
-        const int p = pos / page;
-        slot = pos - p * page;
-        return reinterpret_cast<T*>(base + (2LL * l) * layer_kv_bytes) + (long long)table[p] * page_elems();
-    }
-    template <typename T>
-    __device__ __forceinline__ T* vpage(int l, int pos, int& slot) const {
-        const int p = pos / page;
-        slot = pos - p * page;
-        return reinterpret_cast<T*>(base + (2LL * l + 1) * layer_kv_bytes) + (long long)table[p] * page_elems();
-    }
-    // the same, for an already looked-up physical page
-    template <typename T>
-    __device__ __forceinline__ T* kpage_phys(int l, int phys) const {
-        return reinterpret_cast<T*>(base + (2LL * l) * layer_kv_bytes) + (long long)phys * page_elems();
-    }
-    template <typename T>
-    __device__ __forceinline__ T* vpage_phys(int l, int phys) const {
-        return reinterpret_cast<T*>(base + (2LL * l + 1) * layer_kv_bytes) + (long long)phys * page_elems();
-    }
-};
 
 
 // q, k (rotated) and v of the block rows.  Tiles pair the 16-column blocks
@@ -571,6 +531,7 @@ struct OpQKV {
     NormA<T> a;
     const int* len_dev = nullptr;  // device-resident length: row 0 sits at *len_dev (else at pos0)
     int max_ctx = 0;               // the device length is clamped into [0, max_ctx] (rotary table bound)
+    const int* row_depth = nullptr;  // tree rows: row j is rotated for position pos0 + row_depth[j] (in [0, 15])
     const T* wq;
     const T* wk;
     const T* wv;
@@ -607,7 +568,8 @@ struct OpQKV {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int j = min(4 * (lane >> 4) + ii, M - 1);
-            const long long t = (long long)(st.pos0 + j) * half + dim;
+            const int jp = row_depth ? row_depth[j] : j;  // its KV slot stays pos0 + j
+            const long long t = (long long)(st.pos0 + jp) * half + dim;
             st.cs[ii] = cosT[t];
             st.sn[ii] = sinT[t];
         }
@@ -1176,6 +1138,8 @@ struct AttnArgs {
     KVPages kv;
     int layer, C, B, nq, nkv, group, kps, n_splits;
     int causal_base;    // >= 0: causal, query row j sees keys 0..causal_base+j; -1: no mask
+    const uint32_t* tree_anc;  // causal with a tree: row j sees keys below causal_base and key
+                               // causal_base + i iff bit i of tree_anc[j]; null: the chain above
     const int* len_dev; // non-null (draft only): the context length is *len_dev, not C
     float scale_log2;   // log2(e) / sqrt(d)
     float* part_o;      // [(n_splits+1)][nq][16][d]
@@ -1228,13 +1192,14 @@ struct HeadAcc {
 // hi + lo pair of bf16 values (two MFMAs sharing the V operand), so P keeps
 // ~16 bits.
 template <typename T, int D, class VF>
-__device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], int nvalid, float scale_log2, int grp,
-                                           VF&& vfrag) {
-    // raw scores, masked; the running max is kept in scaled log2 units (the
-    // scale is positive, so the max commutes with it)
+__device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], int nvalid, uint64_t vmask,
+                                           float scale_log2, int grp, VF&& vfrag) {
+    // raw scores, masked (key kk of the chunk takes part iff kk < nvalid and
+    // bit kk of vmask is set); the running max is kept in scaled log2 units
+    // (the scale is positive, so the max commutes with it)
     float sr[4][4];
     float mr = -INFINITY;
-    if (__all(nvalid >= 64)) {
+    if (__all(nvalid >= 64 && vmask == ~0ull)) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -1248,7 +1213,7 @@ __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], in
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int kk = kb * 16 + 4 * grp + ii;
-                sr[kb][ii] = kk < nvalid ? s[kb][ii] : -INFINITY;
+                sr[kb][ii] = (kk < nvalid && ((vmask >> kk) & 1ull)) ? s[kb][ii] : -INFINITY;
                 mr = fmaxf(mr, sr[kb][ii]);
             }
     }
@@ -1364,7 +1329,7 @@ __device__ __forceinline__ Frag<T> lds_frag(const char* base, int row, int ncol,
 // bank-conflict free; each wave then computes its query head(s) (HPW per wave)
 // from LDS.  Scores are formed transposed, S^T = K Q^T, so the probabilities
 // land in the B-operand layout of O^T += V^T P^T and never leave registers.
-template <typename T, int D, int HPW>
+template <typename T, int D, int HPW, bool CAUSAL>
 __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs a) {
     constexpr int CH = kAttnChunk;                  // keys per chunk (64)
     constexpr int KCOL = D * (int)sizeof(T) / 16;   // 16-byte columns of a K row
@@ -1418,6 +1383,8 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
     // with a device-resident length the splits are planned for the capacity;
     // those past the current length have no keys (their partial stays empty)
     const int Cnow = a.len_dev ? min(*a.len_dev, a.C) : a.C;
+    // causal rows: the block keys this lane's query row sees (a chain: rows 0..col)
+    const uint32_t anc = !CAUSAL ? 0u : (a.tree_anc && col < a.B) ? a.tree_anc[col] : ((2u << col) - 1u);
     if (split < a.n_splits) {
         const int kbeg = split * a.kps;
         const int kend = min(Cnow, kbeg + a.kps);
@@ -1497,8 +1464,15 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
             const char* kl = lds + (NS == 2 ? (c & 1) : (c % NS)) * STAGE;
             const char* vl = kl + CH * KCOL * 16;
             const int nvalid = kend - (kbeg + c * CH);
-            // keys this lane's query row may see (causal: positions <= causal_base + row)
-            const int nvis = a.causal_base >= 0 ? min(nvalid, a.causal_base + col + 1 - (kbeg + c * CH)) : nvalid;
+            // keys this lane's query row may see: all written ones, or under the
+            // causal mask every key below causal_base and the tree/chain keys
+            // at causal_base + i that anc allows (lo = chunk index of causal_base)
+            uint64_t vmask = ~0ull;
+            if (CAUSAL) {
+                const int lo = a.causal_base - (kbeg + c * CH);
+                if (lo < 64) vmask = lo >= 0 ? (((1ull << lo) - 1ull) | ((uint64_t)anc << lo))
+                                             : (-lo < 32 ? (uint64_t)(anc >> -lo) : 0ull);
+            }
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
                 if (w + 4 * hh >= a.group) break;
@@ -1516,7 +1490,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb) mma(sc[kb], kf[kb], qf[hh][kc]);
                 }
-                softmax_pv<T, D>(acc[hh], sc, nvis, a.scale_log2, grp, [&](int t, int db) {
+                softmax_pv<T, D>(acc[hh], sc, nvalid, vmask, a.scale_log2, grp, [&](int t, int db) {
                     Frag<T> vf = lds_frag<T>(vl, 16 * db + col, VCOL, (32 * t + 8 * grp) * (int)sizeof(T) / 16);
                     if (nvalid < CH) mask_vfrag(vf, t, grp, nvalid);  // never-written positions of the last chunk
                     return vf;
@@ -1544,7 +1518,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
                     mma(sc[kb], kf, qf[hh][kc]);
                 }
             }
-            softmax_pv<T, D>(acc[hh], sc, a.B, a.scale_log2, grp, [&](int t, int db) {
+            softmax_pv<T, D>(acc[hh], sc, a.B, ~0ull, a.scale_log2, grp, [&](int t, int db) {
                 VRun<T> ra, rb;
                 const T* vr = vb_ + (long long)(16 * db + col) * 16;
                 if (t == 0) ra.load(vr + 4 * grp); else ra.load_masked(vr, 0);
@@ -1654,9 +1628,33 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_t* ids, int n_ids, int mask_id, int V,
                                                     int H, float eps, T* x, float* rstd, unsigned long long* best,
-                                                    float* clear, int clear_n) {
+                                                    float* clear, int clear_n, const int32_t* tree_parent,
+                                                    int* tree_info) {
     __shared__ float red[4];
+    __shared__ int par[16];
     const int j = blockIdx.x;
+    if (tree_parent) {
+        // tree verification: row j's depth and the mask of its ancestors and
+        // itself.  A parent outside [0, row) is read as the root, so every
+        // walk ends at row 0 within 15 steps.
+        if (threadIdx.x < 16) {
+            const int r = threadIdx.x;
+            const int p = r < n_ids ? tree_parent[r] : 0;
+            par[r] = (p >= 0 && p < r) ? p : 0;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int u = j, depth = 0;
+            uint32_t anc = 1u;
+            while (u > 0) {
+                anc |= 1u << u;
+                u = par[u];
+                ++depth;
+            }
+            tree_info[j] = depth;
+            tree_info[16 + j] = (int)anc;
+        }
+    }
     for (int i = j * 256 + threadIdx.x; i < clear_n; i += gridDim.x * 256) clear[i] = 0.f;
     const int tok = j < n_ids ? min(max(ids[j], 0), V - 1) : mask_id;  // out-of-range ids are clamped
     const Frag<T>* src = reinterpret_cast<const Frag<T>*>(embed + (long long)tok * H);
@@ -2251,18 +2249,6 @@ static hipError_t run_tile_gemm(const Op& op, int M, int N, int K, hipStream_t s
 // launchers
 // ============================================================================
 
-template <typename T>
-static KVPages make_pages(const DevCtx& c) {
-    KVPages kv;
-    kv.base = c.kv;
-    kv.table = reinterpret_cast<const int32_t*>(c.ws + c.lay.page_table);
-    kv.layer_kv_bytes = (long long)c.lay.kv_layer_kv;
-    kv.page = c.dm.page;
-    kv.nkv = c.dm.nkv;
-    kv.d = c.dm.d;
-    kv.elem = c.dm.elem;
-    return kv;
-}
 
 #define WS(type, field) reinterpret_cast<type>(c.ws + c.lay.field)
 
@@ -2285,9 +2271,10 @@ struct PassArgs {
     int32_t* tokens;
     void* const* cap;  // causal: 5 capture buffers (feature layers) or null
     long long cap_ld;
-    void* layer_out;   // draft: [Ld][rows][layer_ld] residual after every layer, or null
+    void* layer_out;   // [Ld][rows][layer_ld] residual after every layer (replaces cap), or null
     long long layer_ld;
     const int* len_dev;  // draft: the context length lives on the device (C unused), or null
+    const int32_t* tree_parent;  // causal: the rows form a tree (parent of each row), or null (a chain)
 };
 
 template <typename T>
@@ -2314,8 +2301,9 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     const float eps = (float)d.eps;
     hipError_t e;
 
+    int* tree_info = WS(int*, tree_info);
     hipLaunchKernelGGL((embed_kernel<T>), dim3(B), dim3(256), 0, s, (const T*)c.embed, pa.ids, pa.n_ids, d.mask_id, d.V,
-                       H, eps, x, rstd, best, ss0, ss_n);
+                       H, eps, x, rstd, best, ss0, ss_n, pa.tree_parent, tree_info);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     int kps, ns, nparts;
@@ -2365,6 +2353,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         qkv.pos0 = C;
         qkv.len_dev = pa.len_dev;
         qkv.max_ctx = d.max_ctx;
+        qkv.row_depth = pa.tree_parent ? tree_info : nullptr;
         qkv.tq = nq * D / 32;
         qkv.tk = nkv * D / 32;
         qkv.cosT = cosT;
@@ -2393,15 +2382,21 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         aa.kps = kps;
         aa.n_splits = ns;
         aa.causal_base = pa.causal ? C : -1;
+        aa.tree_anc = pa.tree_parent ? reinterpret_cast<const uint32_t*>(tree_info + 16) : nullptr;
         aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
         aa.part_o = WS(float*, attn_o);
         aa.part_ml = WS(float*, attn_ml);
         c.tracer->begin(DFLASH_TRACE_ATTN, s);
         const dim3 agrid(nparts, nkv), ablk(256);
-        if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1>), agrid, ablk, 0, s, aa);
-        else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2>), agrid, ablk, 0, s, aa);
-        else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1>), agrid, ablk, 0, s, aa);
-        else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2>), agrid, ablk, 0, s, aa);
+        auto attn = [&](auto causal) {
+            constexpr bool CA = decltype(causal)::value;
+            if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1, CA>), agrid, ablk, 0, s, aa);
+            else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2, CA>), agrid, ablk, 0, s, aa);
+            else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1, CA>), agrid, ablk, 0, s, aa);
+            else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2, CA>), agrid, ablk, 0, s, aa);
+        };
+        if (pa.causal) attn(std::true_type{});
+        else attn(std::false_type{});
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(512), 0, s, aa.part_o, aa.part_ml, nparts, nq,
                            D, B, obuf);
@@ -2509,7 +2504,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
 
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits, int32_t* tokens,
                               void* layer_out, long long layer_ld, const int* len_dev, hipStream_t s) {
-    PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0, layer_out, layer_ld, len_dev};
+    PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0, layer_out, layer_ld, len_dev, nullptr};
     c.tracer->begin(DFLASH_TRACE_DRAFT, s);
     hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_DRAFT, s);
@@ -2517,8 +2512,9 @@ hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, flo
 }
 
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits, int32_t* argmax,
-                                 void* const* capture, long long capture_ld, hipStream_t s) {
-    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, nullptr, 0, nullptr};
+                                 void* const* capture, long long capture_ld, hipStream_t s,
+                                 const int32_t* tree_parent, void* layer_out, long long layer_ld) {
+    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, layer_out, layer_ld, nullptr, tree_parent};
     c.tracer->begin(DFLASH_TRACE_TARGET, s);
     hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_TARGET, s);

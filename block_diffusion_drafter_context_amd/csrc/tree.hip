@@ -1,0 +1,412 @@
+// tree.hip -- tree verification (DDTree) around the target pass.
+//
+// "DFlash 深度解析…" §8.2 (DDTree tree verification): one target pass checks a
+// tree of candidate drafts under a node budget instead of one chain.  The
+// target pass itself is the causal forward with a tree mask (kernels.hip);
+// this file holds the small steps around it:
+//  - top-K of the draft's logits per block position, with log-probabilities;
+//  - the best-first candidate tree: the `budget` nodes with the largest sum of
+//    log-probabilities along their root path (ties: shallower, then the
+//    lexicographically smaller rank path), scores added in fp32;
+//  - the accepted path: from the root, follow the child that carries the
+//    target's greedy token after the current node;
+//  - the compaction of the accepted rows behind the root (KV slots of every
+//    layer, captured feature rows), after which the cache holds exactly the
+//    accepted sequence.
+// All of them are latency-bound, tiny launches next to the pass they serve.
+#include "device_common.h"
+#include "kernels.h"
+#include "kv_pages.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace dflash {
+
+namespace {
+
+constexpr int kTopKThreads = 256;
+constexpr int kPartStride = 2 * kTopKMax + 2;  // floats per (row, segment) record
+
+// (value, id) order of the top-K: larger value first, then lower id
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+// (max, sum of exp(x - max)) of two parts, in a fixed operand order
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+    if (m2 == -INFINITY) return;
+    if (m == -INFINITY) {
+        m = m2;
+        s = s2;
+        return;
+    }
+    const float M = fmaxf(m, m2);
+    s = s * expf(m - M) + s2 * expf(m2 - M);
+    m = M;
+}
+
+// One (row, vocabulary segment) per workgroup: every thread keeps a sorted
+// list of its K best (value, id) pairs and its own running (max, sum of exp);
+// then K rounds of a workgroup-wide best pick the segment's K best in order.
+__global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float* logits, long long ld, int V, int K,
+                                                                    float* part) {
+    __shared__ float s_v[kTopKThreads / 64];
+    __shared__ int s_i[kTopKThreads / 64];
+    __shared__ float s_m[kTopKThreads / 64], s_s[kTopKThreads / 64];
+    const int seg = blockIdx.x, r = blockIdx.y, S = gridDim.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int per = (V + S - 1) / S;
+    const int beg = seg * per, end = min(V, beg + per);
+    const float* x = logits + (long long)r * ld;
+
+    float tv[kTopKMax];
+    int ti[kTopKMax];
+#pragma unroll
+    for (int q = 0; q < kTopKMax; ++q) {
+        tv[q] = -INFINITY;
+        ti[q] = 0x7fffffff;
+    }
+    float thr = -INFINITY;  // the K-th value held (ids scanned in ascending order: ties stay out)
+    float m = -INFINITY, sum = 0.f;
+    for (int i = beg + tid; i < end; i += kTopKThreads) {
+        const float v = x[i];
+        if (v > m) {
+            sum = sum * expf(m - v) + 1.f;
+            m = v;
+        } else {
+            sum += expf(v - m);
+        }
+        if (v > thr) {
+            float cv = v;
+            int ci = i;
+#pragma unroll
+            for (int q = 0; q < kTopKMax; ++q) {  // insert, shifting the rest down
+                const bool take = cv > tv[q];
+                const float ov = tv[q];
+                const int oi = ti[q];
+                tv[q] = take ? cv : ov;
+                ti[q] = take ? ci : oi;
+                cv = take ? ov : cv;
+                ci = take ? oi : ci;
+            }
+#pragma unroll
+            for (int q = 0; q < kTopKMax; ++q)
+                if (q == K - 1) thr = tv[q];
+        }
+    }
+    float* rec = part + ((long long)r * S + seg) * kPartStride;
+
+    // segment (max, sum): wave butterfly, then the four waves in order
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(sum, o, 64);
+        // both lanes of a pair combine in the same operand order (lower lane first)
+        if (lane & o) {
+            float mm = m2, ss = s2;
+            lse_combine(mm, ss, m, sum);
+            m = mm;
+            sum = ss;
+        } else {
+            lse_combine(m, sum, m2, s2);
+        }
+    }
+    if (lane == 0) {
+        s_m[w] = m;
+        s_s[w] = sum;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float M = s_m[0], Ssum = s_s[0];
+        for (int i = 1; i < kTopKThreads / 64; ++i) lse_combine(M, Ssum, s_m[i], s_s[i]);
+        rec[2 * kTopKMax] = M;
+        rec[2 * kTopKMax + 1] = Ssum;
+    }
+
+    // K rounds: the best list head over the workgroup leaves its list
+    for (int k = 0; k < K; ++k) {
+        float bv = tv[0];
+        int bi = ti[0];
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float v2 = __shfl_xor(bv, o, 64);
+            const int i2 = __shfl_xor(bi, o, 64);
+            if (ranks_before(v2, i2, bv, bi)) {
+                bv = v2;
+                bi = i2;
+            }
+        }
+        __syncthreads();  // the previous round's reads of s_v / s_i are done
+        if (lane == 0) {
+            s_v[w] = bv;
+            s_i[w] = bi;
+        }
+        __syncthreads();
+        bv = s_v[0];
+        bi = s_i[0];
+        for (int i = 1; i < kTopKThreads / 64; ++i)
+            if (ranks_before(s_v[i], s_i[i], bv, bi)) {
+                bv = s_v[i];
+                bi = s_i[i];
+            }
+        if (tid == 0) {
+            rec[k] = bv;
+            reinterpret_cast<int*>(rec)[kTopKMax + k] = bi;
+        }
+        if (ti[0] == bi && tv[0] == bv) {  // the owner (ids are unique among real entries)
+#pragma unroll
+            for (int q = 0; q + 1 < kTopKMax; ++q) {
+                tv[q] = tv[q + 1];
+                ti[q] = ti[q + 1];
+            }
+            tv[kTopKMax - 1] = -INFINITY;
+            ti[kTopKMax - 1] = 0x7fffffff;
+        }
+    }
+}
+
+// One row per workgroup: the rank of each of the S*K segment candidates among
+// all of them places the row's K best; log-probabilities subtract the row's
+// log-sum-exp, merged from the segments in segment order.
+__global__ __launch_bounds__(512) void topk_merge_kernel(const float* part, int S, int K, int32_t* ids, float* logp) {
+    __shared__ float c_v[kTopKSegs * kTopKMax];
+    __shared__ int c_i[kTopKSegs * kTopKMax];
+    __shared__ float s_lse;
+    const int r = blockIdx.x, tid = threadIdx.x, n = S * K;
+    const float* base = part + (long long)r * S * kPartStride;
+    for (int t = tid; t < n; t += blockDim.x) {
+        const float* rec = base + (long long)(t / K) * kPartStride;
+        c_v[t] = rec[t % K];
+        c_i[t] = reinterpret_cast<const int*>(rec)[kTopKMax + t % K];
+    }
+    if (tid == 0) {
+        float M = -INFINITY, L = 0.f;
+        for (int sgi = 0; sgi < S; ++sgi) {
+            const float* rec = base + (long long)sgi * kPartStride;
+            lse_combine(M, L, rec[2 * kTopKMax], rec[2 * kTopKMax + 1]);
+        }
+        s_lse = M + logf(L);
+    }
+    __syncthreads();
+    const float lse = s_lse;
+    for (int t = tid; t < n; t += blockDim.x) {
+        const float v = c_v[t];
+        const int id = c_i[t];
+        int rank = 0;
+        for (int u = 0; u < n; ++u) rank += ranks_before(c_v[u], c_i[u], v, id) ? 1 : 0;
+        if (rank < K) {
+            ids[(long long)r * K + rank] = id;
+            logp[(long long)r * K + rank] = v - lse;
+        }
+    }
+}
+
+// Candidate order: valid first, larger score, smaller depth, smaller path key.
+struct Cand {
+    float score;
+    int depth;
+    int lane;
+    unsigned long long path;
+    bool ok;
+};
+
+__device__ __forceinline__ bool cand_before(const Cand& a, const Cand& b) {
+    if (a.ok != b.ok) return a.ok;
+    if (a.score != b.score) return a.score > b.score;
+    if (a.depth != b.depth) return a.depth < b.depth;
+    return a.path < b.path;
+}
+
+// One wave.  Lane u < count holds node u: its score, depth, rank path (4 bits
+// per depth, depth 1 in the top bits) and the rank of its next unchosen child.
+// Every step the best of the lanes' next children joins the tree as node
+// `count`; a child never beats its parent or an earlier sibling, so the
+// chosen nodes are the budget best of the whole candidate tree.
+__global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* anchor, int V, const int32_t* ids,
+                                                        const float* logp, int R, int K, int budget, int32_t* tokens,
+                                                        int32_t* parent) {
+    __shared__ float s_lp[15 * kTopKMax];
+    __shared__ int s_id[15 * kTopKMax];
+    const int lane = threadIdx.x;
+    for (int i = lane; i < R * K; i += 64) {
+        s_lp[i] = logp[i];
+        s_id[i] = ids[i];
+    }
+    __syncthreads();
+    float sc = 0.f;
+    int dep = 0, nr = 0, par = -1;
+    unsigned long long path = 0ull;
+    int tok = lane == 0 ? min(max(anchor[0], 0), V - 1) : 0;
+    for (int count = 1; count <= budget; ++count) {
+        Cand c;
+        c.ok = lane < count && dep < R && nr < K;
+        c.score = c.ok ? sc + s_lp[c.ok ? dep * K + nr : 0] : -INFINITY;
+        c.depth = dep + 1;
+        c.path = path | ((unsigned long long)(c.ok ? nr : 0) << (4 * (15 - min(dep, 15))));
+        c.lane = lane;
+        for (int o = 32; o >= 1; o >>= 1) {
+            Cand d;
+            d.ok = __shfl_xor((int)c.ok, o, 64) != 0;
+            d.score = __shfl_xor(c.score, o, 64);
+            d.depth = __shfl_xor(c.depth, o, 64);
+            d.lane = __shfl_xor(c.lane, o, 64);
+            d.path = ((unsigned long long)(unsigned)__shfl_xor((int)(c.path >> 32), o, 64) << 32) |
+                     (unsigned)__shfl_xor((int)(c.path & 0xffffffffull), o, 64);
+            if (cand_before(d, c) || (!cand_before(c, d) && d.lane < c.lane)) c = d;
+        }
+        // every lane now holds the winner; its rank is the path digit at its depth
+        const int rank = (int)((c.path >> (4 * (16 - c.depth))) & 15ull);
+        if (lane == count) {
+            sc = c.score;
+            dep = c.depth;
+            path = c.path;
+            nr = 0;
+            par = c.lane;
+            tok = s_id[min((c.depth - 1) * K + rank, R * K - 1)];
+        }
+        if (lane == c.lane) ++nr;
+    }
+    if (lane <= budget) {
+        tokens[lane] = tok;
+        parent[lane] = par;
+    }
+}
+
+// One wave: lane j holds node j.  From the root, the child (lowest index
+// among equals) whose token is the target's greedy token after the current
+// node is accepted, until none is.  A parent outside [0, j) reads as the root.
+__global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* tokens, const int32_t* parent,
+                                                         const int32_t* target, int M, int32_t* out) {
+    const int lane = threadIdx.x;
+    const bool node = lane < M;
+    const int tok = node ? tokens[lane] : 0;
+    const int p = node ? parent[lane] : 0;
+    const int par = (p >= 0 && p < lane) ? p : 0;
+    const int tgt = node ? target[lane] : 0;
+    int cur = 0, k = 0;
+    int path[15];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) path[i] = 0;
+#pragma unroll
+    for (int step = 0; step < 15; ++step) {
+        const int want = __shfl(tgt, cur, 64);
+        const unsigned long long hit = __ballot(node && lane >= 1 && par == cur && tok == want);
+        if (hit == 0ull) break;
+        cur = __ffsll((long long)hit) - 1;
+        path[step] = cur;
+        k = step + 1;
+    }
+    const int bonus = __shfl(tgt, cur, 64);
+    if (lane == 0) {
+        out[0] = k;
+        out[1] = bonus;
+#pragma unroll
+        for (int i = 0; i < 15; ++i) out[2 + i] = path[i];
+    }
+}
+
+struct CommitArgs {
+    KVPages kv;
+    void* cap[5];
+    long long cap_ld;
+    int H, Ld, pos0, M;
+    const int32_t* result;
+};
+
+// Blocks [0, Ld*nkv*2): one (layer, kv head, K|V) each, a thread per head
+// dimension.  The rest: one (capture buffer, 256-column slice) each.  Every
+// thread loads all of its accepted values before storing any, so sources that
+// are also destinations (path[i] == 1 + i' for i' > i) are read first.
+template <typename T>
+__global__ __launch_bounds__(256) void tree_commit_kernel(CommitArgs a) {
+    const int M = a.M;
+    const int k = min(max(a.result[0], 0), M - 1);
+    int src[15];
+#pragma unroll
+    for (int i = 0; i < 15; ++i) src[i] = i < k ? min(max(a.result[2 + i], 1), M - 1) : 1;
+    const int nkv = a.kv.nkv, d = a.kv.d;
+    const int kv_blocks = a.Ld * nkv * 2;
+    T val[15];
+    if ((int)blockIdx.x < kv_blocks) {
+        const int b = blockIdx.x;
+        const int isv = b & 1, h = (b >> 1) % nkv, l = (b >> 1) / nkv;
+        const int dim = threadIdx.x;
+        if (dim >= d) return;
+        auto at = [&](int pos) -> T* {
+            int slot;
+            if (!isv) return a.kv.kpage<T>(l, pos, slot) + ((long long)h * a.kv.page + slot) * d + dim;
+            T* pg = a.kv.vpage<T>(l, pos, slot);
+            return pg + ((long long)h * d + dim) * a.kv.page + vslot(slot);
+        };
+#pragma unroll
+        for (int i = 0; i < 15; ++i)
+            if (i < k) val[i] = *at(a.pos0 + src[i]);
+#pragma unroll
+        for (int i = 0; i < 15; ++i)
+            if (i < k) *at(a.pos0 + 1 + i) = val[i];
+        return;
+    }
+    const int cb = blockIdx.x - kv_blocks;
+    const int slices = (a.H + 255) / 256;
+    T* buf = reinterpret_cast<T*>(a.cap[cb / slices]);
+    const int col = (cb % slices) * 256 + threadIdx.x;
+    if (!buf || col >= a.H) return;
+#pragma unroll
+    for (int i = 0; i < 15; ++i)
+        if (i < k) val[i] = buf[(long long)src[i] * a.cap_ld + col];
+#pragma unroll
+    for (int i = 0; i < 15; ++i)
+        if (i < k) buf[(long long)(1 + i) * a.cap_ld + col] = val[i];
+}
+
+}  // namespace
+
+hipError_t launch_topk(const DevCtx& c, const float* logits, long long ld, int rows, int K, int32_t* ids, float* logp,
+                       hipStream_t s) {
+    const int V = c.dm.V;
+    const int S = std::max(1, std::min(kTopKSegs, V / 4096));
+    float* part = reinterpret_cast<float*>(c.ws + c.lay.topk_part);
+    hipLaunchKernelGGL(topk_partial_kernel, dim3(S, rows), dim3(kTopKThreads), 0, s, logits, ld, V, K, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(512), 0, s, part, S, K, ids, logp);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_build(const int32_t* anchor, int V, const int32_t* ids, const float* logp, int R, int K,
+                             int budget, int32_t* tokens, int32_t* parent, hipStream_t s) {
+    hipLaunchKernelGGL(tree_build_kernel, dim3(1), dim3(64), 0, s, anchor, V, ids, logp, R, K, budget, tokens, parent);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_accept(const int32_t* tokens, const int32_t* parent, const int32_t* target, int M,
+                              int32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(tree_accept_kernel, dim3(1), dim3(64), 0, s, tokens, parent, target, M, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_commit(const DevCtx& c, int pos0, int M, const int32_t* result, void* const* capture,
+                              long long capture_ld, hipStream_t s) {
+    CommitArgs a;
+    a.H = c.dm.H;
+    a.Ld = c.dm.Ld;
+    a.pos0 = pos0;
+    a.M = M;
+    a.result = result;
+    a.cap_ld = capture_ld;
+    int n_cap = 0;
+    for (int i = 0; i < 5; ++i) {
+        a.cap[i] = capture ? capture[i] : nullptr;
+        n_cap += a.cap[i] != nullptr;
+    }
+    const int blocks = c.dm.Ld * c.dm.nkv * 2 + (n_cap ? 5 * ((c.dm.H + 255) / 256) : 0);
+    if (c.dm.dtype == DFLASH_F32) {
+        a.kv = make_pages<float>(c);
+        hipLaunchKernelGGL(tree_commit_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    } else {
+        a.kv = make_pages<bf16_t>(c);
+        hipLaunchKernelGGL(tree_commit_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -111,3 +111,59 @@ def spec_generate(target: DFlash, draft: DFlash, prompt: torch.Tensor, n_new: in
         anchor.copy_(res[1:2])
         C += k + 1
     return out[:n_new], ks
+
+
+def spec_tree_generate(target: DFlash, draft: DFlash, prompt: torch.Tensor, n_new: int, K: int = 4,
+                       budget: int = 15,
+                       trees_fn: Optional[Callable[[int], Tuple[Sequence[int], Sequence[int]]]] = None
+                       ) -> Tuple[List[int], List[int]]:
+    """DFlash speculative decoding with tree verification (DDTree).
+
+    Per step at context length C with anchor a: draft the block with logits,
+    take the top-K tokens of every drafted position, build the best-first tree
+    of `budget` nodes rooted at a (or take trees_fn(C) -> (node tokens after
+    the root, parents), parents indexing [root, nodes...]), verify it with one
+    tree-masked target call, accept the longest matching root path, move the
+    accepted rows behind the root in the target's cache and captured features,
+    fuse and inject those k + 1 rows into the draft, keep C + k + 1 positions
+    in both caches.  Returns (tokens, k of every step)."""
+    B = draft.shape.block
+    dev = target.device
+    first = prefill(target, prompt, draft)
+    cap = _Capture(target)
+    lg = torch.empty(B, draft.shape.vocab, dtype=torch.float32, device=dev)
+    dtok = torch.empty(B, dtype=torch.int32, device=dev)
+    g = torch.empty(ROWS, dtype=torch.int32, device=dev)
+    res = torch.empty(17, dtype=torch.int32, device=dev)
+    fused = torch.empty(ROWS, draft.shape.hidden, dtype=draft.dtype, device=dev)
+    anchor = first.clone()
+    out = [int(first.item())]
+    ks: List[int] = []
+    C = prompt.shape[0]
+    while len(out) < n_new:
+        if trees_fn is None:
+            draft.draft_block(anchor, tokens=dtok, logits=lg)
+            ids, lp = draft.draft_topk(lg[1:], K)
+            ttok, tpar = draft.build_tree(anchor, ids, lp, budget)
+        else:
+            nodes, parents = trees_fn(C)
+            ttok = torch.empty(len(nodes) + 1, dtype=torch.int32, device=dev)
+            ttok[0:1].copy_(anchor)
+            ttok[1:].copy_(torch.tensor(list(nodes), dtype=torch.int32))
+            tpar = torch.tensor([-1] + list(parents), dtype=torch.int32, device=dev)
+        M = ttok.shape[0]
+        target.target_forward(ttok, argmax=g[:M], capture=cap.views(M), parent=tpar)
+        target.tree_accept(ttok, tpar, g[:M], out=res)
+        target.tree_commit(C, M, res, capture=cap.views(M))
+        host = torch.cat([res, ttok]).cpu()
+        k, bonus = int(host[0]), int(host[1])
+        path = [int(j) for j in host[2:2 + k]]
+        target.rollback(C + k + 1)
+        f = draft.fuse_context(cap.layer_list(k + 1), out=fused[:k + 1])
+        draft.inject_kv(f, C)
+        out.extend(int(host[17 + j]) for j in path)
+        out.append(bonus)
+        ks.append(k)
+        anchor.copy_(res[1:2])
+        C += k + 1
+    return out[:n_new], ks

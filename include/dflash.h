@@ -40,6 +40,8 @@ extern "C" {
 #define DFLASH_MAX_LAYERS 64
 #define DFLASH_NUM_FEATURES 5
 #define DFLASH_MAX_BLOCK 16
+#define DFLASH_TREE_MAX_K 16   /* candidates per depth of a verification tree */
+#define DFLASH_TREE_RESULT 17  /* int32 entries of a tree acceptance result */
 
 typedef enum {
     DFLASH_OK = 0,
@@ -267,6 +269,91 @@ dflash_status dflash_target_forward(dflash_ctx* ctx, const int32_t* tokens, int3
                                     float* logits_out, int32_t* argmax_out,
                                     void* const* capture, int64_t capture_ld, void* stream);
 
+/* ---- Tree verification (DDTree) ------------------------------------------
+ * [A] §8.2 (DDTree tree verification): instead of one chain of drafts, one
+ * target pass checks a tree of candidates under a node budget, so a rejected
+ * draft at one depth can still be followed by another branch.  The passage
+ * names the idea and the budget, not the construction; the readings taken:
+ *  - depth d of the tree holds candidates for position C+d (the anchor is the
+ *    root at C): the draft's top-K tokens of block row d with their
+ *    log-probabilities (log-softmax of that row's logits);
+ *  - a node's score is the sum of the log-probabilities on its root path; the
+ *    tree is the `budget` best nodes, ordered by score (descending), then
+ *    depth, then rank path (lexicographic).  They always form a tree, and they
+ *    maximise the expected number of accepted drafts when positions are taken
+ *    as independent.  Scores are fp32 sums, one rounding per edge;
+ *  - verification follows, from the root, the child whose token is the
+ *    target's greedy token after the current node.
+ * Trees have at most 16 nodes (the root and a budget of up to 15), one
+ * verification pass of up to 16 rows.  Node order: parent[j] < j. */
+
+/* Per row r < rows of logits ([rows][ld] device fp32, ld >= V): the K largest
+ * token ids (ties: lower id first) into ids_out (device int32 [rows][K]) and
+ * their log-probabilities log_softmax(row)[id] into logp_out (device fp32
+ * [rows][K]).  1 <= rows <= 16, 1 <= K <= min(16, V).  For a block drafted by
+ * dflash_draft_block, pass the logits from row 1 on (rows = B - 1). */
+dflash_status dflash_draft_topk(dflash_ctx* ctx, const float* logits, int64_t ld, int32_t rows, int32_t K,
+                                int32_t* ids_out, float* logp_out, void* stream);
+
+/* The verification tree: root = anchor (device int32[1], clamped into
+ * [0, V)), and the `budget` best nodes of the candidate tree whose depth d
+ * (1..depths) offers ids[d-1][0..K-1] with log-probabilities logp[d-1][..]
+ * (device, [depths][K] as written by dflash_draft_topk, entries of a row in
+ * descending order).  tokens_out, parent_out: device int32[budget + 1]; node 0
+ * is the root (parent -1), node j >= 1 has parent_out[j] < j.  1 <= depths <=
+ * 15, 1 <= K <= 16, 0 <= budget <= 15 and no more than the candidate tree
+ * holds (INVAL). */
+dflash_status dflash_build_tree(dflash_ctx* ctx, const int32_t* anchor, const int32_t* ids, const float* logp,
+                                int32_t depths, int32_t K, int32_t budget, int32_t* tokens_out,
+                                int32_t* parent_out, void* stream);
+
+/* dflash_target_forward over the M nodes of a tree (parent: device int32[M],
+ * parent[0] ignored, an entry outside [0, j) is read as 0, the root): row j
+ * is placed at position C + depth(j), its K/V are stored at cache slot C + j,
+ * and it attends to the cache before C and to its ancestors and itself, so
+ * it computes what a causal forward of its root path computes (up to
+ * rounding order).  argmax_out[j] is the target's greedy token after node j.
+ * Afterwards length = C + M; accept with dflash_tree_accept, move the
+ * accepted rows with dflash_tree_commit, then dflash_rollback to C + 1 + k.
+ * Same arguments, errors and capture rules as dflash_target_forward. */
+dflash_status dflash_target_forward_tree(dflash_ctx* ctx, const int32_t* tokens, const int32_t* parent, int32_t M,
+                                         float* logits_out, int32_t* argmax_out, void* const* capture,
+                                         int64_t capture_ld, void* stream);
+
+/* dflash_target_forward (parent NULL) or dflash_target_forward_tree, and in
+ * the same launches the residual stream after every layer: layer_out
+ * (device, [Ld][M][layer_ld] in the context dtype) receives row j of layer
+ * l's output at layer_out[(l*M + j)*layer_ld].  An inspection aid (a test can
+ * feed layer l's input to another implementation of that one layer); no
+ * feature capture.  layer_ld >= H and keeps rows aligned (INVAL otherwise). */
+dflash_status dflash_target_forward_ex(dflash_ctx* ctx, const int32_t* tokens, const int32_t* parent, int32_t M,
+                                       float* logits_out, int32_t* argmax_out, void* layer_out, int64_t layer_ld,
+                                       void* stream);
+
+/* Greedy acceptance on a verified tree of M nodes (tokens, parent, target:
+ * device int32[M]; target[j] = the target's greedy token after node j; a
+ * parent outside [0, j) is read as 0).  From the root, while a child of the
+ * current node carries target[current] (the lowest-index one if several),
+ * move to it.  result_out: device int32[DFLASH_TREE_RESULT] = {k, bonus,
+ * path[0..14]}: k accepted nodes, the target's token after the last one, and
+ * their node indices (path[i] has depth i + 1; unused entries 0).  The prefix
+ * {k, bonus} has the layout of a dflash_verify_accept result. */
+dflash_status dflash_tree_accept(dflash_ctx* ctx, const int32_t* tokens, const int32_t* parent, const int32_t* target,
+                                 int32_t M, int32_t* result_out, void* stream);
+
+/* After dflash_target_forward_tree of M rows at pos0 and dflash_tree_accept:
+ * for i < k, copy the K/V of cache slot pos0 + path[i] to slot pos0 + 1 + i in
+ * every layer, and row path[i] of each non-NULL capture buffer (host array of
+ * DFLASH_NUM_FEATURES device pointers, rows of capture_ld elements, or NULL)
+ * to row 1 + i.  Slots and rows then hold the root and the accepted nodes in
+ * sequence order, which is what a causal forward of that sequence stores (the
+ * nodes were rotated at their depths).  result: device, as written by
+ * dflash_tree_accept (k is clamped to [0, M-1], path entries to [1, M-1]).
+ * Requires pos0 >= 0 and pos0 + M <= length (INVAL); the length is not
+ * changed. */
+dflash_status dflash_tree_commit(dflash_ctx* ctx, int32_t pos0, int32_t M, const int32_t* result,
+                                 void* const* capture, int64_t capture_ld, void* stream);
+
 /* Load already-rotated K and V for positions [pos0, pos0+M) of every layer
  * (restoring a saved cache, or K/V computed elsewhere).  k, v: device
  * [Ld, M, nkv, d] contiguous.  Same pos0/capacity rules as dflash_inject_kv. */
@@ -290,7 +377,8 @@ typedef enum {
     DFLASH_TRACE_DRAFT = 7,    /* the whole dflash_draft_block call */
     DFLASH_TRACE_FUSE = 8,     /* fusion GEMM of dflash_fuse_context (without its RMSNorm) */
     DFLASH_TRACE_INJECT = 9,   /* injection of dflash_inject_kv */
-    DFLASH_TRACE_TARGET = 10   /* the whole dflash_target_forward call */
+    DFLASH_TRACE_TARGET = 10,  /* the whole dflash_target_forward(_tree) call */
+    DFLASH_TRACE_TREE = 11     /* each tree helper call: top-K, tree build, tree accept, tree commit */
 } dflash_trace_class;
 
 /* Tracing aid: while enabled, every launch of the given kernel class is

@@ -61,8 +61,9 @@ def lib():
         L.orc_accept.argtypes = [vp, vp, i32, vp, vp]
         L.orc_target_forward.argtypes = [vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp, vp]
         L.orc_target_forward_tree.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, vp, vp, vp, vp, vp]
+        L.orc_target_layer.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp, i64, vp]
         for f in ("orc_fuse_rows", "orc_inject_rows", "orc_draft_block", "orc_target_forward", "orc_draft_layer",
-                  "orc_lm_head", "orc_target_forward_tree"):
+                  "orc_lm_head", "orc_target_forward_tree", "orc_target_layer"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -305,6 +306,22 @@ def target_forward(model: Model, cache: TargetCache, tokens: Sequence[int], pos0
                                            _dptr(cache.v), *outs)
     assert rc == 0, "not a valid tree" if parent is not None else "capacity"
     return {"argmax": am, "gap": gap, "hidden": hid, "logits": logits}
+
+
+def target_layer(model: Model, layer: int, x_in: np.ndarray, pos0: int, cache: TargetCache,
+                 parent: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Layer `layer` of target_forward alone (causal, or tree with `parent`):
+    rows x_in [n, H] (storage values) at pos0 over cache.k/v[layer] (keys
+    before pos0); writes the rows' K/V into that layer's cache.  Returns [n, H]."""
+    x_in = np.ascontiguousarray(x_in, dtype=np.float64)
+    n = x_in.shape[0]
+    par = np.ascontiguousarray(parent, dtype=np.int32) if parent is not None else None
+    out = np.empty_like(x_in)
+    rc = lib().orc_target_layer(model.ref, layer, _dptr(x_in), n, pos0,
+                                par.ctypes.data if par is not None else None,
+                                cache.k[layer].ctypes.data, cache.v[layer].ctypes.data, cache.cap, _dptr(out))
+    assert rc == 0
+    return out
 
 
 # ---------------------------------------------------------------- generation loops

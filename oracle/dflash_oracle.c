@@ -503,17 +503,15 @@ int orc_target_forward(const orc_model* m, const int32_t* tokens, int32_t n, int
  * and to the slots of its ancestors and itself.  Every row therefore computes
  * what a causal forward over its root-to-row path would compute.  -1 when the
  * parent array is not such a tree. */
-int orc_target_forward_tree(const orc_model* m, const int32_t* tokens, const int32_t* parent, int32_t n,
-                            int64_t pos0, double* cache_k, double* cache_v, int64_t cap,
-                            const int32_t* capture, double* hidden_out,
-                            float* logits_out, int32_t* argmax_out, double* gap_out)
+/* Positions and visibility of tree rows: pos[j] = pos0 + depth(j), vis[j][u]
+ * = 1 for u an ancestor of j or j itself.  -1 when parent is not a tree in
+ * node order (parent[0] = -1, 0 <= parent[j] < j). */
+static int tree_layout(const int32_t* parent, int32_t n, int64_t pos0, int64_t* pos, unsigned char* vis)
 {
-    if (n < 1 || pos0 + n > cap || m->head_dim > 256 || parent[0] != -1) return -1;
+    if (n < 1 || parent[0] != -1) return -1;
     for (int32_t j = 1; j < n; ++j)
         if (parent[j] < 0 || parent[j] >= j) return -1;
-    int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
-    unsigned char* vis = (unsigned char*)calloc((size_t)n * n, 1);
-    if (!pos || !vis) { free(pos); free(vis); return -1; }
+    memset(vis, 0, (size_t)n * n);
     for (int32_t j = 0; j < n; ++j) {
         int64_t depth = 0;
         for (int32_t u = j; u >= 0; u = parent[u]) {  /* walk up to the root */
@@ -522,8 +520,47 @@ int orc_target_forward_tree(const orc_model* m, const int32_t* tokens, const int
         }
         pos[j] = pos0 + depth;
     }
-    const int rc = target_rows(m, tokens, n, pos0, pos, vis, cache_k, cache_v, cap, capture, hidden_out,
-                               logits_out, argmax_out, gap_out);
+    return 0;
+}
+
+int orc_target_forward_tree(const orc_model* m, const int32_t* tokens, const int32_t* parent, int32_t n,
+                            int64_t pos0, double* cache_k, double* cache_v, int64_t cap,
+                            const int32_t* capture, double* hidden_out,
+                            float* logits_out, int32_t* argmax_out, double* gap_out)
+{
+    if (n < 1 || pos0 + n > cap || m->head_dim > 256) return -1;
+    int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+    unsigned char* vis = (unsigned char*)malloc((size_t)n * n);
+    int rc = -1;
+    if (pos && vis && tree_layout(parent, n, pos0, pos, vis) == 0)
+        rc = target_rows(m, tokens, n, pos0, pos, vis, cache_k, cache_v, cap, capture, hidden_out,
+                         logits_out, argmax_out, gap_out);
     free(pos); free(vis);
     return rc;
+}
+
+/* One layer of the causal (parent NULL) or tree forward on its own: rows
+ * x_in[n][H] (storage values, e.g. another implementation's input to layer
+ * l) at pos0, with layer l's dense cache cache_k/v [cap][nkv*d] holding the
+ * keys before pos0; the rows' K/V are written at pos0.. as in the full
+ * forward.  x_out[n][H] receives the residual stream after the layer. */
+int orc_target_layer(const orc_model* m, int32_t l, const double* x_in, int32_t n, int64_t pos0,
+                     const int32_t* parent, double* cache_k, double* cache_v, int64_t cap, double* x_out)
+{
+    const int64_t NK = (int64_t)m->n_kv_heads * m->head_dim;
+    if (n < 1 || pos0 + n > cap || m->head_dim > 256 || l < 0 || l >= m->n_layers) return -1;
+    int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+    unsigned char* vis = parent ? (unsigned char*)malloc((size_t)n * n) : NULL;
+    if (!pos || (parent && (!vis || tree_layout(parent, n, pos0, pos, vis) != 0))) {
+        free(pos); free(vis);
+        return -1;
+    }
+    if (!parent)
+        for (int32_t j = 0; j < n; ++j) pos[j] = pos0 + j;
+    memcpy(x_out, x_in, sizeof(double) * (size_t)n * m->hidden);
+    kv_src ks = { NULL, 0, cache_k, pos0 + n };
+    kv_src vs = { NULL, 0, cache_v, pos0 + n };
+    decoder_layer(m, l, x_out, n, pos, &ks, &vs, cache_k + pos0 * NK, cache_v + pos0 * NK, 1, pos0, vis);
+    free(pos); free(vis);
+    return 0;
 }

@@ -117,6 +117,8 @@ int orc_target_forward_tree(const orc_model* m, const int32_t* tokens, const int
                             int64_t pos0, double* cache_k, double* cache_v, int64_t cap,
                             const int32_t* capture, double* hidden_out,
                             float* logits_out, int32_t* argmax_out, double* gap_out);
+int orc_target_layer(const orc_model* m, int32_t l, const double* x_in, int32_t n, int64_t pos0,
+                     const int32_t* parent, double* cache_k, double* cache_v, int64_t cap, double* x_out);
 
 #ifdef __cplusplus
 }

@@ -128,3 +128,38 @@ def check_layers(orc, model, w, shape, ctx_k, ctx_v, C, anchor, layers, logits, 
         assert head["gap"][j] < 1e-3, (f"row {j}: gpu token {tok[j]} vs oracle {head['tokens'][j]} "
                                        f"(oracle top-2 gap {head['gap'][j]:.3g}) given the GPU's final residual")
     return err, worst_ulps
+
+
+def check_target_layers(orc, model, w, shape, cache, C, tokens, parent, layers, logits, argmax):
+    """check_layers for the causal / tree target forward: layer l of the oracle
+    (its tree mask when parent is given) runs on the GPU's input to that layer
+    over `cache` (an oracle TargetCache holding the same keys before C, into
+    which each layer's rows are written), and must land within 2 bf16 ulps of
+    the GPU's output (fp32: 1e-4 relative); the oracle's LM head on the GPU's
+    final residual bounds logits at 2e-2 (fp32: 1e-4 relative) with tokens
+    exact except where its top-2 gap is below 1e-3.  Returns the largest logit
+    difference, the worst per-layer ulps and the oracle's rows of every layer."""
+    L, n, H = layers.shape[0], layers.shape[1], shape.hidden
+    gl = layers.float().cpu().numpy().astype(np.float64).reshape(L, n, H)
+    x_in = w["embed"][list(np.asarray(tokens))].double().numpy()
+    worst = 0.0
+    for l in range(L):
+        ref = orc.target_layer(model, l, x_in, C, cache, parent)
+        if shape.dtype == "bf16":
+            worst = max(worst, float((np.abs(gl[l] - ref).max(axis=1) / bf16_ulp(np.abs(ref).max(axis=1))).max()))
+        assert_rows_close(gl[l], ref, shape.dtype, f"target layer {l} given the GPU's input")
+        x_in = gl[l]
+    head = orc.lm_head(model, gl[L - 1])
+    lg = np.asarray(logits, dtype=np.float64)
+    ref_lg = head["logits"].astype(np.float64)
+    if shape.dtype == "fp32":
+        err = float((np.abs(lg - ref_lg).max(axis=1) / np.abs(ref_lg).max(axis=1)).max())
+        assert err <= 1e-4, f"LM head logits relative error {err:.3g}"
+    else:
+        err = float(np.abs(lg - ref_lg).max())
+        assert err <= 2e-2, f"LM head logits absolute error {err:.3g} given the GPU's final residual"
+    am = np.asarray(argmax)
+    for j in np.flatnonzero(am != head["tokens"]):
+        assert head["gap"][j] < 1e-3, (f"row {j}: gpu token {am[j]} vs oracle {head['tokens'][j]} "
+                                       f"(oracle top-2 gap {head['gap'][j]:.3g}) given the GPU's final residual")
+    return err, worst

@@ -158,7 +158,8 @@ def test_device_length_capacity_guard(dl, w):
     after = ctx.read_kv(cap - 16, 16)
     torch.cuda.synchronize()
     assert lw.cpu().tolist() == [cap - 8, 1]
-    assert torch.equal(before[0], after[0]) and torch.equal(before[1], after[1])
+    # never-written pool memory may hold NaN patterns: compare the bits
+    assert all(torch.equal(b.view(torch.int16), a.view(torch.int16)) for b, a in zip(before, after))
     res = torch.tensor([15, 3], dtype=torch.int32, device="cuda")
     ctx.keep_accepted(res)  # clamped to the capacity
     assert int(ctx.read_device_length()[0]) == cap

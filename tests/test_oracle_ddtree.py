@@ -264,3 +264,25 @@ def test_compacted_cache_is_the_accepted_sequence_cache(orc):
     orc.target_forward(m, ref, [t["tokens"][0]] + [int(t["tokens"][j]) for j in path], P)
     assert np.array_equal(ck[:P + 1 + k], np.moveaxis(ref.k, 1, 0))
     assert np.array_equal(cv[:P + 1 + k], np.moveaxis(ref.v, 1, 0))
+
+
+@pytest.mark.parametrize("tree", [True, False])
+def test_target_layers_compose_to_the_forward(orc, tree):
+    """The one-layer entry (used to check a GPU pass layer by layer) chained
+    over every layer, then the LM head, is exactly the full forward."""
+    s, w, P, prefix, par, tok = _tree_case(10, 11)
+    par = par if tree else None
+    m = orc.Model(s, w, n_layers=s.target_layers)
+    sel = orc.feature_layers(s.target_layers)
+    full = orc.target_forward(m, _prefilled(orc, m, prefix, P + 11), tok, P, capture=sel, want_logits=True,
+                              parent=par)
+    cache = _prefilled(orc, m, prefix, P + 11)
+    x = w["embed"][list(tok)].double().numpy()
+    hid = []
+    for l in range(s.target_layers):
+        x = orc.target_layer(m, l, x, P, cache, par)
+        hid.append(x)
+    head = orc.lm_head(m, x)
+    assert np.array_equal(head["logits"], full["logits"]) and np.array_equal(head["tokens"], full["argmax"])
+    for i, l in enumerate(sel):
+        assert np.array_equal(hid[l], full["hidden"][i])
