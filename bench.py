@@ -520,6 +520,42 @@ def main():
                                 "hbm_frac_p50": round(vbytes / (pv[1] * 1e-6) / HBM_PEAK, 4),
                                 "verified_rows_per_s": round(16e6 / pv[1], 1)}
         log(f"[bench] target verify: {json.dumps(out['target_verify'])}")
+
+        # tree verification (DDTree) on the same target: top-4 candidates of 15
+        # drafted positions (seeded stand-in logits at the 8B vocabulary), the
+        # best-first tree of 15 nodes, its tree-masked verify pass, acceptance
+        # and the compaction of the accepted rows
+        lgt = torch.randn(15, sv.vocab, generator=gen, device="cuda") * 3.0
+        res = torch.empty(17, dtype=torch.int32, device="cuda")
+
+        def tree_step():
+            ids, lp = ctxv.draft_topk(lgt, 4)
+            tt, tp = ctxv.build_tree(vt[:1], ids, lp, 15)
+            ctxv.target_forward(tt, argmax=va, parent=tp)
+            ctxv.tree_accept(tt, tp, va, out=res)
+            ctxv.tree_commit(Cv, 16, res)
+            ctxv.rollback(Cv)
+        for _ in range(args.warmup):
+            tree_step()
+        torch.cuda.synchronize()
+        per_cls = {}
+        for cls, n_per in ((10, 1), (11, 4)):
+            assert dl.lib().dflash_trace_enable(ctxv.h, cls, nv * n_per) == 0
+            for _ in range(nv):
+                tree_step()
+            buf = (C_.c_float * (nv * n_per))()
+            assert dl.lib().dflash_trace_read_each(ctxv.h, buf, nv * n_per, C_.byref(cnt)) == 0
+            dl.lib().dflash_trace_enable(ctxv.h, 0, 0)
+            per_cls[cls] = np.array(buf[:cnt.value], dtype=np.float64).reshape(nv, n_per) * 1e3
+        helpers = np.median(per_cls[11], axis=0)
+        tv = float(np.median(per_cls[10]))
+        out["ddtree"] = {"workload": "qwen3_8b target, tree of 16 nodes (top-4 per depth, 15 depths) over 4096 cached "
+                                     "tokens, vocab 151936",
+                         "topk_us": round(float(helpers[0]), 1), "build_us": round(float(helpers[1]), 1),
+                         "verify_tree_us_p50": round(tv, 1), "accept_us": round(float(helpers[2]), 1),
+                         "commit_us": round(float(helpers[3]), 1),
+                         "overhead_vs_chain_verify_us": round(float(helpers.sum()) + tv - pv[1], 1)}
+        log(f"[bench] ddtree: {json.dumps(out['ddtree'])}")
         del ctxv, wv
         torch.cuda.empty_cache()
 
