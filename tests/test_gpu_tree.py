@@ -174,7 +174,7 @@ def _oracle_tree(orc, m, s, k, v, C, n, tok, par, sel, fp32_acc=False):
 
 
 @pytest.mark.parametrize("shape", [TR_BF16, TR_BF16_D64, TR_FP32_G5])
-@pytest.mark.parametrize("C,n", [(0, 16), (37, 16), (250, 9), (300, 1), (511, 16)])
+@pytest.mark.parametrize("C,n", [(0, 16), (37, 16), (180, 16), (250, 9), (300, 1), (380, 12), (511, 16)])
 def test_tree_forward_matches_oracle(dl, orc, shape, C, n):
     """At the stated bar, one layer at a time: every layer of the tree pass
     against the oracle's tree-masked layer on the GPU's own input to it (2 bf16
@@ -184,8 +184,9 @@ def test_tree_forward_matches_oracle(dl, orc, shape, C, n):
     the feature capture of the same pass, and end to end against the oracle's
     own tree forward (bf16: the band twice the stated bar that bf16 rounding
     compounding over 8 layers needs; the plain causal forward shows the same
-    end-to-end deviation on these inputs).  C = 250 / 511 put the tree's slots
-    across a 256-key split boundary and at the end of a 64-key chunk."""
+    end-to-end deviation on these inputs).  C = 180 / 380 put the tree's slots
+    across a 192-key split boundary (keys 192 and 384) and 511 at the end of a
+    64-key chunk."""
     s = shape
     w = di.toy_target_weights(s)
     ctx, k, v = _target(dl, s, w, C, page_seed=9)
