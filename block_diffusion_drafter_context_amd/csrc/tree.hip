@@ -43,7 +43,7 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
         return;
     }
     const float M = fmaxf(m, m2);
-    s = s * expf(m - M) + s2 * expf(m2 - M);
+    s = s * __expf(m - M) + s2 * __expf(m2 - M);
     m = M;
 }
 
@@ -52,9 +52,10 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
 // then K rounds of a workgroup-wide best pick the segment's K best in order.
 __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float* logits, long long ld, int V, int K,
                                                                     float* part) {
-    __shared__ float s_v[kTopKThreads / 64];
-    __shared__ int s_i[kTopKThreads / 64];
-    __shared__ float s_m[kTopKThreads / 64], s_s[kTopKThreads / 64];
+    constexpr int W = kTopKThreads / 64;
+    __shared__ float w_v[W][kTopKMax];
+    __shared__ int w_i[W][kTopKMax];
+    __shared__ float s_m[W], s_s[W];
     const int seg = blockIdx.x, r = blockIdx.y, S = gridDim.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int per = (V + S - 1) / S;
@@ -70,13 +71,25 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
     }
     float thr = -INFINITY;  // the K-th value held (ids scanned in ascending order: ties stay out)
     float m = -INFINITY, sum = 0.f;
-    for (int i = beg + tid; i < end; i += kTopKThreads) {
-        const float v = x[i];
+    // U loads in flight per thread, then their values in id order
+    constexpr int U = 8;
+    for (int i0 = beg + tid; i0 < end; i0 += U * kTopKThreads) {
+        float vb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kTopKThreads;
+            vb[u] = i < end ? x[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kTopKThreads;
+        if (i >= end) break;
+        const float v = vb[u];
         if (v > m) {
-            sum = sum * expf(m - v) + 1.f;
+            sum = sum * __expf(m - v) + 1.f;
             m = v;
         } else {
-            sum += expf(v - m);
+            sum += __expf(v - m);
         }
         if (v > thr) {
             float cv = v;
@@ -94,6 +107,7 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
 #pragma unroll
             for (int q = 0; q < kTopKMax; ++q)
                 if (q == K - 1) thr = tv[q];
+        }
         }
     }
     float* rec = part + ((long long)r * S + seg) * kPartStride;
@@ -123,7 +137,8 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
         rec[2 * kTopKMax + 1] = Ssum;
     }
 
-    // K rounds: the best list head over the workgroup leaves its list
+    // each wave: K rounds of the best list head over its lanes (no workgroup
+    // barrier per round); the owner's list drops its head
     for (int k = 0; k < K; ++k) {
         float bv = tv[0];
         int bi = ti[0];
@@ -135,22 +150,9 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
                 bi = i2;
             }
         }
-        __syncthreads();  // the previous round's reads of s_v / s_i are done
         if (lane == 0) {
-            s_v[w] = bv;
-            s_i[w] = bi;
-        }
-        __syncthreads();
-        bv = s_v[0];
-        bi = s_i[0];
-        for (int i = 1; i < kTopKThreads / 64; ++i)
-            if (ranks_before(s_v[i], s_i[i], bv, bi)) {
-                bv = s_v[i];
-                bi = s_i[i];
-            }
-        if (tid == 0) {
-            rec[k] = bv;
-            reinterpret_cast<int*>(rec)[kTopKMax + k] = bi;
+            w_v[w][k] = bv;
+            w_i[w][k] = bi;
         }
         if (ti[0] == bi && tv[0] == bv) {  // the owner (ids are unique among real entries)
 #pragma unroll
@@ -162,6 +164,19 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
             ti[kTopKMax - 1] = 0x7fffffff;
         }
     }
+    __syncthreads();
+    // the segment's K best: each of the W*K wave candidates counts those ranked before it
+    if (tid < W * K) {
+        const float v = w_v[tid / K][tid % K];
+        const int id = w_i[tid / K][tid % K];
+        int rank = 0;
+        for (int u = 0; u < W; ++u)
+            for (int q = 0; q < K; ++q) rank += ranks_before(w_v[u][q], w_i[u][q], v, id) ? 1 : 0;
+        if (rank < K) {
+            rec[rank] = v;
+            reinterpret_cast<int*>(rec)[kTopKMax + rank] = id;
+        }
+    }
 }
 
 // One row per workgroup: the rank of each of the S*K segment candidates among
@@ -170,6 +185,7 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
 __global__ __launch_bounds__(512) void topk_merge_kernel(const float* part, int S, int K, int32_t* ids, float* logp) {
     __shared__ float c_v[kTopKSegs * kTopKMax];
     __shared__ int c_i[kTopKSegs * kTopKMax];
+    __shared__ float s_m[kTopKSegs], s_s[kTopKSegs];
     __shared__ float s_lse;
     const int r = blockIdx.x, tid = threadIdx.x, n = S * K;
     const float* base = part + (long long)r * S * kPartStride;
@@ -178,12 +194,14 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const float* part, int 
         c_v[t] = rec[t % K];
         c_i[t] = reinterpret_cast<const int*>(rec)[kTopKMax + t % K];
     }
+    if (tid < S) {
+        s_m[tid] = base[(long long)tid * kPartStride + 2 * kTopKMax];
+        s_s[tid] = base[(long long)tid * kPartStride + 2 * kTopKMax + 1];
+    }
+    __syncthreads();
     if (tid == 0) {
         float M = -INFINITY, L = 0.f;
-        for (int sgi = 0; sgi < S; ++sgi) {
-            const float* rec = base + (long long)sgi * kPartStride;
-            lse_combine(M, L, rec[2 * kTopKMax], rec[2 * kTopKMax + 1]);
-        }
+        for (int sgi = 0; sgi < S; ++sgi) lse_combine(M, L, s_m[sgi], s_s[sgi]);
         s_lse = M + logf(L);
     }
     __syncthreads();
@@ -191,8 +209,18 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const float* part, int 
     for (int t = tid; t < n; t += blockDim.x) {
         const float v = c_v[t];
         const int id = c_i[t];
+        // each segment's list is in rank order: count its entries ranked
+        // before this one by binary search
         int rank = 0;
-        for (int u = 0; u < n; ++u) rank += ranks_before(c_v[u], c_i[u], v, id) ? 1 : 0;
+        for (int sg = 0; sg < S; ++sg) {
+            int lo = 0, hi = K;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (ranks_before(c_v[sg * K + mid], c_i[sg * K + mid], v, id)) lo = mid + 1;
+                else hi = mid;
+            }
+            rank += lo;
+        }
         if (rank < K) {
             ids[(long long)r * K + rank] = id;
             logp[(long long)r * K + rank] = v - lse;
@@ -200,25 +228,25 @@ __global__ __launch_bounds__(512) void topk_merge_kernel(const float* part, int 
     }
 }
 
-// Candidate order: valid first, larger score, smaller depth, smaller path key.
-struct Cand {
-    float score;
-    int depth;
-    int lane;
-    unsigned long long path;
-    bool ok;
-};
-
-__device__ __forceinline__ bool cand_before(const Cand& a, const Cand& b) {
-    if (a.ok != b.ok) return a.ok;
-    if (a.score != b.score) return a.score > b.score;
-    if (a.depth != b.depth) return a.depth < b.depth;
-    return a.path < b.path;
+// Candidate order as one 128-bit key (larger = better), compared branch-free:
+//   hi = valid (1 bit) | score mapped to an unsigned order (32 bits) | 31 - depth (5 bits)
+//   lo = ~rank path (4 bits per depth, depth 1 in the top bits) with the low
+//        4 bits replaced by 15 - lane (the path never uses them; they only
+//        separate invalid candidates and name the winner's lane).
+__device__ __forceinline__ unsigned order_bits(float f) {
+    const unsigned u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal scores compare equal
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave.  Lane u < count holds node u: its score, depth, rank path (4 bits
-// per depth, depth 1 in the top bits) and the rank of its next unchosen child.
-// Every step the best of the lanes' next children joins the tree as node
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int o) {
+    const unsigned lo = (unsigned)__shfl_xor((int)(unsigned)v, o, 64);
+    const unsigned hi = (unsigned)__shfl_xor((int)(unsigned)(v >> 32), o, 64);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// One wave.  Lane u < count holds node u: its score, depth, rank path and the
+// rank of its next unchosen child.  Every step the best of the lanes' next
+// children (a 16-lane butterfly over the keys above) joins the tree as node
 // `count`; a child never beats its parent or an earlier sibling, so the
 // chosen nodes are the budget best of the whole candidate tree.
 __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* anchor, int V, const int32_t* ids,
@@ -237,33 +265,35 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* anchor, i
     unsigned long long path = 0ull;
     int tok = lane == 0 ? min(max(anchor[0], 0), V - 1) : 0;
     for (int count = 1; count <= budget; ++count) {
-        Cand c;
-        c.ok = lane < count && dep < R && nr < K;
-        c.score = c.ok ? sc + s_lp[c.ok ? dep * K + nr : 0] : -INFINITY;
-        c.depth = dep + 1;
-        c.path = path | ((unsigned long long)(c.ok ? nr : 0) << (4 * (15 - min(dep, 15))));
-        c.lane = lane;
-        for (int o = 32; o >= 1; o >>= 1) {
-            Cand d;
-            d.ok = __shfl_xor((int)c.ok, o, 64) != 0;
-            d.score = __shfl_xor(c.score, o, 64);
-            d.depth = __shfl_xor(c.depth, o, 64);
-            d.lane = __shfl_xor(c.lane, o, 64);
-            d.path = ((unsigned long long)(unsigned)__shfl_xor((int)(c.path >> 32), o, 64) << 32) |
-                     (unsigned)__shfl_xor((int)(c.path & 0xffffffffull), o, 64);
-            if (cand_before(d, c) || (!cand_before(c, d) && d.lane < c.lane)) c = d;
+        const bool ok = lane < count && dep < R && nr < K;
+        const float cs = sc + s_lp[ok ? dep * K + nr : 0];
+        const int cd = min(dep + 1, 15);
+        const unsigned long long cp = path | ((unsigned long long)(ok ? nr : 0) << (4 * (15 - min(dep, 14))));
+        unsigned long long hi = ok ? ((1ull << 37) | ((unsigned long long)order_bits(cs) << 5) | (unsigned)(31 - cd))
+                                   : 0ull;
+        unsigned long long lo = (~cp & ~15ull) | (unsigned)(15 - (lane & 15));
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+            const unsigned long long h2 = shfl_xor64(hi, o), l2 = shfl_xor64(lo, o);
+            const bool take = h2 > hi || (h2 == hi && l2 > lo);
+            hi = take ? h2 : hi;
+            lo = take ? l2 : lo;
         }
-        // every lane now holds the winner; its rank is the path digit at its depth
-        const int rank = (int)((c.path >> (4 * (16 - c.depth))) & 15ull);
+        // lanes 0..15 now hold the winner
+        const int wl = 15 - (int)(lo & 15ull);
+        const int wd = 31 - (int)(hi & 31ull);
+        const unsigned long long wp = ~lo & ~15ull;
+        const int rank = (int)((wp >> (4 * (16 - wd))) & 15ull);
+        const float ws = __shfl(cs, wl, 64);  // the winner's own fp32 score (all lanes take part)
         if (lane == count) {
-            sc = c.score;
-            dep = c.depth;
-            path = c.path;
+            sc = ws;
+            dep = wd;
+            path = wp;
             nr = 0;
-            par = c.lane;
-            tok = s_id[min((c.depth - 1) * K + rank, R * K - 1)];
+            par = wl;
+            tok = s_id[min((wd - 1) * K + rank, R * K - 1)];
         }
-        if (lane == c.lane) ++nr;
+        if (lane == wl) ++nr;
     }
     if (lane <= budget) {
         tokens[lane] = tok;
@@ -363,6 +393,7 @@ __global__ __launch_bounds__(256) void tree_commit_kernel(CommitArgs a) {
 hipError_t launch_topk(const DevCtx& c, const float* logits, long long ld, int rows, int K, int32_t* ids, float* logp,
                        hipStream_t s) {
     const int V = c.dm.V;
+    // segments of at least 4096 ids: every wave then holds K real candidates
     const int S = std::max(1, std::min(kTopKSegs, V / 4096));
     float* part = reinterpret_cast<float*>(c.ws + c.lay.topk_part);
     hipLaunchKernelGGL(topk_partial_kernel, dim3(S, rows), dim3(kTopKThreads), 0, s, logits, ld, V, K, part);
