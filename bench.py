@@ -6,7 +6,8 @@ One step = one pass of the whole draft-side hot path over one block:
   -> verify_accept against a synthetic target argmax
   -> fuse_context of the 16 verified rows' target features (5 layers, Linear + RMSNorm)
   -> inject_kv of those 16 rows into every layer's paged draft KV cache
-  -> rollback to C + k + 1 (then back to C so every step sees the same context)
+  -> keep C + k + 1 positions (then back to C so every step sees the same context)
+with the context length held on the device, so no step reads anything back.
 Inputs are seeded synthetic tensors of the Qwen3-8B-shaped draft (hidden 4096,
 36 target layers, 5 draft layers, 32/8 heads x 128, FFN 12288, vocab 151936,
 bf16) with a 4096-token injected context, already resident in HBM.
@@ -683,6 +684,9 @@ def main():
     # ---- CPU oracle baseline: full steps of the oracle on a bounded sample
     # (steps until 10 s have elapsed, at most 30; the anchor follows each step's bonus token)
     if not args.no_cpu_baseline:
+        # threads pinned close together (read by the OpenMP runtime when the
+        # oracle library loads)
+        os.environ.setdefault("OMP_PROC_BIND", "close")
         import oracle as orc
         m = orc.Model(s, w_cpu)
         k, v = di.context_kv(s, C)
@@ -708,7 +712,8 @@ def main():
                                "kind": "oracle",
                                "sample": f"{n_cpu} full steps (draft block at C={C} + accept + fuse/inject of 16 rows, "
                                          f"anchor from each step's bonus), fp64 oracle, {cpu_s * n_cpu:.1f}s in all, "
-                                         f"{cpu_s:.2f}s per step, {threads} OpenMP threads",
+                                         f"{cpu_s:.2f}s per step, {threads} OpenMP threads "
+                                         f"(OMP_PROC_BIND={os.environ.get('OMP_PROC_BIND')})",
                                **host}
         log(f"[bench] cpu oracle: {n_cpu} steps, {cpu_s:.2f}s per step with {threads} threads; host {host}")
         # the same step on one thread
