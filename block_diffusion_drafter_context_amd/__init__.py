@@ -130,6 +130,10 @@ def lib():
         L.dflash_build_tree.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
         L.dflash_tree_accept.restype = st
         L.dflash_tree_accept.argtypes = [vp, vp, vp, vp, i32, vp, vp]
+        L.dflash_sample_tokens.restype = st
+        L.dflash_sample_tokens.argtypes = [vp, vp, i64, i32, C.c_float, C.c_uint64, vp, vp, vp]
+        L.dflash_verify_sample.restype = st
+        L.dflash_verify_sample.argtypes = [vp, vp, vp, vp, i64, C.c_float, C.c_uint64, vp, vp]
         L.dflash_tree_commit.restype = st
         L.dflash_tree_commit.argtypes = [vp, i32, i32, vp, vp, i64, vp]
         _lib = L
@@ -374,6 +378,32 @@ class DFlash:
             out = torch.empty(17, dtype=torch.int32, device=self.device)
         self._check(lib().dflash_tree_accept(self.h, tokens.data_ptr(), parent.data_ptr(), target.data_ptr(),
                                              tokens.shape[0], out.data_ptr(), _stream(stream)), "tree_accept")
+        return out
+
+    # ---- non-greedy drafting and verification
+    def sample_tokens(self, logits: torch.Tensor, temperature: float, seed: int,
+                      tokens: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+        """Gumbel-max draws (device int32[rows]) and log-sum-exp (fp32[rows]) of logits [rows, >= V] / T."""
+        rows = logits.shape[0]
+        if tokens is None:
+            tokens = torch.empty(rows, dtype=torch.int32, device=self.device)
+        if lse is None:
+            lse = torch.empty(rows, dtype=torch.float32, device=self.device)
+        self._check(lib().dflash_sample_tokens(self.h, logits.data_ptr(), logits.stride(0), rows, float(temperature),
+                                               seed, tokens.data_ptr(), lse.data_ptr(), _stream(stream)),
+                    "sample_tokens")
+        return tokens, lse
+
+    def verify_sample(self, draft: torch.Tensor, draft_logits: torch.Tensor, target_logits: torch.Tensor,
+                      temperature: float, seed: int, out: Optional[torch.Tensor] = None, stream=None):
+        """Speculative sampling over a block: device int32[2] = {k, token}."""
+        assert draft_logits.stride(0) == target_logits.stride(0)
+        if out is None:
+            out = torch.empty(2, dtype=torch.int32, device=self.device)
+        self._check(lib().dflash_verify_sample(self.h, draft.data_ptr(), draft_logits.data_ptr(),
+                                               target_logits.data_ptr(), draft_logits.stride(0),
+                                               float(temperature), seed, out.data_ptr(), _stream(stream)),
+                    "verify_sample")
         return out
 
     def tree_commit(self, pos0: int, M: int, result: torch.Tensor,

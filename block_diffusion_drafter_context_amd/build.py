@@ -18,7 +18,8 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
-    for src, device in (("host.cpp", False), ("api.cpp", False), ("kernels.hip", True), ("tree.hip", True)):
+    for src, device in (("host.cpp", False), ("api.cpp", False), ("kernels.hip", True), ("tree.hip", True),
+                        ("sample.hip", True)):
         obj = os.path.join(objdir, src + ".o")
         cmd = [hipcc] + (HIP_FLAGS if device else ["-O2", "-std=c++17", "-fPIC", "-Wall"])
         cmd += ["-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]

@@ -517,6 +517,43 @@ dflash_status dflash_tree_accept(dflash_ctx* c, const int32_t* tokens, const int
     return DFLASH_OK;
 }
 
+dflash_status dflash_sample_tokens(dflash_ctx* c, const float* logits, int64_t ld, int32_t rows, float temperature,
+                                   uint64_t seed, int32_t* tokens_out, float* lse_out, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!logits || (!tokens_out && !lse_out)) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (rows < 1 || rows > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "rows must be in [1, 16]");
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(c, DFLASH_ERR_INVAL, "temperature must be > 0");
+    if (ld < d.V || !aligned(logits, 4)) return fail(c, DFLASH_ERR_INVAL, "ld must be >= V and logits aligned");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    c->tracer.begin(DFLASH_TRACE_SAMPLE, s);
+    hipError_t e = launch_sample_tokens(c->dev, logits, ld, rows, temperature, seed, tokens_out, lse_out, s);
+    if (e != hipSuccess) return hip_fail(c, e, "sample launch");
+    c->tracer.end(DFLASH_TRACE_SAMPLE, s);
+    return DFLASH_OK;
+}
+
+dflash_status dflash_verify_sample(dflash_ctx* c, const int32_t* draft, const float* draft_logits,
+                                   const float* target_logits, int64_t ld, float temperature, uint64_t seed,
+                                   int32_t* result_out, void* stream) {
+    if (!c) return DFLASH_ERR_INVAL;
+    const Dims& d = c->dev.dm;
+    if (!draft || !draft_logits || !target_logits || !result_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(c, DFLASH_ERR_INVAL, "temperature must be > 0");
+    if (ld < d.V || !aligned(draft_logits, 4) || !aligned(target_logits, 4))
+        return fail(c, DFLASH_ERR_INVAL, "ld must be >= V and logits aligned");
+    dflash_status st = check_device(c);
+    if (st != DFLASH_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    c->tracer.begin(DFLASH_TRACE_SAMPLE, s);
+    hipError_t e = launch_verify_sample(c->dev, draft, draft_logits, target_logits, ld, temperature, seed, result_out, s);
+    if (e != hipSuccess) return hip_fail(c, e, "sampled verification launch");
+    c->tracer.end(DFLASH_TRACE_SAMPLE, s);
+    return DFLASH_OK;
+}
+
 dflash_status dflash_tree_commit(dflash_ctx* c, int32_t pos0, int32_t M, const int32_t* result, void* const* capture,
                                  int64_t capture_ld, void* stream) {
     if (!c) return DFLASH_ERR_INVAL;
@@ -572,7 +609,7 @@ dflash_status dflash_read_kv(dflash_ctx* c, int32_t pos0, int32_t M, void* k_out
 
 dflash_status dflash_trace_enable(dflash_ctx* c, int32_t kernel_class, int32_t max_launches) {
     if (!c) return DFLASH_ERR_INVAL;
-    if (kernel_class < DFLASH_TRACE_OFF || kernel_class > DFLASH_TRACE_TREE || max_launches < 0 ||
+    if (kernel_class < DFLASH_TRACE_OFF || kernel_class > DFLASH_TRACE_SAMPLE || max_launches < 0 ||
         max_launches > (1 << 20))
         return fail(c, DFLASH_ERR_INVAL, "bad trace class or launch count");
     hipError_t e = hipDeviceSynchronize();

@@ -115,6 +115,7 @@ Layout compute_layout(const Dims& d, int num_cus) {
     L.len_dev = take(2 * 4);
     L.tree_info = take(32 * 4);
     L.topk_part = take((size_t)16 * kTopKSegs * (2 * kTopKMax + 2) * 4);
+    L.sample_draw = take(64 + (size_t)((d.V + 1023) / 1024) * 8);
     const int e = d.elem;
     for (int l = 0; l < d.Ld; ++l) {
         L.sw_wq[l] = take(swizzled_bytes(nqd, d.H, e));

@@ -55,7 +55,8 @@ struct Layout {
     size_t attn_o, attn_ml;
     size_t len_dev;       // device-resident length: {length, capacity-error flag}
     size_t tree_info;     // tree verification: per row {depth[16], ancestor mask[16]}
-    size_t topk_part;     // top-K partials: [16 rows][kTopKSegs] x (K values, K ids, max, sum)
+    size_t topk_part;     // top-K / sampling partials: [16 rows][kTopKSegs] x (K values, K ids, max, sum)
+    size_t sample_draw;   // sampled verification: a 64-byte header, then one fp64 weight sum per 1024 ids
     size_t total;
     size_t kv_total;      // bytes of the KV pool
     size_t kv_layer_kv;   // bytes of one (layer, K-or-V) page array

@@ -87,6 +87,14 @@ hipError_t launch_topk(const DevCtx& c, const float* logits, long long ld, int r
 // Best-first candidate tree of `budget` nodes over R depths of K candidates.
 hipError_t launch_tree_build(const int32_t* anchor, int V, const int32_t* ids, const float* logp, int R, int K,
                              int budget, int32_t* tokens, int32_t* parent, hipStream_t s);
+// Gumbel-max draws at temperature T from each of `rows` logit rows (row r draws
+// with generator coordinates (r, id)); tokens and/or the rows' log-sum-exp of z / T.
+hipError_t launch_sample_tokens(const DevCtx& c, const float* logits, long long ld, int rows, float T,
+                                unsigned long long seed, int32_t* tokens, float* lse, hipStream_t s);
+// Speculative sampling over a drafted block: out = {k, token after the accepted drafts}.
+hipError_t launch_verify_sample(const DevCtx& c, const int32_t* draft, const float* draft_logits,
+                                const float* target_logits, long long ld, float T, unsigned long long seed,
+                                int32_t* out, hipStream_t s);
 // Accepted path of a verified tree: out = {k, bonus, path[0..14]}.
 hipError_t launch_tree_accept(const int32_t* tokens, const int32_t* parent, const int32_t* target, int M,
                               int32_t* out, hipStream_t s);

@@ -354,6 +354,42 @@ dflash_status dflash_tree_accept(dflash_ctx* ctx, const int32_t* tokens, const i
 dflash_status dflash_tree_commit(dflash_ctx* ctx, int32_t pos0, int32_t M, const int32_t* result,
                                  void* const* capture, int64_t capture_ld, void* stream);
 
+/* ---- Non-greedy drafting and verification --------------------------------
+ * The rebasdaily DFlash2 page (section 先猜几个，再让主模型拍板) ties DFlash2's
+ * candidate selection to non-greedy samplers but gives no verification rule
+ * for them.  The reading taken is the speculative sampling rule of the
+ * literature (Leviathan, Kalman and Matias 2023; Chen et al. 2023), under
+ * which the emitted tokens follow the target's own sampling distribution.
+ * Random numbers: SplitMix64 as a counter-based generator -- draw n of stream
+ * `seed` is its (n + 1)-th output with n = a * 2^32 + b for a draw's
+ * coordinates (a, b), and a uniform is the top 24 bits times 2^-24 (plus
+ * 2^-25 where a logarithm follows).  A caller gives every step its own seed. */
+
+/* Draw one token per row r < rows of logits ([rows][ld] device fp32, ld >= V)
+ * from softmax(row / temperature) by the Gumbel-max method: the id x with
+ * the largest row[x] / T - log(-log U), U the draw at coordinates (r, x)
+ * (ties: lower id).  tokens_out: device int32[rows] or NULL; lse_out: device
+ * fp32[rows] or NULL, the rows' log-sum-exp of row / T.  1 <= rows <= 16,
+ * temperature > 0 and finite (INVAL otherwise).  For a drafted block pass the
+ * draft's logits from row 1 on: token r is the draft for position C + 1 + r. */
+dflash_status dflash_sample_tokens(dflash_ctx* ctx, const float* logits, int64_t ld, int32_t rows, float temperature,
+                                   uint64_t seed, int32_t* tokens_out, float* lse_out, void* stream);
+
+/* Speculative sampling over a drafted block of B (the context's block) rows:
+ * draft: device int32[B] (entry j >= 1 is the draft for position C + j);
+ * draft_logits, target_logits: device fp32 [B][ld] (draft row j gave draft j;
+ * target row i is the target's prediction for position C + i + 1).  Draft j is
+ * accepted when U * q < p, U the draw at (2^20 + j, 0), q = softmax(draft
+ * row j / T)[d_j], p = softmax(target row j - 1 / T)[d_j]; at the first
+ * rejection the next token is drawn from max(0, p - q) of those rows, after B
+ * - 1 acceptances the bonus from softmax(target row B - 1 / T), with the draw
+ * at (2^20 + 64, 0) (a draw: the first id whose running sum of weights
+ * exceeds U * their total).  result_out: device int32[2] = {k, token}, the
+ * layout of a dflash_verify_accept result. */
+dflash_status dflash_verify_sample(dflash_ctx* ctx, const int32_t* draft, const float* draft_logits,
+                                   const float* target_logits, int64_t ld, float temperature, uint64_t seed,
+                                   int32_t* result_out, void* stream);
+
 /* Load already-rotated K and V for positions [pos0, pos0+M) of every layer
  * (restoring a saved cache, or K/V computed elsewhere).  k, v: device
  * [Ld, M, nkv, d] contiguous.  Same pos0/capacity rules as dflash_inject_kv. */
@@ -378,7 +414,8 @@ typedef enum {
     DFLASH_TRACE_FUSE = 8,     /* fusion GEMM of dflash_fuse_context (without its RMSNorm) */
     DFLASH_TRACE_INJECT = 9,   /* injection of dflash_inject_kv */
     DFLASH_TRACE_TARGET = 10,  /* the whole dflash_target_forward(_tree) call */
-    DFLASH_TRACE_TREE = 11     /* each tree helper call: top-K, tree build, tree accept, tree commit */
+    DFLASH_TRACE_TREE = 11,    /* each tree helper call: top-K, tree build, tree accept, tree commit */
+    DFLASH_TRACE_SAMPLE = 12   /* each dflash_sample_tokens / dflash_verify_sample call */
 } dflash_trace_class;
 
 /* Tracing aid: while enabled, every launch of the given kernel class is

@@ -1,0 +1,208 @@
+"""Non-greedy drafting and verification through the C ABI against the oracle
+(oracle/sampling.py), on the same fp32 logits:
+
+* Gumbel-max draws: tokens exact except where the two best perturbed scores
+  lie closer than 1e-3 (fp32 against fp64 keys), the rows' log-sum-exp of
+  z / T within 1e-6 relative (fp64 sums, returned in fp32);
+* the speculative sampling rule over a drafted block, computed in fp64 on both
+  sides: k exact except where the deciding comparison U * q < p is closer than
+  1e-9 of its sides, the drawn token exact except where U * total lies closer
+  to a running-sum boundary than 1e-12 of sum(p) + sum(q) (the rounding of
+  fp64 probabilities, which the residual max(0, p - q) keeps in absolute
+  terms while its total shrinks where p and q nearly agree).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import dflash_inputs as di
+from oracle import sampling as sp
+from tests.gpu_helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+GAP = 1e-3           # perturbed-score gap under which either draw may come out
+ACCEPT_REL = 1e-9    # relative closeness of U * q and p under which either decision may come out
+DRAW_EPS = 1e-12     # boundary distance, relative to sum(p) + sum(q), under which either draw may come out
+
+
+@pytest.fixture(scope="module")
+def dl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_diffusion_drafter_context_amd as m
+    m.lib()
+    return m
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def _vocab_ctx(dl, V):
+    s = di.Shape(f"s{V}", "bf16", hidden=64, target_layers=8, draft_layers=1, n_q_heads=2, n_kv_heads=1,
+                 head_dim=64, ffn=96, vocab=V, ctx=16, seed=7)
+    return dl.DFlash(s, dev(di.draft_weights(s, need_draft=False, need_lm=False)), max_ctx=64)
+
+
+def _padded(x):
+    """fp32 rows on the device with a row stride 48 beyond V (NaN padding)."""
+    R, V = x.shape
+    buf = torch.full((R, V + 48), float("nan"), dtype=torch.float32)
+    buf[:, :V] = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return buf.cuda()[:, :V]
+
+
+# ------------------------------------------------------------------ drafting
+
+@pytest.mark.parametrize("V,T,rows,scale", [(151936, 1.0, 16, 2.0), (4000, 0.6, 16, 3.0), (4000, 1.7, 9, 1.0),
+                                            (1008, 0.05, 16, 1.0), (1008, 1.0, 1, 0.0)])
+def test_sample_tokens_matches_oracle(dl, V, T, rows, scale):
+    ctx = _vocab_ctx(dl, V)
+    x = di.normal((rows, V), 71, f"samp{V}_{T}", scale, torch.float32).numpy()
+    seed = 0x5EED0000 + V
+    print(f"[sample] V={V} T={T} rows={rows}", flush=True)
+    tok, lse = ctx.sample_tokens(_padded(x), T, seed)
+    sync()
+    ref = sp.sample_tokens(x, T, seed)
+    got = tok.cpu().numpy()
+    ties = 0
+    for r in range(rows):
+        if got[r] != ref["tokens"][r]:
+            assert ref["gap"][r] < GAP, f"row {r}: {got[r]} vs {ref['tokens'][r]}, gap {ref['gap'][r]:.3g}"
+            ties += 1
+    assert ties <= max(1, rows // 8)
+    np.testing.assert_allclose(lse.cpu().numpy().astype(np.float64), ref["lse"], rtol=1e-6, atol=1e-6)
+
+
+def test_sample_tokens_is_seeded(dl):
+    """The same seed gives the same draws on every call; another seed moves
+    them (a flat row over 4000 ids); draws land inside the vocabulary."""
+    V = 4000
+    ctx = _vocab_ctx(dl, V)
+    x = torch.zeros(16, V, dtype=torch.float32, device="cuda")
+    a, _ = ctx.sample_tokens(x, 1.0, 1)
+    b, _ = ctx.sample_tokens(x, 1.0, 1)
+    c, _ = ctx.sample_tokens(x, 1.0, 2)
+    sync()
+    assert torch.equal(a, b) and not torch.equal(a, c)
+    assert int(a.min()) >= 0 and int(a.max()) < V
+    assert len(set(a.cpu().tolist())) > 8      # 16 independent rows of a flat row rarely collide
+
+
+# ------------------------------------------------------------------ verification
+
+def _block(V, B, kind, tag, scale=2.0, noise=0.7):
+    """Draft logits [B, V], target logits [B, V] and a draft block for one of:
+    'near' (target row j - 1 = draft row j + noise: a mix of acceptances),
+    'same' (target row j - 1 == draft row j: every draft accepted),
+    'far' (the target gives every draft almost no mass: rejected at once)."""
+    zd = di.normal((B, V), 81, f"vd{tag}", scale, torch.float32).numpy()
+    zt = np.empty_like(zd)
+    zt[:B - 1] = zd[1:]
+    zt[B - 1] = di.normal((1, V), 81, f"vl{tag}", scale, torch.float32).numpy()[0]
+    if kind == "near":
+        zt += di.normal((B, V), 81, f"vn{tag}", noise, torch.float32).numpy()
+    # drafts drawn from softmax(draft row) by numpy's own Gumbel draws (an input here)
+    g = np.random.default_rng(zlib.crc32(tag.encode())).gumbel(size=(B - 1, V))
+    d = np.zeros(B, dtype=np.int32)
+    d[1:] = np.argmax(zd[1:].astype(np.float64) + g, axis=1)
+    if kind == "far":
+        for j in range(1, B):
+            zt[j - 1, d[j]] = -60.0
+    return zd.astype(np.float32), zt.astype(np.float32), d
+
+
+def _check_verify(got, ref, dl_, tl_, d, T, seed):
+    """k and the drawn token against the oracle's walk, with the closeness
+    exemptions of the module docstring; returns the number of exempted cases."""
+    k, tok = int(got[0]), int(got[1])
+    if k != ref["k"]:
+        j = min(k, ref["k"]) + 1                   # the first decision that differs
+        p = np.exp(sp.log_softmax(tl_[j - 1], T))[d[j]]
+        q = np.exp(sp.log_softmax(dl_[j], T))[d[j]]
+        u = sp.uniform(seed, sp.TAG_ACCEPT + j, 0)
+        assert abs(u * q - p) <= ACCEPT_REL * max(p, u * q), f"k {k} vs {ref['k']} at draft {j}: uq {u*q} p {p}"
+        return 1
+    if tok != ref["bonus"]:
+        B = len(d)
+        if k < B - 1:   # the residual's total, relative to which the oracle states its margin
+            total = np.maximum(0.0, np.exp(sp.log_softmax(tl_[k], T)) - np.exp(sp.log_softmax(dl_[k + 1], T))).sum()
+            tol = DRAW_EPS * 2.0 / total
+        else:
+            tol = DRAW_EPS
+        assert ref["draw_margin"] < tol, f"k={k}: token {tok} vs {ref['bonus']}, margin {ref['draw_margin']} > {tol}"
+        return 1
+    return 0
+
+
+@pytest.mark.parametrize("V", [151936, 4000])
+@pytest.mark.parametrize("kind", ["near", "same", "far"])
+def test_verify_sample_matches_oracle(dl, V, kind):
+    ctx = _vocab_ctx(dl, V)
+    B = 16
+    seeds = range(12) if V > 100000 else range(40)
+    exempt, ks = 0, []
+    for case in range(2 if V > 100000 else 4):
+        zd, zt, d = _block(V, B, kind, f"{kind}{V}_{case}")
+        gd, gt, gdr = _padded(zd), _padded(zt), torch.from_numpy(d).cuda()
+        for T in (1.0, 0.7) if case % 2 == 0 else (1.3,):
+            print(f"[verify-sample] V={V} {kind} case {case} T={T}", flush=True)
+            outs = [ctx.verify_sample(gdr, gd, gt, T, 1000 * case + s) for s in seeds]
+            sync()
+            for s, o in zip(seeds, outs):
+                ref = sp.verify_sample(d, zd, zt, T, 1000 * case + s)
+                exempt += _check_verify(o.cpu().numpy(), ref, zd, zt, d, T, 1000 * case + s)
+                ks.append(ref["k"])
+    print(f"[verify-sample] V={V} {kind}: k mean {np.mean(ks):.2f} min {min(ks)} max {max(ks)}; "
+          f"{exempt} near-tie cases of {len(ks)}", flush=True)
+    assert exempt <= max(1, len(ks) // 50)
+    if kind == "same":
+        assert min(ks) == B - 1
+    if kind == "far":
+        assert max(ks) == 0
+    if kind == "near":
+        assert max(ks) > min(ks)                   # the cases exercise both rejection and the residual draw
+
+
+def test_verify_sample_arbitrary_drafts(dl):
+    """Drafts not drawn from q (some of them far in q's tail): the rule still
+    reads q and p at the given ids; k and the token match the oracle."""
+    V, B = 4000, 16
+    ctx = _vocab_ctx(dl, V)
+    zd, zt, _ = _block(V, B, "near", "arb", noise=0.3)
+    rng = np.random.default_rng(5)
+    exempt = n = 0
+    for case in range(6):
+        d = np.zeros(B, dtype=np.int32)
+        d[1:] = rng.integers(0, V, B - 1)
+        d[1:case + 1] = np.argmax(zt[:case], axis=1)   # a likely prefix of length `case`
+        gdr = torch.from_numpy(d).cuda()
+        outs = [ctx.verify_sample(gdr, _padded(zd), _padded(zt), 1.0, 77 + s) for s in range(10)]
+        sync()
+        for s, o in enumerate(outs):
+            ref = sp.verify_sample(d, zd, zt, 1.0, 77 + s)
+            exempt += _check_verify(o.cpu().numpy(), ref, zd, zt, d, 1.0, 77 + s)
+            n += 1
+    assert exempt <= 2, f"{exempt} near-tie cases of {n}"
+
+
+def test_sample_errors(dl):
+    ctx = _vocab_ctx(dl, 1008)
+    lg = torch.zeros(17, 1008, dtype=torch.float32, device="cuda")
+    d = torch.zeros(16, dtype=torch.int32, device="cuda")
+    for T in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(dl.DFlashError):
+            ctx.sample_tokens(lg[:4], T, 1)
+        with pytest.raises(dl.DFlashError):
+            ctx.verify_sample(d, lg[:16], lg[:16], T, 1)
+    with pytest.raises(dl.DFlashError):
+        ctx.sample_tokens(lg, 1.0, 1)                     # 17 rows
+    narrow = torch.zeros(16, 1000, dtype=torch.float32, device="cuda")
+    with pytest.raises(dl.DFlashError):
+        ctx.sample_tokens(narrow, 1.0, 1)                 # row stride below V
+    with pytest.raises(dl.DFlashError):
+        ctx.verify_sample(d, narrow, narrow, 1.0, 1)
+    sync()
