@@ -557,6 +557,35 @@ def main():
                          "commit_us": round(float(helpers[3]), 1),
                          "overhead_vs_chain_verify_us": round(float(helpers.sum()) + tv - pv[1], 1)}
         log(f"[bench] ddtree: {json.dumps(out['ddtree'])}")
+
+        # non-greedy verification at the 8B vocabulary (T = 1): Gumbel-max draws
+        # of the 15 drafted positions from seeded stand-in draft logits, then the
+        # speculative sampling rule against target logits near the draft's
+        lgd = torch.randn(16, sv.vocab, generator=gen, device="cuda") * 3.0
+        lgv = torch.roll(lgd, -1, 0) + torch.randn(16, sv.vocab, generator=gen, device="cuda")
+        dsm = torch.zeros(16, dtype=torch.int32, device="cuda")
+        rsm = torch.empty(nv, 2, dtype=torch.int32, device="cuda")
+
+        def sample_step(i, r):
+            ctxv.sample_tokens(lgd[1:], 1.0, i, tokens=dsm[1:])
+            ctxv.verify_sample(dsm, lgd, lgv, 1.0, i, out=r)
+        for i in range(args.warmup):
+            sample_step(i, rsm[0])
+        torch.cuda.synchronize()
+        assert dl.lib().dflash_trace_enable(ctxv.h, 12, 2 * nv) == 0
+        for i in range(nv):
+            sample_step(1000 + i, rsm[i])
+        buf = (C_.c_float * (2 * nv))()
+        assert dl.lib().dflash_trace_read_each(ctxv.h, buf, 2 * nv, C_.byref(cnt)) == 0
+        dl.lib().dflash_trace_enable(ctxv.h, 0, 0)
+        su = np.median(np.array(buf[:cnt.value], dtype=np.float64).reshape(nv, 2) * 1e3, axis=0)
+        ksm = rsm[:, 0].float().mean().item()
+        out["sampled_verify"] = {"workload": "T = 1, 15 drafted positions, vocab 151936 (fp32 logits), "
+                                             "target rows near the draft's",
+                                 "sample_drafts_us": round(float(su[0]), 1), "verify_rule_us": round(float(su[1]), 1),
+                                 "mean_k": round(ksm, 2),
+                                 "logit_bytes_per_step": 2 * 16 * sv.vocab * 4 + 15 * sv.vocab * 4}
+        log(f"[bench] sampled verify: {json.dumps(out['sampled_verify'])}")
         del ctxv, wv
         torch.cuda.empty_cache()
 

@@ -382,15 +382,18 @@ class DFlash:
 
     # ---- non-greedy drafting and verification
     def sample_tokens(self, logits: torch.Tensor, temperature: float, seed: int,
-                      tokens: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
-        """Gumbel-max draws (device int32[rows]) and log-sum-exp (fp32[rows]) of logits [rows, >= V] / T."""
+                      tokens: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      want_lse: bool = False, stream=None):
+        """Gumbel-max draws (device int32[rows]) of logits [rows, >= V] / T, and
+        with lse (or want_lse) the rows' log-sum-exp (fp32[rows]).  Returns
+        (tokens, lse or None)."""
         rows = logits.shape[0]
         if tokens is None:
             tokens = torch.empty(rows, dtype=torch.int32, device=self.device)
-        if lse is None:
+        if want_lse and lse is None:
             lse = torch.empty(rows, dtype=torch.float32, device=self.device)
         self._check(lib().dflash_sample_tokens(self.h, logits.data_ptr(), logits.stride(0), rows, float(temperature),
-                                               seed, tokens.data_ptr(), lse.data_ptr(), _stream(stream)),
+                                               seed, tokens.data_ptr(), _p(lse), _stream(stream)),
                     "sample_tokens")
         return tokens, lse
 

@@ -1,4 +1,4 @@
-"""Greedy and DFlash speculative generation over libdflash contexts.
+"""Greedy, sampled and DFlash speculative generation over libdflash contexts.
 
 Orchestration only: every step of the model runs in libdflash calls; torch
 holds the device buffers and moves a few token ids between them.
@@ -38,23 +38,32 @@ class _Capture:
         return lst
 
 
-def prefill(target: DFlash, prompt: torch.Tensor, draft: Optional[DFlash] = None) -> torch.Tensor:
+def prefill(target: DFlash, prompt: torch.Tensor, draft: Optional[DFlash] = None,
+            last_logits: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Run the prompt (device int32[P]) through the target in calls of up to 16
     rows; with a draft, fuse and inject every call's captured features as its
-    context.  Returns the first generated token as device int32[1]."""
+    context.  Returns the greedy first token as device int32[1]; last_logits
+    (device fp32 [1, V]) receives the logits of the prompt's last row."""
     cap = _Capture(target)
     am = torch.empty(ROWS, dtype=torch.int32, device=target.device)
     fused = None
     if draft is not None:
         fused = torch.empty(ROWS, draft.shape.hidden, dtype=draft.dtype, device=draft.device)
+    lg = None
+    if last_logits is not None:
+        lg = torch.empty(ROWS, target.shape.vocab, dtype=torch.float32, device=target.device)
     P = prompt.shape[0]
     M = 0
     for r0 in range(0, P, ROWS):
         M = min(ROWS, P - r0)
-        target.target_forward(prompt[r0:r0 + M], argmax=am[:M], capture=cap.views(M) if draft is not None else None)
+        last = r0 + M == P
+        target.target_forward(prompt[r0:r0 + M], argmax=am[:M], capture=cap.views(M) if draft is not None else None,
+                              logits=lg[:M] if last and lg is not None else None)
         if draft is not None:
             f = draft.fuse_context(cap.layer_list(M), out=fused[:M])
             draft.inject_kv(f, r0)
+    if last_logits is not None:
+        last_logits.copy_(lg[M - 1:M])
     return am[M - 1:M].clone()
 
 
@@ -163,6 +172,69 @@ def spec_tree_generate(target: DFlash, draft: DFlash, prompt: torch.Tensor, n_ne
         draft.inject_kv(f, C)
         out.extend(int(host[17 + j]) for j in path)
         out.append(bonus)
+        ks.append(k)
+        anchor.copy_(res[1:2])
+        C += k + 1
+    return out[:n_new], ks
+
+
+def step_seed(seed: int, step: int) -> int:
+    """The generator stream of one step: seed + (step + 1) * 0x9E3779B97F4A7C15 mod 2^64."""
+    return (seed + (step + 1) * 0x9E3779B97F4A7C15) & 0xFFFFFFFFFFFFFFFF
+
+
+def spec_sample_generate(target: DFlash, draft: DFlash, prompt: torch.Tensor, n_new: int, temperature: float,
+                         seed: int, on_step: Optional[Callable[..., None]] = None) -> Tuple[List[int], List[int]]:
+    """DFlash speculative decoding at temperature T with the speculative
+    sampling rule.
+
+    The first token is a Gumbel-max draw from the prompt's last target row
+    (stream step_seed(seed, 0), row 0).  Per step s >= 1 at context length C
+    with anchor a: draft the block with logits, draw d_1..d_{B-1} from the
+    draft's rows 1..B-1 (stream step_seed(seed, s)), verify [a, d_1..d_{B-1}]
+    with one causal target call for its logits, and apply the rule (same
+    stream): k accepted drafts and the next token.  Fuse and inject all B
+    verified rows into the draft and keep C + k + 1 positions in both caches.
+    on_step(C, seed, block, draft_logits, target_logits, result), when given,
+    sees every step's device buffers.  Returns (tokens, k of every step)."""
+    B = draft.shape.block
+    V = draft.shape.vocab
+    dev = target.device
+    first_lg = torch.empty(1, V, dtype=torch.float32, device=dev)
+    prefill(target, prompt, draft, last_logits=first_lg)
+    first = torch.empty(1, dtype=torch.int32, device=dev)
+    draft.sample_tokens(first_lg, temperature, step_seed(seed, 0), tokens=first)
+    cap = _Capture(target)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+    vin = torch.empty(B, dtype=torch.int32, device=dev)
+    g = torch.empty(B, dtype=torch.int32, device=dev)
+    res = torch.empty(2, dtype=torch.int32, device=dev)
+    dlg = torch.empty(B, V, dtype=torch.float32, device=dev)
+    tlg = torch.empty(B, V, dtype=torch.float32, device=dev)
+    fused = torch.empty(B, draft.shape.hidden, dtype=draft.dtype, device=dev)
+    anchor = first.clone()
+    out = [int(first.item())]
+    ks: List[int] = []
+    C = prompt.shape[0]
+    step = 0
+    while len(out) < n_new:
+        step += 1
+        sd = step_seed(seed, step)
+        draft.draft_block(anchor, tokens=tok, logits=dlg)
+        vin[0:1].copy_(anchor)
+        draft.sample_tokens(dlg[1:], temperature, sd, tokens=vin[1:])
+        target.target_forward(vin, argmax=g, logits=tlg, capture=cap.views(B))
+        draft.verify_sample(vin, dlg, tlg, temperature, sd, out=res)
+        if on_step is not None:
+            on_step(C, sd, vin, dlg, tlg, res)
+        f = draft.fuse_context(cap.layer_list(B), out=fused)
+        draft.inject_kv(f, C)
+        host = torch.cat([res, vin]).cpu()
+        k, nxt = int(host[0]), int(host[1])
+        target.rollback(C + k + 1)
+        draft.rollback(C + k + 1)
+        out.extend(int(t) for t in host[3:3 + k])
+        out.append(nxt)
         ks.append(k)
         anchor.copy_(res[1:2])
         C += k + 1

@@ -384,8 +384,11 @@ dflash_status dflash_sample_tokens(dflash_ctx* ctx, const float* logits, int64_t
  * rejection the next token is drawn from max(0, p - q) of those rows, after B
  * - 1 acceptances the bonus from softmax(target row B - 1 / T), with the draw
  * at (2^20 + 64, 0) (a draw: the first id whose running sum of weights
- * exceeds U * their total).  result_out: device int32[2] = {k, token}, the
- * layout of a dflash_verify_accept result. */
+ * exceeds U * their total).  Probabilities, comparisons and the draw's sums
+ * are fp64 (from the fp32 logits): where draft and target nearly agree the
+ * residual is a difference of nearly equal probabilities.  result_out: device
+ * int32[2] = {k, token}, the layout of a dflash_verify_accept result.  Uses
+ * the context's workspace: calls on one context are ordered by their stream. */
 dflash_status dflash_verify_sample(dflash_ctx* ctx, const int32_t* draft, const float* draft_logits,
                                    const float* target_logits, int64_t ld, float temperature, uint64_t seed,
                                    int32_t* result_out, void* stream);

@@ -64,8 +64,14 @@ def test_sample_tokens_matches_oracle(dl, V, T, rows, scale):
     x = di.normal((rows, V), 71, f"samp{V}_{T}", scale, torch.float32).numpy()
     seed = 0x5EED0000 + V
     print(f"[sample] V={V} T={T} rows={rows}", flush=True)
-    tok, lse = ctx.sample_tokens(_padded(x), T, seed)
+    g = _padded(x)
+    tok, lse = ctx.sample_tokens(g, T, seed, want_lse=True)
+    tok_only, _ = ctx.sample_tokens(g, T, seed)                     # draws alone
+    lse_only = torch.empty(rows, dtype=torch.float32, device="cuda")  # log-sum-exp alone (no token output)
+    assert dl.lib().dflash_sample_tokens(ctx.h, g.data_ptr(), g.stride(0), rows, T, seed, None,
+                                         lse_only.data_ptr(), None) == 0
     sync()
+    assert torch.equal(tok, tok_only) and torch.equal(lse, lse_only)
     ref = sp.sample_tokens(x, T, seed)
     got = tok.cpu().numpy()
     ties = 0
@@ -90,6 +96,29 @@ def test_sample_tokens_is_seeded(dl):
     assert torch.equal(a, b) and not torch.equal(a, c)
     assert int(a.min()) >= 0 and int(a.max()) < V
     assert len(set(a.cpu().tolist())) > 8      # 16 independent rows of a flat row rarely collide
+
+
+@pytest.mark.parametrize("seed,x,wins", [(301, 3207, False), (416, 2393, True)])
+def test_gumbel_draws_near_one(dl, seed, x, wins):
+    """Uniforms within 4 steps of 1 (U = 1 - 0.5 * 2^-24 for id 3207 at seed
+    301, U = 1 - 3.5 * 2^-24 for id 2393 at seed 416; both need 25 bits, so an
+    fp32 U would round to 1.0 and to 1 - 4 * 2^-24).  The id's logit is set so
+    that its exact key trails (seed 301) or beats (seed 416) the best other key
+    by 0.05; a perturbation taken from the rounded U lands on the other side
+    (+inf, and 0.134 lower)."""
+    V = 4000
+    ctx = _vocab_ctx(dl, V)
+    u = np.array([sp.uniform(seed, 0, i, open_interval=True) for i in range(V)])
+    assert 1 - u[x] < 4 * 2.0 ** -24
+    g = -np.log(-np.log(u))
+    other = np.delete(g, x).max()
+    z = np.zeros((1, V), np.float32)
+    z[0, x] = other + (0.05 if wins else -0.05) - g[x]
+    ref = sp.sample_tokens(z, 1.0, seed)
+    assert (ref["tokens"][0] == x) == wins and ref["gap"][0] > 0.04
+    tok, _ = ctx.sample_tokens(torch.from_numpy(z).cuda(), 1.0, seed)
+    sync()
+    assert int(tok[0]) == ref["tokens"][0]
 
 
 # ------------------------------------------------------------------ verification
@@ -206,3 +235,36 @@ def test_sample_errors(dl):
     with pytest.raises(dl.DFlashError):
         ctx.verify_sample(d, narrow, narrow, 1.0, 1)
     sync()
+
+
+def test_sampled_position_follows_the_target_distribution(dl):
+    """The GPU path of one drafted position end to end -- d_1 drawn from q by
+    dflash_sample_tokens, then dflash_verify_sample -- emits at position 1 a
+    token distributed as p = softmax(target row 0 / T) whatever q: token
+    frequencies over 6000 seeds within 4.5 standard errors of p, and the
+    acceptance rate P(k >= 1) within 4.5 standard errors of sum(min(p, q))."""
+    V, B, T, N = 16, 16, 0.8, 6000
+    ctx = _vocab_ctx(dl, V)
+    zd = di.normal((B, V), 91, "dist_d", 1.5, torch.float32).numpy()
+    zt = di.normal((B, V), 91, "dist_t", 1.5, torch.float32).numpy()
+    zt[0, :4] = zd[1, :4] + 0.3                    # overlapping mass on a few ids
+    p = np.exp(sp.log_softmax(zt[0], T))
+    q = np.exp(sp.log_softmax(zd[1], T))
+    gd, gt = torch.from_numpy(zd).cuda(), torch.from_numpy(zt).cuda()
+    toks = torch.zeros(N, B, dtype=torch.int32, device="cuda")
+    res = torch.empty(N, 2, dtype=torch.int32, device="cuda")
+    for i in range(N):
+        ctx.sample_tokens(gd[1:], T, 0xD157 + i, tokens=toks[i, 1:])
+        ctx.verify_sample(toks[i], gd, gt, T, 0xD157 + i, out=res[i])
+    sync()
+    t, r = toks.cpu().numpy(), res.cpu().numpy()
+    emitted = np.where(r[:, 0] >= 1, t[:, 1], r[:, 1])
+    f = np.bincount(emitted, minlength=V) / N
+    se = np.sqrt(p * (1 - p) / N)
+    print(f"[sample dist] max |f - p| / se = {np.max(np.abs(f - p) / np.maximum(se, 1e-12)):.2f}", flush=True)
+    assert (np.abs(f - p) <= 4.5 * se + 1.0 / N).all(), (f, p)
+    a = float(np.minimum(p, q).sum())
+    acc = float((r[:, 0] >= 1).mean())
+    assert abs(acc - a) <= 4.5 * np.sqrt(a * (1 - a) / N), (acc, a)
+    fq = np.bincount(t[:, 1], minlength=V) / N       # the drafts themselves follow q
+    assert (np.abs(fq - q) <= 4.5 * np.sqrt(q * (1 - q) / N) + 1.0 / N).all(), (fq, q)

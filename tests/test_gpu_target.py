@@ -278,6 +278,28 @@ def test_toy_greedy_matches_oracle(dl, toy, toy_oracle):
     assert first == n or ogaps[first] < band, f"free-running greedy diverges at {first} (gap {ogaps[first]:.3g})"
 
 
+def _assert_teacher_forced_greedy(toy, o, band):
+    """Every emitted token o[i] is the target's greedy token given prompt +
+    o[:i] (teacher-forced in 16-row calls), or its logit lies within `band`
+    of that token's.  Returns the indices where they differ."""
+    P, V = toy["prompt"].shape[0], TOY.vocab
+    ref, _ = toy["fresh"]()
+    seq = torch.cat([toy["prompt"], torch.tensor(o[:-1], dtype=torch.int32, device="cuda")])
+    am = torch.empty(seq.shape[0], dtype=torch.int32, device="cuda")
+    lg = torch.empty(seq.shape[0], V, dtype=torch.float32, device="cuda")
+    for r0 in range(0, seq.shape[0], 16):
+        M = min(16, seq.shape[0] - r0)
+        ref.target_forward(seq[r0:r0 + M], argmax=am[r0:r0 + M], logits=lg[r0:r0 + M])
+    sync()
+    pred = am[P - 1:].cpu().numpy()
+    lgp = lg[P - 1:].cpu().numpy()
+    mism = np.flatnonzero(o != pred)
+    for i in mism:
+        gap = float(lgp[i, pred[i]] - lgp[i, o[i]])
+        assert gap <= band, f"token {i}: emitted {o[i]} is {gap:.3g} below the greedy logit"
+    return mism
+
+
 @pytest.mark.parametrize("mode", ["ddtree", "branch"])
 def test_toy_tree_spec_is_lossless(toy, mode):
     """Tree verification ([A] §8.2) keeps greedy output: every emitted token is
@@ -304,23 +326,8 @@ def test_toy_tree_spec_is_lossless(toy, mode):
     out, ks = toy["spec"].spec_tree_generate(tgt, drf, toy["prompt"], n_new, K=4, budget=15,
                                              trees_fn=branch if mode == "branch" else None)
     print(f"[toy tree {mode}] steps {len(ks)} mean k {np.mean(ks):.3f}", flush=True)
-    # teacher-forced greedy over prompt + emitted tokens
-    ref, _ = toy["fresh"]()
-    seq = torch.cat([toy["prompt"], torch.tensor(out[:-1], dtype=torch.int32, device="cuda")])
-    am = torch.empty(seq.shape[0], dtype=torch.int32, device="cuda")
-    lg = torch.empty(seq.shape[0], V, dtype=torch.float32, device="cuda")
-    for r0 in range(0, seq.shape[0], 16):
-        M = min(16, seq.shape[0] - r0)
-        ref.target_forward(seq[r0:r0 + M], argmax=am[r0:r0 + M], logits=lg[r0:r0 + M])
-    sync()
-    pred = am[P - 1:].cpu().numpy()
-    lgp = lg[P - 1:].cpu().numpy()
     o = np.asarray(out)
-    mism = np.flatnonzero(o != pred)
-    band = bf16_logit_tol()
-    for i in mism:
-        gap = float(lgp[i, pred[i]] - lgp[i, o[i]])
-        assert gap <= band, f"token {i}: emitted {o[i]} is {gap:.3g} below the greedy logit"
+    mism = _assert_teacher_forced_greedy(toy, o, bf16_logit_tol())
     print(f"[toy tree {mode}] near-tie tokens {len(mism)} of {len(o)}", flush=True)
     if mode == "branch":
         # the forced branch holds the precomputed greedy tokens, so it is right
@@ -338,6 +345,56 @@ def test_toy_tree_spec_is_lossless(toy, mode):
         # each such step also relies on the previous step's compaction (the
         # accepted branch's K/V moved behind the root), or its verify would drift
         assert checked >= 1 or first < 12
+
+
+def test_toy_sampled_spec_matches_oracle(toy):
+    """Speculative sampling at T = 1 through the whole loop (draft, draws,
+    verify pass, rule, fuse, inject, rollback): at every step (k, next token)
+    is the oracle's rule on that step's fp32 logits, and on the first steps
+    the drafts are the oracle's Gumbel-max draws from the draft's rows (near
+    ties aside); the emitted tokens are each step's accepted drafts and its
+    next token."""
+    from oracle import sampling as sp
+    B = TOY.block
+    steps = []
+    stats = {"draw_ties": 0, "rule_ties": 0}
+
+    def on_step(C, sd, vin, dlg, tlg, res):
+        blk, d_l, t_l, r = vin.cpu().numpy(), dlg.cpu().numpy(), tlg.cpu().numpy(), res.cpu().numpy()
+        if len(steps) < 3:
+            ref = sp.sample_tokens(d_l[1:], 1.0, sd)
+            for j in np.flatnonzero(ref["tokens"] != blk[1:]):
+                assert ref["gap"][j] < 1e-3, f"step at C={C}: draft {j + 1} {blk[j + 1]} vs {ref['tokens'][j]}"
+                stats["draw_ties"] += 1
+        ref = sp.verify_sample(blk, d_l, t_l, 1.0, sd)
+        if (int(r[0]), int(r[1])) != (ref["k"], ref["bonus"]):
+            assert min(ref["accept_margins"] + [ref["draw_margin"]]) < 1e-9, (C, r, ref)
+            stats["rule_ties"] += 1
+        steps.append((blk[1:1 + int(r[0])].tolist(), int(r[1])))
+
+    tgt, drf = toy["fresh"]()
+    out, ks = toy["spec"].spec_sample_generate(tgt, drf, toy["prompt"], 64, 1.0, 1234, on_step=on_step)
+    print(f"[toy sampled] steps {len(ks)} mean k {np.mean(ks):.3f}; {stats}", flush=True)
+    assert stats["draw_ties"] <= 1 and stats["rule_ties"] <= 1
+    emitted = [out[0]]
+    for acc, nxt in steps:
+        emitted += acc + [nxt]
+    assert emitted[:len(out)] == out
+    assert ks == [len(a) for a, _ in steps] and all(0 <= k <= B - 1 for k in ks)
+
+
+def test_toy_sampled_spec_low_temperature_is_greedy(toy):
+    """At T = 1e-4 the draws and the rule reduce to argmaxes: the sampled loop
+    emits the target's greedy tokens, teacher-forced, except where two logits
+    lie within the bf16 band (or within 1e-4 * 17, the reach of a Gumbel
+    perturbation at that temperature)."""
+    tgt, drf = toy["fresh"]()
+    out, ks = toy["spec"].spec_sample_generate(tgt, drf, toy["prompt"], toy["n_new"], 1e-4, 5)
+    o = np.asarray(out)
+    mism = _assert_teacher_forced_greedy(toy, o, bf16_logit_tol() + 17e-4)
+    print(f"[toy sampled T=1e-4] steps {len(ks)} mean k {np.mean(ks):.3f}; near-tie tokens {len(mism)} of {len(o)}",
+          flush=True)
+    assert len(mism) <= len(o) // 20
 
 
 @pytest.mark.parametrize("tree", [False, True])
