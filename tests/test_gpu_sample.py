@@ -268,3 +268,54 @@ def test_sampled_position_follows_the_target_distribution(dl):
     assert abs(acc - a) <= 4.5 * np.sqrt(a * (1 - a) / N), (acc, a)
     fq = np.bincount(t[:, 1], minlength=V) / N       # the drafts themselves follow q
     assert (np.abs(fq - q) <= 4.5 * np.sqrt(q * (1 - q) / N) + 1.0 / N).all(), (fq, q)
+
+
+def test_sampling_masked_vocabulary(dl):
+    """Ids with -inf logits (a masked vocabulary): never drawn, no mass in the
+    log-sum-exp, p = q = 0 there; draws, lse and the rule match the oracle."""
+    V, B = 4000, 16
+    ctx = _vocab_ctx(dl, V)
+    rng = np.random.default_rng(17)
+    mask = rng.random(V) < 0.5
+    zd = di.normal((B, V), 93, "mask_d", 2.0, torch.float32).numpy()
+    zt = np.roll(zd, -1, axis=0) + di.normal((B, V), 93, "mask_t", 0.7, torch.float32).numpy()
+    zd[:, mask] = -np.inf
+    zt[:, mask] = -np.inf
+    gd, gt = _padded(zd), _padded(zt)
+    tok, lse = ctx.sample_tokens(gd[1:], 1.0, 55, want_lse=True)
+    sync()
+    ref = sp.sample_tokens(zd[1:], 1.0, 55)
+    got = tok.cpu().numpy()
+    assert not mask[got].any()
+    assert ((got == ref["tokens"]) | (ref["gap"] < GAP)).all()
+    np.testing.assert_allclose(lse.cpu().numpy().astype(np.float64), ref["lse"], rtol=1e-6, atol=1e-6)
+    d = np.zeros(B, dtype=np.int32)
+    d[1:] = got
+    exempt = 0
+    for s in range(20):
+        o = ctx.verify_sample(torch.from_numpy(d).cuda(), gd, gt, 1.0, 300 + s).cpu().numpy()
+        r = sp.verify_sample(d, zd, zt, 1.0, 300 + s)
+        assert not mask[o[1]]
+        exempt += _check_verify(o, r, zd, zt, d, 1.0, 300 + s)
+    assert exempt <= 1
+
+
+def test_verify_sample_short_block(dl):
+    """A context whose block is 8 rows: the rule walks drafts 1..7, reads 15
+    log-sum-exp rows, and draws the bonus from target row 7."""
+    V, B = 1008, 8
+    s = di.Shape("s1008b8", "bf16", hidden=64, target_layers=8, draft_layers=1, n_q_heads=2, n_kv_heads=1,
+                 head_dim=64, ffn=96, vocab=V, ctx=16, seed=7, block=B)
+    ctx = dl.DFlash(s, dev(di.draft_weights(s, need_draft=False, need_lm=False)), max_ctx=64)
+    ks, exempt = [], 0
+    for kind in ("near", "same", "far"):
+        zd, zt, d = _block(V, B, kind, f"short_{kind}")
+        gd, gt, gdr = _padded(zd), _padded(zt), torch.from_numpy(d).cuda()
+        for seed in range(16):
+            o = ctx.verify_sample(gdr, gd, gt, 0.9, seed).cpu().numpy()
+            r = sp.verify_sample(d, zd, zt, 0.9, seed)
+            exempt += _check_verify(o, r, zd, zt, d, 0.9, seed)
+            ks.append(r["k"])
+            if kind == "same":
+                assert r["k"] == B - 1
+    assert exempt <= 1 and max(ks) == B - 1 and min(ks) == 0
