@@ -525,6 +525,8 @@ dflash_status dflash_sample_tokens(dflash_ctx* c, const float* logits, int64_t l
     if (rows < 1 || rows > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "rows must be in [1, 16]");
     if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(c, DFLASH_ERR_INVAL, "temperature must be > 0");
     if (ld < d.V || !aligned(logits, 4)) return fail(c, DFLASH_ERR_INVAL, "ld must be >= V and logits aligned");
+    if ((tokens_out && !aligned(tokens_out, 4)) || (lse_out && !aligned(lse_out, 4)))
+        return fail(c, DFLASH_ERR_INVAL, "tokens_out / lse_out misaligned");
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -544,6 +546,7 @@ dflash_status dflash_verify_sample(dflash_ctx* c, const int32_t* draft, const fl
     if (!(temperature > 0.f) || !std::isfinite(temperature)) return fail(c, DFLASH_ERR_INVAL, "temperature must be > 0");
     if (ld < d.V || !aligned(draft_logits, 4) || !aligned(target_logits, 4))
         return fail(c, DFLASH_ERR_INVAL, "ld must be >= V and logits aligned");
+    if (!aligned(draft, 4) || !aligned(result_out, 4)) return fail(c, DFLASH_ERR_INVAL, "draft / result_out misaligned");
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);

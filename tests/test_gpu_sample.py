@@ -234,6 +234,14 @@ def test_sample_errors(dl):
         ctx.sample_tokens(narrow, 1.0, 1)                 # row stride below V
     with pytest.raises(dl.DFlashError):
         ctx.verify_sample(d, narrow, narrow, 1.0, 1)
+    # misaligned int32 / fp32 buffers are refused before anything is enqueued
+    L, ok = dl.lib(), torch.zeros(16, dtype=torch.int32, device="cuda")
+    assert L.dflash_sample_tokens(ctx.h, lg.data_ptr(), lg.stride(0), 4, 1.0, 1, ok.data_ptr() + 2, None, None) != 0
+    assert L.dflash_sample_tokens(ctx.h, lg.data_ptr(), lg.stride(0), 4, 1.0, 1, None, ok.data_ptr() + 1, None) != 0
+    assert L.dflash_verify_sample(ctx.h, d.data_ptr() + 2, lg.data_ptr(), lg.data_ptr(), lg.stride(0), 1.0, 1,
+                                  ok.data_ptr(), None) != 0
+    assert L.dflash_verify_sample(ctx.h, d.data_ptr(), lg.data_ptr(), lg.data_ptr(), lg.stride(0), 1.0, 1,
+                                  ok.data_ptr() + 2, None) != 0
     sync()
 
 
