@@ -80,13 +80,20 @@ def test_speculative_step_emits_the_target_distribution(case):
 
 def test_chain_acceptance_extremes():
     """A target equal to the draft accepts every draft (k = 15, the bonus drawn
-    from the last target row); a target that gives the drafts no mass accepts
-    none, and its token is never the rejected draft."""
+    from the last target row: a row peaked at one id gives that id); a target
+    that gives the drafts no mass accepts none, and its token is never the
+    rejected draft."""
     B, V = 16, 40
     z = di.normal((B, V), 5, "chainx", 1.0, torch.float32).numpy()
     d = sp.sample_tokens(z, 1.0, seed=9)["tokens"]
     r = sp.verify_sample(d, z, np.roll(z, -1, axis=0), 1.0, seed=9)
     assert r["k"] == B - 1
+    # the bonus comes from the last target row: peaked at id 7 there, elsewhere as before
+    t = np.roll(z, -1, axis=0)
+    t[B - 1] = -30.0
+    t[B - 1, 7] = 30.0
+    r = sp.verify_sample(d, z, t, 1.0, seed=9)
+    assert r["k"] == B - 1 and r["bonus"] == 7
     far = np.array(z, copy=True)
     for j in range(1, B):
         far[j - 1, d[j]] = -1e4
