@@ -18,8 +18,9 @@
 // Gumbel draw of row r and token x is (r, x); the acceptance draw of draft j
 // is (2^20 + j, 0); the rejection / bonus draw is (2^20 + 64, 0).
 //
-// Precision.  Gumbel keys are fp32 (a draw flips only where two keys lie
-// within fp32 rounding).  The verification works in fp64 from the fp32
+// Precision.  Gumbel keys are fp32, the perturbation good to about 2e-6
+// absolute (a draw flips only where two keys lie that close).  The
+// verification works in fp64 from the fp32
 // logits: where draft and target nearly agree, the residual max(0, p - q)
 // is a difference of nearly equal probabilities, and at a 152K vocabulary an
 // fp32 log-sum-exp (ulp ~1e-6 at ~12) cannot resolve a residual mass of 1e-5.

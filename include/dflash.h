@@ -369,9 +369,13 @@ dflash_status dflash_tree_commit(dflash_ctx* ctx, int32_t pos0, int32_t M, const
  * from softmax(row / temperature) by the Gumbel-max method: the id x with
  * the largest row[x] / T - log(-log U), U the draw at coordinates (r, x)
  * (ties: lower id).  tokens_out: device int32[rows] or NULL; lse_out: device
- * fp32[rows] or NULL, the rows' log-sum-exp of row / T.  1 <= rows <= 16,
- * temperature > 0 and finite (INVAL otherwise).  For a drafted block pass the
- * draft's logits from row 1 on: token r is the draft for position C + 1 + r. */
+ * fp32[rows] or NULL, the rows' log-sum-exp of row / T (fp64 sums; at least
+ * one of the two outputs).  Keys are fp32 with the perturbation good to about
+ * 2e-6 absolute.  1 <= rows <= 16, temperature > 0 and finite, every buffer
+ * 4-byte aligned (INVAL otherwise, nothing enqueued).  For a drafted block
+ * pass the draft's logits from row 1 on: token r is the draft for position
+ * C + 1 + r.  Uses the context's workspace: calls on one context are ordered
+ * by their stream. */
 dflash_status dflash_sample_tokens(dflash_ctx* ctx, const float* logits, int64_t ld, int32_t rows, float temperature,
                                    uint64_t seed, int32_t* tokens_out, float* lse_out, void* stream);
 
@@ -387,8 +391,10 @@ dflash_status dflash_sample_tokens(dflash_ctx* ctx, const float* logits, int64_t
  * exceeds U * their total).  Probabilities, comparisons and the draw's sums
  * are fp64 (from the fp32 logits): where draft and target nearly agree the
  * residual is a difference of nearly equal probabilities.  result_out: device
- * int32[2] = {k, token}, the layout of a dflash_verify_accept result.  Uses
- * the context's workspace: calls on one context are ordered by their stream. */
+ * int32[2] = {k, token}, the layout of a dflash_verify_accept result.
+ * temperature > 0 and finite, ld >= V, every buffer 4-byte aligned (INVAL
+ * otherwise, nothing enqueued).  Uses the context's workspace: calls on one
+ * context are ordered by their stream. */
 dflash_status dflash_verify_sample(dflash_ctx* ctx, const int32_t* draft, const float* draft_logits,
                                    const float* target_logits, int64_t ld, float temperature, uint64_t seed,
                                    int32_t* result_out, void* stream);
