@@ -25,7 +25,7 @@ constexpr int kMaxSplits = 256;          // context splits of the split-KV atten
 constexpr int kMaxSplitPages = 1040;     // KV pages one attention split may touch
 constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
 constexpr int kTopKMax = 16;             // candidates per draft position of a tree (the largest useful K)
-constexpr int kTopKSegs = 32;            // vocabulary segments of the top-K partial pass
+constexpr int kTopKSegs = 64;            // vocabulary segments of the top-K partial pass (one merge lane each)
 
 struct Dims {
     int dtype, H, Lt, Ld, nq, nkv, d, F, V, B, mask_id, page, max_ctx, max_rows, n_pages, elem;

@@ -179,52 +179,55 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
     }
 }
 
-// One row per workgroup: the rank of each of the S*K segment candidates among
-// all of them places the row's K best; log-probabilities subtract the row's
-// log-sum-exp, merged from the segments in segment order.
-__global__ __launch_bounds__(512) void topk_merge_kernel(const float* part, int S, int K, int32_t* ids, float* logp) {
+// One wave per row.  Lane l < S holds segment l's list (its K best in rank
+// order, from the partial pass); K rounds of a 64-lane butterfly pick the best
+// list head (value descending, id ascending), which the owning lane then
+// drops.  The row's log-sum-exp: the segments' largest max, then their sums
+// rescaled to it and added over the wave; log-probabilities subtract it.
+__global__ __launch_bounds__(64) void topk_merge_kernel(const float* part, int S, int K, int32_t* ids, float* logp) {
     __shared__ float c_v[kTopKSegs * kTopKMax];
     __shared__ int c_i[kTopKSegs * kTopKMax];
-    __shared__ float s_m[kTopKSegs], s_s[kTopKSegs];
-    __shared__ float s_lse;
-    const int r = blockIdx.x, tid = threadIdx.x, n = S * K;
+    const int r = blockIdx.x, lane = threadIdx.x;
     const float* base = part + (long long)r * S * kPartStride;
-    for (int t = tid; t < n; t += blockDim.x) {
+    for (int t = lane; t < S * K; t += 64) {
         const float* rec = base + (long long)(t / K) * kPartStride;
         c_v[t] = rec[t % K];
         c_i[t] = reinterpret_cast<const int*>(rec)[kTopKMax + t % K];
     }
-    if (tid < S) {
-        s_m[tid] = base[(long long)tid * kPartStride + 2 * kTopKMax];
-        s_s[tid] = base[(long long)tid * kPartStride + 2 * kTopKMax + 1];
+    float m = -INFINITY, sm = 0.f;
+    if (lane < S) {
+        m = base[(long long)lane * kPartStride + 2 * kTopKMax];
+        sm = base[(long long)lane * kPartStride + 2 * kTopKMax + 1];
     }
+    float M = m;
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float L = m == -INFINITY ? 0.f : sm * __expf(m - M);
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    const float lse = M + logf(L);
     __syncthreads();
-    if (tid == 0) {
-        float M = -INFINITY, L = 0.f;
-        for (int sgi = 0; sgi < S; ++sgi) lse_combine(M, L, s_m[sgi], s_s[sgi]);
-        s_lse = M + logf(L);
-    }
-    __syncthreads();
-    const float lse = s_lse;
-    for (int t = tid; t < n; t += blockDim.x) {
-        const float v = c_v[t];
-        const int id = c_i[t];
-        // each segment's list is in rank order: count its entries ranked
-        // before this one by binary search
-        int rank = 0;
-        for (int sg = 0; sg < S; ++sg) {
-            int lo = 0, hi = K;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (ranks_before(c_v[sg * K + mid], c_i[sg * K + mid], v, id)) lo = mid + 1;
-                else hi = mid;
+    int head = 0;  // this lane's next unchosen entry
+    for (int k = 0; k < K; ++k) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        if (lane < S && head < K) {
+            bv = c_v[lane * K + head];
+            bi = c_i[lane * K + head];
+        }
+        const float mv = bv;
+        const int mi = bi;
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float v2 = __shfl_xor(bv, o, 64);
+            const int i2 = __shfl_xor(bi, o, 64);
+            if (ranks_before(v2, i2, bv, bi)) {
+                bv = v2;
+                bi = i2;
             }
-            rank += lo;
         }
-        if (rank < K) {
-            ids[(long long)r * K + rank] = id;
-            logp[(long long)r * K + rank] = v - lse;
+        if (lane == 0) {
+            ids[(long long)r * K + k] = bi;
+            logp[(long long)r * K + k] = bv - lse;
         }
+        if (lane < S && head < K && mv == bv && mi == bi) ++head;  // the owner (real ids are unique)
     }
 }
 
@@ -393,13 +396,13 @@ __global__ __launch_bounds__(256) void tree_commit_kernel(CommitArgs a) {
 hipError_t launch_topk(const DevCtx& c, const float* logits, long long ld, int rows, int K, int32_t* ids, float* logp,
                        hipStream_t s) {
     const int V = c.dm.V;
-    // segments of at least 4096 ids: every wave then holds K real candidates
-    const int S = std::max(1, std::min(kTopKSegs, V / 4096));
+    // segments of at least 2048 ids: every wave then holds at least K real candidates
+    const int S = std::max(1, std::min(kTopKSegs, V / 2048));
     float* part = reinterpret_cast<float*>(c.ws + c.lay.topk_part);
     hipLaunchKernelGGL(topk_partial_kernel, dim3(S, rows), dim3(kTopKThreads), 0, s, logits, ld, V, K, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(512), 0, s, part, S, K, ids, logp);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(64), 0, s, part, S, K, ids, logp);
     return hipGetLastError();
 }
 
