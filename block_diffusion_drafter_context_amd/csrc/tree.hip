@@ -50,6 +50,9 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
 // One (row, vocabulary segment) per workgroup: every thread keeps a sorted
 // list of its K best (value, id) pairs and its own running (max, sum of exp);
 // then K rounds of a workgroup-wide best pick the segment's K best in order.
+// KM: the list length compiled in (the smallest of 4, 8, 16 that holds K), so
+// an insertion costs KM compare-and-moves.
+template <int KM>
 __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float* logits, long long ld, int V, int K,
                                                                     float* part) {
     constexpr int W = kTopKThreads / 64;
@@ -62,10 +65,10 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
     const int beg = seg * per, end = min(V, beg + per);
     const float* x = logits + (long long)r * ld;
 
-    float tv[kTopKMax];
-    int ti[kTopKMax];
+    float tv[KM];
+    int ti[KM];
 #pragma unroll
-    for (int q = 0; q < kTopKMax; ++q) {
+    for (int q = 0; q < KM; ++q) {
         tv[q] = -INFINITY;
         ti[q] = 0x7fffffff;
     }
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
             float cv = v;
             int ci = i;
 #pragma unroll
-            for (int q = 0; q < kTopKMax; ++q) {  // insert, shifting the rest down
+            for (int q = 0; q < KM; ++q) {  // insert, shifting the rest down
                 const bool take = cv > tv[q];
                 const float ov = tv[q];
                 const int oi = ti[q];
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
                 ci = take ? oi : ci;
             }
 #pragma unroll
-            for (int q = 0; q < kTopKMax; ++q)
+            for (int q = 0; q < KM; ++q)
                 if (q == K - 1) thr = tv[q];
         }
         }
@@ -156,12 +159,12 @@ __global__ __launch_bounds__(kTopKThreads) void topk_partial_kernel(const float*
         }
         if (ti[0] == bi && tv[0] == bv) {  // the owner (ids are unique among real entries)
 #pragma unroll
-            for (int q = 0; q + 1 < kTopKMax; ++q) {
+            for (int q = 0; q + 1 < KM; ++q) {
                 tv[q] = tv[q + 1];
                 ti[q] = ti[q + 1];
             }
-            tv[kTopKMax - 1] = -INFINITY;
-            ti[kTopKMax - 1] = 0x7fffffff;
+            tv[KM - 1] = -INFINITY;
+            ti[KM - 1] = 0x7fffffff;
         }
     }
     __syncthreads();
@@ -399,7 +402,10 @@ hipError_t launch_topk(const DevCtx& c, const float* logits, long long ld, int r
     // segments of at least 2048 ids: every wave then holds at least K real candidates
     const int S = std::max(1, std::min(kTopKSegs, V / 2048));
     float* part = reinterpret_cast<float*>(c.ws + c.lay.topk_part);
-    hipLaunchKernelGGL(topk_partial_kernel, dim3(S, rows), dim3(kTopKThreads), 0, s, logits, ld, V, K, part);
+    const dim3 grid(S, rows);
+    if (K <= 4) hipLaunchKernelGGL(topk_partial_kernel<4>, grid, dim3(kTopKThreads), 0, s, logits, ld, V, K, part);
+    else if (K <= 8) hipLaunchKernelGGL(topk_partial_kernel<8>, grid, dim3(kTopKThreads), 0, s, logits, ld, V, K, part);
+    else hipLaunchKernelGGL(topk_partial_kernel<kTopKMax>, grid, dim3(kTopKThreads), 0, s, logits, ld, V, K, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(64), 0, s, part, S, K, ids, logp);
