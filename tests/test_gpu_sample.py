@@ -327,3 +327,55 @@ def test_verify_sample_short_block(dl):
             if kind == "same":
                 assert r["k"] == B - 1
     assert exempt <= 1 and max(ks) == B - 1 and min(ks) == 0
+
+
+def test_sampling_graph_replay(dl):
+    """The non-greedy calls hold no host read, so a step of them can be
+    captured in a HIP graph: draws of the drafted positions, then the rule.
+    Every replay (with eager work of the same context in between, fresh logits
+    copied in before each) equals the eager calls on the same inputs bit for
+    bit."""
+    V, B = 4000, 16
+    ctx = _vocab_ctx(dl, V)
+    cases = []
+    for i in range(3):
+        zd, zt, _ = _block(V, B, "near", f"graph{i}")
+        cases.append((torch.from_numpy(zd).cuda(), torch.from_numpy(zt).cuda()))
+    dlg = torch.empty(B, V, dtype=torch.float32, device="cuda")
+    tlg = torch.empty(B, V, dtype=torch.float32, device="cuda")
+    blk = torch.zeros(B, dtype=torch.int32, device="cuda")
+    res = torch.empty(2, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+
+    def step():
+        ctx.sample_tokens(dlg[1:], 0.8, 4242, tokens=blk[1:], stream=s)
+        ctx.verify_sample(blk, dlg, tlg, 0.8, 4242, out=res, stream=s)
+
+    eager = []
+    for zd, zt in cases:
+        dlg.copy_(zd)
+        tlg.copy_(zt)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            step()
+        s.synchronize()
+        eager.append((blk.clone(), res.clone()))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    s.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, (zd, zt) in enumerate(cases):
+            dlg.copy_(zd)
+            tlg.copy_(zt)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(blk, eager[i][0]) and torch.equal(res, eager[i][1]), (rep, i)
+            # eager work of the same context between replays (its own draws)
+            ctx.sample_tokens(dlg[:4], 1.3, 99 + rep)
+            torch.cuda.synchronize()
