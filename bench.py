@@ -558,6 +558,32 @@ def main():
                          "overhead_vs_chain_verify_us": round(float(helpers.sum()) + tv - pv[1], 1)}
         log(f"[bench] ddtree: {json.dumps(out['ddtree'])}")
 
+        # the same with a budget of 22 nodes (the pages' larger budget): 23 rows,
+        # verified in two tree passes (nodes 16.. see their ancestors in the cache)
+        va32 = torch.empty(32, dtype=torch.int32, device="cuda")
+
+        def tree22_step():
+            ids, lp = ctxv.draft_topk(lgt, 4)
+            tt, tp = ctxv.build_tree(vt[:1], ids, lp, 22)
+            ctxv.target_forward(tt, argmax=va32[:23], parent=tp)
+            ctxv.tree_accept(tt, tp, va32[:23], out=res)
+            ctxv.tree_commit(Cv, 23, res)
+            ctxv.rollback(Cv)
+        for _ in range(args.warmup):
+            tree22_step()
+        torch.cuda.synchronize()
+        assert dl.lib().dflash_trace_enable(ctxv.h, 10, 2 * nv) == 0
+        for _ in range(nv):
+            tree22_step()
+        buf = (C_.c_float * (2 * nv))()
+        assert dl.lib().dflash_trace_read_each(ctxv.h, buf, 2 * nv, C_.byref(cnt)) == 0
+        dl.lib().dflash_trace_enable(ctxv.h, 0, 0)
+        t22 = np.array(buf[:cnt.value], dtype=np.float64).reshape(nv, 2).sum(axis=1) * 1e3
+        out["ddtree22"] = {"workload": "as ddtree with a tree of 23 nodes (budget 22): two tree-masked passes",
+                           "verify_tree_us_p50": round(float(np.median(t22)), 1),
+                           "vs_chain_verify": round(float(np.median(t22)) / pv[1], 3)}
+        log(f"[bench] ddtree22: {json.dumps(out['ddtree22'])}")
+
         # non-greedy verification at the 8B vocabulary (T = 1): Gumbel-max draws
         # of the 15 drafted positions from seeded stand-in draft logits, then the
         # speculative sampling rule against target logits near the draft's

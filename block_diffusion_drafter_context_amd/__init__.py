@@ -321,7 +321,7 @@ class DFlash:
                        stream=None, parent: Optional[torch.Tensor] = None,
                        layers_out: Optional[torch.Tensor] = None):
         """Causal forward of tokens (device int32[M], M <= 16) at positions length..length+M-1,
-        or with parent (device int32[M]) the tree-masked forward of dflash_target_forward_tree.
+        or with parent (device int32[M], M <= 32) the tree-masked forward of dflash_target_forward_tree.
         capture: 5 tensors [>= M, H] with one common row stride (or None entries).
         layers_out: [Ld, M, H] device tensor receiving every layer's output (no capture then).
         Returns (argmax int32[M], logits fp32[M, V] or None)."""

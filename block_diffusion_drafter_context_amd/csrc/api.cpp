@@ -407,7 +407,8 @@ dflash_status target_forward(dflash_ctx* c, const int32_t* tokens, const int32_t
     const DevCtx& x = c->dev;
     const Dims& d = x.dm;
     if (!tokens || !argmax_out) return fail(c, DFLASH_ERR_INVAL, "null tokens or argmax_out");
-    if (M < 1 || M > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 16]");
+    if (!parent && (M < 1 || M > DFLASH_MAX_BLOCK)) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 16]");
+    if (parent && (M < 1 || M > DFLASH_TREE_MAX_NODES)) return fail(c, DFLASH_ERR_INVAL, "tree nodes must be in [1, 32]");
     if (!x.embed || !x.lm_head || !x.final_norm) return fail(c, DFLASH_ERR_INVAL, "needs embed, lm_head, final_norm");
     for (int l = 0; l < d.Ld; ++l)
         if (!x.attn_norm[l] || !x.wq[l] || !x.wo[l] || !x.mlp_norm[l] || !x.wg[l] || !x.wu[l] || !x.wd[l])
@@ -430,9 +431,22 @@ dflash_status target_forward(dflash_ctx* c, const int32_t* tokens, const int32_t
     if ((long long)c->length + M > d.max_ctx) return fail(c, DFLASH_ERR_CAPACITY, "forward would exceed max_ctx");
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
-    hipError_t e = launch_causal_forward(x, c->length, tokens, M, logits_out, argmax_out, capture, capture_ld,
-                                         static_cast<hipStream_t>(stream), parent, layer_out, layer_ld);
-    if (e != hipSuccess) return hip_fail(c, e, "target forward launch");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // a tree of more than 16 nodes: two passes, nodes 0..15 then 16..M-1, the
+    // second seeing its ancestors among the first pass's nodes in the cache
+    const int C0 = c->length;
+    for (int off = 0; off < M; off += DFLASH_MAX_BLOCK) {
+        const int m = std::min(M - off, (int)DFLASH_MAX_BLOCK);
+        void* cap_off[DFLASH_NUM_FEATURES];
+        if (capture)
+            for (int i = 0; i < DFLASH_NUM_FEATURES; ++i)
+                cap_off[i] = capture[i] ? static_cast<char*>(capture[i]) + (size_t)off * capture_ld * d.elem : nullptr;
+        void* lo = layer_out ? static_cast<char*>(layer_out) + (size_t)off * layer_ld * d.elem : nullptr;
+        hipError_t e = launch_causal_forward(x, C0 + off, tokens + off, m, logits_out ? logits_out + (size_t)off * d.V : nullptr,
+                                             argmax_out + off, capture ? cap_off : nullptr, capture_ld, s, parent,
+                                             lo, layer_ld, off, C0, parent ? M : 0, M);
+        if (e != hipSuccess) return hip_fail(c, e, "target forward launch");
+    }
     c->length += M;
     return DFLASH_OK;
 }
@@ -485,7 +499,7 @@ dflash_status dflash_build_tree(dflash_ctx* c, const int32_t* anchor, const int3
     if (!anchor || !ids || !logp || !tokens_out || !parent_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
     if (depths < 1 || depths > DFLASH_MAX_BLOCK - 1) return fail(c, DFLASH_ERR_INVAL, "depths must be in [1, 15]");
     if (K < 1 || K > DFLASH_TREE_MAX_K) return fail(c, DFLASH_ERR_INVAL, "K must be in [1, 16]");
-    if (budget < 0 || budget > DFLASH_MAX_BLOCK - 1) return fail(c, DFLASH_ERR_INVAL, "budget must be in [0, 15]");
+    if (budget < 0 || budget > DFLASH_TREE_MAX_NODES - 1) return fail(c, DFLASH_ERR_INVAL, "budget must be in [0, 31]");
     long long nodes = 0, layer = 1;  // nodes of the full candidate tree (enough once it reaches the budget)
     for (int i = 0; i < depths && nodes < budget; ++i) {
         layer *= K;
@@ -506,7 +520,7 @@ dflash_status dflash_tree_accept(dflash_ctx* c, const int32_t* tokens, const int
                                  int32_t M, int32_t* result_out, void* stream) {
     if (!c) return DFLASH_ERR_INVAL;
     if (!tokens || !parent || !target || !result_out) return fail(c, DFLASH_ERR_INVAL, "null pointer");
-    if (M < 1 || M > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 16]");
+    if (M < 1 || M > DFLASH_TREE_MAX_NODES) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 32]");
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -562,7 +576,7 @@ dflash_status dflash_tree_commit(dflash_ctx* c, int32_t pos0, int32_t M, const i
     if (!c) return DFLASH_ERR_INVAL;
     const Dims& d = c->dev.dm;
     if (!result) return fail(c, DFLASH_ERR_INVAL, "null result");
-    if (M < 1 || M > DFLASH_MAX_BLOCK) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 16]");
+    if (M < 1 || M > DFLASH_TREE_MAX_NODES) return fail(c, DFLASH_ERR_INVAL, "M must be in [1, 32]");
     const long long lim = c->dev_len ? d.max_ctx : c->length;
     if (pos0 < 0 || (long long)pos0 + M > lim) return fail(c, DFLASH_ERR_INVAL, "rows pos0..pos0+M-1 must be inside the context");
     if (capture) {

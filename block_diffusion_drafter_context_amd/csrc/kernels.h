@@ -72,13 +72,18 @@ hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, flo
                               int32_t* tokens, void* layer_out, long long layer_ld, const int* len_dev,
                               hipStream_t s);
 // Causal forward of M <= 16 tokens at positions C..C+M-1 (K/V appended to the cache).
-// tree_parent (device int32[M], or null): the rows form a tree; row j is placed
-// at C + depth(j) and sees the cache before C plus its ancestors (K/V still at C + j).
-// layer_out (or null): [Ld][M][layer_ld] residual after every layer, in place of capture.
+// tree_parent (device int32[tree_n], or null): the rows are nodes tree_off ..
+// tree_off + M - 1 of a tree of tree_n <= 32 nodes whose root (node 0) sits at
+// tree_base; node u is placed at tree_base + depth(u) and sees the cache before
+// tree_base plus its ancestors (K/V of node u at slot tree_base + u, so C must be
+// tree_base + tree_off).  layer_out (or null): [Ld][layer_rows][layer_ld]
+// residual after every layer (rows of this pass from layer_out on; layer_rows 0:
+// M), in place of capture.
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits,
                                  int32_t* argmax, void* const* capture, long long capture_ld, hipStream_t s,
                                  const int32_t* tree_parent = nullptr, void* layer_out = nullptr,
-                                 long long layer_ld = 0);
+                                 long long layer_ld = 0, int tree_off = 0, int tree_base = 0, int tree_n = 0,
+                                 int layer_rows = 0);
 // Tree verification helpers (tree.hip).
 // Per row r < rows of logits [rows][ld]: the K <= 16 largest ids (ties: lower
 // id first) and their fp32 log-probabilities.

@@ -531,7 +531,8 @@ struct OpQKV {
     NormA<T> a;
     const int* len_dev = nullptr;  // device-resident length: row 0 sits at *len_dev (else at pos0)
     int max_ctx = 0;               // the device length is clamped into [0, max_ctx] (rotary table bound)
-    const int* row_depth = nullptr;  // tree rows: row j is rotated for position pos0 + row_depth[j] (in [0, 15])
+    const int* row_depth = nullptr;  // tree rows: row j is rotated for position rot_base + row_depth[j] (depth < 32)
+    int rot_base = 0;                // tree rows: the position of the tree's root
     const T* wq;
     const T* wk;
     const T* wv;
@@ -568,8 +569,8 @@ struct OpQKV {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int j = min(4 * (lane >> 4) + ii, M - 1);
-            const int jp = row_depth ? row_depth[j] : j;  // its KV slot stays pos0 + j
-            const long long t = (long long)(st.pos0 + jp) * half + dim;
+            // a tree row's KV slot stays pos0 + j; it is rotated for its depth below the root
+            const long long t = (long long)(row_depth ? rot_base + row_depth[j] : st.pos0 + j) * half + dim;
             st.cs[ii] = cosT[t];
             st.sn[ii] = sinT[t];
         }
@@ -1629,22 +1630,23 @@ template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_t* ids, int n_ids, int mask_id, int V,
                                                     int H, float eps, T* x, float* rstd, unsigned long long* best,
                                                     float* clear, int clear_n, const int32_t* tree_parent,
-                                                    int* tree_info) {
+                                                    int tree_off, int tree_n, int* tree_info) {
     __shared__ float red[4];
-    __shared__ int par[16];
+    __shared__ int par[32];
     const int j = blockIdx.x;
     if (tree_parent) {
-        // tree verification: row j's depth and the mask of its ancestors and
-        // itself.  A parent outside [0, row) is read as the root, so every
-        // walk ends at row 0 within 15 steps.
-        if (threadIdx.x < 16) {
+        // tree verification: row j is tree node u = tree_off + j (a tree of
+        // tree_n <= 32 nodes verified in passes of up to 16 rows); its depth
+        // and the mask of its ancestors and itself (bit i: node i).  A parent
+        // outside [0, node) is read as the root, so every walk ends at node 0.
+        if (threadIdx.x < 32) {
             const int r = threadIdx.x;
-            const int p = r < n_ids ? tree_parent[r] : 0;
+            const int p = r < tree_n ? tree_parent[r] : 0;
             par[r] = (p >= 0 && p < r) ? p : 0;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
-            int u = j, depth = 0;
+            int u = tree_off + j, depth = 0;
             uint32_t anc = 1u;
             while (u > 0) {
                 anc |= 1u << u;
@@ -2275,6 +2277,10 @@ struct PassArgs {
     long long layer_ld;
     const int* len_dev;  // draft: the context length lives on the device (C unused), or null
     const int32_t* tree_parent;  // causal: the rows form a tree (parent of each row), or null (a chain)
+    int tree_off = 0;   // tree: node index of this pass's row 0 (a tree of more than 16 nodes takes two passes)
+    int tree_base = 0;  // tree: position (and cache slot) of the root, node 0
+    int tree_n = 0;     // tree: nodes in tree_parent
+    int layer_rows = 0; // rows per layer of layer_out (0: the pass's rows)
 };
 
 template <typename T>
@@ -2303,7 +2309,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
 
     int* tree_info = WS(int*, tree_info);
     hipLaunchKernelGGL((embed_kernel<T>), dim3(B), dim3(256), 0, s, (const T*)c.embed, pa.ids, pa.n_ids, d.mask_id, d.V,
-                       H, eps, x, rstd, best, ss0, ss_n, pa.tree_parent, tree_info);
+                       H, eps, x, rstd, best, ss0, ss_n, pa.tree_parent, pa.tree_off, pa.tree_n, tree_info);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     int kps, ns, nparts;
@@ -2354,6 +2360,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         qkv.len_dev = pa.len_dev;
         qkv.max_ctx = d.max_ctx;
         qkv.row_depth = pa.tree_parent ? tree_info : nullptr;
+        qkv.rot_base = pa.tree_base;
         qkv.tq = nq * D / 32;
         qkv.tk = nkv * D / 32;
         qkv.cosT = cosT;
@@ -2381,7 +2388,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         aa.group = group;
         aa.kps = kps;
         aa.n_splits = ns;
-        aa.causal_base = pa.causal ? C : -1;
+        aa.causal_base = pa.causal ? (pa.tree_parent ? pa.tree_base : C) : -1;
         aa.tree_anc = pa.tree_parent ? reinterpret_cast<const uint32_t*>(tree_info + 16) : nullptr;
         aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
         aa.part_o = WS(float*, attn_o);
@@ -2457,7 +2464,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
             for (int i = 0; i < 5; ++i)
                 if (sel[i] == l && pa.cap[i]) cap = (T*)pa.cap[i];  // layer l's output is a captured feature layer
         if (pa.layer_out) {
-            cap = (T*)pa.layer_out + (long long)l * B * pa.layer_ld;
+            cap = (T*)pa.layer_out + (long long)l * (pa.layer_rows ? pa.layer_rows : B) * pa.layer_ld;
             cap_ld = pa.layer_ld;
         }
         c.tracer->begin(DFLASH_TRACE_DOWN, s);
@@ -2513,8 +2520,10 @@ hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, flo
 
 hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, int M, float* logits, int32_t* argmax,
                                  void* const* capture, long long capture_ld, hipStream_t s,
-                                 const int32_t* tree_parent, void* layer_out, long long layer_ld) {
-    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, layer_out, layer_ld, nullptr, tree_parent};
+                                 const int32_t* tree_parent, void* layer_out, long long layer_ld, int tree_off,
+                                 int tree_base, int tree_n, int layer_rows) {
+    PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, layer_out, layer_ld, nullptr, tree_parent,
+                tree_off, tree_base, tree_n, layer_rows};
     c.tracer->begin(DFLASH_TRACE_TARGET, s);
     hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_TARGET, s);

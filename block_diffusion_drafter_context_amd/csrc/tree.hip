@@ -236,9 +236,7 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const float* part, int S
 
 // Candidate order as one 128-bit key (larger = better), compared branch-free:
 //   hi = valid (1 bit) | score mapped to an unsigned order (32 bits) | 31 - depth (5 bits)
-//   lo = ~rank path (4 bits per depth, depth 1 in the top bits) with the low
-//        4 bits replaced by 15 - lane (the path never uses them; they only
-//        separate invalid candidates and name the winner's lane).
+//   lo = ~rank path (4 bits per depth, depth 1 in the top bits).
 __device__ __forceinline__ unsigned order_bits(float f) {
     const unsigned u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal scores compare equal
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -252,7 +250,7 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, i
 
 // One wave.  Lane u < count holds node u: its score, depth, rank path and the
 // rank of its next unchosen child.  Every step the best of the lanes' next
-// children (a 16-lane butterfly over the keys above) joins the tree as node
+// children (a 32-lane butterfly over the keys above) joins the tree as node
 // `count`; a child never beats its parent or an earlier sibling, so the
 // chosen nodes are the budget best of the whole candidate tree.
 __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* anchor, int V, const int32_t* ids,
@@ -275,20 +273,23 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* anchor, i
         const float cs = sc + s_lp[ok ? dep * K + nr : 0];
         const int cd = min(dep + 1, 15);
         const unsigned long long cp = path | ((unsigned long long)(ok ? nr : 0) << (4 * (15 - min(dep, 14))));
-        unsigned long long hi = ok ? ((1ull << 37) | ((unsigned long long)order_bits(cs) << 5) | (unsigned)(31 - cd))
-                                   : 0ull;
-        unsigned long long lo = (~cp & ~15ull) | (unsigned)(15 - (lane & 15));
+        const unsigned long long hi0 =
+            ok ? ((1ull << 37) | ((unsigned long long)order_bits(cs) << 5) | (unsigned)(31 - cd)) : 0ull;
+        const unsigned long long lo0 = ~cp;
+        unsigned long long hi = hi0, lo = lo0;
 #pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
+        for (int o = 16; o >= 1; o >>= 1) {
             const unsigned long long h2 = shfl_xor64(hi, o), l2 = shfl_xor64(lo, o);
             const bool take = h2 > hi || (h2 == hi && l2 > lo);
             hi = take ? h2 : hi;
             lo = take ? l2 : lo;
         }
-        // lanes 0..15 now hold the winner
-        const int wl = 15 - (int)(lo & 15ull);
+        // lanes 0..31 now hold the winner; its lane is the one whose own key
+        // it is (the keys of real candidates differ in their rank paths)
+        const unsigned long long own = __ballot(ok && hi0 == hi && lo0 == lo);
+        const int wl = own ? __ffsll((long long)own) - 1 : 0;
         const int wd = 31 - (int)(hi & 31ull);
-        const unsigned long long wp = ~lo & ~15ull;
+        const unsigned long long wp = ~lo;
         const int rank = (int)((wp >> (4 * (16 - wd))) & 15ull);
         const float ws = __shfl(cs, wl, 64);  // the winner's own fp32 score (all lanes take part)
         if (lane == count) {
@@ -309,7 +310,9 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* anchor, i
 
 // One wave: lane j holds node j.  From the root, the child (lowest index
 // among equals) whose token is the target's greedy token after the current
-// node is accepted, until none is.  A parent outside [0, j) reads as the root.
+// node is accepted, until none is or 15 nodes are (a block's draft
+// positions; a tree from the builder is no deeper).  A parent outside
+// [0, j) reads as the root.
 __global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* tokens, const int32_t* parent,
                                                          const int32_t* target, int M, int32_t* out) {
     const int lane = threadIdx.x;
@@ -355,7 +358,7 @@ struct CommitArgs {
 template <typename T>
 __global__ __launch_bounds__(256) void tree_commit_kernel(CommitArgs a) {
     const int M = a.M;
-    const int k = min(max(a.result[0], 0), M - 1);
+    const int k = min(max(a.result[0], 0), min(M - 1, 15));  // an accepted path holds at most 15 nodes
     int src[15];
 #pragma unroll
     for (int i = 0; i < 15; ++i) src[i] = i < k ? min(max(a.result[2 + i], 1), M - 1) : 1;

@@ -22,10 +22,10 @@ ROWS = 16  # rows per target call: the largest block libdflash verifies at once
 class _Capture:
     """Device buffers for the five captured target layers of one call."""
 
-    def __init__(self, target: DFlash):
+    def __init__(self, target: DFlash, rows: int = ROWS):
         s = target.shape
         self.sel = feature_layers(s.target_layers)
-        self.slabs = [torch.empty(ROWS, s.hidden, dtype=target.dtype, device=target.device) for _ in range(5)]
+        self.slabs = [torch.empty(rows, s.hidden, dtype=target.dtype, device=target.device) for _ in range(5)]
         self.n_layers = s.target_layers
 
     def views(self, M: int):
@@ -139,10 +139,11 @@ def spec_tree_generate(target: DFlash, draft: DFlash, prompt: torch.Tensor, n_ne
     B = draft.shape.block
     dev = target.device
     first = prefill(target, prompt, draft)
-    cap = _Capture(target)
+    n_max = max(ROWS, budget + 1)  # a tree of more than 16 nodes is verified in two target passes
+    cap = _Capture(target, n_max)
     lg = torch.empty(B, draft.shape.vocab, dtype=torch.float32, device=dev)
     dtok = torch.empty(B, dtype=torch.int32, device=dev)
-    g = torch.empty(ROWS, dtype=torch.int32, device=dev)
+    g = torch.empty(n_max, dtype=torch.int32, device=dev)
     res = torch.empty(17, dtype=torch.int32, device=dev)
     fused = torch.empty(ROWS, draft.shape.hidden, dtype=draft.dtype, device=dev)
     anchor = first.clone()

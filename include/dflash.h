@@ -41,6 +41,7 @@ extern "C" {
 #define DFLASH_NUM_FEATURES 5
 #define DFLASH_MAX_BLOCK 16
 #define DFLASH_TREE_MAX_K 16   /* candidates per depth of a verification tree */
+#define DFLASH_TREE_MAX_NODES 32  /* nodes of a verification tree, root included */
 #define DFLASH_TREE_RESULT 17  /* int32 entries of a tree acceptance result */
 
 typedef enum {
@@ -284,8 +285,9 @@ dflash_status dflash_target_forward(dflash_ctx* ctx, const int32_t* tokens, int3
  *    as independent.  Scores are fp32 sums, one rounding per edge;
  *  - verification follows, from the root, the child whose token is the
  *    target's greedy token after the current node.
- * Trees have at most 16 nodes (the root and a budget of up to 15), one
- * verification pass of up to 16 rows.  Node order: parent[j] < j. */
+ * Trees have at most DFLASH_TREE_MAX_NODES = 32 nodes (the root and a budget
+ * of up to 31); up to 16 nodes are verified in one target pass, 17 to 32 in
+ * two.  Node order: parent[j] < j. */
 
 /* Per row r < rows of logits ([rows][ld] device fp32, ld >= V): the K largest
  * token ids (ties: lower id first) into ids_out (device int32 [rows][K]) and
@@ -301,7 +303,7 @@ dflash_status dflash_draft_topk(dflash_ctx* ctx, const float* logits, int64_t ld
  * (device, [depths][K] as written by dflash_draft_topk, entries of a row in
  * descending order).  tokens_out, parent_out: device int32[budget + 1]; node 0
  * is the root (parent -1), node j >= 1 has parent_out[j] < j.  1 <= depths <=
- * 15, 1 <= K <= 16, 0 <= budget <= 15 and no more than the candidate tree
+ * 15, 1 <= K <= 16, 0 <= budget <= 31 and no more than the candidate tree
  * holds (INVAL). */
 dflash_status dflash_build_tree(dflash_ctx* ctx, const int32_t* anchor, const int32_t* ids, const float* logp,
                                 int32_t depths, int32_t K, int32_t budget, int32_t* tokens_out,
@@ -313,9 +315,13 @@ dflash_status dflash_build_tree(dflash_ctx* ctx, const int32_t* anchor, const in
  * and it attends to the cache before C and to its ancestors and itself, so
  * it computes what a causal forward of its root path computes (up to
  * rounding order).  argmax_out[j] is the target's greedy token after node j.
- * Afterwards length = C + M; accept with dflash_tree_accept, move the
- * accepted rows with dflash_tree_commit, then dflash_rollback to C + 1 + k.
- * Same arguments, errors and capture rules as dflash_target_forward. */
+ * 1 <= M <= 32: nodes 0..15 run as one pass, nodes 16..M-1 as a second that
+ * finds its ancestors among the first pass's nodes in the cache (a chain of
+ * 32 nodes gives what two 16-row dflash_target_forward calls give, bit for
+ * bit).  Afterwards length = C + M; accept
+ * with dflash_tree_accept, move the accepted rows with dflash_tree_commit,
+ * then dflash_rollback to C + 1 + k.  Otherwise the arguments, errors and
+ * capture rules of dflash_target_forward. */
 dflash_status dflash_target_forward_tree(dflash_ctx* ctx, const int32_t* tokens, const int32_t* parent, int32_t M,
                                          float* logits_out, int32_t* argmax_out, void* const* capture,
                                          int64_t capture_ld, void* stream);
@@ -332,9 +338,10 @@ dflash_status dflash_target_forward_ex(dflash_ctx* ctx, const int32_t* tokens, c
 
 /* Greedy acceptance on a verified tree of M nodes (tokens, parent, target:
  * device int32[M]; target[j] = the target's greedy token after node j; a
- * parent outside [0, j) is read as 0).  From the root, while a child of the
- * current node carries target[current] (the lowest-index one if several),
- * move to it.  result_out: device int32[DFLASH_TREE_RESULT] = {k, bonus,
+ * parent outside [0, j) is read as 0; 1 <= M <= 32).  From the root, while a
+ * child of the current node carries target[current] (the lowest-index one if
+ * several) and fewer than 15 nodes are accepted (a block's draft positions; a
+ * tree from dflash_build_tree is no deeper), move to it.  result_out: device int32[DFLASH_TREE_RESULT] = {k, bonus,
  * path[0..14]}: k accepted nodes, the target's token after the last one, and
  * their node indices (path[i] has depth i + 1; unused entries 0).  The prefix
  * {k, bonus} has the layout of a dflash_verify_accept result. */
@@ -348,7 +355,8 @@ dflash_status dflash_tree_accept(dflash_ctx* ctx, const int32_t* tokens, const i
  * to row 1 + i.  Slots and rows then hold the root and the accepted nodes in
  * sequence order, which is what a causal forward of that sequence stores (the
  * nodes were rotated at their depths).  result: device, as written by
- * dflash_tree_accept (k is clamped to [0, M-1], path entries to [1, M-1]).
+ * dflash_tree_accept (k is clamped to [0, min(M-1, 15)], path entries to
+ * [1, M-1]); 1 <= M <= 32.
  * Requires pos0 >= 0 and pos0 + M <= length (INVAL); the length is not
  * changed. */
 dflash_status dflash_tree_commit(dflash_ctx* ctx, int32_t pos0, int32_t M, const int32_t* result,

@@ -300,7 +300,7 @@ def _assert_teacher_forced_greedy(toy, o, band):
     return mism
 
 
-@pytest.mark.parametrize("mode", ["ddtree", "branch"])
+@pytest.mark.parametrize("mode", ["ddtree", "branch", "ddtree22"])
 def test_toy_tree_spec_is_lossless(toy, mode):
     """Tree verification ([A] §8.2) keeps greedy output: every emitted token is
     the target's greedy token given the emitted prefix (teacher-forced in
@@ -308,8 +308,9 @@ def test_toy_tree_spec_is_lossless(toy, mode):
     near-ties inside the bf16 logit band, where the tree pass and the chain
     pass may order two logits differently (their attention sums run in a
     different order).  'ddtree': trees built from the draft's top-4 per
-    position (budget 15); 'branch': a wrong 5-node chain first and the right
-    10-node chain second, so acceptance has to take the second branch."""
+    position (budget 15); 'ddtree22': budget 22 (two target passes per
+    step); 'branch': a wrong 5-node chain first and the right 10-node chain
+    second, so acceptance has to take the second branch."""
     P, V, n_new = toy["prompt"].shape[0], TOY.vocab, toy["n_new"]
     greedy = toy["greedy"]
 
@@ -323,7 +324,8 @@ def test_toy_tree_spec_is_lossless(toy, mode):
         return nodes, parents
 
     tgt, drf = toy["fresh"]()
-    out, ks = toy["spec"].spec_tree_generate(tgt, drf, toy["prompt"], n_new, K=4, budget=15,
+    out, ks = toy["spec"].spec_tree_generate(tgt, drf, toy["prompt"], n_new, K=4,
+                                             budget=22 if mode == "ddtree22" else 15,
                                              trees_fn=branch if mode == "branch" else None)
     print(f"[toy tree {mode}] steps {len(ks)} mean k {np.mean(ks):.3f}", flush=True)
     o = np.asarray(out)

@@ -91,7 +91,8 @@ def _tree_inputs(R, K, V, ties):
 
 @pytest.mark.parametrize("R,K,budget,ties", [(15, 4, 15, False), (15, 16, 15, True), (15, 1, 15, False),
                                              (3, 2, 6, True), (2, 3, 0, False), (15, 8, 9, True),
-                                             (5, 2, 15, False)])
+                                             (5, 2, 15, False), (15, 4, 22, False), (15, 16, 31, True),
+                                             (4, 2, 30, False)])
 def test_build_tree_matches_oracle(dl, R, K, budget, ties):
     V = 4000
     ctx = _vocab_ctx(dl, V)
@@ -129,13 +130,16 @@ def test_tree_accept_matches_oracle(dl):
     ctx = _vocab_ctx(dl, 1008)
     rng = np.random.default_rng(12)
     cases, outs = [], []
-    for t in range(300):
-        n = int(rng.integers(1, 17))
+    for t in range(304):
+        n = int(rng.integers(1, 17 if t % 2 else 33))       # trees of up to 32 nodes
         par = di.random_tree(n, t, "gacc").copy()
         tok = rng.integers(0, 3, n).astype(np.int32)        # duplicate siblings happen
         g = rng.integers(0, 3, n).astype(np.int32)
         if t % 10 == 0 and n > 2:                           # out-of-range parents read as the root
             par[n - 1] = n + 3 if t % 20 == 0 else -7
+        if t >= 300:                                        # chains of 15..32 nodes that match all the way
+            n = (15, 16, 17, 32)[t - 300]
+            par, tok, g = di.chain_tree(n), np.full(n, 2, np.int32), np.full(n, 2, np.int32)
         d = [torch.from_numpy(a).cuda() for a in (tok, par, g)]
         outs.append(ctx.tree_accept(*d))
         cases.append((tok, par, g))
@@ -143,6 +147,9 @@ def test_tree_accept_matches_oracle(dl):
     for (tok, par, g), o in zip(cases, outs):
         clean = np.array([-1] + [p if 0 <= p < j else 0 for j, p in enumerate(par) if j > 0], dtype=np.int32)
         k, bonus, path = ddtree.tree_accept(tok, clean, g)
+        if k > 15:                                          # acceptance stops after 15 nodes
+            k, path = 15, path[:15]
+            bonus = int(g[path[-1]])
         got = o.cpu().numpy().tolist()
         assert got[:2] == [k, bonus] and got[2:2 + k] == path and all(v == 0 for v in got[2 + k:])
 
@@ -174,7 +181,8 @@ def _oracle_tree(orc, m, s, k, v, C, n, tok, par, sel, fp32_acc=False):
 
 
 @pytest.mark.parametrize("shape", [TR_BF16, TR_BF16_D64, TR_FP32_G5])
-@pytest.mark.parametrize("C,n", [(0, 16), (37, 16), (180, 16), (250, 9), (300, 1), (380, 12), (511, 16)])
+@pytest.mark.parametrize("C,n", [(0, 16), (37, 16), (180, 16), (250, 9), (300, 1), (380, 12), (511, 16),
+                                 (0, 23), (250, 32), (380, 17)])
 def test_tree_forward_matches_oracle(dl, orc, shape, C, n):
     """At the stated bar, one layer at a time: every layer of the tree pass
     against the oracle's tree-masked layer on the GPU's own input to it (2 bf16
@@ -186,7 +194,8 @@ def test_tree_forward_matches_oracle(dl, orc, shape, C, n):
     compounding over 8 layers needs; the plain causal forward shows the same
     end-to-end deviation on these inputs).  C = 180 / 380 put the tree's slots
     across a 192-key split boundary (keys 192 and 384) and 511 at the end of a
-    64-key chunk."""
+    64-key chunk.  Trees of 17 to 32 nodes take two passes (nodes 16 and on see
+    their ancestors among the first pass's nodes in the cache)."""
     s = shape
     w = di.toy_target_weights(s)
     ctx, k, v = _target(dl, s, w, C, page_seed=9)
@@ -233,19 +242,27 @@ def test_tree_forward_matches_oracle(dl, orc, shape, C, n):
 
 
 @pytest.mark.parametrize("shape", [TR_BF16, TR_FP32_G5])
-@pytest.mark.parametrize("C", [0, 200, 250])
-def test_chain_tree_is_the_causal_forward(dl, shape, C):
+@pytest.mark.parametrize("C,n", [(0, 16), (200, 16), (250, 16), (0, 32), (250, 32)])
+def test_chain_tree_is_the_causal_forward(dl, shape, C, n):
     """A tree that is a chain runs the same arithmetic as the causal forward:
-    logits, tokens, captures and KV bit-identical."""
+    logits, tokens, captures and KV bit-identical.  32 nodes: one two-pass tree
+    call against two 16-row causal calls."""
     s = shape
     ctx, _, _ = _target(dl, s, di.toy_target_weights(s), C, page_seed=3)
-    tok = torch.from_numpy(di.uniform_int(16, 0, s.vocab - 1, s.seed, "chain").numpy()).cuda()
+    tok = torch.from_numpy(di.uniform_int(n, 0, s.vocab - 1, s.seed, "chain").numpy()).cuda()
     outs = []
-    for parent in (None, torch.from_numpy(di.chain_tree(16)).cuda()):
+    for parent in (None, torch.from_numpy(di.chain_tree(n)).cuda()):
         ctx.rollback(C)
-        cap = [torch.empty(16, s.hidden, dtype=s.torch_dtype, device="cuda") for _ in range(5)]
-        am, lg = ctx.target_forward(tok, want_logits=True, capture=cap, parent=parent)
-        k, v = ctx.read_kv(C, 16)
+        cap = [torch.empty(n, s.hidden, dtype=s.torch_dtype, device="cuda") for _ in range(5)]
+        am = torch.empty(n, dtype=torch.int32, device="cuda")
+        lg = torch.empty(n, s.vocab, dtype=torch.float32, device="cuda")
+        if parent is None:
+            for r0 in range(0, n, 16):
+                ctx.target_forward(tok[r0:r0 + 16], argmax=am[r0:r0 + 16], logits=lg[r0:r0 + 16],
+                                   capture=[c[r0:r0 + 16] for c in cap])
+        else:
+            ctx.target_forward(tok, argmax=am, logits=lg, capture=cap, parent=parent)
+        k, v = ctx.read_kv(C, n)
         sync()
         outs.append([am.cpu(), lg.cpu(), k.cpu(), v.cpu()] + [c.cpu() for c in cap])
     for a, b in zip(*outs):
@@ -255,9 +272,10 @@ def test_chain_tree_is_the_causal_forward(dl, shape, C):
 # ------------------------------------------------------------------ compaction
 
 @pytest.mark.parametrize("shape", [TR_BF16, TR_FP32_G5])
-def test_tree_commit_moves_accepted_rows(dl, orc, shape):
+@pytest.mark.parametrize("n", [16, 32])
+def test_tree_commit_moves_accepted_rows(dl, orc, shape, n):
     s = shape
-    C, n = 120, 16
+    C = 120
     ctx, _, _ = _target(dl, s, di.toy_target_weights(s), C, page_seed=5)
     x = di.normal((15, s.vocab), 63, "commit", 2.0, torch.float32)
     ids, lp = ddtree.topk_logprobs(x.numpy(), 3)
@@ -295,7 +313,7 @@ def test_tree_errors(dl):
     z = torch.zeros(17, 17, dtype=torch.int32, device="cuda")
     f = torch.zeros(17, 17, dtype=torch.float32, device="cuda")
     a = torch.zeros(1, dtype=torch.int32, device="cuda")
-    for R, K, budget in ((3, 1, 4), (15, 17, 3), (16, 2, 3), (15, 2, 16), (2, 2, -1)):
+    for R, K, budget in ((3, 1, 4), (15, 17, 3), (16, 2, 3), (15, 2, 32), (2, 2, -1)):
         with pytest.raises(dl.DFlashError):
             ctx.build_tree(a, z[:R, :K], f[:R, :K], budget)
     lg = torch.zeros(17, 1008, dtype=torch.float32, device="cuda")
@@ -306,4 +324,7 @@ def test_tree_errors(dl):
     res = torch.zeros(17, dtype=torch.int32, device="cuda")
     with pytest.raises(dl.DFlashError):
         ctx.tree_commit(0, 4, res)                  # rows beyond the length
+    t33 = torch.zeros(33, dtype=torch.int32, device="cuda")
+    with pytest.raises(dl.DFlashError):
+        ctx.tree_accept(t33, t33, t33)              # more than 32 nodes
     sync()
