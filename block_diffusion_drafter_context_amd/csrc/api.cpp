@@ -203,8 +203,8 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, v
                           hipSuccess) ||
         (e = hipMemsetAsync(x.ws + L.tile_cnt, 0, (size_t)L.max_tiles * 4, s)) != hipSuccess ||
         (e = hipMemsetAsync(x.ws + L.counters, 0, 64 * 4, s)) != hipSuccess ||
-        (e = hipMemsetAsync(x.ws + L.best, 0, 16 * 8, s)) != hipSuccess ||
-        (e = hipMemsetAsync(x.ws + L.ss_part, 0, (size_t)L.ss_stride * 16 * 4 * 2, s)) != hipSuccess ||
+        (e = hipMemsetAsync(x.ws + L.best, 0, (size_t)kPassRowsMax * 8, s)) != hipSuccess ||
+        (e = hipMemsetAsync(x.ws + L.ss_part, 0, (size_t)L.ss_stride * kPassRowsMax * 4 * 2, s)) != hipSuccess ||
         (e = hipStreamSynchronize(s)) != hipSuccess) {
         delete c;
         return DFLASH_ERR_HIP;
@@ -432,11 +432,14 @@ dflash_status target_forward(dflash_ctx* c, const int32_t* tokens, const int32_t
     dflash_status st = check_device(c);
     if (st != DFLASH_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // a tree of more than 16 nodes: two passes, nodes 0..15 then 16..M-1, the
-    // second seeing its ancestors among the first pass's nodes in the cache
+    // a tree of more than 16 nodes: one pass of up to 32 rows where the
+    // kernels allow it (each weight is read once for all rows), else two
+    // passes, nodes 0..15 then 16..M-1, the second seeing its ancestors among
+    // the first pass's nodes in the cache
     const int C0 = c->length;
-    for (int off = 0; off < M; off += DFLASH_MAX_BLOCK) {
-        const int m = std::min(M - off, (int)DFLASH_MAX_BLOCK);
+    const int per_pass = parent && wide_pass_supported(x) ? DFLASH_TREE_MAX_NODES : DFLASH_MAX_BLOCK;
+    for (int off = 0; off < M; off += per_pass) {
+        const int m = std::min(M - off, per_pass);
         void* cap_off[DFLASH_NUM_FEATURES];
         if (capture)
             for (int i = 0; i < DFLASH_NUM_FEATURES; ++i)

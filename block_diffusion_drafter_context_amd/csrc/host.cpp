@@ -82,17 +82,19 @@ Layout compute_layout(const Dims& d, int num_cus) {
     L.rope_cos = take((size_t)L.n_rope_pos * (d.d / 2) * 4);
     L.rope_sin = take((size_t)L.n_rope_pos * (d.d / 2) * 4);
     L.page_table = take((size_t)std::max(d.n_pages, 1) * 4);
-    L.x = take((size_t)16 * d.H * es);
-    L.q = take((size_t)16 * d.nq * d.d * es);
+    // rows of a pass: a 16-row block, or up to 32 verified tree nodes
+    const size_t R = kPassRowsMax;
+    L.x = take(R * d.H * es);
+    L.q = take(R * d.nq * d.d * es);
     L.kblk = take((size_t)16 * d.nkv * d.d * es);
     L.vblkT = take((size_t)16 * d.nkv * d.d * es);
-    L.obuf = take((size_t)16 * d.nq * d.d * es);
-    L.hbuf = take((size_t)16 * d.F * es);
-    L.rstd = take(16 * 4);
+    L.obuf = take(R * d.nq * d.d * es);
+    L.hbuf = take(R * d.F * es);
+    L.rstd = take(R * 4);
     const int blk = 16 * kSkinnyNT;
     L.max_ss_tiles = (d.H + blk - 1) / blk;
     L.ss_stride = (L.max_ss_tiles + 15) / 16 * 16;
-    L.ss_part = take((size_t)L.ss_stride * 16 * 4 * 2);  // two buffers (see the draft pass)
+    L.ss_part = take((size_t)L.ss_stride * R * 4 * 2);  // two buffers (see the draft pass)
     // 4 waves per CU: measured best for every skinny-GEMM shape of the draft
     // pass (fewer concurrent weight streams keep DRAM pages open longer)
     L.nwaves = std::max(num_cus, 1) * 4;
@@ -108,12 +110,12 @@ Layout compute_layout(const Dims& d, int num_cus) {
     L.max_tiles = (int)t;
     L.tile_cnt = take((size_t)L.max_tiles * 4);
     L.counters = take(64 * 4);
-    L.best = take(16 * 8);
-    const size_t parts = (size_t)(kMaxSplits + 1) * d.nq * 16;
+    L.best = take(R * 8);
+    const size_t parts = (size_t)(kMaxSplits + 1) * d.nq * R;
     L.attn_o = take(parts * d.d * 4);
     L.attn_ml = take(parts * 2 * 4);
     L.len_dev = take(2 * 4);
-    L.tree_info = take(32 * 4);
+    L.tree_info = take(2 * R * 4);
     L.topk_part = take((size_t)16 * kTopKSegs * (2 * kTopKMax + 2) * 4);
     L.sample_draw = take(64 + (size_t)((d.V + 1023) / 1024) * 8);
     const int e = d.elem;

@@ -26,6 +26,7 @@ constexpr int kMaxSplitPages = 1040;     // KV pages one attention split may tou
 constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
 constexpr int kTopKMax = 16;             // candidates per draft position of a tree (the largest useful K)
 constexpr int kTopKSegs = 64;            // vocabulary segments of the top-K partial pass (one merge lane each)
+constexpr int kPassRowsMax = 32;         // rows of one decoder pass: a 16-row block, or a verified tree of up to 32 nodes
 
 struct Dims {
     int dtype, H, Lt, Ld, nq, nkv, d, F, V, B, mask_id, page, max_ctx, max_rows, n_pages, elem;
@@ -54,7 +55,7 @@ struct Layout {
     size_t rstd, ss_part, partial, tile_cnt, counters, best;
     size_t attn_o, attn_ml;
     size_t len_dev;       // device-resident length: {length, capacity-error flag}
-    size_t tree_info;     // tree verification: per row {depth[16], ancestor mask[16]}
+    size_t tree_info;     // tree verification: depth[32], then ancestor mask[32]
     size_t topk_part;     // top-K / sampling partials: [16 rows][kTopKSegs] x (K values, K ids, max, sum)
     size_t sample_draw;   // sampled verification: a 64-byte header, then one fp64 weight sum per 1024 ids
     size_t total;
@@ -63,7 +64,7 @@ struct Layout {
     int nwaves;           // skinny-GEMM waves per launch
     int max_tiles;        // largest tile count of any skinny GEMM
     int max_ss_tiles;     // tiles of an N = H skinny GEMM (row sum-of-squares partials)
-    int ss_stride;        // row stride of the partials ([16 rows][ss_stride], zero past the tiles)
+    int ss_stride;        // row stride of the partials ([32 rows][ss_stride], zero past the tiles)
     int n_rope_pos;       // positions covered by the rotary table
 };
 

@@ -71,7 +71,8 @@ hipError_t launch_read_probe(const void* buf, long long bytes, int num_cus, unsi
 hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, float* logits,
                               int32_t* tokens, void* layer_out, long long layer_ld, const int* len_dev,
                               hipStream_t s);
-// Causal forward of M <= 16 tokens at positions C..C+M-1 (K/V appended to the cache).
+// Causal forward of M <= 16 tokens at positions C..C+M-1 (K/V appended to the cache),
+// or of a tree's 17..32 nodes in one pass when wide_pass_supported(c).
 // tree_parent (device int32[tree_n], or null): the rows are nodes tree_off ..
 // tree_off + M - 1 of a tree of tree_n <= 32 nodes whose root (node 0) sits at
 // tree_base; node u is placed at tree_base + depth(u) and sees the cache before
@@ -84,6 +85,10 @@ hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, 
                                  const int32_t* tree_parent = nullptr, void* layer_out = nullptr,
                                  long long layer_ld = 0, int tree_off = 0, int tree_base = 0, int tree_n = 0,
                                  int layer_rows = 0);
+// Whether a causal pass can take up to 32 rows at once (bf16, and every
+// projection on the workgroup-local kernel); otherwise a tree of more than 16
+// nodes is verified in passes of 16.
+bool wide_pass_supported(const DevCtx& c);
 // Tree verification helpers (tree.hip).
 // Per row r < rows of logits [rows][ld]: the K <= 16 largest ids (ties: lower
 // id first) and their fp32 log-probabilities.

@@ -72,7 +72,7 @@ constexpr int kSSPerLane = 40;  // row-statistics partials one lane sums (H <= 4
 
 // u = round(x * rstd[row] * gain[k])  (RMSNorm applied on load).  rstd comes
 // either from rstd[] or, when ss is set, from the per-32-column-tile row sums
-// of squares the producing GEMM wrote ([16 rows][ss_stride], zero past the
+// of squares the producing GEMM wrote ([rows][ss_stride], zero past the
 // last tile): lane (row j, group g) sums the g-th quarter of row j's tiles in
 // order (16-byte loads), then the four quarters are added (a fixed order).
 template <typename T>
@@ -95,8 +95,9 @@ struct NormA {
     };
     // tiles per quarter, a multiple of 4 (so 4 * quarter <= ss_stride)
     __device__ __forceinline__ int quarter() const { return ((ss_tiles + 3) / 4 + 3) / 4 * 4; }
-    __device__ __forceinline__ void pre_issue(Pre& p, int lane) const {
-        const int j = lane & 15, g = lane >> 4;
+    // r0: the first row of the lane's 16-row tile (a 32-row pass has two)
+    __device__ __forceinline__ void pre_issue(Pre& p, int lane, int r0 = 0) const {
+        const int j = r0 + (lane & 15), g = lane >> 4;
         if (!ss) {
             p.v[0] = rstd[j];
             return;
@@ -138,7 +139,7 @@ struct NormA {
 
 struct NoPre {
     struct Pre {};
-    __device__ __forceinline__ void pre_issue(Pre&, int) const {}
+    __device__ __forceinline__ void pre_issue(Pre&, int, int = 0) const {}
     __device__ __forceinline__ float pre_finish(const Pre&, int) const { return 0.f; }
 };
 
@@ -512,20 +513,186 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_kernel(Op op, WGCommo
     op.wave_end(st, lane);
 }
 
+// The same kernel for RT = Op::kRT > 1 row tiles of 16 (a pass of up to 32
+// rows): every weight fragment feeds one MFMA per row tile, so the weights are
+// read once for all rows.  Kept apart from the 16-row kernel above, whose
+// instruction schedule the draft pass is tuned on.
+template <typename T, class Op, int W, int MINWG, int KP, int DEPTH>
+__global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_rows_kernel(Op op, WGCommon c) {
+    constexpr int NT = Op::kNT;  // 16-column blocks per tile
+    constexpr int RT = Op::kRT;  // 16-row tiles of A (two for a 32-row pass): each weight fragment feeds RT MFMAs
+    extern __shared__ f32x4_t wg_red[];  // [tile][wave][row tile][block][lane]: one 16-byte access per lane
+    using AL = decltype(op.a);
+    using Raw = typename AL::Raw;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row = lane & 15, grp = lane >> 4;
+    bool row_ok[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) row_ok[r] = 16 * r + row < c.M;
+    typename AL::Pre pr[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) op.a.pre_issue(pr[r], lane, 16 * r);
+    typename Op::State st;
+    op.wave_begin(st);
+
+    const int t0 = blockIdx.x * c.tpw;
+    const int nt = min(c.tpw, c.ntiles - t0);
+    const int ch0 = wv * c.cpw;
+    const int ch1 = min(ch0 + c.cpw, c.nchunks);
+    const int chl = (ch1 > ch0 ? ch1 : c.nchunks) - 1;  // last chunk a load touches (a wave past K re-reads it, masked)
+    const int gpt = c.cpw / KP;                          // load groups per tile
+    const int total = nt * gpt;
+    int arow[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) arow[r] = row_ok[r] ? 16 * r + row : 0;
+    const int klast = c.K - 8;  // last valid 8-element group of an activation row
+
+    struct Group {
+        Frag<T> w[NT][KP];
+        Raw a[RT][KP];
+    };
+    f32x4_t acc[RT * NT];  // [row tile][block]
+#pragma unroll
+    for (int b = 0; b < RT * NT; ++b) acc[b] = zero4();
+
+    auto load_group = [&](int n, Group& g) {
+        const int ti = n / gpt;
+        const int tile = t0 + ti;
+        const int cb = ch0 + (n - ti * gpt) * KP;
+        const T* ws[NT];
+#pragma unroll
+        for (int b = 0; b < NT; ++b) {
+            const T* q = op.b_rows(tile, b, c.nchunks);
+            ws[b] = q ? q : op.b_rows(tile, 0, c.nchunks);  // blocks past N re-read block 0 (never stored)
+        }
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            const int ch = min(cb + p, chl);
+            const int k = min(ch * 32 + grp * 8, klast);
+#pragma unroll
+            for (int b = 0; b < NT; ++b) g.w[b][p].load_sw(ws[b] + (long long)ch * 512, lane);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) op.a.load(g.a[r][p], arow[r], k);
+        }
+    };
+    float pre[RT];
+    auto compute = [&](int n, const Group& g) {
+        const int ti = n / gpt;
+        const int cb = ch0 + (n - ti * gpt) * KP;
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                Frag<T> a;
+                op.a.finish(a, g.a[r][p], pre[r]);
+                const bool ok = row_ok[r] && (cb + p < ch1) && ((cb + p) * 32 + grp * 8 < c.K);
+                a.mask(ok ? 0xFFFFFFFFu : 0u);
+#pragma unroll
+                for (int b = 0; b < NT; ++b) mma(acc[r * NT + b], a, g.w[b][p]);
+            }
+        }
+        mfma_settle();
+        if (n - ti * gpt == gpt - 1) {  // the tile's last group
+            if constexpr (Op::kInLoop) {
+                // all waves finish the tile together, wave wv taking rows
+                // 16 r + 4 g + wv: partials in a double buffer, summed in wave order
+                const int buf = ti & 1;
+#pragma unroll
+                for (int b = 0; b < RT * NT; ++b) {
+                    wg_red[((buf * W + wv) * RT * NT + b) * 64 + lane] = acc[b];
+                    acc[b] = zero4();
+                }
+                stage_barrier();
+                const float* red = reinterpret_cast<const float*>(wg_red);
+                float v[RT * NT];
+#pragma unroll
+                for (int b = 0; b < RT * NT; ++b) {
+                    v[b] = 0.f;
+#pragma unroll
+                    for (int q = 0; q < W; ++q) v[b] += red[(((buf * W + q) * RT * NT + b) * 64 + lane) * 4 + wv];
+                }
+                op.finish_rows(t0 + ti, v, lane, wv, st);
+            } else {  // park the partial (LDS only) for the epilogue after the stream
+#pragma unroll
+                for (int b = 0; b < RT * NT; ++b) {
+                    wg_red[((ti * W + wv) * RT * NT + b) * 64 + lane] = acc[b];
+                    acc[b] = zero4();
+                }
+            }
+        }
+    };
+
+    // DEPTH groups in flight: group n lives in ring slot n % DEPTH
+    Group g[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_group(min(d, total - 1), g[d]);
+    __builtin_amdgcn_sched_barrier(0);
+    // epilogue inputs of the wave's first tile (it finishes tiles wv, wv + W,
+    // ...), issued behind the first weight groups: loads complete in issue
+    // order for the wait counter, so issued ahead they would delay the first
+    // group (measured: QKV's first group 5.1 -> 4.2 us with its rotary loads)
+    if (wv < nt) op.prefetch(t0 + wv, lane, st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) pre[r] = op.a.pre_finish(pr[r], lane);  // its loads went out before any weight load
+    int n = 0;
+    for (; n + 2 * DEPTH - 1 < total; n += DEPTH) {  // every group loaded here exists
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            compute(n + d, g[d]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_group(n + d + DEPTH, g[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the last DEPTH .. 2 DEPTH - 1 groups (groups n .. n + DEPTH - 1 already loaded)
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        if (n + d < total) compute(n + d, g[d]);
+        if (n + d + DEPTH < total) load_group(n + d + DEPTH, g[d]);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (n + DEPTH + d < total) compute(n + DEPTH + d, g[d]);
+
+    if (c.clear)
+        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < c.clear_n; i += gridDim.x * blockDim.x) c.clear[i] = 0.f;
+    if constexpr (!Op::kInLoop) {
+        __syncthreads();
+        for (int i = wv; i < nt; i += W) {
+            if (i != wv) op.prefetch(t0 + i, lane, st);  // a later tile's inputs (more than W tiles per workgroup)
+            f32x4_t sum[RT * NT];
+    #pragma unroll
+            for (int b = 0; b < RT * NT; ++b) sum[b] = zero4();
+            for (int q = 0; q < W; ++q)
+    #pragma unroll
+                for (int b = 0; b < RT * NT; ++b) {
+                    const f32x4_t v = wg_red[((i * W + q) * RT * NT + b) * 64 + lane];
+    #pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) sum[b][ii] += v[ii];
+                }
+            op.epilogue(t0 + i, sum, lane, st);
+        }
+    }
+    op.wave_end(st, lane);
+}
+
 // Ops ------------------------------------------------------------------------
 
 
 
 // q, k (rotated) and v of the block rows.  Tiles pair the 16-column blocks
-// (16i, 16i + d/2) of one head so each rotary pair sits in one lane.
-template <typename T>
+// (16i, 16i + d/2) of one head so each rotary pair sits in one lane.  RT: 16-row
+// tiles of the pass (2: up to 32 rows, workgroup-local kernel only).
+template <typename T, int RT = 1>
 struct OpQKV {
     static constexpr int kNT = 2;  // 16-column blocks per tile
+    static constexpr int kRT = RT;
     static constexpr bool kInLoop = false;
     static constexpr int kWGDepth = 2;  // load groups in flight
     struct State {
-        float cs[4], sn[4];  // rotary cos/sin of the lane's rows, loaded ahead of the exchange
-        int pos0;            // position of row 0
+        float cs[RT][4], sn[RT][4];  // rotary cos/sin of the lane's rows, loaded ahead of the exchange
+        int pos0;                    // position of row 0
     };
     static constexpr bool kDoneHook = false;
     NormA<T> a;
@@ -541,7 +708,7 @@ struct OpQKV {
     const float* cosT;
     const float* sinT;
     T* qout;
-    T* kout;      // block keys [16][nkv*d], or null: keys go to the cache
+    T* kout;      // block keys [16][nkv*d], or null: keys go to the cache (always for RT = 2)
     T* vTout;     // block values [nkv][d][16], or null: values go to the cache
     KVPages kv;   // cache pages of `layer` (used when kout is null)
     int layer;
@@ -567,13 +734,15 @@ struct OpQKV {
         decode(tile, kind, h, i);
         const int dim = 16 * i + (lane & 15), half = d / 2;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int j = min(4 * (lane >> 4) + ii, M - 1);
-            // a tree row's KV slot stays pos0 + j; it is rotated for its depth below the root
-            const long long t = (long long)(row_depth ? rot_base + row_depth[j] : st.pos0 + j) * half + dim;
-            st.cs[ii] = cosT[t];
-            st.sn[ii] = sinT[t];
-        }
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int j = min(16 * r + 4 * (lane >> 4) + ii, M - 1);
+                // a tree row's KV slot stays pos0 + j; it is rotated for its depth below the root
+                const long long t = (long long)(row_depth ? rot_base + row_depth[j] : st.pos0 + j) * half + dim;
+                st.cs[r][ii] = cosT[t];
+                st.sn[r][ii] = sinT[t];
+            }
     }
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
@@ -582,12 +751,13 @@ struct OpQKV {
         decode(tile, kind, h, i);
         const int dim = 16 * i + (lane & 15), half = d / 2;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int j = 4 * (lane >> 4) + ii;
+        for (int q = 0; q < 4 * RT; ++q) {
+            const int r = q >> 2, ii = q & 3;
+            const int j = 16 * r + 4 * (lane >> 4) + ii;
             if (j >= M) continue;
-            float x0 = acc[0][ii], x1 = acc[1][ii];
+            float x0 = acc[2 * r][ii], x1 = acc[2 * r + 1][ii];
             if (kind != 2) {
-                const float cs = st.cs[ii], sn = st.sn[ii];
+                const float cs = st.cs[r][ii], sn = st.sn[r][ii];
                 const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
                 x0 = r0;
                 x1 = r1;
@@ -626,20 +796,22 @@ struct OpQKV {
 // can turn them into rstd (fixed summation order); with 16-column tiles the two
 // tiles of a 32-column slot add their sums into the slot, cleared beforehand
 // (two addends in either order give the same fp32 sum).
-template <typename T, int NT_ = 2>
+template <typename T, int NT_ = 2, int RT = 1>
 struct OpResid {
     static constexpr int kNT = NT_;  // 16-column blocks per tile
+    static constexpr int kRT = RT;   // 16-row tiles (2: workgroup-local kernel only)
     static constexpr bool kInLoop = false;
     static constexpr int kWGDepth = 2;  // load groups in flight (a third measured no faster)
     struct State {
-        float xv[NT_][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
+        float xv[RT][NT_][4];  // the residual values of the current tile, loaded ahead of the partial-sum exchange
     };
     static constexpr bool kDoneHook = NT_ == 2;
+    static_assert(RT == 1 || NT_ == 1, "32-row passes use 16-column tiles");
     PlainA<T> a;
     const T* w;
     int N, K, M;
     T* x;
-    float* ss_part;          // [16 rows][ss_stride] per-32-column row sums of squares
+    float* ss_part;          // [rows][ss_stride] per-32-column row sums of squares
     int ss_stride;
     float* rstd_out;
     float eps;
@@ -653,39 +825,44 @@ struct OpResid {
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void prefetch(int tile, int lane, State& st) const {
 #pragma unroll
-        for (int b = 0; b < NT_; ++b) {
-            const int n = min(16 * NT_ * tile + 16 * b + (lane & 15), N - 1);
+        for (int r = 0; r < RT; ++r)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int j = min(4 * (lane >> 4) + ii, M - 1);
-                st.xv[b][ii] = Elem<T>::to_f32(x[(long long)j * N + n]);
+            for (int b = 0; b < NT_; ++b) {
+                const int n = min(16 * NT_ * tile + 16 * b + (lane & 15), N - 1);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int j = min(16 * r + 4 * (lane >> 4) + ii, M - 1);
+                    st.xv[r][b][ii] = Elem<T>::to_f32(x[(long long)j * N + n]);
+                }
             }
-        }
     }
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State& st) const {
-        float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < NT_; ++b) {
-            const int n = 16 * NT_ * tile + 16 * b + (lane & 15);
-            if (n >= N) continue;
+        for (int r = 0; r < RT; ++r) {
+            float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < NT_; ++b) {
+                const int n = 16 * NT_ * tile + 16 * b + (lane & 15);
+                if (n >= N) continue;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int j = 16 * r + 4 * (lane >> 4) + ii;
+                    if (j >= M) continue;
+                    T* p = x + (long long)j * N + n;
+                    const float xn = Elem<T>::round(st.xv[r][b][ii] + Elem<T>::round(acc[r * NT_ + b][ii]));
+                    *p = Elem<T>::from_f32(xn);
+                    if (cap) cap[(long long)j * cap_ld + n] = Elem<T>::from_f32(xn);
+                    sq[ii] += xn * xn;
+                }
+            }
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const int j = 4 * (lane >> 4) + ii;
-                if (j >= M) continue;
-                T* p = x + (long long)j * N + n;
-                const float xn = Elem<T>::round(st.xv[b][ii] + Elem<T>::round(acc[b][ii]));
-                *p = Elem<T>::from_f32(xn);
-                if (cap) cap[(long long)j * cap_ld + n] = Elem<T>::from_f32(xn);
-                sq[ii] += xn * xn;
-            }
-        }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const float s = group16_sum(sq[ii]);
-            float* slot = ss_part + (long long)(4 * (lane >> 4) + ii) * ss_stride + (NT_ == 2 ? tile : tile >> 1);
-            if ((lane & 15) == 0) {
-                if constexpr (NT_ == 2) st_agent(slot, s);
-                else __hip_atomic_fetch_add(slot, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const float s = group16_sum(sq[ii]);
+                float* slot = ss_part + (long long)(16 * r + 4 * (lane >> 4) + ii) * ss_stride + (NT_ == 2 ? tile : tile >> 1);
+                if ((lane & 15) == 0) {
+                    if constexpr (NT_ == 2) st_agent(slot, s);
+                    else __hip_atomic_fetch_add(slot, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
     }
@@ -712,9 +889,10 @@ struct OpResid {
 };
 
 // h = round(silu(u . Wg^T) * (u . Wu^T)); tile t pairs column block t of Wg and Wu.
-template <typename T>
+template <typename T, int RT = 1>
 struct OpSwiGLU {
     static constexpr int kNT = 2;  // 16-column blocks per tile
+    static constexpr int kRT = RT;  // 16-row tiles (2: workgroup-local kernel only)
     static constexpr bool kInLoop = false;
     static constexpr int kWGDepth = 2;  // load groups in flight (a third measured no faster)
     using State = NoState;
@@ -734,10 +912,11 @@ struct OpSwiGLU {
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
         const int n = 16 * tile + (lane & 15);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int j = 4 * (lane >> 4) + ii;
+        for (int q = 0; q < 4 * RT; ++q) {
+            const int r = q >> 2, ii = q & 3;
+            const int j = 16 * r + 4 * (lane >> 4) + ii;
             if (j >= M) continue;
-            const float g = acc[0][ii], u = acc[1][ii];
+            const float g = acc[2 * r][ii], u = acc[2 * r + 1][ii];
             const float sg = g / (1.0f + __expf(-g));
             h[(long long)j * F + n] = Elem<T>::from_f32(sg * u);
         }
@@ -850,29 +1029,30 @@ struct OpLMHead {
 };
 
 // LM head with a fused argmax on the workgroup-local kernel: 32-column tiles,
-// finished inside the stream by all four waves (wave wv owns rows 4 g + wv of
-// every tile, so each of the 16 rows has one owner per workgroup).  The fp32
-// logits go out through a range-checked buffer store that drops rows >= M,
-// columns >= V and everything when no logits buffer is given, so the stream's
-// instruction sequence has no branch around a memory access.  Per row the
-// owner keeps (value, lowest id), reduces it over its 16 lanes and publishes a
-// packed (value, ~id) key with a 64-bit atomic max (order independent); the
-// last workgroup writes the tokens.
-template <typename T>
+// finished inside the stream by all four waves (wave wv owns rows
+// 16 r + 4 g + wv of every tile, so each row has one owner per workgroup).
+// The fp32 logits go out through a range-checked buffer store that drops
+// rows >= M, columns >= V and everything when no logits buffer is given, so
+// the stream's instruction sequence has no branch around a memory access.  Per
+// row the owner keeps (value, lowest id), reduces it over its 16 lanes and
+// publishes a packed (value, ~id) key with a 64-bit atomic max (order
+// independent); the last workgroup writes the tokens.  RT: 16-row tiles.
+template <typename T, int RT = 1>
 struct OpLMHeadWG {
     static constexpr int kNT = 8;
+    static constexpr int kRT = RT;
     static constexpr bool kInLoop = true;
     static constexpr int kWGDepth = 2;
     struct State {
-        float v;
-        int idx;
+        float v[RT];
+        int idx[RT];
         __amdgpu_buffer_rsrc_t out;
     };
     NormA<T> a;
     const T* w;
     int V, K, M;
     float* logits;                 // [M, V] or null
-    unsigned long long* best;      // [16] packed keys, zero on entry
+    unsigned long long* best;      // [16 RT] packed keys, zero on entry
     unsigned* wg_cnt;              // workgroup completion counter
     int32_t* tokens;               // [M]
     __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
@@ -880,43 +1060,53 @@ struct OpLMHeadWG {
         return n0 < V ? sw_stream(w, n0 / 16, nch) : nullptr;
     }
     __device__ __forceinline__ void wave_begin(State& s) const {
-        s.v = -INFINITY;
-        s.idx = 0x7FFFFFFF;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            s.v[r] = -INFINITY;
+            s.idx[r] = 0x7FFFFFFF;
+        }
         // 0x00020000: the gfx9 buffer descriptor's format word (raw 32-bit data)
         s.out = __builtin_amdgcn_make_buffer_rsrc(logits, 0, logits ? (int)((long long)M * V * 4) : 0, 0x00020000);
     }
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
-    __device__ __forceinline__ void finish_rows(int tile, const float (&v)[kNT], int lane, int wv, State& s) const {
-        const int row = 4 * (lane >> 4) + wv;
+    __device__ __forceinline__ void finish_rows(int tile, const float (&v)[RT * kNT], int lane, int wv, State& s) const {
 #pragma unroll
-        for (int b = 0; b < kNT; ++b) {
-            const int n = 16 * kNT * tile + 16 * b + (lane & 15);
-            const bool ok = n < V;
-            const int off = ok && row < M ? (row * V + n) * 4 : 0x7FFFFFF0;  // out of range: dropped
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v[b]), s.out, off, 0, 0);
-            if (ok && (v[b] > s.v || (v[b] == s.v && n < s.idx))) {
-                s.v = v[b];
-                s.idx = n;
+        for (int r = 0; r < RT; ++r) {
+            const int row = 16 * r + 4 * (lane >> 4) + wv;
+#pragma unroll
+            for (int b = 0; b < kNT; ++b) {
+                const int n = 16 * kNT * tile + 16 * b + (lane & 15);
+                const bool ok = n < V;
+                const int off = ok && row < M ? (row * V + n) * 4 : 0x7FFFFFF0;  // out of range: dropped
+                const float x = v[r * kNT + b];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), s.out, off, 0, 0);
+                if (ok && (x > s.v[r] || (x == s.v[r] && n < s.idx[r]))) {
+                    s.v[r] = x;
+                    s.idx[r] = n;
+                }
             }
         }
     }
     __device__ void wave_end(State& s, int lane) const {
         __shared__ unsigned last;
-        float v = s.v;
-        int id = s.idx;
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-            const float ov = __shfl_xor(v, m, 64);
-            const int oi = __shfl_xor(id, m, 64);
-            if (ov > v || (ov == v && oi < id)) {
-                v = ov;
-                id = oi;
+        for (int r = 0; r < RT; ++r) {
+            float v = s.v[r];
+            int id = s.idx[r];
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                const float ov = __shfl_xor(v, m, 64);
+                const int oi = __shfl_xor(id, m, 64);
+                if (ov > v || (ov == v && oi < id)) {
+                    v = ov;
+                    id = oi;
+                }
             }
-        }
-        const int row = 4 * (lane >> 4) + (threadIdx.x >> 6);
-        if ((lane & 15) == 0 && row < M && id != 0x7FFFFFFF) {
-            const unsigned long long key = ((unsigned long long)ordered_bits(v) << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)id);
-            atomicMax(best + row, key);
+            const int row = 16 * r + 4 * (lane >> 4) + (threadIdx.x >> 6);
+            if ((lane & 15) == 0 && row < M && id != 0x7FFFFFFF) {
+                const unsigned long long key = ((unsigned long long)ordered_bits(v) << 32) | (unsigned)(0xFFFFFFFFu - (unsigned)id);
+                atomicMax(best + row, key);
+            }
         }
         wait_vmem();
         __syncthreads();
@@ -924,7 +1114,7 @@ struct OpLMHeadWG {
         __syncthreads();
         if (last) {
             compiler_fence();
-            if (threadIdx.x < 16) {
+            if (threadIdx.x < 16 * RT) {
                 const int j = threadIdx.x;
                 if (j < M) {
                     const unsigned long long key = atomicOr(best + j, 0ull);
@@ -1107,14 +1297,19 @@ static hipError_t run_skinny_wg(const DevCtx& c, const Op& op, int M, int K, int
     wc.cpw = ((wc.nchunks + W - 1) / W + KP - 1) / KP * KP;
     wc.clear = clear;
     wc.clear_n = clear_n;
-    const size_t lds = (size_t)(Op::kInLoop ? 2 : wc.tpw) * W * NT * 64 * sizeof(f32x4_t);
+    const size_t lds = (size_t)(Op::kInLoop ? 2 : wc.tpw) * W * Op::kRT * NT * 64 * sizeof(f32x4_t);
     // The occupancy hint of two workgroups per CU caps the kernel at 256
     // architectural VGPRs (it needs < 190, no spills); it measured at least as
     // fast as one workgroup per CU, which also allocates AGPRs.  (The AGPR
     // build once gave wrong results: its accumulator copies were read right
     // after a taken branch without the MFMA wait states; mfma_settle() now
-    // pads every group.)
-    hipLaunchKernelGGL((skinny_wg_kernel<T, Op, W, 2, KP, Op::kWGDepth>), dim3(grid), dim3(64 * W), lds, s, op, wc);
+    // pads every group.)  Two row tiles double the activation registers, so
+    // that form is built for one workgroup per CU (the grid never has more).
+    if constexpr (Op::kRT == 1)
+        hipLaunchKernelGGL((skinny_wg_kernel<T, Op, W, 2, KP, Op::kWGDepth>), dim3(grid), dim3(64 * W), lds, s, op, wc);
+    else
+        hipLaunchKernelGGL((skinny_wg_rows_kernel<T, Op, W, 1, KP, Op::kWGDepth>), dim3(grid), dim3(64 * W), lds, s, op,
+                           wc);
     return hipGetLastError();
 }
 
@@ -1133,7 +1328,7 @@ static hipError_t run_layer_gemm(const DevCtx& c, const Op& op, int M, int K, in
 // ============================================================================
 
 struct AttnArgs {
-    const void* q;      // [16][nq*d]
+    const void* q;      // [B][nq*d] (B <= 32; blockIdx.z picks rows 16 z .. 16 z + 15)
     const void* kblk;   // [16][nkv*d]
     const void* vblkT;  // [nkv][d][16]
     KVPages kv;
@@ -1143,8 +1338,9 @@ struct AttnArgs {
                                // causal_base + i iff bit i of tree_anc[j]; null: the chain above
     const int* len_dev; // non-null (draft only): the context length is *len_dev, not C
     float scale_log2;   // log2(e) / sqrt(d)
-    float* part_o;      // [(n_splits+1)][nq][16][d]
-    float* part_ml;     // [(n_splits+1)][nq][16][2]
+    int rows_ld;        // rows per (split, head) of the partials: 16, or 32 for a 32-row pass
+    float* part_o;      // [(n_splits+1)][nq][rows_ld][d]
+    float* part_ml;     // [(n_splits+1)][nq][rows_ld][2]
 };
 
 // Four consecutive positions of one V^T row (one half of a P.V operand slot set).
@@ -1344,7 +1540,9 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = blockIdx.y, split = blockIdx.x;
     const int grp = lane >> 4, col = lane & 15;
-    const T* q = reinterpret_cast<const T*>(a.q);
+    // rows 16 z .. 16 z + 15 of the pass (a second half only in a 32-row causal pass)
+    const int r0 = 16 * blockIdx.z, nrows = min(16, a.B - r0);
+    const T* q = reinterpret_cast<const T*>(a.q) + (long long)r0 * a.nq * D;
 
     Frag<T> qf[HPW][D / 32];
     HeadAcc<D> acc[HPW];
@@ -1354,7 +1552,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
             const int hq = g * a.group + min(w + 4 * hh, a.group - 1);
 #pragma unroll
             for (int kc = 0; kc < D / 32; ++kc) {
-                if (col < a.B) qf[hh][kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
+                if (col < nrows) qf[hh][kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
                 else qf[hh][kc].zero();
             }
             acc[hh].m = -INFINITY;
@@ -1370,7 +1568,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
             const int hq = g * a.group + min(hi, a.group - 1);
 #pragma unroll
             for (int kc = 0; kc < D / 32; ++kc) {
-                if (col < a.B) qf[hh][kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
+                if (col < nrows) qf[hh][kc].load(q + (long long)col * a.nq * D + hq * D + kc * 32 + grp * 8);
                 else qf[hh][kc].zero();
             }
             acc[hh].m = -INFINITY;
@@ -1384,8 +1582,10 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
     // with a device-resident length the splits are planned for the capacity;
     // those past the current length have no keys (their partial stays empty)
     const int Cnow = a.len_dev ? min(*a.len_dev, a.C) : a.C;
-    // causal rows: the block keys this lane's query row sees (a chain: rows 0..col)
-    const uint32_t anc = !CAUSAL ? 0u : (a.tree_anc && col < a.B) ? a.tree_anc[col] : ((2u << col) - 1u);
+    // causal rows: the block keys this lane's query row r sees (a chain: rows 0..r;
+    // for r = 31 the shift wraps to 0 and the mask is all 32 keys)
+    const int qr = r0 + col;
+    const uint32_t anc = !CAUSAL ? 0u : (a.tree_anc && col < nrows) ? a.tree_anc[qr] : ((2u << qr) - 1u);
     if (split < a.n_splits) {
         const int kbeg = split * a.kps;
         const int kend = min(Cnow, kbeg + a.kps);
@@ -1535,7 +1735,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
     for (int hh = 0; hh < HPW; ++hh) {
         if (w + 4 * hh >= a.group) break;
         const int hq = g * a.group + w + 4 * hh;
-        const long long pidx = ((long long)split * a.nq + hq) * 16;
+        const long long pidx = ((long long)split * a.nq + hq) * a.rows_ld + r0;
 #pragma unroll
         for (int db = 0; db < D / 16; ++db)
 #pragma unroll
@@ -1553,14 +1753,14 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
 // in LDS, then 4 groups of D threads each sum a quarter of the splits.
 template <typename T>
 __global__ __launch_bounds__(512) void attn_merge_kernel(const float* part_o, const float* part_ml, int n_parts,
-                                                         int nq, int d, int B, T* out) {
+                                                         int nq, int d, int B, int rows_ld, T* out) {
     __shared__ float wgt[kMaxSplits + 1];
     __shared__ float red[4][128];
     __shared__ float stat[2];
-    const int hq = blockIdx.x / 16, j = blockIdx.x % 16;
+    const int hq = blockIdx.x / rows_ld, j = blockIdx.x % rows_ld;
     if (j >= B) return;
     const int tid = threadIdx.x;
-    for (int s = tid; s < n_parts; s += 512) wgt[s] = part_ml[(((long long)s * nq + hq) * 16 + j) * 2];
+    for (int s = tid; s < n_parts; s += 512) wgt[s] = part_ml[(((long long)s * nq + hq) * rows_ld + j) * 2];
     __syncthreads();
     if (tid < 64) {
         float M = -INFINITY;
@@ -1573,7 +1773,7 @@ __global__ __launch_bounds__(512) void attn_merge_kernel(const float* part_o, co
     float Lp = 0.f;
     for (int s = tid; s < n_parts; s += 512) {
         const float wv = exp2f(wgt[s] - M);
-        Lp += wv * part_ml[(((long long)s * nq + hq) * 16 + j) * 2 + 1];
+        Lp += wv * part_ml[(((long long)s * nq + hq) * rows_ld + j) * 2 + 1];
         wgt[s] = wv;
     }
     // sum of L over the block (fixed order: per-thread partials, then tree)
@@ -1590,8 +1790,8 @@ __global__ __launch_bounds__(512) void attn_merge_kernel(const float* part_o, co
     if (dim < d) {
         int s = grp;
         for (; s + 12 < n_parts; s += 16) {
-            const long long b = ((long long)s * nq + hq) * 16 + j;
-            const long long st = (long long)4 * nq * 16;
+            const long long b = ((long long)s * nq + hq) * rows_ld + j;
+            const long long st = (long long)4 * nq * rows_ld;
             const float a0 = part_o[b * d + dim], a1 = part_o[(b + st) * d + dim];
             const float a2 = part_o[(b + 2 * st) * d + dim], a3 = part_o[(b + 3 * st) * d + dim];
             acc += wgt[s] * a0;
@@ -1599,7 +1799,7 @@ __global__ __launch_bounds__(512) void attn_merge_kernel(const float* part_o, co
             acc += wgt[s + 8] * a2;
             acc += wgt[s + 12] * a3;
         }
-        for (; s < n_parts; s += 4) acc += wgt[s] * part_o[(((long long)s * nq + hq) * 16 + j) * d + dim];
+        for (; s < n_parts; s += 4) acc += wgt[s] * part_o[(((long long)s * nq + hq) * rows_ld + j) * d + dim];
     }
     red[grp][dim] = acc;
     __syncthreads();
@@ -1636,9 +1836,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_
     const int j = blockIdx.x;
     if (tree_parent) {
         // tree verification: row j is tree node u = tree_off + j (a tree of
-        // tree_n <= 32 nodes verified in passes of up to 16 rows); its depth
-        // and the mask of its ancestors and itself (bit i: node i).  A parent
-        // outside [0, node) is read as the root, so every walk ends at node 0.
+        // tree_n <= 32 nodes verified in one pass, or in passes of up to 16
+        // rows); its depth (tree_info[j]) and the mask of its ancestors and
+        // itself (tree_info[32 + j]; bit i: node i).  A parent outside
+        // [0, node) is read as the root, so every walk ends at node 0.
         if (threadIdx.x < 32) {
             const int r = threadIdx.x;
             const int p = r < tree_n ? tree_parent[r] : 0;
@@ -1654,7 +1855,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const int32_
                 ++depth;
             }
             tree_info[j] = depth;
-            tree_info[16 + j] = (int)anc;
+            tree_info[32 + j] = (int)anc;
         }
     }
     for (int i = j * 256 + threadIdx.x; i < clear_n; i += gridDim.x * 256) clear[i] = 0.f;
@@ -2283,7 +2484,23 @@ struct PassArgs {
     int layer_rows = 0; // rows per layer of layer_out (0: the pass's rows)
 };
 
-template <typename T>
+// Whether every projection of a pass runs on the workgroup-local kernel (bf16,
+// evenly filled plans): only that kernel takes two 16-row tiles, so only then
+// can rows 16..31 share the pass (and its weight reads) with rows 0..15.
+static bool wg_plan_all(const DevCtx& c) {
+    const Dims& d = c.dm;
+    if (d.elem != 2 || d.V % 16 != 0 || c.num_cus < 1) return false;
+    const int ss_tiles = (d.H + 31) / 32;
+    if (ss_tiles > 4 * kSSPerLane) return false;  // lazy row statistics
+    const int qkv_tiles = (d.nq * d.d + 2 * d.nkv * d.d) / 32;
+    return wg_plan_balanced(d.H / 16, c.num_cus) && wg_plan_balanced(qkv_tiles, c.num_cus) &&
+           wg_plan_balanced(d.F / 16, c.num_cus) && wg_plan_balanced((d.V + 127) / 128, c.num_cus);
+}
+
+bool wide_pass_supported(const DevCtx& c) { return wg_plan_all(c); }
+
+// RT: 16-row tiles (2 for a causal pass of 17..32 rows; needs wg_plan_all).
+template <typename T, int RT>
 static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     const Dims& d = c.dm;
     const int H = d.H, B = pa.rows, nq = d.nq, nkv = d.nkv, D = d.d, F = d.F, C = pa.C;
@@ -2298,8 +2515,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     // writes ss0 (read by gate/up) and clears ss1; the down projection writes
     // ss1 (read by the next QKV or the LM head) and clears ss0
     float* ss0 = WS(float*, ss_part);
-    float* ss1 = ss0 + 16LL * c.lay.ss_stride;
-    const int ss_n = 16 * c.lay.ss_stride;
+    float* ss1 = ss0 + 16LL * RT * c.lay.ss_stride;
+    const int ss_n = 16 * RT * c.lay.ss_stride;
     unsigned long long* best = WS(unsigned long long*, best);
     unsigned* counters = WS(unsigned*, counters);
     const float* cosT = WS(const float*, rope_cos);
@@ -2333,6 +2550,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     const int ss_tiles = (H + 16 * OpResid<T>::kNT - 1) / (16 * OpResid<T>::kNT);
     const bool lazy_stats = ss_tiles <= 4 * kSSPerLane;
     const bool resid_wg = sizeof(T) == 2 && lazy_stats && wg_plan_balanced(H / 16, c.num_cus);
+    if (RT > 1 && (B > 16 * RT || !wg_plan_all(c))) return hipErrorInvalidValue;
     auto norm_in = [&](const void* gain, bool after_resid, const float* ss) {
         NormA<T> na{x, H, rstd, (const T*)gain};
         if (after_resid && lazy_stats) {
@@ -2346,7 +2564,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     };
 
     for (int l = 0; l < d.Ld; ++l) {
-        OpQKV<T> qkv;
+        OpQKV<T, RT> qkv;
         qkv.a = norm_in(c.attn_norm[l], l > 0, ss1);
         qkv.wq = (const T*)c.sw_wq[l];
         qkv.wk = (const T*)c.sw_wk[l];
@@ -2359,7 +2577,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         qkv.pos0 = C;
         qkv.len_dev = pa.len_dev;
         qkv.max_ctx = d.max_ctx;
-        qkv.row_depth = pa.tree_parent ? tree_info : nullptr;
+        qkv.row_depth = pa.tree_parent ? tree_info : nullptr;  // depths, then ancestor masks (32 each)
         qkv.rot_base = pa.tree_base;
         qkv.tq = nq * D / 32;
         qkv.tk = nkv * D / 32;
@@ -2371,7 +2589,9 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         qkv.kv = make_pages<T>(c);
         qkv.layer = l;
         c.tracer->begin(DFLASH_TRACE_QKV, s);
-        if ((e = run_layer_gemm<T>(c, qkv, B, H, qkv.tq + 2 * qkv.tk, s)) != hipSuccess) return e;
+        if constexpr (RT == 1) e = run_layer_gemm<T>(c, qkv, B, H, qkv.tq + 2 * qkv.tk, s);
+        else e = run_skinny_wg<T>(c, qkv, B, H, qkv.tq + 2 * qkv.tk, s);
+        if (e != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_QKV, s);
 
         AttnArgs aa;
@@ -2389,12 +2609,13 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         aa.kps = kps;
         aa.n_splits = ns;
         aa.causal_base = pa.causal ? (pa.tree_parent ? pa.tree_base : C) : -1;
-        aa.tree_anc = pa.tree_parent ? reinterpret_cast<const uint32_t*>(tree_info + 16) : nullptr;
+        aa.tree_anc = pa.tree_parent ? reinterpret_cast<const uint32_t*>(tree_info + 32) : nullptr;
+        aa.rows_ld = 16 * RT;
         aa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
         aa.part_o = WS(float*, attn_o);
         aa.part_ml = WS(float*, attn_ml);
         c.tracer->begin(DFLASH_TRACE_ATTN, s);
-        const dim3 agrid(nparts, nkv), ablk(256);
+        const dim3 agrid(nparts, nkv, (B + 15) / 16), ablk(256);
         auto attn = [&](auto causal) {
             constexpr bool CA = decltype(causal)::value;
             if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1, CA>), agrid, ablk, 0, s, aa);
@@ -2405,8 +2626,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         if (pa.causal) attn(std::true_type{});
         else attn(std::false_type{});
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16), dim3(512), 0, s, aa.part_o, aa.part_ml, nparts, nq,
-                           D, B, obuf);
+        hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(nq * 16 * RT), dim3(512), 0, s, aa.part_o, aa.part_ml, nparts,
+                           nq, D, B, 16 * RT, obuf);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_ATTN, s);
 
@@ -2429,24 +2650,27 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         // have the same N, so both take the same branch.
         auto run_resid = [&](const void* w, int K, const T* a, float* ss_out, float* ss_clear, T* cap,
                              long long cap_ld) {
-            if (resid_wg) {
-                OpResid<T, 1> op;
+            if (RT > 1 || resid_wg) {
+                OpResid<T, 1, RT> op;
                 resid_op(op, w, K, a, ss_out);
                 op.cap = cap;
                 op.cap_ld = cap_ld;
                 return run_skinny_wg<T>(c, op, B, K, H / 16, s, ss_clear, ss_n);
             }
-            OpResid<T, 2> op;  // 32-column tiles: each stores its sums (no clearing needed)
-            resid_op(op, w, K, a, ss_out);
-            op.cap = cap;
-            op.cap_ld = cap_ld;
-            return run_skinny<T>(c, op, B, K, (H + 31) / 32, s);
+            if constexpr (RT == 1) {
+                OpResid<T, 2> op;  // 32-column tiles: each stores its sums (no clearing needed)
+                resid_op(op, w, K, a, ss_out);
+                op.cap = cap;
+                op.cap_ld = cap_ld;
+                return run_skinny<T>(c, op, B, K, (H + 31) / 32, s);
+            }
+            return hipErrorInvalidValue;
         };
         c.tracer->begin(DFLASH_TRACE_O_PROJ, s);
         if ((e = run_resid(c.sw_wo[l], nq * D, obuf, ss0, ss1, nullptr, 0)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_O_PROJ, s);
 
-        OpSwiGLU<T> sw;
+        OpSwiGLU<T, RT> sw;
         sw.a = norm_in(c.mlp_norm[l], true, ss0);
         sw.wg = (const T*)c.sw_wg[l];
         sw.wu = (const T*)c.sw_wu[l];
@@ -2455,7 +2679,9 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         sw.M = B;
         sw.h = hbuf;
         c.tracer->begin(DFLASH_TRACE_GATE_UP, s);
-        if ((e = run_layer_gemm<T>(c, sw, B, H, F / 16, s)) != hipSuccess) return e;
+        if constexpr (RT == 1) e = run_layer_gemm<T>(c, sw, B, H, F / 16, s);
+        else e = run_skinny_wg<T>(c, sw, B, H, F / 16, s);
+        if (e != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_GATE_UP, s);
 
         T* cap = nullptr;
@@ -2477,7 +2703,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     bool lm_done = false;
     if constexpr (sizeof(T) == 2) {
         if (d.V % 16 == 0 && wg_plan_balanced(lm_tiles_wg, c.num_cus)) {
-            OpLMHeadWG<T> lm;
+            OpLMHeadWG<T, RT> lm;
             lm.a = norm_in(c.final_norm, d.Ld > 0, ss1);
             lm.w = (const T*)c.sw_lm;
             lm.V = d.V;
@@ -2491,7 +2717,9 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
             lm_done = true;
         }
     }
-    if (!lm_done) {
+    if constexpr (RT > 1) {
+        if (!lm_done) return hipErrorInvalidValue;
+    } else if (!lm_done) {
         OpLMHead<T> lm;
         lm.a = norm_in(c.final_norm, d.Ld > 0, ss1);
         lm.w = (const T*)c.sw_lm;
@@ -2513,7 +2741,7 @@ hipError_t launch_draft_block(const DevCtx& c, int C, const int32_t* anchor, flo
                               void* layer_out, long long layer_ld, const int* len_dev, hipStream_t s) {
     PassArgs pa{C, anchor, 1, c.dm.B, false, logits, tokens, nullptr, 0, layer_out, layer_ld, len_dev, nullptr};
     c.tracer->begin(DFLASH_TRACE_DRAFT, s);
-    hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
+    hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float, 1>(c, pa, s) : pass_t<bf16_t, 1>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_DRAFT, s);
     return e;
 }
@@ -2525,7 +2753,11 @@ hipError_t launch_causal_forward(const DevCtx& c, int C, const int32_t* tokens, 
     PassArgs pa{C, tokens, M, M, true, logits, argmax, capture, capture_ld, layer_out, layer_ld, nullptr, tree_parent,
                 tree_off, tree_base, tree_n, layer_rows};
     c.tracer->begin(DFLASH_TRACE_TARGET, s);
-    hipError_t e = c.dm.dtype == DFLASH_F32 ? pass_t<float>(c, pa, s) : pass_t<bf16_t>(c, pa, s);
+    hipError_t e;
+    if (M > 16)  // one pass of up to 32 rows (the caller checked wide_pass_supported)
+        e = c.dm.dtype == DFLASH_F32 ? hipErrorInvalidValue : pass_t<bf16_t, 2>(c, pa, s);
+    else
+        e = c.dm.dtype == DFLASH_F32 ? pass_t<float, 1>(c, pa, s) : pass_t<bf16_t, 1>(c, pa, s);
     if (e == hipSuccess) c.tracer->end(DFLASH_TRACE_TARGET, s);
     return e;
 }

@@ -286,8 +286,9 @@ dflash_status dflash_target_forward(dflash_ctx* ctx, const int32_t* tokens, int3
  *  - verification follows, from the root, the child whose token is the
  *    target's greedy token after the current node.
  * Trees have at most DFLASH_TREE_MAX_NODES = 32 nodes (the root and a budget
- * of up to 31); up to 16 nodes are verified in one target pass, 17 to 32 in
- * two.  Node order: parent[j] < j. */
+ * of up to 31), verified in one target pass (bf16 contexts whose projections
+ * fit the 32-row kernels; otherwise 17 to 32 nodes take two passes).  Node
+ * order: parent[j] < j. */
 
 /* Per row r < rows of logits ([rows][ld] device fp32, ld >= V): the K largest
  * token ids (ties: lower id first) into ids_out (device int32 [rows][K]) and
@@ -315,10 +316,13 @@ dflash_status dflash_build_tree(dflash_ctx* ctx, const int32_t* anchor, const in
  * and it attends to the cache before C and to its ancestors and itself, so
  * it computes what a causal forward of its root path computes (up to
  * rounding order).  argmax_out[j] is the target's greedy token after node j.
- * 1 <= M <= 32: nodes 0..15 run as one pass, nodes 16..M-1 as a second that
- * finds its ancestors among the first pass's nodes in the cache (a chain of
- * 32 nodes gives what two 16-row dflash_target_forward calls give, bit for
- * bit).  Afterwards length = C + M; accept
+ * 1 <= M <= 32, in one pass that reads every weight once for all rows; where
+ * the context's kernels cannot take more than 16 rows (fp32, or projections
+ * whose tiles fill the compute units unevenly), nodes 16..M-1 run as a second
+ * pass that finds their ancestors among the first pass's nodes in the cache.
+ * Either way row j's results are those of the 16-row arithmetic (a chain of 32
+ * nodes gives what two 16-row dflash_target_forward calls give, bit for bit).
+ * Afterwards length = C + M; accept
  * with dflash_tree_accept, move the accepted rows with dflash_tree_commit,
  * then dflash_rollback to C + 1 + k.  Otherwise the arguments, errors and
  * capture rules of dflash_target_forward. */
