@@ -135,6 +135,24 @@ struct NormA {
         for (int e = 0; e < 8; ++e) v[e] = r.x.get(e) * s * r.g.get(e);
         f.set8(v);
     }
+    // RN row tiles of one chunk: their x fragments and one shared gain fragment
+    template <int RN>
+    struct RawN {
+        Frag<T> x[RN], g;
+    };
+    template <int RN>
+    __device__ __forceinline__ void load_n(RawN<RN>& r, const int (&row)[RN], int k) const {
+#pragma unroll
+        for (int i = 0; i < RN; ++i) r.x[i].load(x + (long long)row[i] * ld + k);
+        r.g.load(gain + k);
+    }
+    template <int RN>
+    __device__ __forceinline__ void finish_n(Frag<T>& f, const RawN<RN>& r, int i, float s) const {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = r.x[i].get(e) * s * r.g.get(e);
+        f.set8(v);
+    }
 };
 
 struct NoPre {
@@ -155,6 +173,19 @@ struct PlainA : NoPre {
     };
     __device__ __forceinline__ void load(Raw& r, int row, int k) const { r.x.load(x + row * ld + k); }
     __device__ __forceinline__ void finish(Frag<T>& f, const Raw& r, float) const { f = r.x; }
+    template <int RN>
+    struct RawN {
+        Frag<T> x[RN];
+    };
+    template <int RN>
+    __device__ __forceinline__ void load_n(RawN<RN>& r, const int (&row)[RN], int k) const {
+#pragma unroll
+        for (int i = 0; i < RN; ++i) r.x[i].load(x + row[i] * ld + k);
+    }
+    template <int RN>
+    __device__ __forceinline__ void finish_n(Frag<T>& f, const RawN<RN>& r, int i, float) const {
+        f = r.x[i];
+    }
 };
 
 // five hidden-state slabs read as one concatenated row (never materialised)
@@ -523,7 +554,7 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_rows_kernel(Op op, WG
     constexpr int RT = Op::kRT;  // 16-row tiles of A (two for a 32-row pass): each weight fragment feeds RT MFMAs
     extern __shared__ f32x4_t wg_red[];  // [tile][wave][row tile][block][lane]: one 16-byte access per lane
     using AL = decltype(op.a);
-    using Raw = typename AL::Raw;
+    using RawN = typename AL::template RawN<RT>;  // one chunk of every row tile
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row = lane & 15, grp = lane >> 4;
     bool row_ok[RT];
@@ -549,7 +580,7 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_rows_kernel(Op op, WG
 
     struct Group {
         Frag<T> w[NT][KP];
-        Raw a[RT][KP];
+        RawN a[KP];
     };
     f32x4_t acc[RT * NT];  // [row tile][block]
 #pragma unroll
@@ -571,8 +602,7 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_rows_kernel(Op op, WG
             const int k = min(ch * 32 + grp * 8, klast);
 #pragma unroll
             for (int b = 0; b < NT; ++b) g.w[b][p].load_sw(ws[b] + (long long)ch * 512, lane);
-#pragma unroll
-            for (int r = 0; r < RT; ++r) op.a.load(g.a[r][p], arow[r], k);
+            op.a.load_n(g.a[p], arow, k);
         }
     };
     float pre[RT];
@@ -584,7 +614,7 @@ __global__ __launch_bounds__(64 * W, MINWG) void skinny_wg_rows_kernel(Op op, WG
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 Frag<T> a;
-                op.a.finish(a, g.a[r][p], pre[r]);
+                op.a.finish_n(a, g.a[p], r, pre[r]);
                 const bool ok = row_ok[r] && (cb + p < ch1) && ((cb + p) * 32 + grp * 8 < c.K);
                 a.mask(ok ? 0xFFFFFFFFu : 0u);
 #pragma unroll
@@ -888,11 +918,15 @@ struct OpResid {
     }
 };
 
-// h = round(silu(u . Wg^T) * (u . Wu^T)); tile t pairs column block t of Wg and Wu.
-template <typename T, int RT = 1>
+// h = round(silu(u . Wg^T) * (u . Wu^T)).  Tile t holds the P column-block
+// pairs P t .. P t + P - 1 (pair i: column block i of Wg and of Wu), so one
+// activation load feeds 2 P weight blocks: with P pairs per tile a workgroup
+// reads its rows of A once instead of once per pair-tile.
+template <typename T, int RT = 1, int P = 1>
 struct OpSwiGLU {
-    static constexpr int kNT = 2;  // 16-column blocks per tile
-    static constexpr int kRT = RT;  // 16-row tiles (2: workgroup-local kernel only)
+    static constexpr int kNT = 2 * P;  // 16-column blocks per tile
+    static constexpr int kRT = RT;     // 16-row tiles (2: workgroup-local kernel only)
+    static constexpr int kKP = P == 1 ? 0 : (P <= 3 ? 2 : 1);  // chunks per load group (0: the default)
     static constexpr bool kInLoop = false;
     static constexpr int kWGDepth = 2;  // load groups in flight (a third measured no faster)
     using State = NoState;
@@ -903,22 +937,28 @@ struct OpSwiGLU {
     int F, K, M;
     T* h;
     __device__ __forceinline__ const T* b_rows(int tile, int blk, int nch) const {
-        return sw_stream(blk == 0 ? wg : wu, tile, nch);
+        const int pair = P * tile + (blk >> 1);
+        if (P > 1 && 16 * pair >= F) return nullptr;
+        return sw_stream((blk & 1) == 0 ? wg : wu, pair, nch);
     }
     __device__ __forceinline__ void wave_begin(State&) const {}
     __device__ __forceinline__ void prefetch(int, int, State&) const {}
     __device__ __forceinline__ void wave_end(State&, int) const {}
     __device__ __forceinline__ void done_hook(int, int) const {}
     __device__ __forceinline__ void epilogue(int tile, const f32x4_t* acc, int lane, State&) const {
-        const int n = 16 * tile + (lane & 15);
 #pragma unroll
-        for (int q = 0; q < 4 * RT; ++q) {
-            const int r = q >> 2, ii = q & 3;
-            const int j = 16 * r + 4 * (lane >> 4) + ii;
-            if (j >= M) continue;
-            const float g = acc[2 * r][ii], u = acc[2 * r + 1][ii];
-            const float sg = g / (1.0f + __expf(-g));
-            h[(long long)j * F + n] = Elem<T>::from_f32(sg * u);
+        for (int i = 0; i < P; ++i) {
+            const int n = 16 * (P * tile + i) + (lane & 15);
+            if (P > 1 && n >= F) continue;
+#pragma unroll
+            for (int q = 0; q < 4 * RT; ++q) {
+                const int r = q >> 2, ii = q & 3;
+                const int j = 16 * r + 4 * (lane >> 4) + ii;
+                if (j >= M) continue;
+                const float g = acc[r * kNT + 2 * i][ii], u = acc[r * kNT + 2 * i + 1][ii];
+                const float sg = g / (1.0f + __expf(-g));
+                h[(long long)j * F + n] = Elem<T>::from_f32(sg * u);
+            }
         }
     }
 };
@@ -1264,6 +1304,16 @@ static hipError_t run_skinny(const DevCtx& c, const Op& op, int M, int K, int nt
     return hipGetLastError();
 }
 
+// An op's chunks per load group (kKP), if it sets one.
+template <class Op, class = void>
+struct OpKP {
+    static constexpr int value = 0;
+};
+template <class Op>
+struct OpKP<Op, std::void_t<decltype(Op::kKP)>> {
+    static constexpr int value = Op::kKP;
+};
+
 // Workgroup-local split-K plan: one workgroup per CU, each owning
 // ceil(ntiles / CUs) consecutive tiles (measured: two workgroups on some CUs
 // and eight waves per tile were both slower).  A load group carries 8 KB of
@@ -1285,7 +1335,7 @@ template <typename T, class Op>
 static hipError_t run_skinny_wg(const DevCtx& c, const Op& op, int M, int K, int ntiles, hipStream_t s,
                                 float* clear = nullptr, int clear_n = 0) {
     constexpr int NT = Op::kNT;
-    constexpr int KP = NT == 1 && sizeof(T) == 2 ? 8 : (NT >= 8 ? 2 : 4);
+    constexpr int KP = OpKP<Op>::value ? OpKP<Op>::value : (NT == 1 && sizeof(T) == 2 ? 8 : (NT >= 8 ? 2 : 4));
     constexpr int W = 4;
     WGCommon wc;
     wc.M = M;
@@ -2499,6 +2549,18 @@ static bool wg_plan_all(const DevCtx& c) {
 
 bool wide_pass_supported(const DevCtx& c) { return wg_plan_all(c); }
 
+// Column-block pairs per gate/up tile (bf16): 3 or 5 where the F/16 pairs
+// spread over the CUs at exactly that many per CU (8B: 768 pairs = 3 per CU;
+// 27B: 1088 pairs, 5 per CU on 218 CUs), else 1.
+template <typename T>
+static int gate_up_pairs(const DevCtx& c) {
+    if (sizeof(T) != 2 || c.num_cus < 1) return 1;
+    const int pairs = c.dm.F / 16;
+    const int per = (pairs + c.num_cus - 1) / c.num_cus;
+    if (per != 3 && per != 5) return 1;
+    return wg_plan_balanced((pairs + per - 1) / per, c.num_cus) ? per : 1;
+}
+
 // RT: 16-row tiles (2 for a causal pass of 17..32 rows; needs wg_plan_all).
 template <typename T, int RT>
 static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
@@ -2551,6 +2613,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     const bool lazy_stats = ss_tiles <= 4 * kSSPerLane;
     const bool resid_wg = sizeof(T) == 2 && lazy_stats && wg_plan_balanced(H / 16, c.num_cus);
     if (RT > 1 && (B > 16 * RT || !wg_plan_all(c))) return hipErrorInvalidValue;
+    const int gu_pairs = gate_up_pairs<T>(c);
     auto norm_in = [&](const void* gain, bool after_resid, const float* ss) {
         NormA<T> na{x, H, rstd, (const T*)gain};
         if (after_resid && lazy_stats) {
@@ -2670,17 +2733,29 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         if ((e = run_resid(c.sw_wo[l], nq * D, obuf, ss0, ss1, nullptr, 0)) != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_O_PROJ, s);
 
-        OpSwiGLU<T, RT> sw;
-        sw.a = norm_in(c.mlp_norm[l], true, ss0);
-        sw.wg = (const T*)c.sw_wg[l];
-        sw.wu = (const T*)c.sw_wu[l];
-        sw.F = F;
-        sw.K = H;
-        sw.M = B;
-        sw.h = hbuf;
+        // gate/up: P column-block pairs per tile when every CU then holds one
+        // tile of P pairs (its rows of A read once, not once per pair)
+        auto gate_up = [&](auto pc) {
+            constexpr int P = decltype(pc)::value;
+            OpSwiGLU<T, RT, P> sw;
+            sw.a = norm_in(c.mlp_norm[l], true, ss0);
+            sw.wg = (const T*)c.sw_wg[l];
+            sw.wu = (const T*)c.sw_wu[l];
+            sw.F = F;
+            sw.K = H;
+            sw.M = B;
+            sw.h = hbuf;
+            if constexpr (RT == 1 && P == 1) return run_layer_gemm<T>(c, sw, B, H, F / 16, s);
+            else return run_skinny_wg<T>(c, sw, B, H, (F / 16 + P - 1) / P, s);
+        };
         c.tracer->begin(DFLASH_TRACE_GATE_UP, s);
-        if constexpr (RT == 1) e = run_layer_gemm<T>(c, sw, B, H, F / 16, s);
-        else e = run_skinny_wg<T>(c, sw, B, H, F / 16, s);
+        if constexpr (sizeof(T) == 2) {
+            if (gu_pairs == 3) e = gate_up(std::integral_constant<int, 3>{});
+            else if (gu_pairs == 5) e = gate_up(std::integral_constant<int, 5>{});
+            else e = gate_up(std::integral_constant<int, 1>{});
+        } else {
+            e = gate_up(std::integral_constant<int, 1>{});
+        }
         if (e != hipSuccess) return e;
         c.tracer->end(DFLASH_TRACE_GATE_UP, s);
 
