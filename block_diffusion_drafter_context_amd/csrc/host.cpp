@@ -154,7 +154,7 @@ std::vector<int32_t> make_page_table(int n_pages, uint64_t seed) {
     return p;
 }
 
-void attn_split_plan(int C, int nkv, int num_cus, int page, int* kps, int* ns) {
+void attn_split_plan(int C, int nkv, int num_cus, int page, int* kps, int* ns, int wg_per_cu) {
     if (C <= 0) {
         *kps = kAttnChunk;
         *ns = 0;
@@ -166,7 +166,7 @@ void attn_split_plan(int C, int nkv, int num_cus, int page, int* kps, int* ns) {
     // first-chunk latency, partial write and merge read -- is then amortised).
     // On MI355X at 36K keys one round beats 1.5 rounds (3 workgroups per CU) by
     // about 36 us per draft pass; at 4K the three-chunk minimum decides.
-    long long target = std::max(1LL, (long long)kAttnWGPerCU * num_cus / std::max(nkv, 1) - 1);
+    long long target = std::max(1LL, (long long)wg_per_cu * num_cus / std::max(nkv, 1) - 1);
     long long per = (C + target - 1) / target;
     per = ((per + kAttnChunk - 1) / kAttnChunk) * kAttnChunk;
     per = std::max<long long>(per, 3 * kAttnChunk);

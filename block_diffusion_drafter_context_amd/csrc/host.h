@@ -19,8 +19,13 @@ constexpr int kSkinnyWavesPerWG = 4;     // skinny (M <= 16) GEMM: 256-thread wo
 constexpr int kSkinnyNT = 2;             // 16-column blocks per skinny tile (most ops)
 constexpr int kSkinnyMaxNT = 4;          // the widest skinny tile (LM head)
 constexpr int kAttnChunk = 64;           // keys per attention step
-constexpr int kAttnStages = 2;           // attention chunks resident in LDS per workgroup
-constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU
+constexpr int kAttnStages = 2;           // attention chunks resident in LDS per workgroup (fp32)
+constexpr int kAttnStagesBF16 = 2;       // the same for bf16 (4 stages on one workgroup per CU measured slower)
+constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU with two stages
+// Attention workgroups that fit a CU with NS stages of up to 32 KB each.
+constexpr int attn_wg_per_cu(int ns) { return ns <= 2 ? kAttnWGPerCU : 1; }
+template <typename T>
+constexpr int attn_stages() { return sizeof(T) == 2 ? kAttnStagesBF16 : kAttnStages; }
 constexpr int kMaxSplits = 256;          // context splits of the split-KV attention
 constexpr int kMaxSplitPages = 1040;     // KV pages one attention split may touch
 constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
@@ -83,7 +88,8 @@ void feature_layers(int target_layers, int32_t out[5]);
 
 // Attention split plan for a context of C keys: keys per split (multiple of
 // kAttnChunk) and number of context splits (the block keys get one more).
-void attn_split_plan(int C, int nkv, int num_cus, int page, int* keys_per_split, int* n_splits);
+void attn_split_plan(int C, int nkv, int num_cus, int page, int* keys_per_split, int* n_splits,
+                     int wg_per_cu = kAttnWGPerCU);
 
 // Keys per split of the causal forward: fixed for a context (it depends on
 // max_ctx only), so split boundaries sit at the same absolute positions in

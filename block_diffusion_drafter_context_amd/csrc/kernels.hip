@@ -1570,20 +1570,44 @@ __device__ __forceinline__ Frag<T> lds_frag(const char* base, int row, int ncol,
     return lds_frag_t(base, row, ncol, c16, static_cast<T*>(nullptr));
 }
 
+// A 16-byte-per-lane direct global->LDS load (global_load_lds_dwordx4; M0 =
+// the LDS destination of lane 0) issued from inline asm.  Issued through the
+// builtin, the compiler's wait analysis counts it as pending LDS data and puts
+// a vmcnt(0) before the next LDS read of the buffer, which waits for the
+// prefetched chunk too and serialises the pipeline.  The caller waits for
+// these loads itself (vmcnt, then a barrier) before reading what they wrote.
+// Loads unknown to the compiler only make its own waits on other loads
+// stricter (completion is in order).  No register receives data, so nothing
+// is left pending on a register.
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
+    const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)((lds_char_t*)lds_dst));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(src) : "memory", "m0");
+}
+
+// An empty instruction that reads a fragment's registers: the compiler
+// must have the loads that wrote them finished before it.
+__device__ __forceinline__ void use_regs(const Frag<bf16_t>& f) {
+    asm volatile("" ::"v"(f.v.x), "v"(f.v.y), "v"(f.v.z), "v"(f.v.w));
+}
+__device__ __forceinline__ void use_regs(const Frag<float>& f) {
+    asm volatile("" ::"v"(f.a.x), "v"(f.a.y), "v"(f.a.z), "v"(f.a.w), "v"(f.b.x), "v"(f.b.y), "v"(f.b.z), "v"(f.b.w));
+}
+
 // One workgroup (4 waves) = one (split, kv head).  Each 64-key chunk of the
 // split is brought into LDS once with direct global->LDS 16-byte loads (double
 // buffered), its 16-byte columns XOR-swizzled by row so fragment reads are
 // bank-conflict free; each wave then computes its query head(s) (HPW per wave)
 // from LDS.  Scores are formed transposed, S^T = K Q^T, so the probabilities
 // land in the B-operand layout of O^T += V^T P^T and never leave registers.
-template <typename T, int D, int HPW, bool CAUSAL>
-__global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs a) {
+template <typename T, int D, int HPW, bool CAUSAL, int NS_>
+__global__ __launch_bounds__(256, attn_wg_per_cu(NS_)) void attn_split_kernel(AttnArgs a) {
     constexpr int CH = kAttnChunk;                  // keys per chunk (64)
     constexpr int KCOL = D * (int)sizeof(T) / 16;   // 16-byte columns of a K row
     constexpr int VCOL = CH * (int)sizeof(T) / 16;  // 16-byte columns of a V^T row
     constexpr int NI = (CH * KCOL + D * VCOL) / 64 / 4;  // direct loads per wave per chunk
     constexpr int STAGE = (CH * KCOL + D * VCOL) * 16;   // bytes per stage
-    constexpr int NS = kAttnStages;  // chunks in LDS: one computed while the next streams in
+    constexpr int NS = NS_;  // chunks in LDS: one computed while the next NS - 1 stream in
     __shared__ __attribute__((aligned(16))) char lds[NS * STAGE];
     __shared__ int s_pages[kMaxSplitPages];
 
@@ -1596,7 +1620,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
 
     Frag<T> qf[HPW][D / 32];
     HeadAcc<D> acc[HPW];
-    if constexpr (NS == 2) {  // Q first: the code shape the compiler handles for the 2-stage form
+    {  // Q first, ahead of the first chunk's loads
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
             const int hq = g * a.group + min(w + 4 * hh, a.group - 1);
@@ -1628,7 +1652,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
         }
     };
 
-    constexpr bool kEarlyQ = NS == 2;
+    constexpr bool kEarlyQ = true;
     // with a device-resident length the splits are planned for the capacity;
     // those past the current length have no keys (their partial stays empty)
     const int Cnow = a.len_dev ? min(*a.len_dev, a.C) : a.C;
@@ -1683,17 +1707,22 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
             for (int j = 0; j < NI; ++j) {
                 const int inst = wu * NI + j;
                 const char* src = cbase + (kwave ? min(krow[j], rmax) * D * (int)sizeof(T) : 0) + off[j];
-                __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(base + inst * 1024), 16, 0, 0);
+                lds_dma16(src, base + inst * 1024);
             }
         };
+        // The Q fragments (and a tree row's ancestor mask) are read only inside
+        // the conditional per-head block of the chunk loop, so the compiler's
+        // wait analysis keeps them pending at the loop header and would wait
+        // for every load in flight before each chunk's first use: a use here
+        // retires them before any chunk load is issued.
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+            for (int kc = 0; kc < D / 32; ++kc) use_regs(qf[hh][kc]);
+        if (CAUSAL) asm volatile("" ::"v"(anc));
         // prologue: chunks 0 .. NS-2 in flight before anything else
-        if constexpr (NS == 2) {
-            if (nch > 0) issue(0, 0);
-        } else {
-            for (int c = 0; c < NS - 1; ++c)
-                if (c < nch) issue(c, c);
-            load_q();
-        }
+        for (int c = 0; c < NS - 1; ++c)
+            if (c < nch) issue(c, c);
         for (int c = 0; c < nch; ++c) {
             if constexpr (NS == 2) {
                 if (c + 1 < nch) {
@@ -1712,7 +1741,7 @@ __global__ __launch_bounds__(256, kAttnWGPerCU) void attn_split_kernel(AttnArgs 
                 else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             stage_barrier();  // every wave's pieces of chunk c are in LDS
-            const char* kl = lds + (NS == 2 ? (c & 1) : (c % NS)) * STAGE;
+            const char* kl = lds + (c % NS) * STAGE;
             const char* vl = kl + CH * KCOL * 16;
             const int nvalid = kend - (kbeg + c * CH);
             // keys this lane's query row may see: all written ones, or under the
@@ -2599,7 +2628,8 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     } else {
         // a device-resident length is planned for the capacity (the splits
         // past the current length stay empty)
-        attn_split_plan(pa.len_dev ? d.max_ctx : C, nkv, c.num_cus, d.page, &kps, &ns);
+        attn_split_plan(pa.len_dev ? d.max_ctx : C, nkv, c.num_cus, d.page, &kps, &ns,
+                        attn_wg_per_cu(attn_stages<T>()));
         nparts = ns + 1;  // + the block's own keys
     }
     const int group = nq / nkv;
@@ -2681,10 +2711,11 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         const dim3 agrid(nparts, nkv, (B + 15) / 16), ablk(256);
         auto attn = [&](auto causal) {
             constexpr bool CA = decltype(causal)::value;
-            if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1, CA>), agrid, ablk, 0, s, aa);
-            else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2, CA>), agrid, ablk, 0, s, aa);
-            else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1, CA>), agrid, ablk, 0, s, aa);
-            else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2, CA>), agrid, ablk, 0, s, aa);
+            constexpr int NS = attn_stages<T>();
+            if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1, CA, NS>), agrid, ablk, 0, s, aa);
+            else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2, CA, NS>), agrid, ablk, 0, s, aa);
+            else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1, CA, NS>), agrid, ablk, 0, s, aa);
+            else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2, CA, NS>), agrid, ablk, 0, s, aa);
         };
         if (pa.causal) attn(std::true_type{});
         else attn(std::false_type{});
