@@ -19,15 +19,22 @@ constexpr int kSkinnyWavesPerWG = 4;     // skinny (M <= 16) GEMM: 256-thread wo
 constexpr int kSkinnyNT = 2;             // 16-column blocks per skinny tile (most ops)
 constexpr int kSkinnyMaxNT = 4;          // the widest skinny tile (LM head)
 constexpr int kAttnChunk = 64;           // keys per attention step
+constexpr int kMaxSplitPages = 1040;     // KV pages one attention split may touch
 constexpr int kAttnStages = 2;           // attention chunks resident in LDS per workgroup (fp32)
-constexpr int kAttnStagesBF16 = 2;       // the same for bf16 (4 stages on one workgroup per CU measured slower)
-constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU with two stages
-// Attention workgroups that fit a CU with NS stages of up to 32 KB each.
-constexpr int attn_wg_per_cu(int ns) { return ns <= 2 ? kAttnWGPerCU : 1; }
+constexpr int kAttnStagesBF16 = 2;       // the same for bf16 (its chunks are kAttnChunkBF16 keys)
+constexpr int kAttnChunkBF16 = 64;       // keys per bf16 attention chunk
+constexpr int kAttnWGPerCU = 2;          // attention workgroups per CU
+constexpr int kLDSBytesPerCU = 160 * 1024;
+// Attention workgroups that fit a CU: NS stages of CH keys (K rows and V^T rows
+// of row_bytes each) plus the staged page ids, at most kAttnWGPerCU.
+constexpr int attn_wg_per_cu(int ns, int ch, int row_bytes) {
+    return (ns * ch * row_bytes * 2 + kMaxSplitPages * 4 + 64) * kAttnWGPerCU <= kLDSBytesPerCU ? kAttnWGPerCU : 1;
+}
 template <typename T>
 constexpr int attn_stages() { return sizeof(T) == 2 ? kAttnStagesBF16 : kAttnStages; }
+template <typename T>
+constexpr int attn_chunk() { return sizeof(T) == 2 ? kAttnChunkBF16 : kAttnChunk; }
 constexpr int kMaxSplits = 256;          // context splits of the split-KV attention
-constexpr int kMaxSplitPages = 1040;     // KV pages one attention split may touch
 constexpr int kBigBM = 64, kBigBN = 64;  // large-M GEMM tile
 constexpr int kTopKMax = 16;             // candidates per draft position of a tree (the largest useful K)
 constexpr int kTopKSegs = 64;            // vocabulary segments of the top-K partial pass (one merge lane each)

@@ -1432,23 +1432,26 @@ struct HeadAcc {
     f32x4_t o[D / 16];
 };
 
-// Softmax update for 64 keys whose S^T blocks are s[0..3] (keys kb*16 + 4grp + ii)
-// and P.V with V fragments from vfrag(t, db) (keys 32t + {4grp..4grp+3, 16+4grp..}).
+// Softmax update for 16 NKB keys whose S^T blocks are s[0..NKB-1] (keys kb*16 +
+// 4grp + ii) and P.V with V fragments from vfrag(t, db) (keys 32t + {4grp..4grp+3,
+// 16+4grp..}, t < NKB/2).
 // Keys >= nvalid (this lane's query row) are masked; a row with no visible key
 // yet keeps m = -inf, l = 0, o = 0.  For bf16 the probabilities enter as a
 // hi + lo pair of bf16 values (two MFMAs sharing the V operand), so P keeps
 // ~16 bits.
-template <typename T, int D, class VF>
-__device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], int nvalid, uint64_t vmask,
+template <typename T, int D, int NKB, class VF>
+__device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t (&s)[NKB], int nvalid, uint64_t vmask,
                                            float scale_log2, int grp, VF&& vfrag) {
+    constexpr int NK = 16 * NKB;  // keys of the step
+    constexpr uint64_t kAll = NK == 64 ? ~0ull : ((1ull << NK) - 1ull);
     // raw scores, masked (key kk of the chunk takes part iff kk < nvalid and
     // bit kk of vmask is set); the running max is kept in scaled log2 units
     // (the scale is positive, so the max commutes with it)
-    float sr[4][4];
+    float sr[NKB][4];
     float mr = -INFINITY;
-    if (__all(nvalid >= 64 && vmask == ~0ull)) {
+    if (__all(nvalid >= NK && (vmask & kAll) == kAll)) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 sr[kb][ii] = s[kb][ii];
@@ -1456,7 +1459,7 @@ __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], in
             }
     } else {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int kk = kb * 16 + 4 * grp + ii;
@@ -1468,10 +1471,10 @@ __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], in
     const float mx = fmaxf(h.m, mr * scale_log2);
     const float mref = mx == -INFINITY ? 0.f : mx;  // all keys masked so far: exp2(-inf) = 0
     const float alpha = __builtin_amdgcn_exp2f(h.m - mref);
-    float p[4][4];
+    float p[NKB][4];
     float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const float e = __builtin_amdgcn_exp2f(fmaf(sr[kb][ii], scale_log2, -mref));
@@ -1485,7 +1488,7 @@ __device__ __forceinline__ void softmax_pv(HeadAcc<D>& h, const f32x4_t s[4], in
     for (int db = 0; db < D / 16; ++db) h.o[db] *= alpha;
     constexpr bool kSplitP = sizeof(T) == 2;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NKB / 2; ++t) {
         float pv[8], pl[8];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) { pv[ii] = p[2 * t][ii]; pv[4 + ii] = p[2 * t + 1][ii]; }
@@ -1549,7 +1552,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // bank groups: rows of >= 256 bytes key on row % ncol, 128-byte rows (two per
 // 256 bytes) on the row bits above that.
 __host__ __device__ __forceinline__ int lds_key(int row, int ncol) {
-    return ncol >= 16 ? row % ncol : (row >> 1) % ncol;
+    return ncol >= 16 ? row % ncol : (row / (16 / ncol)) % ncol;
 }
 
 // Fragment read from an LDS tile of rows of `ncol` 16-byte columns whose
@@ -1600,9 +1603,10 @@ __device__ __forceinline__ void use_regs(const Frag<float>& f) {
 // bank-conflict free; each wave then computes its query head(s) (HPW per wave)
 // from LDS.  Scores are formed transposed, S^T = K Q^T, so the probabilities
 // land in the B-operand layout of O^T += V^T P^T and never leave registers.
-template <typename T, int D, int HPW, bool CAUSAL, int NS_>
-__global__ __launch_bounds__(256, attn_wg_per_cu(NS_)) void attn_split_kernel(AttnArgs a) {
-    constexpr int CH = kAttnChunk;                  // keys per chunk (64)
+template <typename T, int D, int HPW, bool CAUSAL, int NS_, int CH_>
+__global__ __launch_bounds__(256, attn_wg_per_cu(NS_, CH_, D * (int)sizeof(T))) void attn_split_kernel(AttnArgs a) {
+    constexpr int CH = CH_;                         // keys per chunk (64 or 32)
+    constexpr int NKB = CH / 16;                    // 16-key blocks per chunk
     constexpr int KCOL = D * (int)sizeof(T) / 16;   // 16-byte columns of a K row
     constexpr int VCOL = CH * (int)sizeof(T) / 16;  // 16-byte columns of a V^T row
     constexpr int NI = (CH * KCOL + D * VCOL) / 64 / 4;  // direct loads per wave per chunk
@@ -1756,21 +1760,21 @@ __global__ __launch_bounds__(256, attn_wg_per_cu(NS_)) void attn_split_kernel(At
 #pragma unroll
             for (int hh = 0; hh < HPW; ++hh) {
                 if (w + 4 * hh >= a.group) break;
-                f32x4_t sc[4];
+                f32x4_t sc[NKB];
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) sc[kb] = zero4();
-                // per 32-dim slice: the four 16-key K fragments, then four
+                for (int kb = 0; kb < NKB; ++kb) sc[kb] = zero4();
+                // per 32-dim slice: the NKB 16-key K fragments, then NKB
                 // independent MFMAs (one accumulator per 16 keys)
 #pragma unroll
                 for (int kc = 0; kc < D / 32; ++kc) {
-                    Frag<T> kf[4];
+                    Frag<T> kf[NKB];
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
+                    for (int kb = 0; kb < NKB; ++kb)
                         kf[kb] = lds_frag<T>(kl, kb * 16 + col, KCOL, (kc * 32 + grp * 8) * (int)sizeof(T) / 16);
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) mma(sc[kb], kf[kb], qf[hh][kc]);
+                    for (int kb = 0; kb < NKB; ++kb) mma(sc[kb], kf[kb], qf[hh][kc]);
                 }
-                softmax_pv<T, D>(acc[hh], sc, nvalid, vmask, a.scale_log2, grp, [&](int t, int db) {
+                softmax_pv<T, D, NKB>(acc[hh], sc, nvalid, vmask, a.scale_log2, grp, [&](int t, int db) {
                     Frag<T> vf = lds_frag<T>(vl, 16 * db + col, VCOL, (32 * t + 8 * grp) * (int)sizeof(T) / 16);
                     if (nvalid < CH) mask_vfrag(vf, t, grp, nvalid);  // never-written positions of the last chunk
                     return vf;
@@ -1798,7 +1802,7 @@ __global__ __launch_bounds__(256, attn_wg_per_cu(NS_)) void attn_split_kernel(At
                     mma(sc[kb], kf, qf[hh][kc]);
                 }
             }
-            softmax_pv<T, D>(acc[hh], sc, a.B, ~0ull, a.scale_log2, grp, [&](int t, int db) {
+            softmax_pv<T, D, 4>(acc[hh], sc, a.B, ~0ull, a.scale_log2, grp, [&](int t, int db) {
                 VRun<T> ra, rb;
                 const T* vr = vb_ + (long long)(16 * db + col) * 16;
                 if (t == 0) ra.load(vr + 4 * grp); else ra.load_masked(vr, 0);
@@ -2628,8 +2632,7 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
     } else {
         // a device-resident length is planned for the capacity (the splits
         // past the current length stay empty)
-        attn_split_plan(pa.len_dev ? d.max_ctx : C, nkv, c.num_cus, d.page, &kps, &ns,
-                        attn_wg_per_cu(attn_stages<T>()));
+        attn_split_plan(pa.len_dev ? d.max_ctx : C, nkv, c.num_cus, d.page, &kps, &ns);
         nparts = ns + 1;  // + the block's own keys
     }
     const int group = nq / nkv;
@@ -2711,11 +2714,11 @@ static hipError_t pass_t(const DevCtx& c, const PassArgs& pa, hipStream_t s) {
         const dim3 agrid(nparts, nkv, (B + 15) / 16), ablk(256);
         auto attn = [&](auto causal) {
             constexpr bool CA = decltype(causal)::value;
-            constexpr int NS = attn_stages<T>();
-            if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1, CA, NS>), agrid, ablk, 0, s, aa);
-            else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2, CA, NS>), agrid, ablk, 0, s, aa);
-            else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1, CA, NS>), agrid, ablk, 0, s, aa);
-            else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2, CA, NS>), agrid, ablk, 0, s, aa);
+            constexpr int NS = attn_stages<T>(), CHK = attn_chunk<T>();
+            if (D == 128 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 128, 1, CA, NS, CHK>), agrid, ablk, 0, s, aa);
+            else if (D == 128) hipLaunchKernelGGL((attn_split_kernel<T, 128, 2, CA, NS, CHK>), agrid, ablk, 0, s, aa);
+            else if (D == 64 && group <= 4) hipLaunchKernelGGL((attn_split_kernel<T, 64, 1, CA, NS, CHK>), agrid, ablk, 0, s, aa);
+            else if (D == 64) hipLaunchKernelGGL((attn_split_kernel<T, 64, 2, CA, NS, CHK>), agrid, ablk, 0, s, aa);
         };
         if (pa.causal) attn(std::true_type{});
         else attn(std::false_type{});
