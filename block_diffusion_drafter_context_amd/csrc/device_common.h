@@ -188,15 +188,22 @@ __device__ __forceinline__ void mfma_settle() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ float cross4_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+// The pair (lane l, lane l ^ 16) and (lane l, lane l ^ 32) exchanges as VALU
+// row swaps (gfx950 v_permlane16_swap / v_permlane32_swap) instead of LDS
+// crossbar shuffles: swapping a register with itself leaves, in every lane, the
+// lower-row value in the first result and the upper-row value in the second,
+// so both lanes of a pair form the same sum (lower + upper) or max.
+__device__ __forceinline__ float xor16_pair(float v, bool max_op) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return max_op ? fmaxf(a, b) : a + b;
 }
-__device__ __forceinline__ float cross4_sum(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+__device__ __forceinline__ float xor32_pair(float v, bool max_op) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return max_op ? fmaxf(a, b) : a + b;
 }
+__device__ __forceinline__ float cross4_max(float v) { return xor32_pair(xor16_pair(v, true), true); }
+__device__ __forceinline__ float cross4_sum(float v) { return xor32_pair(xor16_pair(v, false), false); }
 
 }  // namespace dflash
