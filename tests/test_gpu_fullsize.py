@@ -132,14 +132,16 @@ def test_prefill_fuse_inject_32k_sampled(dl, orc):
 
 
 @pytest.mark.timeout(1500)
-@pytest.mark.parametrize("mode", ["chain", "tree"])
+@pytest.mark.parametrize("mode", ["chain", "tree", "tree23"])
 def test_qwen3_8b_target_verify_4k(dl, orc, mode):
     """The verify side of a step at the Qwen3-8B target shape ([A] §1.2
     parallel verification, §8.2 tree verification; [B] 技术内幕): a forward of
     16 rows through 36 target layers (hidden 4096, 32/8 heads x 128, FFN
     12288, vocab 151936) over a 4096-token paged target KV cache of seeded
-    values -- a causal block ('chain') or a 16-node tree built best-first from
-    seeded top-4 candidates ('tree').  At the stated bar, layer by layer: each
+    values -- a causal block ('chain'), a 16-node tree built best-first from
+    seeded top-4 candidates ('tree'), or a 23-node tree (budget 22, one pass
+    of 23 rows through the kernels' two-row-tile form: 'tree23').  At the
+    stated bar, layer by layer: each
     layer against the oracle's layer on the GPU's own input to it (2 bf16
     ulps), the tree rows' K/V likewise, the logits against the oracle's LM head
     on the GPU's final residual (2e-2) with tokens exact except top-2 gaps
@@ -149,14 +151,14 @@ def test_qwen3_8b_target_verify_4k(dl, orc, mode):
     from oracle import ddtree
     from tests.gpu_helpers import check_target_layers
     s = di.SHAPES["qwen3_8b_4k"].replace(name="qwen3_8b_target", draft_layers=36)
-    C, M, L = 4096, 16, 36
+    C, M, L = 4096, 23 if mode == "tree23" else 16, 36
     w = di.toy_target_weights(s)
     ctx = dl.DFlash(s, dev(w), max_ctx=C + 64, page_seed=23)
     k, v = di.context_kv(s, C, tag="target_kv")
     ctx.load_kv(k.cuda(), v.cuda())
     toks = di.uniform_int(M, 0, s.vocab, s.seed, "verify_rows").numpy()
     par = None
-    if mode == "tree":
+    if mode != "chain":
         x = di.normal((15, s.vocab), s.seed, "verify_tree", 3.0, torch.float32).numpy()
         ids, lp = ddtree.topk_logprobs(x, 4)
         t = ddtree.build_tree(int(toks[0]), ids, lp.astype(np.float32), M - 1)
