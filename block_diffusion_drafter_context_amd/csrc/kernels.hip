@@ -11,6 +11,8 @@
 //    bf16 pass: QKV+RoPE, O+residual, gate/up+SwiGLU, down+residual and the LM
 //    head+argmax.  Each workgroup owns whole output tiles and its 4 waves split
 //    a tile's K range; the partial sums meet in LDS (no device-scope exchange).
+//    skinny_wg_rows_kernel is its form for two 16-row tiles (a verified tree of
+//    17..32 nodes in one pass).
 //  * skinny_kernel<T, Op>  -- the stream-K form of the same GEMM: the per-step
 //    fusion/injection of 16 verified rows, fp32 passes, and projections whose
 //    tiles would fill the CUs unevenly on the kernel above.  Work is split "stream-K" style: the
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(Op op, SkinnyCommon c) {
 // The split depends on N and K alone (batch invariant), and the order of the
 // sums is fixed (deterministic).
 struct WGCommon {
-    int M;          // valid rows (<= 16)
+    int M;          // valid rows (<= 16; <= 32 on the row-tile kernel)
     int K;          // reduction length (multiple of 8)
     int nchunks;    // ceil(K / 32)
     int ntiles;
@@ -1379,8 +1381,8 @@ static hipError_t run_layer_gemm(const DevCtx& c, const Op& op, int M, int K, in
 
 struct AttnArgs {
     const void* q;      // [B][nq*d] (B <= 32; blockIdx.z picks rows 16 z .. 16 z + 15)
-    const void* kblk;   // [16][nkv*d]
-    const void* vblkT;  // [nkv][d][16]
+    const void* kblk;   // [16][nkv*d] (draft passes only)
+    const void* vblkT;  // [nkv][d][16] (draft passes only)
     KVPages kv;
     int layer, C, B, nq, nkv, group, kps, n_splits;
     int causal_base;    // >= 0: causal, query row j sees keys 0..causal_base+j; -1: no mask
