@@ -1584,11 +1584,18 @@ __device__ __forceinline__ Frag<T> lds_frag(const char* base, int row, int ncol,
 // Loads unknown to the compiler only make its own waits on other loads
 // stricter (completion is in order).  No register receives data, so nothing
 // is left pending on a register.
+// M0 is a register the compiler reserves, so it warns that the clobber may be
+// ignored: it would not save a value of its own in M0 around the statement.
+// Only kernels in which the compiler itself never touches M0 may call this;
+// tests/test_isa_guards.py checks that on the built device code.
 typedef __attribute__((address_space(3))) char lds_char_t;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void* src, char* lds_dst) {
     const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long)((lds_char_t*)lds_dst));
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(src) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // An empty instruction that reads a fragment's registers: the compiler
 // must have the loads that wrote them finished before it.
