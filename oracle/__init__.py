@@ -20,18 +20,21 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dflash_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# DFLASH_ORACLE_LIB points the loader at another build of the same source
+# (the mutation test of the pins builds deliberately altered copies apart)
+_LIB = os.environ.get("DFLASH_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 MAX_LAYERS = 64
 
 
-def build(force: bool = True) -> str:
+def build(force: bool = True, src: str = _SRC, out: Optional[str] = None) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
-    if force or not os.path.exists(_LIB):
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
-               "-o", _LIB + ".tmp", _SRC, "-lm"]
+    out = out or _LIB
+    if force or not os.path.exists(out):
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-I", _HERE,
+               "-o", out + ".tmp", src, "-lm"]
         subprocess.check_call(cmd)
-        os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+        os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None
