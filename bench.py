@@ -173,12 +173,13 @@ def main():
         draft -> synthetic target -> accept -> fuse the 16 verified rows ->
         inject them at the length -> keep the anchor and the k accepted rows ->
         back to C0 (every step sees the same context) -> the bonus token is the
-        next anchor.  No host read anywhere, so steps are enqueued back to back
-        and the step can be captured in a HIP graph (static buffers)."""
-        anchor = torch.tensor([di.anchor_token(s)], dtype=torch.int32, device="cuda")
+        next anchor, read in place from the accept result {k, bonus}.  No host
+        read anywhere, so steps are enqueued back to back and the step can be
+        captured in a HIP graph (static buffers)."""
         tok = torch.empty(B, dtype=torch.int32, device="cuda")
         g = torch.empty(B, dtype=torch.int32, device="cuda")
-        res = torch.empty(2, dtype=torch.int32, device="cuda")
+        res = torch.tensor([0, di.anchor_token(s)], dtype=torch.int32, device="cuda")
+        anchor = res[1:2]  # the first step's anchor, then each step's bonus token
         fused = torch.empty(16, s.hidden, dtype=s.torch_dtype, device="cuda")
 
         def step():
@@ -189,7 +190,6 @@ def main():
             ctx.inject_kv(fused, -1)
             ctx.keep_accepted(res)
             ctx.set_length_async(C0)
-            anchor.copy_(res[1:2])
 
         step.res = res
         return step
