@@ -154,19 +154,18 @@ def main():
     step_hidden = [di.target_hidden(s, l, 16, tag="step").cuda() if l in sel else None
                    for l in range(s.target_layers)]
     u, r, last = di.target_coins(s)
-    # the synthetic target argmax of a block, as three device ops per step:
-    # g[j] = (d[j+1] + r'[j]) mod V with r'[j] = 0 where the target agrees
-    # (u[j+1] < p) and r[j+1] otherwise, and g[B-1] = last
+    # the synthetic target argmax of a block, as two device ops per step:
+    # g[j] = (d[j+1] + r'[j]) mod V for j < B-1, with r'[j] = 0 where the
+    # target agrees (u[j+1] < p) and r[j+1] otherwise; g[B-1] = last is set
+    # once when the buffer is made
     B = s.block
-    sel_idx = torch.tensor(list(range(1, B)) + [0], dtype=torch.int64, device="cuda")
-    keep = torch.tensor([1] * (B - 1) + [0], dtype=torch.int32, device="cuda")
-    add = torch.tensor([0 if float(u[j]) < di.SYNTH_AGREE_P else int(r[j]) for j in range(1, B)] + [last],
+    add = torch.tensor([0 if float(u[j]) < di.SYNTH_AGREE_P else int(r[j]) for j in range(1, B)],
                        dtype=torch.int32, device="cuda")
 
     def synthetic_target(tokens, g_buf):
-        torch.index_select(tokens, 0, sel_idx, out=g_buf)
-        g_buf.mul_(keep).add_(add)
-        return g_buf.remainder_(s.vocab)
+        torch.add(tokens[1:B], add, out=g_buf[:B - 1])
+        g_buf[:B - 1].remainder_(s.vocab)
+        return g_buf
 
     def make_step(ctx, C0):
         """One device-resident step on ctx (its length lives on the device):
@@ -177,7 +176,7 @@ def main():
         read anywhere, so steps are enqueued back to back and the step can be
         captured in a HIP graph (static buffers)."""
         tok = torch.empty(B, dtype=torch.int32, device="cuda")
-        g = torch.empty(B, dtype=torch.int32, device="cuda")
+        g = torch.full((B,), last, dtype=torch.int32, device="cuda")
         res = torch.tensor([0, di.anchor_token(s)], dtype=torch.int32, device="cuda")
         anchor = res[1:2]  # the first step's anchor, then each step's bonus token
         fused = torch.empty(16, s.hidden, dtype=s.torch_dtype, device="cuda")
